@@ -1,0 +1,43 @@
+"""CPU oracle of the connector-agnostic KV-cache block checksum.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The HIP library and
+its Python binding never import it, and it imports nothing from them: the two
+share no code, headers, tables or helpers.
+
+What it computes is defined on the vLLM API page
+"vllm.distributed.kv_transfer.kv_checksum.checksum" (module docstring):
+
+* slice checksum  s = sum_j x_j * (2j + 1)  mod 2^64       (docstring item 1)
+* block checksum  c = sum_{layer, head} m * s  mod 2^64,
+  m = 2 * (layer * H + head) + 1,  H = MAX_KV_HEADS_PER_LAYER   (item 2)
+* Mamba running-state rows, one slice per global row       (Mamba paragraph)
+
+Two independent implementations live here:
+
+``kv_checksum``  numpy, vectorised per (position, cache); the oracle proper.
+``brute``        pure-Python integers, one piece at a time; for tiny inputs,
+                 used to pin the numpy oracle.
+
+Pins (tests/test_oracle_*.py): brute force on tiny inputs, closed forms
+(single nonzero piece, all-ones pieces, zero cache, single-byte probes of the
+byte -> piece mapping), and the invariants the page states (additivity over
+block sizes, layout independence, TP/PP partial sums, single-piece detection,
+exclusion of slots at or past ``num_tokens``).
+
+Parity unpinned: the Mamba slice contents (which rows of which states form a
+slice, and in which order) follow this package's reading of the Mamba
+paragraph; no value printed on the pages fixes it, so only closed forms and
+brute force of the same reading pin it.
+"""
+
+from .kv_checksum import (  # noqa: F401
+    BLOCK_CHECKSUM_BYTES,
+    MAX_KV_HEADS_PER_LAYER,
+    LAYOUTS,
+    num_valid_tokens,
+    slice_factor,
+    checksum_blocks,
+    checksum_states,
+)
+from . import brute  # noqa: F401

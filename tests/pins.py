@@ -1,0 +1,385 @@
+"""Pins of the checksum oracle: checks against facts the pages and mathematics fix.
+
+Every check takes the oracle module ``o`` (``oracle.kv_checksum`` or a mutated
+copy of it) so that the same checks also prove they catch planted mistakes
+(tests/test_oracle_mutants.py).  Formulas are from the vLLM API page
+"vllm.distributed.kv_transfer.kv_checksum.checksum", module docstring:
+item 1 (slice checksum), item 2 (block checksum and factor m), the paragraph on
+detection and additivity, the paragraph on TP/PP partials and layouts, and the
+Mamba paragraph.
+
+Each check states its expected value independently of the oracle's code: by
+counting, by a closed form, by an invariant, or through the pure-Python brute
+force ``oracle.brute``.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import brute
+from paged_kv_cache_kvck_amd import workloads as wl
+
+H = 1 << 16
+M64 = (1 << 64) - 1
+
+
+# ------------------------------------------------------------------ helpers
+
+def row_u8(pool, layout, plane, b, i, h):
+    """Writable uint8 view of the (plane, block, slot, head) row of a pool."""
+    p8 = pool.view(np.uint8)
+    if layout == "NHD":
+        return p8[plane, b, i, h]
+    if layout == "HND":
+        return p8[plane, b, h, i]
+    assert plane == 0 and h == 0
+    return p8[b, i]
+
+
+def factor(layer, head):
+    return (2 * (layer * H + head) + 1) & M64
+
+
+def make_case(rng, layout="NHD", elem="bf16", layers=(0, 1), nh=2, d=64, bs=4, lengths=(9, 3, 12),
+              start=None, extra=None, head_begin=0, head_count=None, bases=None, pool_blocks=None,
+              zero=False):
+    req, nb = wl.page_requests(rng, list(lengths), bs, pool_blocks=pool_blocks, start_pos=start,
+                               extra_blocks=extra, spare_frac=0.5)
+    shape = wl.pool_shape(layout, nb, bs, 1 if layout == "MLA" else nh, d)
+    pools = [np.zeros(shape, wl.HOST_BITS[elem]) if zero else wl.host_random_bits(rng, shape, elem)
+             for _ in layers]
+    n = (1 if layout == "MLA" else nh) - head_begin if head_count is None else head_count
+    bases = [head_begin] * len(layers) if bases is None else list(bases)
+    return dict(caches=pools, layout=layout, layer_numbers=list(layers), global_head_base=bases,
+                block_table=req.block_table, num_blocks=req.num_blocks, start_pos=req.start_pos,
+                num_tokens=req.num_tokens, head_begin=head_begin, head_count=n), req
+
+
+def run_blocks(o, case):
+    return o.checksum_blocks(**case)
+
+
+def listed(case):
+    return [(r, k) for r in range(len(case["num_blocks"])) for k in range(int(case["num_blocks"][r]))]
+
+
+# ------------------------------------------------------------------ pins
+
+def pin_num_valid_tokens(o):
+    """Tokens of a block position among the first num_tokens, counted."""
+    for bs in (1, 3, 16):
+        for pos in range(7):
+            for n in range(0, 7 * bs + 5):
+                want = sum(1 for t in range(pos * bs, (pos + 1) * bs) if t < n)
+                assert o.num_valid_tokens(pos, bs, n) == want, (pos, bs, n)
+
+
+def pin_brute(o, seed=11, cases=None):
+    """numpy oracle == pure-Python brute force on tiny random inputs."""
+    rng = np.random.default_rng(seed)
+    specs = cases or [
+        dict(layout="NHD", elem="bf16"),
+        dict(layout="HND", elem="fp16", layers=(3, 7), nh=3, d=8, bs=5, lengths=(11, 1, 5)),
+        dict(layout="NHD", elem="fp8", layers=(0,), nh=2, d=16, bs=3, lengths=(7,), start=(1,), extra=(2,)),
+        dict(layout="MLA", elem="bf16", layers=(0, 1, 2), d=12, bs=4, lengths=(6, 9)),
+        dict(layout="HND", elem="bf16", layers=(5,), nh=4, d=8, bs=4, lengths=(10, 4),
+             head_begin=1, head_count=2, bases=(9,)),
+        dict(layout="NHD", elem="fp32", layers=(1, 0), nh=2, d=4, bs=2, lengths=(5, 0, 2), extra=(0, 1, 1)),
+    ]
+    for spec in specs:
+        case, _ = make_case(rng, **spec)
+        got = run_blocks(o, case)
+        want = brute.blocks(**case)
+        for (r, k), c in want.items():
+            assert int(got[r, k]) == c, (spec, r, k)
+
+
+def pin_zero(o):
+    rng = np.random.default_rng(1)
+    case, _ = make_case(rng, zero=True)
+    assert not np.any(run_blocks(o, case))
+
+
+def pin_single_piece(o, seed=5, trials=40):
+    """One nonzero piece x at (layer L, global head g, token t, piece q):
+    c = x * m(L, g) * (2(tP + q) + 1) mod 2^64 at its position, 0 elsewhere."""
+    rng = np.random.default_rng(seed)
+    for trial in range(trials):
+        layout = ("NHD", "HND", "MLA")[trial % 3]
+        nh = 1 if layout == "MLA" else 3
+        d, bs = 8, 4
+        layers = (int(rng.integers(0, 40)), int(rng.integers(40, 90)))
+        base = int(rng.integers(0, 5)) if layout != "MLA" else 0
+        case, req = make_case(rng, layout=layout, layers=layers, nh=nh, d=d, bs=bs, lengths=(13, 7),
+                              start=(1, 0), zero=True, bases=(base, base))
+        planes = 1 if layout == "MLA" else 2
+        row_bytes = d * 2
+        P = planes * row_bytes // 8
+        r = int(rng.integers(0, 2))
+        k = int(rng.integers(0, int(req.num_blocks[r])))
+        pos = int(req.start_pos[r]) + k
+        v = min(bs, int(req.num_tokens[r]) - pos * bs)
+        i = int(rng.integers(0, v))
+        h = int(rng.integers(0, nh))
+        li = int(rng.integers(0, 2))
+        q = int(rng.integers(0, P))
+        x = int(rng.integers(1, 1 << 63)) * 2 + int(rng.integers(0, 2))
+        plane, within = divmod(q, P // planes)
+        b = int(req.block_table[r, k])
+        row_u8(case["caches"][li], layout, plane, b, i, h)[8 * within:8 * within + 8] = \
+            np.frombuffer(x.to_bytes(8, "little"), np.uint8)
+        t = pos * bs + i
+        want = x * factor(layers[li], base + h) * (2 * (t * P + q) + 1) & M64
+        got = run_blocks(o, case)
+        for (rr, kk) in listed(case):
+            assert int(got[rr, kk]) == (want if (rr, kk) == (r, k) else 0), (trial, rr, kk)
+
+
+def pin_all_ones(o):
+    """Every piece = 1: s = sum_{j=t0 P}^{t1 P - 1} (2j+1) = P^2 (t1^2 - t0^2), so
+    c = P^2 (t1^2 - t0^2) * sum of m over the layers and global heads."""
+    rng = np.random.default_rng(2)
+    for layout, nh, d, bs, layers, base, hb, hc in [
+            ("NHD", 2, 64, 16, (0, 1), 0, 0, None),        # the tiny config's shape
+            ("HND", 4, 16, 8, (3, 11, 12), 6, 1, 2),
+            ("MLA", 1, 24, 4, (0, 60), 0, 0, None)]:
+        case, req = make_case(rng, layout=layout, layers=layers, nh=nh, d=d, bs=bs, lengths=(50, 21),
+                              start=(0, 1), zero=True, head_begin=hb, head_count=hc, bases=(base,) * len(layers))
+        for pool in case["caches"]:
+            pool.view("<u8")[...] = 1
+        planes = 1 if layout == "MLA" else 2
+        P = planes * d * 2 // 8
+        n = case["head_count"]
+        sum_m = sum(factor(L, base + g) for L in layers for g in range(n))
+        got = run_blocks(o, case)
+        for r, k in listed(case):
+            pos = int(req.start_pos[r]) + k
+            t0 = pos * bs
+            t1 = min(int(req.num_tokens[r]), t0 + bs)
+            t1 = max(t1, t0)
+            want = P * P * (t1 * t1 - t0 * t0) * sum_m & M64
+            assert int(got[r, k]) == want, (layout, r, k)
+    # the tiny config: 2 layers x 2 heads, head 64 bf16: sum of m = 262152
+    assert sum(factor(L, g) for L in (0, 1) for g in (0, 1)) == 262152
+
+
+def pin_byte_probe(o):
+    """Byte->piece mapping: a single byte B at byte beta of token t's K (plane 0)
+    or V (plane 1) row is piece q = plane * P/2 + beta // 8 with value
+    B << 8 (beta mod 8) (little-endian pieces, K then V)."""
+    rng = np.random.default_rng(3)
+    for layout in ("NHD", "HND", "MLA"):
+        nh = 1 if layout == "MLA" else 2
+        d, bs = 16, 4
+        for trial in range(12):
+            case, req = make_case(rng, layout=layout, layers=(2,), nh=nh, d=d, bs=bs, lengths=(15,),
+                                  start=(1,), zero=True)
+            planes = 1 if layout == "MLA" else 2
+            P = planes * d * 2 // 8
+            k = int(rng.integers(0, int(req.num_blocks[0])))
+            pos = 1 + k
+            v = min(bs, 15 - pos * bs)
+            i = int(rng.integers(0, v))
+            h = int(rng.integers(0, nh))
+            plane = int(rng.integers(0, planes))
+            beta = int(rng.integers(0, d * 2))
+            byte = int(rng.integers(1, 256))
+            b = int(req.block_table[0, k])
+            row_u8(case["caches"][0], layout, plane, b, i, h)[beta] = byte
+            q = plane * (P // planes) + beta // 8
+            x = byte << (8 * (beta % 8))
+            t = pos * bs + i
+            want = x * factor(2, h) * (2 * (t * P + q) + 1) & M64
+            assert int(run_blocks(o, case)[0, k]) == want, (layout, trial)
+
+
+def pin_linearity(o):
+    """c(X (+) Y) = c(X) + c(Y) mod 2^64, (+) = piecewise uint64 addition."""
+    rng = np.random.default_rng(4)
+    for layout in ("NHD", "HND"):
+        cx, _ = make_case(rng, layout=layout)
+        cy = dict(cx)
+        cy["caches"] = [wl.host_random_bits(rng, p.shape, "bf16") for p in cx["caches"]]
+        cz = dict(cx)
+        with np.errstate(over="ignore"):
+            cz["caches"] = [(a.view("<u8") + b.view("<u8")).view(a.dtype) for a, b in zip(cx["caches"], cy["caches"])]
+            want = run_blocks(o, cx) + run_blocks(o, cy)
+        assert np.array_equal(run_blocks(o, cz), want)
+
+
+# ------------------------------------------------------------------ invariants on the page
+
+def pin_additivity_block_size(o):
+    """Checksums of consecutive blocks add up to that of the tokens they hold,
+    so block sizes 16 and 64 agree on each request's sum."""
+    rng = np.random.default_rng(6)
+    lengths = [130, 64, 17, 200]
+    c16, r16 = make_case(rng, layout="NHD", layers=(0, 3), nh=2, d=8, bs=16, lengths=lengths)
+    c64, r64 = make_case(rng, layout="NHD", layers=(0, 3), nh=2, d=8, bs=64, lengths=lengths, zero=True)
+    for src, dst in zip(c16["caches"], c64["caches"]):
+        wl.repage_numpy(src, "NHD", r16, dst, "NHD", r64)
+    a = run_blocks(o, c16)
+    b = run_blocks(o, c64)
+    with np.errstate(over="ignore"):
+        assert np.array_equal(a.sum(axis=1, dtype=np.uint64), b.sum(axis=1, dtype=np.uint64))
+
+
+def pin_layout_independence(o):
+    """NHD and HND pools holding the same tokens give the same checksums."""
+    rng = np.random.default_rng(7)
+    cn, rq = make_case(rng, layout="NHD", layers=(1, 4), nh=3, d=8, bs=4, lengths=(9, 14))
+    ch = dict(cn)
+    ch["layout"] = "HND"
+    ch["caches"] = [np.ascontiguousarray(p.transpose(0, 1, 3, 2, 4)) for p in cn["caches"]]
+    assert np.array_equal(run_blocks(o, cn), run_blocks(o, ch))
+
+
+def pin_tp_pp_partials(o):
+    """Head shards weighted by global head, and layer subsets, sum to c."""
+    rng = np.random.default_rng(8)
+    full, _ = make_case(rng, layout="HND", layers=(0, 1, 2), nh=4, d=8, bs=4, lengths=(10, 6))
+    want = run_blocks(o, full)
+    tot = np.zeros_like(want)
+    with np.errstate(over="ignore"):
+        for hb in (0, 2):
+            part = dict(full, head_begin=hb, head_count=2, global_head_base=[hb] * 3)
+            tot = tot + run_blocks(o, part)
+        assert np.array_equal(tot, want)
+        tot = np.zeros_like(want)
+        for sel in ((0,), (1, 2)):
+            part = dict(full, caches=[full["caches"][i] for i in sel],
+                        layer_numbers=[full["layer_numbers"][i] for i in sel],
+                        global_head_base=[0] * len(sel))
+            tot = tot + run_blocks(o, part)
+        assert np.array_equal(tot, want)
+    # a shard pool that holds only heads 2..3 (as a TP rank would) with global base 2
+    shard = dict(full, caches=[np.ascontiguousarray(p[:, :, 2:4]) for p in full["caches"]],
+                 head_begin=0, head_count=2, global_head_base=[2] * 3)
+    mine = dict(full, head_begin=2, head_count=2, global_head_base=[2] * 3)
+    assert np.array_equal(run_blocks(o, shard), run_blocks(o, mine))
+
+
+def pin_exclusion(o):
+    """Slots at or past num_tokens, unlisted blocks, and positions past the
+    request's tokens do not enter the checksum."""
+    rng = np.random.default_rng(9)
+    case, req = make_case(rng, layout="NHD", layers=(0, 1), nh=2, d=8, bs=4, lengths=(10, 3), extra=(1, 2))
+    want = run_blocks(o, case)
+    listed_ids = {int(req.block_table[r, k]) for r, k in listed(case)}
+    junk = dict(case)
+    junk["caches"] = [p.copy() for p in case["caches"]]
+    for p in junk["caches"]:
+        for b in range(p.shape[1]):
+            if b not in listed_ids:
+                p[:, b] = wl.host_random_bits(rng, p[:, b].shape, "bf16")
+        for r, k in listed(case):
+            pos = int(req.start_pos[r]) + k
+            v = sum(1 for t in range(pos * 4, pos * 4 + 4) if t < int(req.num_tokens[r]))
+            b = int(req.block_table[r, k])
+            p[:, b, v:] = wl.host_random_bits(rng, p[:, b, v:].shape, "bf16")
+    assert np.array_equal(run_blocks(o, junk), want)
+    for r, k in listed(case):
+        if (int(req.start_pos[r]) + k) * 4 >= int(req.num_tokens[r]):
+            assert int(want[r, k]) == 0
+
+
+def pin_detection(o, exhaustive=False):
+    """Any single-piece change changes c (odd factors); swapped tokens, blocks,
+    heads or layers change c for random data (distinct factors)."""
+    rng = np.random.default_rng(10)
+    w = wl.tiny()
+    pools = w.host_pools()
+    base = dict(caches=pools, layout="NHD", layer_numbers=w.layer_numbers, global_head_base=[0, 0],
+                block_table=w.req.block_table, num_blocks=w.req.num_blocks, start_pos=w.req.start_pos,
+                num_tokens=w.req.num_tokens, head_begin=0, head_count=2)
+    want = run_blocks(o, base)
+    n_tok = int(w.req.num_tokens[0])
+    P = 32
+    pieces = [(li, t, h, q) for li in range(2) for t in range(n_tok) for h in range(2) for q in range(P)]
+    if not exhaustive:
+        pieces = [pieces[i] for i in rng.choice(len(pieces), 96, replace=False)]
+    for li, t, h, q in pieces:
+        k, i = divmod(t, 16)
+        b = int(w.req.block_table[0, k])
+        plane, within = divmod(q, P // 2)
+        row = row_u8(pools[li], "NHD", plane, b, i, h)
+        saved = row[8 * within:8 * within + 8].copy()
+        row[8 * within + int(rng.integers(0, 8))] ^= np.uint8(1 << int(rng.integers(0, 8)))
+        got = o.checksum_position(pools, "NHD", w.layer_numbers, [0, 0], b, k, n_tok)
+        row[8 * within:8 * within + 8] = saved
+        assert got != int(want[0, k]), (li, t, h, q)
+    # swaps
+    b0, b1 = int(w.req.block_table[0, 0]), int(w.req.block_table[0, 1])
+
+    def total(case):
+        with np.errstate(over="ignore"):
+            return int(run_blocks(o, case).sum(dtype=np.uint64))
+
+    ref = total(base)
+    sw = [p.copy() for p in pools]
+    for p in sw:
+        p[:, b0, [3, 9]] = p[:, b0, [9, 3]]            # two tokens of a block
+    assert total(dict(base, caches=sw)) != ref
+    bt = w.req.block_table.copy()
+    bt[0, [0, 1]] = bt[0, [1, 0]]                       # two blocks
+    assert total(dict(base, block_table=bt)) != ref
+    sw = [p.copy() for p in pools]
+    for p in sw:
+        p[:, :, :, [0, 1]] = p[:, :, :, [1, 0]]          # two heads
+    assert total(dict(base, caches=sw)) != ref
+    assert total(dict(base, caches=[pools[1], pools[0]])) != ref   # two layers
+    del b1
+
+
+# ------------------------------------------------------------------ Mamba rows
+
+def make_states(rng, layers=(1, 3), rows=3, slots=4, shapes=((2, 3), (5,)), elems=("fp32", "fp16"), zero=False):
+    out = []
+    for _ in layers:
+        sts = []
+        for shp, el in zip(shapes, elems):
+            full = (slots, rows) + tuple(shp)
+            sts.append(np.zeros(full, wl.HOST_BITS[el]) if zero else wl.host_random_bits(rng, full, el))
+        out.append(sts)
+    return out
+
+
+def pin_mamba(o):
+    """Brute force, a single element, all-ones rows (s = E^2), row and layer
+    shards -- for the reading: slice = row g of every state, concatenated."""
+    rng = np.random.default_rng(12)
+    st = make_states(rng)
+    slots = np.array([2, 0, 3], np.int32)
+    args = dict(layer_numbers=[1, 3], global_row_base=[0, 0], slot_ids=slots)
+    got = o.checksum_states(st, **args)
+    want = brute.states(st, **args)
+    assert [int(x) for x in got] == want
+    # single element: state 1 (fp16), row 2, element 3 of the row, layer 3
+    zs = make_states(rng, zero=True)
+    zs[1][1][2, 2, 3] = 0xBEEF
+    e = 6 + 3                                           # after the 2x3 fp32 row of state 0
+    want = 0xBEEF * factor(3, 2) * (2 * e + 1) & M64
+    got = o.checksum_states(zs, layer_numbers=[1, 3], global_row_base=[0, 0], slot_ids=np.array([2, 1], np.int32))
+    assert int(got[0]) == want and int(got[1]) == 0
+    # all ones: s = sum_{e<E} (2e+1) = E^2
+    ones = make_states(rng, zero=True)
+    for sts in ones:
+        for a in sts:
+            a[...] = 1
+    E = 6 + 5
+    got = o.checksum_states(ones, layer_numbers=[1, 3], global_row_base=[4, 4], slot_ids=np.array([0], np.int32))
+    assert int(got[0]) == sum(factor(L, 4 + g) for L in (1, 3) for g in range(3)) * E * E & M64
+    # row shards with global row numbering sum to the whole
+    full = o.checksum_states(st, **args)
+    with np.errstate(over="ignore"):
+        parts = (o.checksum_states(st, layer_numbers=[1, 3], global_row_base=[0, 0], slot_ids=slots,
+                                   row_begin=0, row_count=1)
+                 + o.checksum_states(st, layer_numbers=[1, 3], global_row_base=[1, 1], slot_ids=slots,
+                                     row_begin=1, row_count=2))
+    assert np.array_equal(parts, full)
+
+
+ALL_PINS = [pin_num_valid_tokens, pin_brute, pin_zero, pin_single_piece, pin_all_ones, pin_byte_probe,
+            pin_linearity, pin_additivity_block_size, pin_layout_independence, pin_tp_pp_partials,
+            pin_exclusion, pin_detection, pin_mamba]
