@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the KV-cache block checksum on one MI355X.
+
+One step = one kvck_checksum_blocks call over the whole batch of the
+Llama-3-8B-shaped cache (32 layers x 8 KV heads x head 128, bf16 normal(0,1)
+values, block 16, HND pool, 256 requests of 512..8192 tokens): plan, main
+pass over every valid K/V byte, second pass.  Inputs are resident in HBM
+before timing starts.
+
+    python bench.py [--steps K] [--warmup W] [--workload llama3_8b|gpt2|hybrid_attn]
+
+Prints one JSON line: throughput in checksummed KV GB/s (valid cache bytes /
+step time), the roofline of the main pass (its own HIP events on its stream,
+via the library's instrumentation), and the CPU oracle's rate on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_kvck_amd", "csrc", "*"))) + \
+            [os.path.join(ROOT, "include", "kvck.h")]:
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload: str):
+    """HBM bytes per launch of the main pass from the committed rocprofv3
+    counter summary, or None when the kernel sources changed since."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_sources_sha256") != kernel_sources_sha():
+        return None
+    return int(t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"])
+
+
+def make_workload(name):
+    from paged_kv_cache_kvck_amd import workloads as wl
+    if name == "llama3_8b":
+        return wl.llama3_8b(), ("llama3-8b-shaped paged KV cache: 32 layers x 8 KV heads x head 128 bf16 "
+                                "normal(0,1), block 16, HND, 256 requests of 512-8192 tokens")
+    if name == "gpt2":
+        return wl.gpt2(), ("gpt2-shaped paged KV cache: 12 layers x 12 KV heads x head 64 fp16 random bits, "
+                           "block 16, NHD pool (2,18545,16,12,64) per layer, 64 requests of 128-2048 tokens")
+    if name == "hybrid_attn":
+        return wl.hybrid()[0], ("hybrid model attention group: 24 layers x 8 KV heads x head 128 bf16, block 16, "
+                                "HND, 128 requests of 512-8192 tokens")
+    raise SystemExit(f"unknown workload {name}")
+
+
+def cpu_baseline(pools, w, seconds, seed=0):
+    """The oracle, as it stands, on a bounded random sample of listed positions
+    (host copies of their blocks are made outside the timed region)."""
+    import numpy as np
+    import torch
+    import oracle
+    from paged_kv_cache_kvck_amd import workloads as wl
+
+    rng = np.random.default_rng(seed)
+    allpos = w.req.listed()
+    order = rng.permutation(len(allpos))
+    done, nbytes, elapsed, i = 0, 0, 0.0, 0
+    row = w.heads_used * w.planes * w.head_size * wl.ELEM_BYTES[w.elem] * w.num_layers
+    while elapsed < seconds and i < len(order):
+        chunk = [allpos[j] for j in order[i:i + 32]]
+        i += 32
+        ids = sorted({int(w.req.block_table[r, k]) for r, k in chunk})
+        remap = {b: n for n, b in enumerate(ids)}
+        idx = torch.tensor(ids, dtype=torch.int64, device=pools[0].device)
+        mini = []
+        for p in pools:
+            sub = p.index_select(0 if w.layout == "MLA" else 1, idx).contiguous()
+            mini.append(sub.view(torch.int16).cpu().numpy().view(np.uint16))
+        t0 = time.perf_counter()
+        for r, k in chunk:
+            oracle.kv_checksum.checksum_position(mini, w.layout, w.layer_numbers, w.bases,
+                                                 remap[int(w.req.block_table[r, k])], int(w.req.start_pos[r]) + k,
+                                                 int(w.req.num_tokens[r]), w.head_begin, w.head_count)
+        elapsed += time.perf_counter() - t0
+        for r, k in chunk:
+            pos = int(w.req.start_pos[r]) + k
+            v = min(w.req.block_size, max(0, int(w.req.num_tokens[r]) - pos * w.req.block_size))
+            nbytes += v * row
+        done += len(chunk)
+    return {"value": nbytes / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} random listed positions of the same workload ({nbytes} valid bytes, all layers and "
+                      f"heads), numpy single-threaded, {elapsed:.1f} s of oracle time; host copies excluded"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-shard", action="store_true", help="skip the TP-shard timing")
+    ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
+                    help="after timing, run one plain device copy of this many GiB (counter calibration)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (the checksum path is "
+              f"single-GPU; partial sums of head or layer shards add up across GPUs)", file=sys.stderr)
+        return 1
+
+    import torch
+    import paged_kv_cache_kvck_amd as kvck
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    w, desc = make_workload(args.workload)
+    print(f"[bench] building {args.workload}: pools {w.shape} x {w.num_layers}", file=sys.stderr, flush=True)
+    pools = w.device_pools()
+    req = w.req
+    bt = torch.from_numpy(req.block_table).to(dev)
+    nb = torch.from_numpy(req.num_blocks).to(dev)
+    sp = torch.from_numpy(req.start_pos).to(dev)
+    nt = torch.from_numpy(req.num_tokens).to(dev)
+    out = torch.zeros((req.num_reqs, req.max_blocks), dtype=torch.uint64, device=dev)
+    ws = torch.empty(kvck.kvck_blocks_workspace_bytes(w.num_layers, req.num_reqs, req.max_blocks),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(head_begin=w.head_begin, head_count=w.head_count, bases=None):
+        kvck.kvck_checksum_blocks(pools, w.layout, w.layer_numbers, bt, nb, sp, nt, global_head_base=bases,
+                                  head_begin=head_begin, head_count=head_count, out=out, workspace=ws,
+                                  stream=stream)
+
+    valid = w.valid_bytes()
+    kvck.kvck_instrument(True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kvck.kvck_instrument_read()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    main_ms, calls = kvck.kvck_instrument_read()
+    main_avg = main_ms / max(calls, 1)
+    achieved = valid / (main_avg * 1e-3) / 1e9
+
+    extra = {"valid_bytes_per_step": valid, "main_pass_ms": main_avg, "listed_positions": int(req.num_blocks.sum()),
+             "metadata_bytes_per_step": int(req.num_blocks.sum()) * (4 + 8 + 32) + req.num_reqs * 20}
+    if not args.no_shard and w.layout == "HND" and w.num_heads == 8:
+        # TP = 4 shard over heads {2, 3}, global numbering from 2
+        shard_bytes = valid // 4
+        for _ in range(2):
+            step(2, 2, [2] * w.num_layers)
+        torch.cuda.synchronize()
+        kvck.kvck_instrument_read()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step(2, 2, [2] * w.num_layers)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sms = e0.elapsed_time(e1) / args.steps
+        smain, sc = kvck.kvck_instrument_read()
+        extra["tp4_shard_heads_2_3"] = {"valid_bytes": shard_bytes, "ms_per_step": sms,
+                                        "GB_per_s": shard_bytes / (sms * 1e-3) / 1e9,
+                                        "main_pass_ms": smain / max(sc, 1),
+                                        "main_pass_GB_per_s": shard_bytes / (smain / max(sc, 1) * 1e-3) / 1e9}
+    kvck.kvck_instrument(False)
+    if args.copy_calibration_gib > 0:
+        n = int(args.copy_calibration_gib * (1 << 30))
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        extra["copy_calibration_bytes"] = n
+        del a, b
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(pools, w, args.cpu_seconds)
+        cpu["host_cpu"] = _cpu_model()
+
+    line = {
+        "metric": "checksummed KV GB/s (bit-exact vs CPU oracle)",
+        "value": valid / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u64",
+        "data": "synthetic",
+        "config": {"workload": desc, "num_layers": w.num_layers, "kv_heads": w.heads_used, "head_size": w.head_size,
+                   "block_size": req.block_size, "layout": w.layout, "num_requests": req.num_reqs,
+                   "tokens": w.valid_tokens(), "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": committed_traffic(args.workload)},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip() + f" ({os.cpu_count()} logical CPUs visible)"
+    except OSError:
+        pass
+    return f"{os.cpu_count()} logical CPUs"
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,220 @@
+/*
+ * kvck.h -- C ABI of libkvck: connector-agnostic checksums of paged KV-cache
+ * blocks on AMD Instinct MI355X (gfx950).
+ *
+ * The checksum is the one defined on the vLLM API page
+ * "vllm.distributed.kv_transfer.kv_checksum.checksum" (module docstring):
+ *
+ *   item 1  A slice is the K and V of one layer and one KV head of a block,
+ *           token by token, cut into little-endian 8-byte pieces x_j with
+ *           j = t*P + p (t: token position in the request, p: piece within
+ *           the token, P pieces per token):
+ *               s = sum_j x_j * (2j + 1)                    mod 2^64
+ *   item 2  A block position's checksum weighs every slice by an odd factor:
+ *               c = sum_{layer, head} m * s                 mod 2^64
+ *               m = 2 * (layer * H + global_head) + 1,  H = 65536
+ *   Mamba   A Mamba group's block is the request's running state at position
+ *           0; each global row of its states is one slice whose pieces are
+ *           the 2- or 4-byte elements read unsigned.
+ *
+ * Conventions shared by every entry point:
+ *  - Pointers marked "device" are HIP device pointers on the current device;
+ *    pointers marked "host" are read during the call only.  The library
+ *    allocates no memory and keeps no pointer after it returns; the caller
+ *    owns every buffer.
+ *  - Calls are asynchronous and ordered on `stream`.  Results are valid once
+ *    the stream has reached the call; the cache bytes must not change until
+ *    then (checksums are taken "when their KV is final").
+ *  - A negative return value means the call launched nothing.  Errors found
+ *    only on the device (a bad block id, a bad request entry, a bad state
+ *    slot) are reported by OR-ing KVCK_FLAG_* bits into *error_flags (if not
+ *    NULL); the library never clears that word.
+ *  - All checksum arithmetic is unsigned 64-bit integer arithmetic; results
+ *    are bit-exact and independent of launch shape and scheduling.
+ *  - Thread-safe; calls that share a workspace must be stream-ordered.
+ */
+#ifndef KVCK_H_
+#define KVCK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVCK_ABI_VERSION 1
+
+/* H of the slice factor; groups with more KV heads per layer (or Mamba rows)
+ * are not checksummed (page attribute MAX_KV_HEADS_PER_LAYER = 1 << 16). */
+#define KVCK_MAX_KV_HEADS_PER_LAYER 65536
+/* Largest accepted layer number: keeps every factor m below 2^32. */
+#define KVCK_MAX_LAYER_NUMBER 32767
+/* Caches (layers) per kvck_checksum_blocks call and Mamba layers per
+ * kvck_checksum_states call. */
+#define KVCK_MAX_CACHES 4096
+/* States per Mamba layer. */
+#define KVCK_MAX_STATES_PER_LAYER 4
+
+typedef enum kvck_status {
+  KVCK_OK = 0,
+  KVCK_ERR_INVALID_ARGUMENT = -1, /* null pointer, negative size, bad stride */
+  KVCK_ERR_UNSUPPORTED = -2,      /* > H heads/rows, layer > KVCK_MAX_LAYER_NUMBER,
+                                     row bytes not a multiple of 8, element
+                                     width not 2 or 4, too many caches */
+  KVCK_ERR_MISALIGNED = -3,       /* base pointer or stride not 8-byte aligned */
+  KVCK_ERR_WORKSPACE = -4,        /* workspace missing or too small */
+  KVCK_ERR_HIP = -5,              /* a HIP runtime call failed */
+  KVCK_ERR_NO_DEVICE = -6         /* no gfx950 device is current */
+} kvck_status;
+
+/* Bits OR-ed into *error_flags by the kernels. */
+#define KVCK_FLAG_BAD_BLOCK_ID 1u   /* a position with valid slots names a block
+                                       outside [0, num_blocks); it contributes 0 */
+#define KVCK_FLAG_BAD_REQUEST 2u    /* num_blocks_per_req outside [0, max_blocks]
+                                       or start_pos < 0; the request is skipped */
+#define KVCK_FLAG_BAD_STATE_SLOT 4u /* a Mamba slot id outside [0, num_slots);
+                                       the request's value is 0 */
+
+/* A hipStream_t; NULL is the null stream. */
+typedef void* kvck_stream_t;
+
+/*
+ * Byte layout of one layer's paged KV pool, shared by every cache of a call.
+ * A row is the head_size elements of one (plane, block, slot, head) and must
+ * be contiguous; its address is
+ *   base + plane*plane_stride + block*block_stride + slot*slot_stride + head*head_stride.
+ * vLLM NHD pool (2, num_blocks, block_size, num_heads, head_size) (page
+ * "[vLLM 源码解析] KV Cache", section "reshape kv_cache") and the head-major HND
+ * pool (2, num_blocks, num_heads, block_size, head_size) are two stride sets
+ * of this struct; an MLA latent pool (num_blocks, block_size, head_size) has
+ * planes = 1, num_heads = 1.
+ */
+typedef struct kvck_kv_layout {
+  int32_t planes;       /* 2: plane 0 = K, plane 1 = V;  1: one latent plane */
+  int32_t block_size;   /* slots per block, >= 1 */
+  int32_t num_heads;    /* KV heads held by the pool tensor, >= 1 */
+  int32_t row_bytes;    /* head_size * element bytes; multiple of 8 */
+  int64_t num_blocks;   /* blocks in the pool; valid ids are [0, num_blocks) */
+  int64_t plane_stride; /* bytes; ignored when planes == 1 */
+  int64_t block_stride; /* bytes */
+  int64_t slot_stride;  /* bytes */
+  int64_t head_stride;  /* bytes; ignored when num_heads == 1 */
+} kvck_kv_layout;
+
+/*
+ * kvck_checksum_blocks -- per block position checksums of paged K/V.
+ *
+ * A token's slice bytes are its K row then its V row (planes == 2) or its
+ * latent row (planes == 1); P = planes*row_bytes/8.  Request r lists
+ * num_blocks_per_req[r] blocks, block_table[r*block_table_row_stride + k]
+ * at block position start_pos[r] + k (the page's KVChecksumBlocks: "the
+ * position of the first block and the ids of the blocks at consecutive
+ * positions"); position pos holds tokens pos*block_size .. +block_size-1 of
+ * the request, and slots at or past num_tokens[r] are not checksummed.
+ *
+ * Caches: cache_ptrs[i] (host array of device pointers) is layer
+ * layer_numbers[i]; the call covers its local heads head_begin ..
+ * head_begin+head_count-1, and local head head_begin+k is global head
+ * global_head_base[i]+k (TP shard: a subset of heads with global numbering;
+ * PP stage: a subset of layers -- partial results sum to the full value).
+ *
+ * Output: out[r*max_blocks + k] (device, uint64) for every listed position
+ * k < num_blocks_per_req[r]; other entries are not written.  With
+ * accumulate != 0 the checksum is added (mod 2^64) to what out holds.
+ *
+ * Workspace: device, at least kvck_blocks_workspace_bytes(num_caches,
+ * num_reqs, max_blocks) bytes, 256-byte aligned; its contents on entry are
+ * ignored.
+ */
+kvck_status kvck_checksum_blocks(
+    const kvck_kv_layout* layout,          /* host */
+    const void* const* cache_ptrs,         /* host [num_caches] of device pointers */
+    const int32_t* layer_numbers,          /* host [num_caches], 0..KVCK_MAX_LAYER_NUMBER */
+    const int32_t* global_head_base,       /* host [num_caches] */
+    int32_t num_caches,                    /* 1..KVCK_MAX_CACHES */
+    int32_t head_begin, int32_t head_count,
+    const int32_t* block_table,            /* device [num_reqs, block_table_row_stride] */
+    int64_t block_table_row_stride,        /* elements, >= max_blocks */
+    const int32_t* num_blocks_per_req,     /* device [num_reqs] */
+    const int64_t* start_pos,              /* device [num_reqs] */
+    const int64_t* num_tokens,             /* device [num_reqs] */
+    int32_t num_reqs, int32_t max_blocks,
+    uint64_t* out,                         /* device [num_reqs * max_blocks] */
+    int32_t accumulate,
+    void* workspace, size_t workspace_bytes,
+    uint32_t* error_flags,                 /* device, optional */
+    kvck_stream_t stream);
+
+size_t kvck_blocks_workspace_bytes(int32_t num_caches, int32_t num_reqs, int32_t max_blocks);
+
+/*
+ * Shape of one Mamba state, shared by every Mamba layer of a call.  A state
+ * tensor is (num_slots, num_rows, ...); the row is the TP-split dimension and
+ * its row_elems elements must be contiguous.
+ */
+typedef struct kvck_state_desc {
+  int64_t slot_stride;  /* bytes between state slots */
+  int64_t row_stride;   /* bytes between rows */
+  int32_t row_elems;    /* elements per row */
+  int32_t elem_bytes;   /* 2 or 4 (read unsigned) */
+} kvck_state_desc;
+
+/*
+ * kvck_checksum_states -- Mamba running-state checksums (position 0).
+ *
+ * Slice g of a Mamba layer is local row row_begin+g (global row
+ * global_row_base[l]+g) of every state of the layer, concatenated in the
+ * order of `states`, elements numbered from 0 across the concatenation:
+ *   s = sum_e x_e (2e + 1),  c = sum_{layer, g} m * s,  m = 2(layer*H + g_global) + 1.
+ * Request r's state slot is slot_ids[r]; out[r] receives its checksum (added
+ * to out[r] when accumulate != 0).
+ *
+ * state_ptrs holds num_layers*states_per_layer device pointers, layer-major
+ * (state_ptrs[l*states_per_layer + i] is state i of layer l).
+ * Workspace: device, kvck_states_workspace_bytes(num_layers, row_count,
+ * num_reqs) bytes, 256-byte aligned.
+ */
+kvck_status kvck_checksum_states(
+    const kvck_state_desc* states, int32_t states_per_layer,  /* host [states_per_layer], 1..4 */
+    const void* const* state_ptrs,         /* host [num_layers*states_per_layer] of device pointers */
+    const int32_t* layer_numbers,          /* host [num_layers] */
+    const int32_t* global_row_base,        /* host [num_layers] */
+    int32_t num_layers,
+    int32_t num_slots, int32_t num_rows,   /* extent of every state tensor */
+    int32_t row_begin, int32_t row_count,
+    const int32_t* slot_ids,               /* device [num_reqs] */
+    int32_t num_reqs,
+    uint64_t* out,                         /* device [num_reqs] */
+    int32_t accumulate,
+    void* workspace, size_t workspace_bytes,
+    uint32_t* error_flags,                 /* device, optional */
+    kvck_stream_t stream);
+
+size_t kvck_states_workspace_bytes(int32_t num_layers, int32_t row_count, int32_t num_reqs);
+
+/*
+ * Instrumentation (optional, process-wide).  While enabled, every
+ * kvck_checksum_blocks / kvck_checksum_states call records one pair of HIP
+ * events on its stream around its main pass -- the kernel launches that
+ * stream the cache bytes -- so a benchmark can time that kernel alone.
+ * kvck_instrument_read waits for the recorded events, returns the summed
+ * elapsed milliseconds and the number of calls timed, and starts a new tally.
+ */
+kvck_status kvck_instrument(int32_t enable);
+kvck_status kvck_instrument_read(double* total_ms, int64_t* calls);
+
+/* Human-readable name of a kvck_status value (static storage). */
+const char* kvck_status_string(int32_t status);
+
+/* 1 if the current HIP device is a gfx950 GPU, else 0. */
+int32_t kvck_platform_supported(void);
+
+/* KVCK_ABI_VERSION of the loaded library. */
+int32_t kvck_abi_version(void);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* KVCK_H_ */

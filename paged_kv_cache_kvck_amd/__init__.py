@@ -1,1 +1,29 @@
-"""KV-cache block checksums on MI355X (gfx950)."""
+"""KV-cache block checksums on MI355X (gfx950).
+
+The checksum of the vLLM API page
+"vllm.distributed.kv_transfer.kv_checksum.checksum", computed by hand-written
+HIP kernels in ``libkvck.so`` behind a C ABI (include/kvck.h).  The names
+below are the C entry points, taking torch tensors; the library is loaded on
+first use and its absence is an error, never a fallback.
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTS,
+    KVCK_FLAG_BAD_BLOCK_ID,
+    KVCK_FLAG_BAD_REQUEST,
+    KVCK_FLAG_BAD_STATE_SLOT,
+    KvckDeviceError,
+    KvckError,
+    kv_layout,
+    kvck_abi_version,
+    kvck_blocks_workspace_bytes,
+    kvck_checksum_blocks,
+    kvck_checksum_states,
+    kvck_instrument,
+    kvck_instrument_read,
+    kvck_platform_supported,
+    kvck_states_workspace_bytes,
+    kvck_status_string,
+    load_library,
+    state_desc,
+)

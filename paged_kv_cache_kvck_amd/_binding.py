@@ -1,0 +1,325 @@
+"""ctypes binding of libkvck (include/kvck.h): argument marshalling only.
+
+Every step of the checksum runs in the HIP kernels of ``libkvck.so``; this
+module turns torch tensors into pointers, byte strides and sizes, picks the
+current HIP stream, and raises on a negative status.  There is no fallback:
+if the library is missing or the device is not a gfx950 GPU, calls fail.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("KVCK_LIB", os.path.join(_PKG, "libkvck.so"))
+
+KVCK_OK = 0
+STATUS_NAMES = {
+    0: "KVCK_OK", -1: "KVCK_ERR_INVALID_ARGUMENT", -2: "KVCK_ERR_UNSUPPORTED", -3: "KVCK_ERR_MISALIGNED",
+    -4: "KVCK_ERR_WORKSPACE", -5: "KVCK_ERR_HIP", -6: "KVCK_ERR_NO_DEVICE",
+}
+KVCK_FLAG_BAD_BLOCK_ID = 1
+KVCK_FLAG_BAD_REQUEST = 2
+KVCK_FLAG_BAD_STATE_SLOT = 4
+
+# symbols include/kvck.h declares
+EXPORTS = ("kvck_checksum_blocks", "kvck_blocks_workspace_bytes", "kvck_checksum_states",
+           "kvck_states_workspace_bytes", "kvck_instrument", "kvck_instrument_read", "kvck_status_string",
+           "kvck_platform_supported", "kvck_abi_version")
+
+
+class KvckError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{STATUS_NAMES.get(status, status)}{': ' + what if what else ''}")
+
+
+class KvckDeviceError(RuntimeError):
+    """Error bits the kernels raised in *error_flags."""
+
+    def __init__(self, flags: int):
+        self.flags = flags
+        names = [n for bit, n in ((1, "BAD_BLOCK_ID"), (2, "BAD_REQUEST"), (4, "BAD_STATE_SLOT")) if flags & bit]
+        super().__init__("device reported " + "|".join(names))
+
+
+class kvck_kv_layout(ctypes.Structure):
+    _fields_ = [("planes", ctypes.c_int32), ("block_size", ctypes.c_int32), ("num_heads", ctypes.c_int32),
+                ("row_bytes", ctypes.c_int32), ("num_blocks", ctypes.c_int64), ("plane_stride", ctypes.c_int64),
+                ("block_stride", ctypes.c_int64), ("slot_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64)]
+
+
+class kvck_state_desc(ctypes.Structure):
+    _fields_ = [("slot_stride", ctypes.c_int64), ("row_stride", ctypes.c_int64), ("row_elems", ctypes.c_int32),
+                ("elem_bytes", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str | None = None) -> ctypes.CDLL:
+    """Load libkvck.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m paged_kv_cache_kvck_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.kvck_checksum_blocks.restype = i32
+    lib.kvck_checksum_blocks.argtypes = [
+        ctypes.POINTER(kvck_kv_layout), ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(i32), i32,
+        i32, i32, vp, i64, vp, vp, vp, i32, i32, vp, i32, vp, sz, vp, vp]
+    lib.kvck_blocks_workspace_bytes.restype = sz
+    lib.kvck_blocks_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.kvck_checksum_states.restype = i32
+    lib.kvck_checksum_states.argtypes = [
+        ctypes.POINTER(kvck_state_desc), i32, ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(i32), i32,
+        i32, i32, i32, i32, vp, i32, vp, i32, vp, sz, vp, vp]
+    lib.kvck_states_workspace_bytes.restype = sz
+    lib.kvck_states_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.kvck_status_string.restype = ctypes.c_char_p
+    lib.kvck_status_string.argtypes = [i32]
+    lib.kvck_platform_supported.restype = i32
+    lib.kvck_platform_supported.argtypes = []
+    lib.kvck_abi_version.restype = i32
+    lib.kvck_abi_version.argtypes = []
+    lib.kvck_instrument.restype = i32
+    lib.kvck_instrument.argtypes = [i32]
+    lib.kvck_instrument_read.restype = i32
+    lib.kvck_instrument_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def kvck_status_string(status: int) -> str:
+    return load_library().kvck_status_string(int(status)).decode()
+
+
+def kvck_platform_supported() -> bool:
+    return bool(load_library().kvck_platform_supported())
+
+
+def kvck_abi_version() -> int:
+    return int(load_library().kvck_abi_version())
+
+
+def kvck_instrument(enable: bool) -> None:
+    """Record HIP events around every call's main pass (see include/kvck.h)."""
+    _check(load_library().kvck_instrument(int(bool(enable))), "kvck_instrument")
+
+
+def kvck_instrument_read() -> tuple[float, int]:
+    """(summed main-pass milliseconds, calls timed) since the last read."""
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    _check(load_library().kvck_instrument_read(ctypes.byref(ms), ctypes.byref(n)), "kvck_instrument_read")
+    return ms.value, n.value
+
+
+def kvck_blocks_workspace_bytes(num_caches: int, num_reqs: int, max_blocks: int) -> int:
+    return int(load_library().kvck_blocks_workspace_bytes(num_caches, num_reqs, max_blocks))
+
+
+def kvck_states_workspace_bytes(num_layers: int, row_count: int, num_reqs: int) -> int:
+    return int(load_library().kvck_states_workspace_bytes(num_layers, row_count, num_reqs))
+
+
+def _check(status: int, what: str = ""):
+    if status != KVCK_OK:
+        raise KvckError(int(status), what)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream, device) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# ----------------------------------------------------------------- layouts
+
+def kv_layout(cache: torch.Tensor, layout: str) -> kvck_kv_layout:
+    """Byte layout of a pool tensor in semantic shape:
+    NHD (2, num_blocks, block_size, num_heads, head_size),
+    HND (2, num_blocks, num_heads, block_size, head_size),
+    MLA (num_blocks, block_size, head_size)."""
+    es = cache.element_size()
+    st = [s * es for s in cache.stride()]
+    sh = cache.shape
+    if cache.stride(-1) != 1:
+        raise ValueError("the head_size dimension must be contiguous")
+    L = kvck_kv_layout()
+    if layout == "NHD":
+        if cache.dim() != 5 or sh[0] != 2:
+            raise ValueError("NHD pools are (2, num_blocks, block_size, num_heads, head_size)")
+        L.planes, L.num_blocks, L.block_size, L.num_heads = 2, sh[1], sh[2], sh[3]
+        L.plane_stride, L.block_stride, L.slot_stride, L.head_stride = st[0], st[1], st[2], st[3]
+    elif layout == "HND":
+        if cache.dim() != 5 or sh[0] != 2:
+            raise ValueError("HND pools are (2, num_blocks, num_heads, block_size, head_size)")
+        L.planes, L.num_blocks, L.num_heads, L.block_size = 2, sh[1], sh[2], sh[3]
+        L.plane_stride, L.block_stride, L.head_stride, L.slot_stride = st[0], st[1], st[2], st[3]
+    elif layout == "MLA":
+        if cache.dim() != 3:
+            raise ValueError("MLA pools are (num_blocks, block_size, head_size)")
+        L.planes, L.num_blocks, L.block_size, L.num_heads = 1, sh[0], sh[1], 1
+        L.plane_stride, L.block_stride, L.slot_stride, L.head_stride = 0, st[0], st[1], 0
+    else:
+        raise ValueError(f"unknown layout {layout!r}")
+    L.row_bytes = sh[-1] * es
+    return L
+
+
+def _meta(t: torch.Tensor, dtype, name, device, n=None):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or t.device != device:
+        raise ValueError(f"{name} must be a {dtype} tensor on {device}")
+    if n is not None and (t.dim() != 1 or t.shape[0] != n or not t.is_contiguous()):
+        raise ValueError(f"{name} must be contiguous with {n} entries")
+    return t
+
+
+def kvck_checksum_blocks(caches: Sequence[torch.Tensor], layout: str, layer_numbers: Sequence[int],
+                         block_table: torch.Tensor, num_blocks_per_req: torch.Tensor, start_pos: torch.Tensor,
+                         num_tokens: torch.Tensor, global_head_base=None, head_begin: int = 0,
+                         head_count: int | None = None, out: torch.Tensor | None = None, accumulate: bool = False,
+                         workspace: torch.Tensor | None = None, error_flags: torch.Tensor | None = None,
+                         stream=None, check: bool = False) -> torch.Tensor:
+    """Per block position checksums of paged K/V (see include/kvck.h).
+
+    Returns ``out``: uint64 (num_reqs, max_blocks) on the caches' device;
+    entries past a request's listed positions are left as they were.
+    ``check=True`` zeroes a flag word, synchronizes, and raises
+    ``KvckDeviceError`` if the kernels flagged a bad block id or request.
+    """
+    lib = load_library()
+    caches = list(caches)
+    if not caches:
+        raise ValueError("no caches")
+    dev = caches[0].device
+    L = kv_layout(caches[0], layout)
+    for c in caches[1:]:
+        if c.shape != caches[0].shape or c.stride() != caches[0].stride() or c.dtype != caches[0].dtype \
+                or c.device != dev:
+            raise ValueError("every cache of a call must share shape, strides, dtype and device")
+    n = len(caches)
+    if head_count is None:
+        head_count = L.num_heads - head_begin
+    if global_head_base is None:
+        global_head_base = [head_begin] * n
+    elif isinstance(global_head_base, int):
+        global_head_base = [global_head_base] * n
+    if len(layer_numbers) != n or len(global_head_base) != n:
+        raise ValueError("one layer number and one global head base per cache")
+    _meta(block_table, torch.int32, "block_table", dev)
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be 2-D with contiguous rows")
+    R, max_blocks = block_table.shape
+    _meta(num_blocks_per_req, torch.int32, "num_blocks_per_req", dev, R)
+    _meta(start_pos, torch.int64, "start_pos", dev, R)
+    _meta(num_tokens, torch.int64, "num_tokens", dev, R)
+    if out is None:
+        out = torch.zeros((R, max_blocks), dtype=torch.uint64, device=dev)
+    elif out.dtype not in (torch.uint64, torch.int64) or out.device != dev or not out.is_contiguous() \
+            or out.numel() < R * max_blocks:
+        raise ValueError("out must be a contiguous uint64 tensor of num_reqs*max_blocks entries")
+    need = int(lib.kvck_blocks_workspace_bytes(n, R, max_blocks))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if check and error_flags is None:
+        error_flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    ptrs = (ctypes.c_void_p * n)(*[c.data_ptr() for c in caches])
+    layers = (ctypes.c_int32 * n)(*[int(x) for x in layer_numbers])
+    bases = (ctypes.c_int32 * n)(*[int(x) for x in global_head_base])
+    st = lib.kvck_checksum_blocks(
+        ctypes.byref(L), ptrs, layers, bases, n, int(head_begin), int(head_count),
+        block_table.data_ptr(), block_table.stride(0), num_blocks_per_req.data_ptr(), start_pos.data_ptr(),
+        num_tokens.data_ptr(), R, max_blocks, out.data_ptr(), int(bool(accumulate)), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _ptr(error_flags), _stream_handle(stream, dev))
+    _check(st, "kvck_checksum_blocks")
+    if check:
+        torch.cuda.synchronize(dev)
+        flags = int(error_flags.item())
+        if flags:
+            raise KvckDeviceError(flags)
+    return out
+
+
+def state_desc(state: torch.Tensor) -> kvck_state_desc:
+    """Shape of a Mamba state (num_slots, num_rows, ...) with contiguous rows."""
+    if state.dim() < 3:
+        raise ValueError("a state is (num_slots, num_rows, ...)")
+    es = state.element_size()
+    row = state[0, 0]
+    if not row.is_contiguous():
+        raise ValueError("each state row must be contiguous")
+    d = kvck_state_desc()
+    d.slot_stride, d.row_stride = state.stride(0) * es, state.stride(1) * es
+    d.row_elems, d.elem_bytes = row.numel(), es
+    return d
+
+
+def kvck_checksum_states(layer_states: Sequence[Sequence[torch.Tensor]], layer_numbers: Sequence[int],
+                         slot_ids: torch.Tensor, global_row_base=None, row_begin: int = 0,
+                         row_count: int | None = None, out: torch.Tensor | None = None, accumulate: bool = False,
+                         workspace: torch.Tensor | None = None, error_flags: torch.Tensor | None = None,
+                         stream=None, check: bool = False) -> torch.Tensor:
+    """Mamba running-state checksums, one uint64 per request (position 0)."""
+    lib = load_library()
+    layer_states = [list(s) for s in layer_states]
+    nl = len(layer_states)
+    if nl == 0 or not layer_states[0]:
+        raise ValueError("no states")
+    ref = layer_states[0]
+    k = len(ref)
+    dev = ref[0].device
+    for sts in layer_states:
+        if len(sts) != k:
+            raise ValueError("every layer must hold the same states")
+        for a, b in zip(sts, ref):
+            if a.shape != b.shape or a.stride() != b.stride() or a.dtype != b.dtype or a.device != dev:
+                raise ValueError("states of every layer must share shape, strides, dtype and device")
+    slots, rows = ref[0].shape[0], ref[0].shape[1]
+    for s in ref:
+        if s.shape[0] != slots or s.shape[1] != rows:
+            raise ValueError("states of a layer must share (num_slots, num_rows)")
+    if row_count is None:
+        row_count = rows - row_begin
+    if global_row_base is None:
+        global_row_base = [row_begin] * nl
+    elif isinstance(global_row_base, int):
+        global_row_base = [global_row_base] * nl
+    _meta(slot_ids, torch.int32, "slot_ids", dev)
+    R = slot_ids.numel()
+    if not slot_ids.is_contiguous():
+        raise ValueError("slot_ids must be contiguous")
+    if out is None:
+        out = torch.zeros(R, dtype=torch.uint64, device=dev)
+    descs = (kvck_state_desc * k)(*[state_desc(s) for s in ref])
+    ptrs = (ctypes.c_void_p * (nl * k))(*[s.data_ptr() for sts in layer_states for s in sts])
+    layers = (ctypes.c_int32 * nl)(*[int(x) for x in layer_numbers])
+    bases = (ctypes.c_int32 * nl)(*[int(x) for x in global_row_base])
+    need = int(lib.kvck_states_workspace_bytes(nl, row_count, R))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if check and error_flags is None:
+        error_flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = lib.kvck_checksum_states(
+        descs, k, ptrs, layers, bases, nl, slots, rows, int(row_begin), int(row_count), slot_ids.data_ptr(), R,
+        out.data_ptr(), int(bool(accumulate)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _ptr(error_flags), _stream_handle(stream, dev))
+    _check(st, "kvck_checksum_states")
+    if check:
+        torch.cuda.synchronize(dev)
+        flags = int(error_flags.item())
+        if flags:
+            raise KvckDeviceError(flags)
+    return out

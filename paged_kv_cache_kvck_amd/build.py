@@ -1,0 +1,68 @@
+"""Build libkvck.so in-tree for gfx950 with hipcc.
+
+    python -m paged_kv_cache_kvck_amd.build [--save-temps DIR]
+
+The library is a plain C-ABI shared object (include/kvck.h); the Python
+binding loads it with ctypes, so no torch C++ extension is involved.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libkvck.so")
+ARCH = "gfx950"
+
+# Packed-FP32 instructions are kept out of every kernel (no FP32 math is used
+# anyway; the flag keeps the compiler from forming them).
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", "-fvisibility=hidden",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    exe = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(exe):
+        raise RuntimeError("hipcc not found: the HIP library cannot be built")
+    return exe
+
+
+def sources():
+    return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
+
+
+def build(save_temps: str | None = None, verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
+           *sources(), "-o", tmp]
+    cwd = None
+    if save_temps:
+        os.makedirs(save_temps, exist_ok=True)
+        cmd.insert(1, "-save-temps")
+        cwd = save_temps
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True, cwd=cwd)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--save-temps", default=None, help="keep intermediate files (ISA) in this directory")
+    ap.add_argument("-v", "--verbose", action="store_true")
+    args = ap.parse_args(argv)
+    print(build(args.save_temps, args.verbose))
+
+
+if __name__ == "__main__":
+    sys.exit(main())

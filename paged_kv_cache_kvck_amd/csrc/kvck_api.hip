@@ -1,0 +1,350 @@
+// C ABI of libkvck: argument validation, launch shapes, workspace carving.
+// Every check that can be made on the host is made before the first HIP call,
+// so a rejected call touches no device state.
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "kvck_internal.h"
+
+#define KVCK_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace kvck {
+namespace {
+
+constexpr int64_t kH = KVCK_MAX_KV_HEADS_PER_LAYER;
+
+bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)a) == 0; }
+
+// gfx950 check of the current device, cached per device id.
+kvck_status current_device(int* dev_out) {
+  static std::mutex mu;
+  static int known[64];  // 0 unknown, 1 gfx950, -1 other
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) return KVCK_ERR_NO_DEVICE;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return KVCK_ERR_NO_DEVICE;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    if (dev >= 0 && dev < 64 && known[dev] == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return KVCK_ERR_HIP;
+      known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    }
+    if (dev < 0 || dev >= 64 || known[dev] != 1) return KVCK_ERR_NO_DEVICE;
+  }
+  *dev_out = dev;
+  return KVCK_OK;
+}
+
+// Lane-table shape: the smallest S whose 64*S lane-chunks cover a whole block
+// row set of one (plane, head); larger row sets are split into equal groups.
+bool choose_shape(int32_t block_size, int32_t row_bytes, int chunk, BlocksShape* shp) {
+  const int64_t cpr = row_bytes / chunk;
+  const int64_t max_chunks = (int64_t)kWave * 16;
+  if (cpr > max_chunks) return false;
+  const int64_t groups = ((int64_t)block_size * cpr + max_chunks - 1) / max_chunks;
+  const int64_t rg = (block_size + groups - 1) / groups;
+  const int64_t need = (rg * cpr + kWave - 1) / kWave;
+  int s = 1;
+  while (s < need) s <<= 1;
+  shp->chunk = chunk;
+  shp->slots = s;
+  shp->rows_per_group = (int)rg;
+  return true;
+}
+
+// Event pairs around main passes while instrumentation is on.
+struct Instrument {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> start, stop;
+  size_t used = 0;
+};
+Instrument g_instr;
+
+// Returns a (start, stop) pair to record, or nulls when instrumentation is off.
+bool instrument_pair(hipEvent_t* s, hipEvent_t* e) {
+  std::lock_guard<std::mutex> g(g_instr.mu);
+  if (!g_instr.on) return false;
+  if (g_instr.used == g_instr.start.size()) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return false;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return false;
+    }
+    g_instr.start.push_back(a);
+    g_instr.stop.push_back(b);
+  }
+  *s = g_instr.start[g_instr.used];
+  *e = g_instr.stop[g_instr.used];
+  ++g_instr.used;
+  return true;
+}
+
+}  // namespace
+}  // namespace kvck
+
+using namespace kvck;
+
+KVCK_EXPORT kvck_status kvck_instrument(int32_t enable) {
+  std::lock_guard<std::mutex> g(g_instr.mu);
+  g_instr.on = enable != 0;
+  g_instr.used = 0;
+  return KVCK_OK;
+}
+
+KVCK_EXPORT kvck_status kvck_instrument_read(double* total_ms, int64_t* calls) {
+  if (!total_ms || !calls) return KVCK_ERR_INVALID_ARGUMENT;
+  std::lock_guard<std::mutex> g(g_instr.mu);
+  double tot = 0.0;
+  for (size_t i = 0; i < g_instr.used; ++i) {
+    if (hipEventSynchronize(g_instr.stop[i]) != hipSuccess) return KVCK_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_instr.start[i], g_instr.stop[i]) != hipSuccess) return KVCK_ERR_HIP;
+    tot += ms;
+  }
+  *total_ms = tot;
+  *calls = (int64_t)g_instr.used;
+  g_instr.used = 0;
+  return KVCK_OK;
+}
+
+KVCK_EXPORT int32_t kvck_abi_version(void) { return KVCK_ABI_VERSION; }
+
+KVCK_EXPORT const char* kvck_status_string(int32_t status) {
+  switch (status) {
+    case KVCK_OK: return "KVCK_OK";
+    case KVCK_ERR_INVALID_ARGUMENT: return "KVCK_ERR_INVALID_ARGUMENT";
+    case KVCK_ERR_UNSUPPORTED: return "KVCK_ERR_UNSUPPORTED";
+    case KVCK_ERR_MISALIGNED: return "KVCK_ERR_MISALIGNED";
+    case KVCK_ERR_WORKSPACE: return "KVCK_ERR_WORKSPACE";
+    case KVCK_ERR_HIP: return "KVCK_ERR_HIP";
+    case KVCK_ERR_NO_DEVICE: return "KVCK_ERR_NO_DEVICE";
+  }
+  return "KVCK_UNKNOWN_STATUS";
+}
+
+KVCK_EXPORT int32_t kvck_platform_supported(void) {
+  int dev = 0;
+  return current_device(&dev) == KVCK_OK ? 1 : 0;
+}
+
+KVCK_EXPORT size_t kvck_blocks_workspace_bytes(int32_t num_caches, int32_t num_reqs, int32_t max_blocks) {
+  if (num_caches < 1 || num_reqs < 0 || max_blocks < 0) return 0;
+  return BlocksWorkspace::make(num_caches, num_reqs, max_blocks).total;
+}
+
+KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const void* const* cache_ptrs,
+                                             const int32_t* layer_numbers, const int32_t* global_head_base,
+                                             int32_t num_caches, int32_t head_begin, int32_t head_count,
+                                             const int32_t* block_table, int64_t block_table_row_stride,
+                                             const int32_t* num_blocks_per_req, const int64_t* start_pos,
+                                             const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks,
+                                             uint64_t* out, int32_t accumulate, void* workspace,
+                                             size_t workspace_bytes, uint32_t* error_flags,
+                                             kvck_stream_t stream) {
+  // ---- layout
+  if (!layout || !cache_ptrs || !layer_numbers || !global_head_base) return KVCK_ERR_INVALID_ARGUMENT;
+  const kvck_kv_layout L = *layout;
+  if (L.planes != 1 && L.planes != 2) return KVCK_ERR_INVALID_ARGUMENT;
+  if (L.block_size < 1 || L.num_heads < 1 || L.row_bytes < 1 || L.num_blocks < 0) return KVCK_ERR_INVALID_ARGUMENT;
+  if (L.plane_stride < 0 || L.block_stride < 0 || L.slot_stride < 0 || L.head_stride < 0)
+    return KVCK_ERR_INVALID_ARGUMENT;
+  if (L.row_bytes % 8 != 0) return KVCK_ERR_UNSUPPORTED;
+  if (num_caches < 1 || num_caches > KVCK_MAX_CACHES) return KVCK_ERR_UNSUPPORTED;
+  if (head_begin < 0 || head_count < 1 || (int64_t)head_begin + head_count > L.num_heads)
+    return KVCK_ERR_INVALID_ARGUMENT;
+  for (int32_t i = 0; i < num_caches; ++i) {
+    if (!cache_ptrs[i]) return KVCK_ERR_INVALID_ARGUMENT;
+    if (layer_numbers[i] < 0 || global_head_base[i] < 0) return KVCK_ERR_INVALID_ARGUMENT;
+    if (layer_numbers[i] > KVCK_MAX_LAYER_NUMBER) return KVCK_ERR_UNSUPPORTED;
+    if ((int64_t)global_head_base[i] + head_count > kH) return KVCK_ERR_UNSUPPORTED;
+  }
+  // ---- requests
+  if (num_reqs < 0 || max_blocks < 0) return KVCK_ERR_INVALID_ARGUMENT;
+  if (num_reqs == 0 || max_blocks == 0) return KVCK_OK;
+  if (!block_table || !num_blocks_per_req || !start_pos || !num_tokens || !out) return KVCK_ERR_INVALID_ARGUMENT;
+  if (block_table_row_stride < max_blocks) return KVCK_ERR_INVALID_ARGUMENT;
+  if ((int64_t)num_reqs * max_blocks >= (int64_t)1 << 31) return KVCK_ERR_UNSUPPORTED;
+  // ---- alignment: 16-byte lane loads when everything allows, else 8-byte
+  int chunk = 16;
+  for (int pass = 0; pass < 2; ++pass) {
+    bool ok = L.row_bytes % chunk == 0 && L.block_stride % chunk == 0 &&
+              (L.planes == 1 || L.plane_stride % chunk == 0) && (L.block_size == 1 || L.slot_stride % chunk == 0) &&
+              (L.num_heads == 1 || L.head_stride % chunk == 0);
+    for (int32_t i = 0; ok && i < num_caches; ++i) ok = aligned(cache_ptrs[i], chunk);
+    if (ok) break;
+    if (chunk == 8) return KVCK_ERR_MISALIGNED;
+    chunk = 8;
+  }
+  BlocksShape shp;
+  if (!choose_shape(L.block_size, L.row_bytes, chunk, &shp)) return KVCK_ERR_UNSUPPORTED;
+  // lane-table offsets and piece terms are 32-bit
+  if ((int64_t)shp.rows_per_group * L.slot_stride + L.row_bytes >= ((int64_t)1 << 31)) return KVCK_ERR_UNSUPPORTED;
+  const int64_t pieces = (int64_t)L.planes * L.row_bytes / 8;
+  if (2 * (int64_t)shp.rows_per_group * pieces + 4 * (L.row_bytes / chunk) >= ((int64_t)1 << 32))
+    return KVCK_ERR_UNSUPPORTED;
+  // ---- workspace
+  const BlocksWorkspace w = BlocksWorkspace::make(num_caches, num_reqs, max_blocks);
+  if (!workspace || workspace_bytes < w.total || !aligned(workspace, (int64_t)kAlign)) return KVCK_ERR_WORKSPACE;
+
+  int dev = 0;
+  const kvck_status ds = current_device(&dev);
+  if (ds != KVCK_OK) return ds;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  if (launch_plan(block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens, num_reqs,
+                  max_blocks, L.block_size, L.num_blocks, workspace, error_flags, st) != hipSuccess)
+    return KVCK_ERR_HIP;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int64_t max_items = (int64_t)num_reqs * max_blocks;
+  BlocksArgs a;
+  memset(&a, 0, sizeof(a));
+  a.plane_stride = L.plane_stride;
+  a.block_stride = L.block_stride;
+  a.slot_stride = L.slot_stride;
+  a.head_stride = L.head_stride;
+  a.recs = reinterpret_cast<const PosRecord*>(ws + w.recs_off);
+  a.n_items = reinterpret_cast<const uint32_t*>(ws);
+  a.partials = reinterpret_cast<uint64_t*>(ws + w.partials_off);
+  a.out = out;
+  a.max_items = max_items;
+  a.planes = L.planes;
+  a.heads = head_count;
+  a.row_bytes = L.row_bytes;
+  a.pieces = (int32_t)pieces;
+  a.rows_per_group = shp.rows_per_group;
+  a.chunks_per_row = L.row_bytes / chunk;
+  a.direct = num_caches == 1;
+  a.accumulate = accumulate != 0;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  const bool timed = instrument_pair(&ev0, &ev1);
+  if (timed && hipEventRecord(ev0, st) != hipSuccess) return KVCK_ERR_HIP;
+  for (int32_t c0 = 0; c0 < num_caches; c0 += kCachesPerLaunch) {
+    const int32_t n = num_caches - c0 < kCachesPerLaunch ? num_caches - c0 : kCachesPerLaunch;
+    a.num_caches = n;
+    a.cache_offset = c0;
+    for (int32_t i = 0; i < n; ++i) {
+      a.base[i] = static_cast<const uint8_t*>(cache_ptrs[c0 + i]) + (int64_t)head_begin * L.head_stride;
+      a.mbase[i] = (uint32_t)(2 * ((int64_t)layer_numbers[c0 + i] * kH + global_head_base[c0 + i]) + 1);
+    }
+    const int grid = blocks_grid(shp, dev, max_items * n);
+    if (launch_blocks(a, shp, grid, st) != hipSuccess) return KVCK_ERR_HIP;
+  }
+  if (timed && hipEventRecord(ev1, st) != hipSuccess) return KVCK_ERR_HIP;
+  if (num_caches > 1) {
+    if (launch_reduce(a.partials, max_items, num_caches, a.n_items, 0, a.recs, out, a.accumulate, st) != hipSuccess)
+      return KVCK_ERR_HIP;
+  }
+  return KVCK_OK;
+}
+
+namespace {
+constexpr int32_t kRowsPerTask = 8;
+int32_t row_groups(int32_t row_count) { return (row_count + kRowsPerTask - 1) / kRowsPerTask; }
+}  // namespace
+
+KVCK_EXPORT size_t kvck_states_workspace_bytes(int32_t num_layers, int32_t row_count, int32_t num_reqs) {
+  if (num_layers < 1 || row_count < 1 || num_reqs < 0) return 0;
+  const int64_t splits = (int64_t)num_layers * row_groups(row_count);
+  return kAlign + (splits > 1 ? align_up(sizeof(uint64_t) * (size_t)splits * (size_t)num_reqs) : 0);
+}
+
+KVCK_EXPORT kvck_status kvck_checksum_states(const kvck_state_desc* states, int32_t states_per_layer,
+                                             const void* const* state_ptrs, const int32_t* layer_numbers,
+                                             const int32_t* global_row_base, int32_t num_layers, int32_t num_slots,
+                                             int32_t num_rows, int32_t row_begin, int32_t row_count,
+                                             const int32_t* slot_ids, int32_t num_reqs, uint64_t* out,
+                                             int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                             uint32_t* error_flags, kvck_stream_t stream) {
+  if (!states || !state_ptrs || !layer_numbers || !global_row_base) return KVCK_ERR_INVALID_ARGUMENT;
+  if (states_per_layer < 1 || states_per_layer > KVCK_MAX_STATES_PER_LAYER) return KVCK_ERR_UNSUPPORTED;
+  if (num_layers < 1 || num_layers > KVCK_MAX_CACHES) return KVCK_ERR_UNSUPPORTED;
+  if (num_slots < 1 || num_rows < 1 || row_begin < 0 || row_count < 1 || (int64_t)row_begin + row_count > num_rows)
+    return KVCK_ERR_INVALID_ARGUMENT;
+  int64_t elems = 0;
+  for (int32_t i = 0; i < states_per_layer; ++i) {
+    const kvck_state_desc& d = states[i];
+    if (d.row_elems < 1 || d.slot_stride < 0 || d.row_stride < 0) return KVCK_ERR_INVALID_ARGUMENT;
+    if (d.elem_bytes != 2 && d.elem_bytes != 4) return KVCK_ERR_UNSUPPORTED;
+    if (((int64_t)d.row_elems * d.elem_bytes) % 16 != 0) return KVCK_ERR_UNSUPPORTED;
+    if (d.slot_stride % 16 != 0 || d.row_stride % 16 != 0) return KVCK_ERR_MISALIGNED;
+    elems += d.row_elems;
+  }
+  if (elems >= ((int64_t)1 << 31) - 8) return KVCK_ERR_UNSUPPORTED;
+  for (int32_t l = 0; l < num_layers; ++l) {
+    if (layer_numbers[l] < 0 || global_row_base[l] < 0) return KVCK_ERR_INVALID_ARGUMENT;
+    if (layer_numbers[l] > KVCK_MAX_LAYER_NUMBER) return KVCK_ERR_UNSUPPORTED;
+    if ((int64_t)global_row_base[l] + row_count > kH) return KVCK_ERR_UNSUPPORTED;
+    for (int32_t i = 0; i < states_per_layer; ++i) {
+      const void* p = state_ptrs[(int64_t)l * states_per_layer + i];
+      if (!p) return KVCK_ERR_INVALID_ARGUMENT;
+      if (!aligned(p, 16)) return KVCK_ERR_MISALIGNED;
+    }
+  }
+  if (num_reqs < 0) return KVCK_ERR_INVALID_ARGUMENT;
+  if (num_reqs == 0) return KVCK_OK;
+  if (!slot_ids || !out) return KVCK_ERR_INVALID_ARGUMENT;
+  const int32_t groups = row_groups(row_count);
+  const int64_t splits = (int64_t)num_layers * groups;
+  if (splits * num_reqs >= ((int64_t)1 << 40)) return KVCK_ERR_UNSUPPORTED;
+  const size_t need = kvck_states_workspace_bytes(num_layers, row_count, num_reqs);
+  if (splits > 1 && (!workspace || workspace_bytes < need || !aligned(workspace, (int64_t)kAlign)))
+    return KVCK_ERR_WORKSPACE;
+
+  int dev = 0;
+  const kvck_status ds = current_device(&dev);
+  if (ds != KVCK_OK) return ds;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  StatesArgs a;
+  memset(&a, 0, sizeof(a));
+  int32_t eoff = 0;
+  for (int32_t i = 0; i < states_per_layer; ++i) {
+    a.slot_stride[i] = states[i].slot_stride;
+    a.row_stride[i] = states[i].row_stride;
+    a.row_chunks[i] = (int32_t)((int64_t)states[i].row_elems * states[i].elem_bytes / 16);
+    a.elem_bytes[i] = states[i].elem_bytes;
+    a.elem_off[i] = eoff;
+    eoff += states[i].row_elems;
+  }
+  a.slot_ids = slot_ids;
+  a.partials = splits > 1 ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + kAlign) : nullptr;
+  a.out = out;
+  a.error_flags = error_flags;
+  a.nstates = states_per_layer;
+  a.num_slots = num_slots;
+  a.num_reqs = num_reqs;
+  a.row_begin = row_begin;
+  a.row_count = row_count;
+  a.rows_per_task = kRowsPerTask;
+  a.groups_per_layer = groups;
+  a.direct = splits == 1;
+  a.accumulate = accumulate != 0;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  const bool timed = instrument_pair(&ev0, &ev1);
+  if (timed && hipEventRecord(ev0, st) != hipSuccess) return KVCK_ERR_HIP;
+  for (int32_t l0 = 0; l0 < num_layers; l0 += kLayersPerStatesLaunch) {
+    const int32_t n = num_layers - l0 < kLayersPerStatesLaunch ? num_layers - l0 : kLayersPerStatesLaunch;
+    a.num_layers = n;
+    a.split_offset = l0 * groups;
+    for (int32_t l = 0; l < n; ++l) {
+      for (int32_t i = 0; i < states_per_layer; ++i)
+        a.ptr[l][i] = static_cast<const uint8_t*>(state_ptrs[(int64_t)(l0 + l) * states_per_layer + i]);
+      a.mbase[l] = (uint32_t)(2 * ((int64_t)layer_numbers[l0 + l] * kH + global_row_base[l0 + l]) + 1);
+    }
+    const int grid = states_grid(dev, (int64_t)n * groups * num_reqs);
+    if (launch_states(a, grid, st) != hipSuccess) return KVCK_ERR_HIP;
+  }
+  if (timed && hipEventRecord(ev1, st) != hipSuccess) return KVCK_ERR_HIP;
+  if (splits > 1) {
+    if (launch_reduce(a.partials, num_reqs, (int32_t)splits, nullptr, num_reqs, nullptr, out, a.accumulate, st) !=
+        hipSuccess)
+      return KVCK_ERR_HIP;
+  }
+  return KVCK_OK;
+}

@@ -1,0 +1,356 @@
+// Paged K/V block checksums on gfx950.
+//
+// Definition (vLLM API page "vllm.distributed.kv_transfer.kv_checksum.checksum",
+// module docstring items 1 and 2):
+//   s(layer, head) = sum_j x_j (2j + 1),  j = t*P + p,  x_j little-endian uint64
+//   c(position)    = sum_{layer, head} m s,  m = 2 (layer*65536 + global_head) + 1
+// all mod 2^64.
+//
+// Three launches per call, all on the caller's stream:
+//   plan    request arrays -> compact list of listed positions (PosRecord):
+//           block id, first token t0 = pos*block_size, valid slots
+//           v = min(block_size, max(0, num_tokens - t0)) (page helper
+//           num_valid_tokens), output index.  Bad ids and requests are flagged.
+//   blocks  one wavefront per task (cache, position): streams the valid rows of
+//           the block's pages with 16-byte loads and accumulates
+//           sum over pieces of x * m * (2j + 1) in 64-bit registers, then
+//           reduces the 64 lanes and writes one uint64 per task.
+//   reduce  sums the per-cache partials of each position in a fixed order
+//           (skipped when the call has one cache).  Addition mod 2^64 is
+//           associative and commutative, so results are bit-exact whatever
+//           the task order or launch shape.
+#include "kvck_internal.h"
+
+namespace kvck {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int CHUNK>
+struct ChunkType;
+template <>
+struct ChunkType<16> {
+  using T = u32x4;
+};
+template <>
+struct ChunkType<8> {
+  using T = u32x2;
+};
+
+// Cache bytes are read exactly once: buffer loads with the non-temporal bit.
+// The base address of the run lives in the (uniform) resource descriptor and
+// each lane supplies a 32-bit byte offset.  A lane whose offset is kOOB or more
+// is past num_records: a buffer load then returns zeros and touches no memory,
+// which is how masked-off lanes and heads are handled without branches.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kNonTemporal = 2;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)kOOB, 0x00020000);
+}
+
+template <int CHUNK>
+__device__ __forceinline__ typename ChunkType<CHUNK>::T load_chunk(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (CHUNK == 16)
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNonTemporal);
+  else
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kNonTemporal);
+}
+
+// Sum of a 64-bit value over the 64 lanes of a wavefront (every lane gets it).
+__device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ----------------------------------------------------------------- plan
+
+// Exclusive prefix sum of the listed positions per request (one workgroup).
+__global__ __launch_bounds__(1024) void plan_scan_kernel(const int32_t* __restrict__ nbpr,
+                                                         const int64_t* __restrict__ start_pos,
+                                                         int32_t num_reqs, int32_t max_blocks,
+                                                         int64_t max_start, int32_t* __restrict__ prefix,
+                                                         uint32_t* __restrict__ n_items,
+                                                         uint32_t* __restrict__ error_flags) {
+  __shared__ int32_t buf[1024];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < num_reqs; base += 1024) {
+    const int r = base + tid;
+    int n = 0;
+    if (r < num_reqs) {
+      n = nbpr[r];
+      const int64_t s = start_pos[r];
+      if (n < 0 || n > max_blocks || s < 0 || s > max_start) {
+        if (error_flags) atomicOr(error_flags, KVCK_FLAG_BAD_REQUEST);
+        n = 0;
+      }
+    }
+    buf[tid] = n;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const int t = tid >= o ? buf[tid - o] : 0;
+      __syncthreads();
+      buf[tid] += t;
+      __syncthreads();
+    }
+    const int incl = buf[tid];
+    const int c = carry;
+    if (r < num_reqs) prefix[r] = c + incl - n;
+    __syncthreads();
+    if (tid == 1023) carry = c + incl;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    prefix[num_reqs] = carry;
+    *n_items = (uint32_t)carry;
+  }
+}
+
+// One thread per (request, listed position): the position's record.
+__global__ __launch_bounds__(256) void plan_fill_kernel(
+    const int32_t* __restrict__ block_table, int64_t bt_stride, const int64_t* __restrict__ start_pos,
+    const int64_t* __restrict__ num_tokens, int32_t num_reqs, int32_t max_blocks, int32_t block_size,
+    int64_t num_blocks, const int32_t* __restrict__ prefix, PosRecord* __restrict__ recs,
+    uint32_t* __restrict__ error_flags) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)num_reqs * max_blocks) return;
+  const int32_t r = (int32_t)(idx / max_blocks);
+  const int32_t k = (int32_t)(idx - (int64_t)r * max_blocks);
+  const int32_t p0 = prefix[r];
+  if (k >= prefix[r + 1] - p0) return;
+  const int64_t t0 = (start_pos[r] + k) * (int64_t)block_size;
+  const int64_t left = num_tokens[r] - t0;
+  int32_t v = left <= 0 ? 0 : (left >= block_size ? block_size : (int32_t)left);
+  const int32_t b = block_table[(int64_t)r * bt_stride + k];
+  if (v > 0 && (b < 0 || (int64_t)b >= num_blocks)) {
+    if (error_flags) atomicOr(error_flags, KVCK_FLAG_BAD_BLOCK_ID);
+    v = 0;
+  }
+  PosRecord rec;
+  rec.t0 = t0;
+  rec.out_idx = idx;
+  rec.block = b;
+  rec.valid = v;
+  rec.pad = 0;
+  recs[p0 + k] = rec;
+}
+
+// ----------------------------------------------------------------- main pass
+//
+// Task = (cache, listed position), one wavefront each; waves stride over the
+// tasks cache-major, so the waves resident at any time read one layer's pool.
+//
+// Lane table: a row group is up to `rows_per_group` consecutive slots of one
+// (plane, head); its rows hold rows_per_group*chunks_per_row chunks of CHUNK
+// bytes, and lane l owns chunks l, l+64, .., l+64(S-1): slot row[s], byte
+// offset off[s] inside the group, and piece term urel[s] = 2*(row*P + q),
+// q the chunk's first piece inside its plane row.  The same table serves every
+// plane, head, cache and position, so the inner loop only adds offsets.
+//
+// For a chunk of pieces xa (piece q) and xb (piece q+1) of token t, plane pl,
+// head h:  xa*m*u + xb*m*(u + 2) = m*((xa + xb)*u + 2*xb),  u = 2(tP + q) + 1.
+template <int CHUNK, int S, int HU>
+__global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs a) {
+  using V = typename ChunkType<CHUNK>::T;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  const int64_t n_items = (int64_t)*a.n_items;
+  const int64_t total = n_items * a.num_caches;
+  if (wave >= total) return;
+
+  const uint64_t P = (uint64_t)a.pieces;
+  const int cpr = a.chunks_per_row;
+  const int rg = a.rows_per_group;
+  int row[S];
+  uint32_t off[S];
+  uint32_t urel[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int f = lane + kWave * s;
+    const int r = f / cpr;
+    const int c = f - r * cpr;
+    row[s] = r < rg ? r : 0x7fffffff;
+    off[s] = (uint32_t)((int64_t)r * a.slot_stride + (int64_t)c * CHUNK);
+    urel[s] = (uint32_t)(2u * (uint32_t)r * (uint32_t)P + (uint32_t)(CHUNK / 4) * (uint32_t)c);
+  }
+  const uint64_t plane_term = 2ull * (P / (uint64_t)a.planes);
+
+  for (int64_t task = wave; task < total; task += nwaves) {
+    const int64_t cache = task / n_items;
+    const int64_t item = task - cache * n_items;
+    const PosRecord* rp = a.recs + item;
+    // the record is the same for the whole wave
+    const int32_t v = __builtin_amdgcn_readfirstlane(rp->valid);
+    const int32_t blk = __builtin_amdgcn_readfirstlane(rp->block);
+    const uint64_t t0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(rp->t0 >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)rp->t0);
+    const int64_t out_idx = rp->out_idx;
+    uint64_t acc = 0;
+    if (v > 0) {
+      const uint8_t* pb = a.base[cache] + (int64_t)blk * a.block_stride;
+      const uint32_t mb = a.mbase[cache];
+      for (int g0 = 0; g0 < v; g0 += rg) {
+        const int rows = min(rg, v - g0);
+        const uint8_t* gbase = pb + (int64_t)g0 * a.slot_stride;
+        const uint64_t ug = 2ull * (t0 + (uint64_t)g0) * P + 1ull;
+        uint32_t voff[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) voff[s] = row[s] < rows ? off[s] : kOOB;
+        for (int pl = 0; pl < a.planes; ++pl) {
+          const uint8_t* pbase = gbase + (int64_t)pl * a.plane_stride;
+          const uint64_t up = ug + (uint64_t)pl * plane_term;
+          uint64_t u[S];
+#pragma unroll
+          for (int s = 0; s < S; ++s) u[s] = up + urel[s];
+          for (int h0 = 0; h0 < a.heads; h0 += HU) {
+            V x[HU][S];
+#pragma unroll
+            for (int h = 0; h < HU; ++h) {
+              const uint32_t hmask = h0 + h < a.heads ? 0u : kOOB;
+              const __amdgpu_buffer_rsrc_t rs = make_rsrc(pbase + (int64_t)(h0 + h) * a.head_stride);
+#pragma unroll
+              for (int s = 0; s < S; ++s) x[h][s] = load_chunk<CHUNK>(rs, voff[s] | hmask);
+            }
+#pragma unroll
+            for (int h = 0; h < HU; ++h) {
+              uint64_t sh = 0;
+#pragma unroll
+              for (int s = 0; s < S; ++s) {
+                const uint64_t xa = (uint64_t)x[h][s].x | ((uint64_t)x[h][s].y << 32);
+                if constexpr (CHUNK == 16) {
+                  const uint64_t xb = (uint64_t)x[h][s].z | ((uint64_t)x[h][s].w << 32);
+                  sh += (xa + xb) * u[s] + (xb << 1);
+                } else {
+                  sh += xa * u[s];
+                }
+              }
+              acc += sh * (uint64_t)(mb + 2u * (uint32_t)(h0 + h));
+            }
+          }
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      if (a.direct) {
+        uint64_t* o = a.out + out_idx;
+        *o = a.accumulate ? *o + acc : acc;
+      } else {
+        a.partials[(int64_t)(a.cache_offset + cache) * a.max_items + item] = acc;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- second pass
+
+__global__ __launch_bounds__(256) void reduce_kernel(const uint64_t* __restrict__ partials, int64_t stride,
+                                                     int32_t splits, const uint32_t* __restrict__ n_items,
+                                                     int64_t n_fixed, const PosRecord* __restrict__ recs,
+                                                     uint64_t* __restrict__ out, int32_t accumulate) {
+  const int64_t n = n_items ? (int64_t)*n_items : n_fixed;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    uint64_t s = 0;
+    for (int32_t sp = 0; sp < splits; ++sp) s += partials[(int64_t)sp * stride + i];
+    const int64_t o = recs ? recs[i].out_idx : i;
+    out[o] = accumulate ? out[o] + s : s;
+  }
+}
+
+template <int CHUNK, int S>
+constexpr auto pick_kernel() {
+  return &blocks_kernel<CHUNK, S, (16 / S > 0 ? 16 / S : 1)>;
+}
+
+using BlocksFn = void (*)(const BlocksArgs);
+
+BlocksFn blocks_fn(const BlocksShape& shp) {
+  if (shp.chunk == 16) {
+    switch (shp.slots) {
+      case 1: return pick_kernel<16, 1>();
+      case 2: return pick_kernel<16, 2>();
+      case 4: return pick_kernel<16, 4>();
+      case 8: return pick_kernel<16, 8>();
+      case 16: return pick_kernel<16, 16>();
+    }
+  } else {
+    switch (shp.slots) {
+      case 1: return pick_kernel<8, 1>();
+      case 2: return pick_kernel<8, 2>();
+      case 4: return pick_kernel<8, 4>();
+      case 8: return pick_kernel<8, 8>();
+      case 16: return pick_kernel<8, 16>();
+    }
+  }
+  return nullptr;
+}
+
+int device_cus(int device) {
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
+
+}  // namespace
+
+hipError_t launch_plan(const int32_t* block_table, int64_t bt_stride, const int32_t* nbpr,
+                       const int64_t* start_pos, const int64_t* num_tokens, int32_t num_reqs,
+                       int32_t max_blocks, int32_t block_size, int64_t num_blocks, void* workspace,
+                       uint32_t* error_flags, hipStream_t stream) {
+  const BlocksWorkspace w = BlocksWorkspace::make(1, num_reqs, max_blocks);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint32_t* n_items = reinterpret_cast<uint32_t*>(ws);
+  int32_t* prefix = reinterpret_cast<int32_t*>(ws + w.prefix_off);
+  PosRecord* recs = reinterpret_cast<PosRecord*>(ws + w.recs_off);
+  const int64_t max_start = INT64_MAX / block_size - max_blocks;
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, nbpr, start_pos, num_reqs, max_blocks,
+                     max_start, prefix, n_items, error_flags);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t items = (int64_t)num_reqs * max_blocks;
+  const int64_t grid = (items + 255) / 256;
+  hipLaunchKernelGGL(plan_fill_kernel, dim3((unsigned)grid), dim3(256), 0, stream, block_table, bt_stride,
+                     start_pos, num_tokens, num_reqs, max_blocks, block_size, num_blocks, prefix, recs,
+                     error_flags);
+  return hipGetLastError();
+}
+
+int blocks_grid(const BlocksShape& shp, int device, int64_t max_tasks) {
+  BlocksFn fn = blocks_fn(shp);
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kBlockThreads,
+                                                   0) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 2;
+  const int64_t waves_per_block = kBlockThreads / kWave;
+  const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
+  const int64_t cap = (int64_t)per_cu * device_cus(device);
+  return (int)(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
+hipError_t launch_blocks(const BlocksArgs& a, const BlocksShape& shp, int grid, hipStream_t stream) {
+  BlocksFn fn = blocks_fn(shp);
+  if (!fn) return hipErrorInvalidValue;
+  void* args[] = {const_cast<BlocksArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(kBlockThreads), args, 0, stream);
+}
+
+hipError_t launch_reduce(const uint64_t* partials, int64_t stride, int32_t splits, const uint32_t* n_items,
+                         int64_t n_fixed, const PosRecord* recs, uint64_t* out, int32_t accumulate,
+                         hipStream_t stream) {
+  int64_t grid = (stride + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream, partials, stride, splits, n_items,
+                     n_fixed, recs, out, accumulate);
+  return hipGetLastError();
+}
+
+}  // namespace kvck

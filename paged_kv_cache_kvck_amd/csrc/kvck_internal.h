@@ -1,0 +1,103 @@
+// Internal declarations of libkvck: kernel argument blocks, workspace layout
+// and launchers.  Not part of the ABI (see include/kvck.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvck.h"
+
+namespace kvck {
+
+constexpr int kWave = 64;
+constexpr int kBlockThreads = 256;          // 4 independent waves per workgroup
+constexpr int kCachesPerLaunch = 64;        // caches carried in one argument block
+constexpr int kLayersPerStatesLaunch = 32;  // Mamba layers carried in one argument block
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// One listed block position, built on the device from the request arrays.
+struct alignas(16) PosRecord {
+  int64_t t0;       // first token the position holds: pos * block_size
+  int64_t out_idx;  // r * max_blocks + k
+  int32_t block;    // physical block id
+  int32_t valid;    // slots to checksum (0: none, or a bad id)
+  int64_t pad;
+};
+static_assert(sizeof(PosRecord) == 32, "record is 32 bytes");
+
+// Workspace of kvck_checksum_blocks:
+//   [header 256 B: uint32 n_items] [prefix int32 x (R+1)] [records] [partials]
+struct BlocksWorkspace {
+  size_t prefix_off, recs_off, partials_off, total;
+  static BlocksWorkspace make(int32_t num_caches, int32_t num_reqs, int32_t max_blocks) {
+    BlocksWorkspace w;
+    const size_t items = (size_t)num_reqs * (size_t)max_blocks;
+    w.prefix_off = kAlign;
+    w.recs_off = w.prefix_off + align_up(sizeof(int32_t) * ((size_t)num_reqs + 1));
+    w.partials_off = w.recs_off + align_up(sizeof(PosRecord) * items);
+    w.total = w.partials_off + (num_caches > 1 ? align_up(sizeof(uint64_t) * items * (size_t)num_caches) : 0);
+    return w;
+  }
+};
+
+// Per-launch arguments of the paged K/V kernel (passed by value).
+struct BlocksArgs {
+  int64_t plane_stride, block_stride, slot_stride, head_stride;  // bytes
+  const PosRecord* recs;
+  const uint32_t* n_items;   // device: listed positions
+  uint64_t* partials;        // [num_caches][max_items] when not direct
+  uint64_t* out;
+  int64_t max_items;
+  int32_t planes, heads, row_bytes, pieces;  // pieces = P per token
+  int32_t rows_per_group;                    // rows covered by one lane table
+  int32_t chunks_per_row;
+  int32_t num_caches;                        // caches in this launch
+  int32_t cache_offset;                      // index of the first cache of this launch
+  int32_t direct;                            // write out[] directly (single cache overall)
+  int32_t accumulate;
+  const uint8_t* base[kCachesPerLaunch];     // pool base + head_begin*head_stride
+  uint32_t mbase[kCachesPerLaunch];          // 2*(layer*H + global_head_base) + 1
+};
+
+struct StatesArgs {
+  int64_t slot_stride[KVCK_MAX_STATES_PER_LAYER];
+  int64_t row_stride[KVCK_MAX_STATES_PER_LAYER];
+  int32_t row_chunks[KVCK_MAX_STATES_PER_LAYER];  // 16-byte chunks per row
+  int32_t elem_bytes[KVCK_MAX_STATES_PER_LAYER];
+  int32_t elem_off[KVCK_MAX_STATES_PER_LAYER];    // element number of the row's first element
+  const int32_t* slot_ids;
+  uint64_t* partials;  // [splits][num_reqs]
+  uint64_t* out;
+  uint32_t* error_flags;
+  int32_t nstates, num_layers, num_slots, num_reqs;
+  int32_t row_begin, row_count, rows_per_task, groups_per_layer;
+  int32_t split_offset;  // split index of this launch's first (layer, group)
+  int32_t direct, accumulate;
+  const uint8_t* ptr[kLayersPerStatesLaunch][KVCK_MAX_STATES_PER_LAYER];
+  uint32_t mbase[kLayersPerStatesLaunch];  // 2*(layer*H + global_row_base) + 1
+};
+
+// Kernel shape chosen on the host for one kvck_checksum_blocks call.
+struct BlocksShape {
+  int chunk;     // 16 or 8 bytes per lane load
+  int slots;     // lane-table slots S (1, 2, 4, 8, 16)
+  int rows_per_group;
+};
+
+// launchers (return hipSuccess or the first HIP error)
+hipError_t launch_plan(const int32_t* block_table, int64_t bt_stride, const int32_t* nbpr,
+                       const int64_t* start_pos, const int64_t* num_tokens, int32_t num_reqs,
+                       int32_t max_blocks, int32_t block_size, int64_t num_blocks, void* workspace,
+                       uint32_t* error_flags, hipStream_t stream);
+hipError_t launch_blocks(const BlocksArgs& a, const BlocksShape& shp, int grid, hipStream_t stream);
+int blocks_grid(const BlocksShape& shp, int device, int64_t max_tasks);
+hipError_t launch_reduce(const uint64_t* partials, int64_t stride, int32_t splits, const uint32_t* n_items,
+                         int64_t n_fixed, const PosRecord* recs, uint64_t* out, int32_t accumulate,
+                         hipStream_t stream);
+hipError_t launch_states(const StatesArgs& a, int grid, hipStream_t stream);
+int states_grid(int device, int64_t tasks);
+
+}  // namespace kvck

@@ -1,0 +1,128 @@
+// Mamba running-state checksums on gfx950.
+//
+// Mamba paragraph of the vLLM API page
+// "vllm.distributed.kv_transfer.kv_checksum.checksum": a Mamba group's block is
+// the request's running state at position 0, and a layer with a known TP split
+// has one slice per global row of its states, whose pieces are its 2- or 4-byte
+// elements read unsigned.  Slice g = row g of every state of the layer,
+// concatenated in state order, elements numbered e = 0, 1, ..:
+//   s = sum_e x_e (2e + 1),  c = sum_{layer, g} m s,  m = 2 (layer*65536 + g) + 1.
+//
+// Task = (layer, group of rows, request), one wavefront each.  Lanes stream the
+// row's 16-byte chunks; a chunk of 4-byte elements x0..x3 starting at element e
+// adds sum_i x_i (2(e+i) + 1); a chunk of 2-byte elements x0..x7 adds
+// u*X + 2*Y with u = 2e + 1, X = sum x_i, Y = sum i*x_i (both fit 32 bits).
+#include "kvck_internal.h"
+
+namespace kvck {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 load16(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t chunk_u32(u32x4 x, uint32_t u) {
+  return (uint64_t)x.x * u + (uint64_t)x.y * (u + 2u) + (uint64_t)x.z * (u + 4u) + (uint64_t)x.w * (u + 6u);
+}
+
+__device__ __forceinline__ uint64_t chunk_u16(u32x4 x, uint32_t u) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t X = 0, Y = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = w[i] & 0xffffu, hi = w[i] >> 16;
+    X += lo + hi;
+    Y += (2u * i) * lo + (2u * i + 1u) * hi;
+  }
+  return (uint64_t)X * u + 2ull * Y;
+}
+
+constexpr int kUnroll = 8;
+
+__global__ __launch_bounds__(kBlockThreads) void states_kernel(const StatesArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  const int64_t splits = (int64_t)a.num_layers * a.groups_per_layer;
+  const int64_t total = splits * a.num_reqs;
+  for (int64_t task = wave; task < total; task += nwaves) {
+    const int32_t split = (int32_t)(task / a.num_reqs);
+    const int32_t r = (int32_t)(task - (int64_t)split * a.num_reqs);
+    const int32_t l = split / a.groups_per_layer;
+    const int32_t grp = split - l * a.groups_per_layer;
+    const int32_t slot = a.slot_ids[r];
+    uint64_t acc = 0;
+    if (slot < 0 || slot >= a.num_slots) {
+      if (lane == 0 && a.error_flags) atomicOr(a.error_flags, KVCK_FLAG_BAD_STATE_SLOT);
+    } else {
+      const int32_t g_begin = grp * a.rows_per_task;
+      const int32_t g_end = min(a.row_count, g_begin + a.rows_per_task);
+      for (int32_t g = g_begin; g < g_end; ++g) {
+        uint64_t s = 0;
+        for (int st = 0; st < a.nstates; ++st) {
+          const uint8_t* rowp = a.ptr[l][st] + (int64_t)slot * a.slot_stride[st] +
+                                (int64_t)(a.row_begin + g) * a.row_stride[st];
+          const int32_t nch = a.row_chunks[st];
+          const bool wide = a.elem_bytes[st] == 4;
+          const uint32_t e0 = (uint32_t)a.elem_off[st];
+          const uint32_t per_chunk = wide ? 4u : 8u;
+          for (int32_t c0 = 0; c0 < nch; c0 += kWave * kUnroll) {
+            u32x4 x[kUnroll];
+#pragma unroll
+            for (int k = 0; k < kUnroll; ++k) {
+              const int32_t c = c0 + k * kWave + lane;
+              x[k] = c < nch ? load16(rowp + (int64_t)c * 16) : u32x4(0);
+            }
+#pragma unroll
+            for (int k = 0; k < kUnroll; ++k) {
+              const uint32_t c = (uint32_t)(c0 + k * kWave + lane);
+              const uint32_t u = 2u * (e0 + c * per_chunk) + 1u;
+              s += wide ? chunk_u32(x[k], u) : chunk_u16(x[k], u);
+            }
+          }
+        }
+        acc += s * (uint64_t)(a.mbase[l] + 2u * (uint32_t)g);
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      if (a.direct) {
+        a.out[r] = a.accumulate ? a.out[r] + acc : acc;
+      } else {
+        a.partials[(int64_t)(a.split_offset + split) * a.num_reqs + r] = acc;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int states_grid(int device, int64_t tasks) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&states_kernel),
+                                                   kBlockThreads, 0) != hipSuccess ||
+      per_cu <= 0)
+    per_cu = 2;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int64_t need = (tasks + (kBlockThreads / kWave) - 1) / (kBlockThreads / kWave);
+  const int64_t cap = (int64_t)per_cu * cus;
+  return (int)(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
+hipError_t launch_states(const StatesArgs& a, int grid, hipStream_t stream) {
+  void* args[] = {const_cast<StatesArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&states_kernel), dim3(grid), dim3(kBlockThreads), args, 0,
+                         stream);
+}
+
+}  // namespace kvck

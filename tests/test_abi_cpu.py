@@ -1,0 +1,143 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/kvck.h
+declares, and rejects bad arguments before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import paged_kv_cache_kvck_amd as kvck
+from paged_kv_cache_kvck_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000001000  # a device address that validation never dereferences
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "kvck.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:kvck_status|size_t|const char\s*\*|int32_t)\s+(kvck_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = kvck.load_library()
+    decl = header_functions()
+    assert len(decl) == 9
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert sorted(B.EXPORTS) == decl
+    assert kvck.kvck_abi_version() == 1
+    assert kvck.kvck_status_string(-4) == "KVCK_ERR_WORKSPACE"
+    assert kvck.kvck_status_string(7) == "KVCK_UNKNOWN_STATUS"
+
+
+def test_workspace_sizes():
+    assert kvck.kvck_blocks_workspace_bytes(0, 1, 1) == 0
+    one = kvck.kvck_blocks_workspace_bytes(1, 256, 512)
+    many = kvck.kvck_blocks_workspace_bytes(32, 256, 512)
+    assert one % 256 == 0 and many % 256 == 0
+    assert many - one >= 32 * 256 * 512 * 8
+    assert kvck.kvck_states_workspace_bytes(24, 64, 128) >= 24 * 8 * 128 * 8
+
+
+def _layout(**kw):
+    L = B.kvck_kv_layout()
+    d = dict(planes=2, block_size=16, num_heads=8, row_bytes=256, num_blocks=100, plane_stride=100 * 32768,
+             block_stride=32768, slot_stride=256, head_stride=4096)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(L, k, v)
+    return L
+
+
+def _call(L=None, ncaches=2, layers=(0, 1), bases=(0, 0), head_begin=0, head_count=8, num_reqs=4, max_blocks=8,
+          bt_stride=8, ws_bytes=None, ptr=FAKE, out=FAKE, ws=FAKE):
+    lib = kvck.load_library()
+    L = L or _layout()
+    ptrs = (ctypes.c_void_p * ncaches)(*([ptr] * ncaches))
+    ly = (ctypes.c_int32 * ncaches)(*layers)
+    bs = (ctypes.c_int32 * ncaches)(*bases)
+    need = lib.kvck_blocks_workspace_bytes(ncaches, num_reqs, max_blocks)
+    return lib.kvck_checksum_blocks(ctypes.byref(L), ptrs, ly, bs, ncaches, head_begin, head_count, FAKE, bt_stride,
+                                    FAKE, FAKE, FAKE, num_reqs, max_blocks, out, 0, ws,
+                                    need if ws_bytes is None else ws_bytes, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=_layout(planes=3)), -1),
+    (dict(L=_layout(block_size=0)), -1),
+    (dict(L=_layout(row_bytes=12)), -2),            # not whole 8-byte pieces
+    (dict(L=_layout(slot_stride=-256)), -1),
+    (dict(head_count=0), -1),
+    (dict(head_begin=7, head_count=2), -1),
+    (dict(bases=(0, 65535)), -2),                    # more than MAX_KV_HEADS_PER_LAYER heads
+    (dict(layers=(0, 40000)), -2),                   # layer number too large for a 32-bit factor
+    (dict(layers=(0, -1)), -1),
+    (dict(ptr=0), -1),
+    (dict(out=0), -1),
+    (dict(bt_stride=4), -1),
+    (dict(ws_bytes=64), -4),
+    (dict(ws=FAKE + 8), -4),                          # workspace not 256-byte aligned
+    (dict(ptr=FAKE + 4, L=_layout(row_bytes=8, slot_stride=8, head_stride=128, block_stride=2048)), -3),
+    (dict(L=_layout(row_bytes=16 * 1024 * 2)), -2),  # a row longer than one lane table covers
+])
+def test_blocks_rejects_before_launch(kw, status):
+    assert _call(**kw) == status
+
+
+def test_blocks_zero_requests_is_a_no_op():
+    assert _call(num_reqs=0) == 0
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU answer")
+def test_valid_call_without_gpu_reports_no_device():
+    assert _call() == -6
+    assert kvck.kvck_platform_supported() is False
+
+
+def test_states_rejects_before_launch():
+    lib = kvck.load_library()
+    D = (B.kvck_state_desc * 2)()
+    D[0].slot_stride, D[0].row_stride, D[0].row_elems, D[0].elem_bytes = 64 * 8192, 8192, 2048, 4
+    D[1].slot_stride, D[1].row_stride, D[1].row_elems, D[1].elem_bytes = 64 * 2048, 2048, 1024, 2
+    ptrs = (ctypes.c_void_p * 4)(*([FAKE] * 4))
+    ly = (ctypes.c_int32 * 2)(1, 3)
+    base = (ctypes.c_int32 * 2)(0, 0)
+
+    def call(nstates=2, elem=None, rows=(0, 64), nrows=64, ws=FAKE, ws_bytes=1 << 20, num_reqs=8):
+        if elem:
+            D[1].elem_bytes = elem
+        try:
+            return lib.kvck_checksum_states(D, nstates, ptrs, ly, base, 2, 160, nrows, rows[0], rows[1], FAKE,
+                                            num_reqs, FAKE, 0, ws, ws_bytes, None, None)
+        finally:
+            D[1].elem_bytes = 2
+
+    assert call(elem=1) == -2
+    assert call(elem=8) == -2
+    assert call(nstates=5) == -2
+    assert call(rows=(60, 8)) == -1
+    assert call(ws_bytes=8) == -4
+    assert call(num_reqs=0) == 0
+    if not torch.cuda.is_available():
+        assert call() == -6
+
+
+def test_binding_argument_checks():
+    pools = [torch.zeros((2, 4, 16, 2, 64), dtype=torch.bfloat16)]
+    L = kvck.kv_layout(pools[0], "NHD")
+    assert (L.planes, L.block_size, L.num_heads, L.row_bytes, L.num_blocks) == (2, 16, 2, 128, 4)
+    assert (L.plane_stride, L.block_stride, L.slot_stride, L.head_stride) == (4 * 4096, 4096, 256, 128)
+    H = kvck.kv_layout(pools[0].permute(0, 1, 3, 2, 4), "HND")
+    assert (H.block_size, H.num_heads, H.slot_stride, H.head_stride) == (16, 2, 256, 128)
+    M = kvck.kv_layout(torch.zeros((5, 64, 576), dtype=torch.bfloat16), "MLA")
+    assert (M.planes, M.num_heads, M.row_bytes, M.block_stride) == (1, 1, 1152, 64 * 1152)
+    with pytest.raises(ValueError):
+        kvck.kv_layout(pools[0].transpose(3, 4), "NHD")
+    bt = torch.zeros((1, 4), dtype=torch.int64)
+    with pytest.raises(ValueError):
+        kvck.kvck_checksum_blocks(pools, "NHD", [0], bt, torch.zeros(1, dtype=torch.int32),
+                                  torch.zeros(1, dtype=torch.int64), torch.zeros(1, dtype=torch.int64))

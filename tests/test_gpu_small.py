@@ -1,0 +1,234 @@
+"""HIP path == oracle, element by element, on small seeded inputs (GPU).
+
+Sizes the oracle finishes in seconds that still span several lane tables,
+several head batches and ragged tails; plus edge cases: empty batches,
+positions past the last token, bad block ids and requests, accumulate,
+several launches of caches, the 8-byte load path, streams, determinism.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_kvck_amd as kvck
+from paged_kv_cache_kvck_amd import workloads as wl
+from gpu_helpers import (DEV, SENTINEL, assert_match, assert_unlisted_untouched, gpu_blocks, log, oracle_at,
+                         to_device_bits)
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, layout, elem, layers, heads, head_size, block_size, lengths, extra
+    ("nhd_bf16", "NHD", "bf16", [0, 1, 2], 2, 64, 16, [50, 17, 33, 1, 64], None),
+    ("hnd_bf16_d128", "HND", "bf16", [0, 5, 31], 8, 128, 16, [77, 130, 16, 5], None),
+    ("nhd_fp16_12h", "NHD", "fp16", [3, 4], 12, 64, 16, [100, 31, 2], [0, 2, 1]),
+    ("hnd_fp16_12h", "HND", "fp16", [7], 12, 64, 16, [100, 31, 2], None),
+    ("nhd_bs64", "NHD", "fp16", [0, 1], 12, 64, 64, [300, 65, 63], None),
+    ("nhd_fp8", "NHD", "fp8", [0, 11], 12, 64, 16, [90, 7], None),
+    ("nhd_fp8_bs64", "NHD", "fp8", [2], 12, 64, 64, [200, 64], None),
+    ("mla_bs64", "MLA", "bf16", [0, 1, 60], 1, 576, 64, [130, 64, 3], None),
+    ("mla_bs16", "MLA", "bf16", [9, 10], 1, 576, 16, [70, 16], None),
+    ("hnd_bs1", "HND", "bf16", [1, 2], 3, 16, 1, [5, 2], None),
+    ("nhd_bs3_odd", "NHD", "fp32", [4], 5, 12, 3, [10, 4, 9], None),
+    ("nhd_8byte_rows", "NHD", "bf16", [0, 3], 3, 4, 4, [13, 6], None),
+    ("hnd_big_heads", "HND", "bf16", [2], 32, 128, 16, [40], None),
+]
+
+
+def _host_case(seed, layout, elem, layers, nh, d, bs, lengths, extra, start=None):
+    rng = np.random.default_rng(seed)
+    req, nb = wl.page_requests(rng, lengths, bs, start_pos=start, extra_blocks=extra, spare_frac=0.3)
+    shape = wl.pool_shape(layout, nb, bs, nh, d)
+    pools = [wl.host_random_bits(rng, shape, elem) for _ in layers]
+    return req, pools
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_parity_small(case):
+    name, layout, elem, layers, nh, d, bs, lengths, extra = case
+    log(f"[parity_small] {name}")
+    req, hpools = _host_case(abs(hash(name)) % 1000, layout, elem, layers, nh, d, bs, lengths, extra)
+    dpools = [to_device_bits(p) for p in hpools]
+    got = gpu_blocks(dpools, layout, layers, req)
+    want = oracle.checksum_blocks(hpools, layout, layers, [0] * len(layers), req.block_table, req.num_blocks,
+                                  req.start_pos, req.num_tokens)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k]), (name, r, k)
+    assert_unlisted_untouched(got, req)
+
+
+def test_tiny_config_golden():
+    """The tiny workload on the GPU equals the oracle's committed values."""
+    import json
+    import os
+    w = wl.tiny()
+    log("[tiny] config 1")
+    pools = [to_device_bits(p) for p in w.host_pools()]
+    got = gpu_blocks(pools, w.layout, w.layer_numbers, w.req)
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "tiny_oracle.json")) as f:
+        gold = json.load(f)
+    assert [str(int(x)) for x in got[0, :4]] == gold["checksums"]
+
+
+def test_start_pos_heads_subset_and_global_base():
+    log("[heads subset]")
+    rng = np.random.default_rng(5)
+    req, nb = wl.page_requests(rng, [90, 40, 200], 16, start_pos=[2, 0, 5], extra_blocks=[1, 0, 2], spare_frac=0.2)
+    pools_h = [wl.host_random_bits(rng, wl.pool_shape("HND", nb, 16, 8, 128), "bf16") for _ in range(3)]
+    pools = [to_device_bits(p) for p in pools_h]
+    layers = [4, 9, 30000]
+    bases = [16, 18, 65534 - 2]
+    got = gpu_blocks(pools, "HND", layers, req, bases=bases, head_begin=3, head_count=2)
+    want = oracle.checksum_blocks(pools_h, "HND", layers, bases, req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens, head_begin=3, head_count=2)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k])
+
+
+def test_tp_shards_sum_and_pp_split_sum():
+    log("[tp/pp partial sums]")
+    rng = np.random.default_rng(6)
+    req, nb = wl.page_requests(rng, [300, 77, 16], 16, spare_frac=0.1)
+    pools = [to_device_bits(wl.host_random_bits(rng, wl.pool_shape("HND", nb, 16, 8, 128), "bf16"))
+             for _ in range(4)]
+    layers = [0, 1, 2, 3]
+    full = gpu_blocks(pools, "HND", layers, req)
+    with np.errstate(over="ignore"):
+        tot = np.zeros_like(full)
+        for h in range(0, 8, 2):
+            tot += gpu_blocks(pools, "HND", layers, req, bases=[h] * 4, head_begin=h, head_count=2)
+        pp = gpu_blocks(pools[:1], "HND", layers[:1], req) + gpu_blocks(pools[1:], "HND", layers[1:], req)
+    for r, k in req.listed():
+        assert tot[r, k] == full[r, k] and pp[r, k] == full[r, k]
+
+
+def test_accumulate_adds_mod_2_64():
+    log("[accumulate]")
+    rng = np.random.default_rng(7)
+    req, nb = wl.page_requests(rng, [64, 100], 16, spare_frac=0.1)
+    pools = [to_device_bits(wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 16, 2, 64), "bf16"))
+             for _ in range(2)]
+    base = gpu_blocks(pools, "NHD", [0, 1], req)
+    init = rng.integers(0, 2**63, size=base.shape, dtype=np.int64).view(np.uint64) * np.uint64(2) + np.uint64(1)
+    out = torch.from_numpy(init.view(np.int64).copy()).to(DEV).view(torch.uint64)
+    got = gpu_blocks(pools, "NHD", [0, 1], req, out=out, accumulate=True)
+    with np.errstate(over="ignore"):
+        for r, k in req.listed():
+            assert got[r, k] == init[r, k] + base[r, k]
+    # a single cache takes the direct-write path
+    one = gpu_blocks(pools[:1], "NHD", [0], req)
+    out = torch.from_numpy(init.view(np.int64).copy()).to(DEV).view(torch.uint64)
+    got = gpu_blocks(pools[:1], "NHD", [0], req, out=out, accumulate=True)
+    with np.errstate(over="ignore"):
+        for r, k in req.listed():
+            assert got[r, k] == init[r, k] + one[r, k]
+
+
+def test_many_caches_several_launches():
+    """More caches than one argument block carries (several main launches)."""
+    log("[70 caches]")
+    rng = np.random.default_rng(8)
+    req, nb = wl.page_requests(rng, [40, 9], 16, spare_frac=0.5)
+    hp = [wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 16, 2, 16), "bf16") for _ in range(70)]
+    layers = list(range(100, 170))
+    got = gpu_blocks([to_device_bits(p) for p in hp], "NHD", layers, req)
+    want = oracle.checksum_blocks(hp, "NHD", layers, [0] * 70, req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k])
+
+
+def test_empty_and_past_end_positions():
+    log("[empty]")
+    rng = np.random.default_rng(9)
+    # a request with no listed positions, one with only positions past its tokens
+    req, nb = wl.page_requests(rng, [0, 5, 40], 16, start_pos=[0, 1, 0], extra_blocks=[0, 2, 1], spare_frac=0.5)
+    hp = [wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 16, 2, 64), "bf16")]
+    got = gpu_blocks([to_device_bits(hp[0])], "NHD", [0], req)
+    want = oracle.checksum_blocks(hp, "NHD", [0], [0], req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k])
+    assert_unlisted_untouched(got, req)
+    # zero requests: nothing launched, nothing written
+    bt = torch.zeros((0, 4), dtype=torch.int32, device=DEV)
+    e32 = torch.zeros(0, dtype=torch.int32, device=DEV)
+    e64 = torch.zeros(0, dtype=torch.int64, device=DEV)
+    out = kvck.kvck_checksum_blocks([to_device_bits(hp[0])], "NHD", [0], bt, e32, e64, e64)
+    assert out.numel() == 0
+
+
+def test_bad_block_id_and_bad_request_flagged():
+    log("[flags]")
+    rng = np.random.default_rng(10)
+    req, nb = wl.page_requests(rng, [40, 40], 16, spare_frac=0.5)
+    pool = to_device_bits(wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 16, 2, 64), "bf16"))
+    bad = wl.Requests(16, req.num_tokens, req.start_pos, req.num_blocks, req.block_table.copy())
+    bad.block_table[0, 1] = nb + 5
+    with pytest.raises(kvck.KvckDeviceError) as ei:
+        gpu_blocks([pool], "NHD", [0], bad)
+    assert ei.value.flags & kvck.KVCK_FLAG_BAD_BLOCK_ID
+    bad2 = wl.Requests(16, req.num_tokens, req.start_pos.copy(), req.num_blocks, req.block_table)
+    bad2.start_pos[1] = -3
+    with pytest.raises(kvck.KvckDeviceError) as ei:
+        gpu_blocks([pool], "NHD", [0], bad2)
+    assert ei.value.flags & kvck.KVCK_FLAG_BAD_REQUEST
+    # an invalid id where no slot is valid is never read and not an error
+    past = wl.Requests(16, np.array([10, 40]), req.start_pos, np.array([2, 3], np.int32), req.block_table.copy())
+    past.block_table[0, 1] = -1
+    got = gpu_blocks([pool], "NHD", [0], past)
+    assert got[0, 1] == 0
+
+
+def test_host_rejects_before_launch():
+    log("[host errors]")
+    rng = np.random.default_rng(11)
+    req, nb = wl.page_requests(rng, [20], 16, spare_frac=0.5)
+    pool = to_device_bits(wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 16, 2, 64), "bf16"))
+    with pytest.raises(kvck.KvckError) as ei:
+        gpu_blocks([pool], "NHD", [0], req, bases=[65535])
+    assert ei.value.status == -2
+    with pytest.raises(kvck.KvckError) as ei:
+        gpu_blocks([pool], "NHD", [40000], req)
+    assert ei.value.status == -2
+    with pytest.raises(kvck.KvckError) as ei:
+        gpu_blocks([pool], "NHD", [0], req, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert ei.value.status == -4
+
+
+def test_determinism_and_streams():
+    log("[determinism]")
+    rng = np.random.default_rng(12)
+    req, nb = wl.page_requests(rng, list(rng.integers(1, 600, 40)), 16, spare_frac=0.1)
+    pools = [to_device_bits(wl.host_random_bits(rng, wl.pool_shape("HND", nb, 16, 8, 128), "bf16"))
+             for _ in range(5)]
+    a = gpu_blocks(pools, "HND", list(range(5)), req)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = gpu_blocks(pools, "HND", list(range(5)), req, stream=s)
+    ws = torch.empty(kvck.kvck_blocks_workspace_bytes(5, req.num_reqs, req.max_blocks), dtype=torch.uint8,
+                     device=DEV)
+    c = gpu_blocks(pools, "HND", list(range(5)), req, workspace=ws)
+    d = gpu_blocks(pools, "HND", list(range(5)), req, workspace=ws)
+    assert np.array_equal(a, b) and np.array_equal(a, c) and np.array_equal(a, d)
+
+
+def test_states_small_parity():
+    log("[states small]")
+    rng = np.random.default_rng(13)
+    layers = [1, 3, 5]
+    shapes = [(6, 8, 4), (6, 2, 16)]     # rows x (...) : fp32 row 128 B, fp16 row 64 B
+    elems = ["fp32", "fp16"]
+    hs = [[wl.host_random_bits(rng, (9,) + s, e) for s, e in zip(shapes, elems)] for _ in layers]
+    slots = np.array([4, 0, 8, 2], np.int32)
+    ds = [[to_device_bits(a) for a in l] for l in hs]
+    sid = torch.from_numpy(slots).to(DEV)
+    for rb, rc, base in [(0, None, 0), (1, 3, 10), (5, 1, 7)]:
+        got = kvck.kvck_checksum_states(ds, layers, sid, global_row_base=base, row_begin=rb, row_count=rc,
+                                        check=True)
+        want = oracle.checksum_states(hs, layers, [base] * 3, slots, row_begin=rb, row_count=rc)
+        assert np.array_equal(got.cpu().numpy(), want), (rb, rc)
+    bad = torch.tensor([0, 9], dtype=torch.int32, device=DEV)
+    with pytest.raises(kvck.KvckDeviceError):
+        kvck.kvck_checksum_states(ds, layers, bad, check=True)
