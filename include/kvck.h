@@ -126,6 +126,11 @@ typedef struct kvck_kv_layout {
  * Workspace: device, at least kvck_blocks_workspace_bytes(num_caches,
  * num_reqs, max_blocks) bytes, 256-byte aligned; its contents on entry are
  * ignored.
+ *
+ * Schedule: large batches (many tasks per resident wavefront) keep two load
+ * batches in flight and give each task four layers; small ones use one layer
+ * per task at higher occupancy.  The environment variable KVCK_SCHEDULE =
+ * "pipelined" or "simple" forces one of the two; results are bit-identical.
  */
 kvck_status kvck_checksum_blocks(
     const kvck_kv_layout* layout,          /* host */

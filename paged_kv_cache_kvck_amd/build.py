@@ -3,7 +3,9 @@
     python -m paged_kv_cache_kvck_amd.build [--save-temps DIR]
 
 The library is a plain C-ABI shared object (include/kvck.h); the Python
-binding loads it with ctypes, so no torch C++ extension is involved.
+binding loads it with ctypes, so no torch C++ extension is involved.  The
+build also makes ``hbm_read_probe``, a plain streaming-read kernel that
+measures the HBM read bandwidth a trivial kernel reaches.
 """
 
 from __future__ import annotations
@@ -18,6 +20,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libkvck.so")
+PROBE = os.path.join(PKG, "hbm_read_probe")
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are kept out of every kernel (no FP32 math is used
@@ -53,6 +56,11 @@ def build(save_temps: str | None = None, verbose: bool = False) -> str:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True, cwd=cwd)
     os.replace(tmp, LIB)
+    # the plain-read bandwidth probe the benchmark's roofline discussion refers to
+    probe_tmp = PROBE + ".tmp"
+    subprocess.run([hipcc(), *[f for f in HIP_FLAGS if f not in ("-shared", "-fPIC", "-fvisibility=hidden")],
+                    os.path.join(PKG, "probe", "hbm_read_probe.hip"), "-o", probe_tmp], check=True)
+    os.replace(probe_tmp, PROBE)
     return LIB
 
 

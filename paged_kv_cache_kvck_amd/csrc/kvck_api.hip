@@ -1,6 +1,7 @@
 // C ABI of libkvck: argument validation, launch shapes, workspace carving.
 // Every check that can be made on the host is made before the first HIP call,
 // so a rejected call touches no device state.
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -52,7 +53,34 @@ bool choose_shape(int32_t block_size, int32_t row_bytes, int chunk, BlocksShape*
   shp->chunk = chunk;
   shp->slots = s;
   shp->rows_per_group = (int)rg;
+  shp->pipelined = false;
+  shp->caches_per_task = 1;
   return true;
+}
+
+// Schedule: with many tasks per resident wave, keep two unit buffers in
+// flight and let one task cover kPipeCaches caches, so a wave's loads do not
+// drain at every unit or task boundary.  Small batches keep one cache per task
+// and higher occupancy (their run time is dominated by ramp-up and tail).
+// Wide lane tables (S > 4) would need more than half the register file
+// double-buffered and stay unpipelined.
+constexpr int kPipeCaches = 4;
+constexpr int64_t kPipeMinTasksPerWave = 64;
+static_assert(kCachesPerLaunch % kPipeCaches == 0, "launch groups must not straddle launches");
+
+void choose_schedule(BlocksShape* shp, int32_t num_caches, int64_t max_items, int cus) {
+  const int64_t waves = (int64_t)cus * 8;  // resident waves of the pipelined kernel (2 per SIMD)
+  const int64_t tasks = max_items * ((num_caches + kPipeCaches - 1) / kPipeCaches);
+  bool pipe = shp->slots <= 4 && num_caches > 1 && tasks >= kPipeMinTasksPerWave * waves;
+  // KVCK_SCHEDULE=pipelined|simple overrides the choice (results are identical either way)
+  if (const char* force = getenv("KVCK_SCHEDULE")) {
+    if (strcmp(force, "pipelined") == 0) pipe = true;
+    if (strcmp(force, "simple") == 0) pipe = false;
+  }
+  if (pipe) {
+    shp->pipelined = true;
+    shp->caches_per_task = kPipeCaches;
+  }
 }
 
 // Event pairs around main passes while instrumentation is on.
@@ -195,6 +223,11 @@ KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const
   const kvck_status ds = current_device(&dev);
   if (ds != KVCK_OK) return ds;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  choose_schedule(&shp, num_caches, (int64_t)num_reqs * max_blocks, cus);
+  const int32_t lpt = shp.caches_per_task;
+  const int32_t total_groups = (num_caches + lpt - 1) / lpt;
 
   if (launch_plan(block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens, num_reqs,
                   max_blocks, L.block_size, L.num_blocks, workspace, error_flags, st) != hipSuccess)
@@ -219,7 +252,8 @@ KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const
   a.pieces = (int32_t)pieces;
   a.rows_per_group = shp.rows_per_group;
   a.chunks_per_row = L.row_bytes / chunk;
-  a.direct = num_caches == 1;
+  a.caches_per_task = lpt;
+  a.direct = total_groups == 1;
   a.accumulate = accumulate != 0;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   const bool timed = instrument_pair(&ev0, &ev1);
@@ -227,17 +261,17 @@ KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const
   for (int32_t c0 = 0; c0 < num_caches; c0 += kCachesPerLaunch) {
     const int32_t n = num_caches - c0 < kCachesPerLaunch ? num_caches - c0 : kCachesPerLaunch;
     a.num_caches = n;
-    a.cache_offset = c0;
+    a.group_offset = c0 / lpt;
     for (int32_t i = 0; i < n; ++i) {
       a.base[i] = static_cast<const uint8_t*>(cache_ptrs[c0 + i]) + (int64_t)head_begin * L.head_stride;
       a.mbase[i] = (uint32_t)(2 * ((int64_t)layer_numbers[c0 + i] * kH + global_head_base[c0 + i]) + 1);
     }
-    const int grid = blocks_grid(shp, dev, max_items * n);
+    const int grid = blocks_grid(shp, dev, max_items * ((n + lpt - 1) / lpt));
     if (launch_blocks(a, shp, grid, st) != hipSuccess) return KVCK_ERR_HIP;
   }
   if (timed && hipEventRecord(ev1, st) != hipSuccess) return KVCK_ERR_HIP;
-  if (num_caches > 1) {
-    if (launch_reduce(a.partials, max_items, num_caches, a.n_items, 0, a.recs, out, a.accumulate, st) != hipSuccess)
+  if (total_groups > 1) {
+    if (launch_reduce(a.partials, max_items, total_groups, a.n_items, 0, a.recs, out, a.accumulate, st) != hipSuccess)
       return KVCK_ERR_HIP;
   }
   return KVCK_OK;

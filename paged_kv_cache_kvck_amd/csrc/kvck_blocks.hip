@@ -142,8 +142,10 @@ __global__ __launch_bounds__(256) void plan_fill_kernel(
 
 // ----------------------------------------------------------------- main pass
 //
-// Task = (cache, listed position), one wavefront each; waves stride over the
-// tasks cache-major, so the waves resident at any time read one layer's pool.
+// Task = (group of `caches_per_task` caches, listed position), one wavefront
+// each; waves stride over the tasks group-major, so the waves resident at any
+// time read a few layers' pools.  A task's result is one uint64 (a partial
+// over its caches), reduced by the second pass unless the call has one group.
 //
 // Lane table: a row group is up to `rows_per_group` consecutive slots of one
 // (plane, head); its rows hold rows_per_group*chunks_per_row chunks of CHUNK
@@ -152,38 +154,75 @@ __global__ __launch_bounds__(256) void plan_fill_kernel(
 // q the chunk's first piece inside its plane row.  The same table serves every
 // plane, head, cache and position, so the inner loop only adds offsets.
 //
-// For a chunk of pieces xa (piece q) and xb (piece q+1) of token t, plane pl,
-// head h:  xa*m*u + xb*m*(u + 2) = m*((xa + xb)*u + 2*xb),  u = 2(tP + q) + 1.
-template <int CHUNK, int S, int HU>
+// A unit is the loads of one (cache, row group, plane, batch of HU heads):
+// HU*S chunks per lane.  For a chunk of pieces xa (piece q) and xb (piece q+1)
+// of token t, plane pl, head h:
+//   xa*m*u + xb*m*(u + 2) = m*((xa + xb)*u + 2*xb),  u = 2(tP + q) + 1,
+// u per lane and plane, m uniform per head.
+//
+// PIPE = false: each unit's loads are issued, then consumed.
+// PIPE = true:  two unit buffers in ping-pong, so the loads of unit i+1 are in
+//               flight while unit i is consumed, across the caches of a task.
+template <int S>
+struct LaneTable {
+  int row[S];
+  uint32_t off[S];
+  uint32_t urel[S];
+  template <int CHUNK>
+  __device__ __forceinline__ void init(int lane, const BlocksArgs& a) {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int f = lane + kWave * s;
+      const int r = f / a.chunks_per_row;
+      const int c = f - r * a.chunks_per_row;
+      row[s] = r < a.rows_per_group ? r : 0x7fffffff;
+      off[s] = (uint32_t)((int64_t)r * a.slot_stride + (int64_t)c * CHUNK);
+      urel[s] = (uint32_t)(2u * (uint32_t)r * (uint32_t)a.pieces + (uint32_t)(CHUNK / 4) * (uint32_t)c);
+    }
+  }
+};
+
+// Position of the next unit of a task: cache, row group, plane, head batch.
+struct UnitCursor {
+  int cache, group, plane, hbatch;
+  __device__ __forceinline__ void next(int nhb, int planes, int ngr) {
+    if (++hbatch == nhb) {
+      hbatch = 0;
+      if (++plane == planes) {
+        plane = 0;
+        if (++group == ngr) {
+          group = 0;
+          ++cache;
+        }
+      }
+    }
+  }
+};
+
+template <int CHUNK, int S, int HU, bool PIPE>
 __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs a) {
   using V = typename ChunkType<CHUNK>::T;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
   const int64_t n_items = (int64_t)*a.n_items;
-  const int64_t total = n_items * a.num_caches;
+  const int lpt = a.caches_per_task;
+  const int ngroups = (a.num_caches + lpt - 1) / lpt;
+  const int64_t total = n_items * ngroups;
   if (wave >= total) return;
 
+  LaneTable<S> lt;
+  lt.template init<CHUNK>(lane, a);
   const uint64_t P = (uint64_t)a.pieces;
-  const int cpr = a.chunks_per_row;
   const int rg = a.rows_per_group;
-  int row[S];
-  uint32_t off[S];
-  uint32_t urel[S];
-#pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const int f = lane + kWave * s;
-    const int r = f / cpr;
-    const int c = f - r * cpr;
-    row[s] = r < rg ? r : 0x7fffffff;
-    off[s] = (uint32_t)((int64_t)r * a.slot_stride + (int64_t)c * CHUNK);
-    urel[s] = (uint32_t)(2u * (uint32_t)r * (uint32_t)P + (uint32_t)(CHUNK / 4) * (uint32_t)c);
-  }
   const uint64_t plane_term = 2ull * (P / (uint64_t)a.planes);
+  const int nhb = (a.heads + HU - 1) / HU;
 
   for (int64_t task = wave; task < total; task += nwaves) {
-    const int64_t cache = task / n_items;
-    const int64_t item = task - cache * n_items;
+    const int64_t grp = task / n_items;
+    const int64_t item = task - grp * n_items;
+    const int c_begin = (int)grp * lpt;
+    const int c_end = min(a.num_caches, c_begin + lpt);
     const PosRecord* rp = a.recs + item;
     // the record is the same for the whole wave
     const int32_t v = __builtin_amdgcn_readfirstlane(rp->valid);
@@ -193,46 +232,66 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
     const int64_t out_idx = rp->out_idx;
     uint64_t acc = 0;
     if (v > 0) {
-      const uint8_t* pb = a.base[cache] + (int64_t)blk * a.block_stride;
-      const uint32_t mb = a.mbase[cache];
-      for (int g0 = 0; g0 < v; g0 += rg) {
-        const int rows = min(rg, v - g0);
-        const uint8_t* gbase = pb + (int64_t)g0 * a.slot_stride;
-        const uint64_t ug = 2ull * (t0 + (uint64_t)g0) * P + 1ull;
+      const int64_t blk_off = (int64_t)blk * a.block_stride;
+      const int ngr = (v + rg - 1) / rg;
+      const int nunits = ngr * a.planes * nhb * (c_end - c_begin);
+      UnitCursor ic{c_begin, 0, 0, 0}, cc{c_begin, 0, 0, 0};
+
+      auto issue = [&](V(&x)[HU][S]) {
+        const int rows = min(rg, v - ic.group * rg);
+        const uint8_t* base = a.base[ic.cache] + blk_off + (int64_t)(ic.group * rg) * a.slot_stride +
+                              (int64_t)ic.plane * a.plane_stride;
         uint32_t voff[S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) voff[s] = row[s] < rows ? off[s] : kOOB;
-        for (int pl = 0; pl < a.planes; ++pl) {
-          const uint8_t* pbase = gbase + (int64_t)pl * a.plane_stride;
-          const uint64_t up = ug + (uint64_t)pl * plane_term;
-          uint64_t u[S];
+        for (int s = 0; s < S; ++s) voff[s] = lt.row[s] < rows ? lt.off[s] : kOOB;
 #pragma unroll
-          for (int s = 0; s < S; ++s) u[s] = up + urel[s];
-          for (int h0 = 0; h0 < a.heads; h0 += HU) {
-            V x[HU][S];
+        for (int h = 0; h < HU; ++h) {
+          const int hh = ic.hbatch * HU + h;
+          const uint32_t hmask = hh < a.heads ? 0u : kOOB;
+          const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)hh * a.head_stride);
 #pragma unroll
-            for (int h = 0; h < HU; ++h) {
-              const uint32_t hmask = h0 + h < a.heads ? 0u : kOOB;
-              const __amdgpu_buffer_rsrc_t rs = make_rsrc(pbase + (int64_t)(h0 + h) * a.head_stride);
+          for (int s = 0; s < S; ++s) x[h][s] = load_chunk<CHUNK>(rs, voff[s] | hmask);
+        }
+        ic.next(nhb, a.planes, ngr);
+      };
+      auto consume = [&](const V(&x)[HU][S]) {
+        const uint64_t up = 2ull * (t0 + (uint64_t)(cc.group * rg)) * P + 1ull + (uint64_t)cc.plane * plane_term;
+        const uint32_t mb = a.mbase[cc.cache];
 #pragma unroll
-              for (int s = 0; s < S; ++s) x[h][s] = load_chunk<CHUNK>(rs, voff[s] | hmask);
-            }
+        for (int h = 0; h < HU; ++h) {
+          uint64_t sh = 0;
 #pragma unroll
-            for (int h = 0; h < HU; ++h) {
-              uint64_t sh = 0;
-#pragma unroll
-              for (int s = 0; s < S; ++s) {
-                const uint64_t xa = (uint64_t)x[h][s].x | ((uint64_t)x[h][s].y << 32);
-                if constexpr (CHUNK == 16) {
-                  const uint64_t xb = (uint64_t)x[h][s].z | ((uint64_t)x[h][s].w << 32);
-                  sh += (xa + xb) * u[s] + (xb << 1);
-                } else {
-                  sh += xa * u[s];
-                }
-              }
-              acc += sh * (uint64_t)(mb + 2u * (uint32_t)(h0 + h));
+          for (int s = 0; s < S; ++s) {
+            const uint64_t u = up + lt.urel[s];
+            const uint64_t xa = (uint64_t)x[h][s].x | ((uint64_t)x[h][s].y << 32);
+            if constexpr (CHUNK == 16) {
+              const uint64_t xb = (uint64_t)x[h][s].z | ((uint64_t)x[h][s].w << 32);
+              sh += (xa + xb) * u + (xb << 1);
+            } else {
+              sh += xa * u;
             }
           }
+          acc += sh * (uint64_t)(mb + 2u * (uint32_t)(cc.hbatch * HU + h));
+        }
+        cc.next(nhb, a.planes, ngr);
+      };
+
+      if constexpr (PIPE) {
+        V A[HU][S], B[HU][S];
+        issue(A);
+        for (int ui = 0; ui < nunits; ui += 2) {
+          if (ui + 1 < nunits) issue(B);
+          consume(A);
+          if (ui + 1 < nunits) {
+            if (ui + 2 < nunits) issue(A);
+            consume(B);
+          }
+        }
+      } else {
+        for (int ui = 0; ui < nunits; ++ui) {
+          V A[HU][S];
+          issue(A);
+          consume(A);
         }
       }
     }
@@ -242,7 +301,7 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
         uint64_t* o = a.out + out_idx;
         *o = a.accumulate ? *o + acc : acc;
       } else {
-        a.partials[(int64_t)(a.cache_offset + cache) * a.max_items + item] = acc;
+        a.partials[(int64_t)(a.group_offset + grp) * a.max_items + item] = acc;
       }
     }
   }
@@ -263,32 +322,37 @@ __global__ __launch_bounds__(256) void reduce_kernel(const uint64_t* __restrict_
   }
 }
 
-template <int CHUNK, int S>
+template <int CHUNK, int S, bool PIPE>
 constexpr auto pick_kernel() {
-  return &blocks_kernel<CHUNK, S, (16 / S > 0 ? 16 / S : 1)>;
+  return &blocks_kernel<CHUNK, S, (16 / S > 0 ? 16 / S : 1), PIPE>;
 }
 
 using BlocksFn = void (*)(const BlocksArgs);
 
-BlocksFn blocks_fn(const BlocksShape& shp) {
+template <bool PIPE>
+BlocksFn blocks_fn_for(const BlocksShape& shp) {
   if (shp.chunk == 16) {
     switch (shp.slots) {
-      case 1: return pick_kernel<16, 1>();
-      case 2: return pick_kernel<16, 2>();
-      case 4: return pick_kernel<16, 4>();
-      case 8: return pick_kernel<16, 8>();
-      case 16: return pick_kernel<16, 16>();
+      case 1: return pick_kernel<16, 1, PIPE>();
+      case 2: return pick_kernel<16, 2, PIPE>();
+      case 4: return pick_kernel<16, 4, PIPE>();
+      case 8: return pick_kernel<16, 8, PIPE>();
+      case 16: return pick_kernel<16, 16, PIPE>();
     }
   } else {
     switch (shp.slots) {
-      case 1: return pick_kernel<8, 1>();
-      case 2: return pick_kernel<8, 2>();
-      case 4: return pick_kernel<8, 4>();
-      case 8: return pick_kernel<8, 8>();
-      case 16: return pick_kernel<8, 16>();
+      case 1: return pick_kernel<8, 1, PIPE>();
+      case 2: return pick_kernel<8, 2, PIPE>();
+      case 4: return pick_kernel<8, 4, PIPE>();
+      case 8: return pick_kernel<8, 8, PIPE>();
+      case 16: return pick_kernel<8, 16, PIPE>();
     }
   }
   return nullptr;
+}
+
+BlocksFn blocks_fn(const BlocksShape& shp) {
+  return shp.pipelined ? blocks_fn_for<true>(shp) : blocks_fn_for<false>(shp);
 }
 
 int device_cus(int device) {

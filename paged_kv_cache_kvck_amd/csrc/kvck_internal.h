@@ -55,8 +55,9 @@ struct BlocksArgs {
   int32_t rows_per_group;                    // rows covered by one lane table
   int32_t chunks_per_row;
   int32_t num_caches;                        // caches in this launch
-  int32_t cache_offset;                      // index of the first cache of this launch
-  int32_t direct;                            // write out[] directly (single cache overall)
+  int32_t caches_per_task;                   // caches one task covers (a partial's group)
+  int32_t group_offset;                      // partial row of this launch's first group
+  int32_t direct;                            // write out[] directly (one group overall)
   int32_t accumulate;
   const uint8_t* base[kCachesPerLaunch];     // pool base + head_begin*head_stride
   uint32_t mbase[kCachesPerLaunch];          // 2*(layer*H + global_head_base) + 1
@@ -82,9 +83,11 @@ struct StatesArgs {
 
 // Kernel shape chosen on the host for one kvck_checksum_blocks call.
 struct BlocksShape {
-  int chunk;     // 16 or 8 bytes per lane load
-  int slots;     // lane-table slots S (1, 2, 4, 8, 16)
+  int chunk;      // 16 or 8 bytes per lane load
+  int slots;      // lane-table slots S (1, 2, 4, 8, 16)
   int rows_per_group;
+  bool pipelined; // two unit buffers in flight, several caches per task
+  int caches_per_task;
 };
 
 // launchers (return hipSuccess or the first HIP error)

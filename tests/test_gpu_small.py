@@ -6,6 +6,9 @@ positions past the last token, bad block ids and requests, accumulate,
 several launches of caches, the 8-byte load path, streams, determinism.
 """
 
+import os
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -17,6 +20,14 @@ from gpu_helpers import (DEV, SENTINEL, assert_match, assert_unlisted_untouched,
                          to_device_bits)
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(params=["simple", "pipelined"])
+def schedule(request, monkeypatch):
+    """Run the test under both main-pass schedules (KVCK_SCHEDULE)."""
+    monkeypatch.setenv("KVCK_SCHEDULE", request.param)
+    return request.param
+
 
 CASES = [
     # name, layout, elem, layers, heads, head_size, block_size, lengths, extra
@@ -45,10 +56,10 @@ def _host_case(seed, layout, elem, layers, nh, d, bs, lengths, extra, start=None
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_parity_small(case):
+def test_parity_small(case, schedule):
     name, layout, elem, layers, nh, d, bs, lengths, extra = case
-    log(f"[parity_small] {name}")
-    req, hpools = _host_case(abs(hash(name)) % 1000, layout, elem, layers, nh, d, bs, lengths, extra)
+    log(f"[parity_small] {name} {schedule}")
+    req, hpools = _host_case(zlib.crc32(name.encode()) % 1000, layout, elem, layers, nh, d, bs, lengths, extra)
     dpools = [to_device_bits(p) for p in hpools]
     got = gpu_blocks(dpools, layout, layers, req)
     want = oracle.checksum_blocks(hpools, layout, layers, [0] * len(layers), req.block_table, req.num_blocks,
@@ -71,7 +82,7 @@ def test_tiny_config_golden():
     assert [str(int(x)) for x in got[0, :4]] == gold["checksums"]
 
 
-def test_start_pos_heads_subset_and_global_base():
+def test_start_pos_heads_subset_and_global_base(schedule):
     log("[heads subset]")
     rng = np.random.default_rng(5)
     req, nb = wl.page_requests(rng, [90, 40, 200], 16, start_pos=[2, 0, 5], extra_blocks=[1, 0, 2], spare_frac=0.2)
@@ -86,7 +97,7 @@ def test_start_pos_heads_subset_and_global_base():
         assert int(got[r, k]) == int(want[r, k])
 
 
-def test_tp_shards_sum_and_pp_split_sum():
+def test_tp_shards_sum_and_pp_split_sum(schedule):
     log("[tp/pp partial sums]")
     rng = np.random.default_rng(6)
     req, nb = wl.page_requests(rng, [300, 77, 16], 16, spare_frac=0.1)
@@ -103,7 +114,7 @@ def test_tp_shards_sum_and_pp_split_sum():
         assert tot[r, k] == full[r, k] and pp[r, k] == full[r, k]
 
 
-def test_accumulate_adds_mod_2_64():
+def test_accumulate_adds_mod_2_64(schedule):
     log("[accumulate]")
     rng = np.random.default_rng(7)
     req, nb = wl.page_requests(rng, [64, 100], 16, spare_frac=0.1)
@@ -125,7 +136,7 @@ def test_accumulate_adds_mod_2_64():
             assert got[r, k] == init[r, k] + one[r, k]
 
 
-def test_many_caches_several_launches():
+def test_many_caches_several_launches(schedule):
     """More caches than one argument block carries (several main launches)."""
     log("[70 caches]")
     rng = np.random.default_rng(8)
@@ -139,7 +150,7 @@ def test_many_caches_several_launches():
         assert int(got[r, k]) == int(want[r, k])
 
 
-def test_empty_and_past_end_positions():
+def test_empty_and_past_end_positions(schedule):
     log("[empty]")
     rng = np.random.default_rng(9)
     # a request with no listed positions, one with only positions past its tokens
@@ -212,6 +223,13 @@ def test_determinism_and_streams():
     c = gpu_blocks(pools, "HND", list(range(5)), req, workspace=ws)
     d = gpu_blocks(pools, "HND", list(range(5)), req, workspace=ws)
     assert np.array_equal(a, b) and np.array_equal(a, c) and np.array_equal(a, d)
+    for sched in ("simple", "pipelined"):
+        os.environ["KVCK_SCHEDULE"] = sched
+        try:
+            e = gpu_blocks(pools, "HND", list(range(5)), req, workspace=ws)
+        finally:
+            del os.environ["KVCK_SCHEDULE"]
+        assert np.array_equal(a, e), sched
 
 
 def test_states_small_parity():
