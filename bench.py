@@ -114,6 +114,7 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-shard", action="store_true", help="skip the TP-shard timing")
+    ap.add_argument("--no-states", action="store_true", help="skip the Mamba-state timing")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="after timing, run one plain device copy of this many GiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -185,6 +186,37 @@ def main(argv=None):
                                         "GB_per_s": shard_bytes / (sms * 1e-3) / 1e9,
                                         "main_pass_ms": smain / max(sc, 1),
                                         "main_pass_GB_per_s": shard_bytes / (smain / max(sc, 1) * 1e-3) / 1e9}
+    if not args.no_states:
+        # Mamba running-state rows: the hybrid workload's 24 Mamba layers
+        from paged_kv_cache_kvck_amd import workloads as wl
+        mamba = wl.hybrid()[1]
+        states = mamba.device_states()
+        sid = torch.from_numpy(mamba.slot_ids).to(dev)
+        sout = torch.zeros(len(mamba.slot_ids), dtype=torch.uint64, device=dev)
+        sws = torch.empty(max(256, kvck.kvck_states_workspace_bytes(len(mamba.layer_numbers), mamba.rows_used,
+                                                                    len(mamba.slot_ids))), dtype=torch.uint8,
+                          device=dev)
+
+        def sstep():
+            kvck.kvck_checksum_states(states, mamba.layer_numbers, sid, out=sout, workspace=sws, stream=stream)
+
+        for _ in range(2):
+            sstep()
+        torch.cuda.synchronize()
+        kvck.kvck_instrument_read()
+        e0.record(stream)
+        for _ in range(args.steps):
+            sstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sms = e0.elapsed_time(e1) / args.steps
+        smain, sc = kvck.kvck_instrument_read()
+        sb = mamba.valid_bytes()
+        extra["mamba_states"] = {"workload": "24 Mamba layers x 128 requests x 64 rows of fp32 SSM [128x16] + fp16 "
+                                             "conv [4x256] state", "valid_bytes": sb, "ms_per_step": sms,
+                                 "GB_per_s": sb / (sms * 1e-3) / 1e9, "main_pass_ms": smain / max(sc, 1),
+                                 "main_pass_GB_per_s": sb / (smain / max(sc, 1) * 1e-3) / 1e9}
+        del states
     kvck.kvck_instrument(False)
     if args.copy_calibration_gib > 0:
         n = int(args.copy_calibration_gib * (1 << 30))

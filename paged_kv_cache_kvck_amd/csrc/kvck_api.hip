@@ -55,22 +55,30 @@ bool choose_shape(int32_t block_size, int32_t row_bytes, int chunk, BlocksShape*
   shp->rows_per_group = (int)rg;
   shp->pipelined = false;
   shp->caches_per_task = 1;
+  shp->planes_per_unit = 1;
   return true;
 }
 
 // Schedule: with many tasks per resident wave, keep two unit buffers in
-// flight and let one task cover kPipeCaches caches, so a wave's loads do not
-// drain at every unit or task boundary.  Small batches keep one cache per task
-// and higher occupancy (their run time is dominated by ramp-up and tail).
-// Wide lane tables (S > 4) would need more than half the register file
-// double-buffered and stay unpipelined.
-constexpr int kPipeCaches = 4;
+// flight and let one task cover several caches, so a wave's loads do not
+// drain at every unit boundary and rarely at a task boundary (a boundary
+// costs about one memory latency plus the reduction).  A task covers enough
+// caches to stream about kPipeTaskBytes of a full block, capped at
+// kPipeMaxCaches.  Small batches keep one cache per task and higher occupancy
+// (their run time is dominated by ramp-up and tail).  Wide lane tables (S > 4)
+// would need more than half the register file double-buffered and stay
+// unpipelined.
+constexpr int64_t kPipeTaskBytes = 256 * 1024;
+constexpr int kPipeMaxCaches = 16;
 constexpr int64_t kPipeMinTasksPerWave = 64;
-static_assert(kCachesPerLaunch % kPipeCaches == 0, "launch groups must not straddle launches");
+static_assert(kCachesPerLaunch % kPipeMaxCaches == 0, "launch groups must not straddle launches");
 
-void choose_schedule(BlocksShape* shp, int32_t num_caches, int64_t max_items, int cus) {
+void choose_schedule(BlocksShape* shp, int32_t num_caches, int64_t max_items, int64_t block_bytes, int planes,
+                     int heads, int cus) {
   const int64_t waves = (int64_t)cus * 8;  // resident waves of the pipelined kernel (2 per SIMD)
-  const int64_t tasks = max_items * ((num_caches + kPipeCaches - 1) / kPipeCaches);
+  int lpt = 1;
+  while (lpt < kPipeMaxCaches && (int64_t)(2 * lpt) * block_bytes <= kPipeTaskBytes) lpt *= 2;
+  const int64_t tasks = max_items * ((num_caches + lpt - 1) / lpt);
   bool pipe = shp->slots <= 4 && num_caches > 1 && tasks >= kPipeMinTasksPerWave * waves;
   // KVCK_SCHEDULE=pipelined|simple overrides the choice (results are identical either way)
   if (const char* force = getenv("KVCK_SCHEDULE")) {
@@ -79,7 +87,10 @@ void choose_schedule(BlocksShape* shp, int32_t num_caches, int64_t max_items, in
   }
   if (pipe) {
     shp->pipelined = true;
-    shp->caches_per_task = kPipeCaches;
+    shp->caches_per_task = lpt;
+    // a unit holds 16/S head slots; with half of them or fewer used, carry K and V together
+    const int hu = 16 / shp->slots;
+    if (planes == 2 && shp->slots <= 4 && 2 * heads <= hu) shp->planes_per_unit = 2;
   }
 }
 
@@ -225,7 +236,8 @@ KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const
   hipStream_t st = static_cast<hipStream_t>(stream);
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  choose_schedule(&shp, num_caches, (int64_t)num_reqs * max_blocks, cus);
+  choose_schedule(&shp, num_caches, (int64_t)num_reqs * max_blocks,
+                  (int64_t)head_count * L.planes * L.block_size * L.row_bytes, L.planes, head_count, cus);
   const int32_t lpt = shp.caches_per_task;
   const int32_t total_groups = (num_caches + lpt - 1) / lpt;
 

@@ -154,8 +154,9 @@ __global__ __launch_bounds__(256) void plan_fill_kernel(
 // q the chunk's first piece inside its plane row.  The same table serves every
 // plane, head, cache and position, so the inner loop only adds offsets.
 //
-// A unit is the loads of one (cache, row group, plane, batch of HU heads):
-// HU*S chunks per lane.  For a chunk of pieces xa (piece q) and xb (piece q+1)
+// A unit is the loads of one (cache, row group, PU planes, batch of HU heads):
+// PU*HU*S chunks per lane (PU = 2 lets a unit carry K and V when a call has
+// too few heads to fill HU).  For a chunk of pieces xa (piece q) and xb (piece q+1)
 // of token t, plane pl, head h:
 //   xa*m*u + xb*m*(u + 2) = m*((xa + xb)*u + 2*xb),  u = 2(tP + q) + 1,
 // u per lane and plane, m uniform per head.
@@ -199,7 +200,7 @@ struct UnitCursor {
   }
 };
 
-template <int CHUNK, int S, int HU, bool PIPE>
+template <int CHUNK, int S, int HU, int PU, bool PIPE>
 __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs a) {
   using V = typename ChunkType<CHUNK>::T;
   const int lane = threadIdx.x & (kWave - 1);
@@ -234,50 +235,59 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
     if (v > 0) {
       const int64_t blk_off = (int64_t)blk * a.block_stride;
       const int ngr = (v + rg - 1) / rg;
-      const int nunits = ngr * a.planes * nhb * (c_end - c_begin);
+      const int nplanes = a.planes / PU;  // plane steps per row group (PU divides planes)
+      const int nunits = ngr * nplanes * nhb * (c_end - c_begin);
       UnitCursor ic{c_begin, 0, 0, 0}, cc{c_begin, 0, 0, 0};
 
-      auto issue = [&](V(&x)[HU][S]) {
+      auto issue = [&](V(&x)[PU][HU][S]) {
         const int rows = min(rg, v - ic.group * rg);
         const uint8_t* base = a.base[ic.cache] + blk_off + (int64_t)(ic.group * rg) * a.slot_stride +
-                              (int64_t)ic.plane * a.plane_stride;
+                              (int64_t)(ic.plane * PU) * a.plane_stride;
         uint32_t voff[S];
 #pragma unroll
         for (int s = 0; s < S; ++s) voff[s] = lt.row[s] < rows ? lt.off[s] : kOOB;
 #pragma unroll
-        for (int h = 0; h < HU; ++h) {
-          const int hh = ic.hbatch * HU + h;
-          const uint32_t hmask = hh < a.heads ? 0u : kOOB;
-          const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)hh * a.head_stride);
+        for (int p = 0; p < PU; ++p) {
 #pragma unroll
-          for (int s = 0; s < S; ++s) x[h][s] = load_chunk<CHUNK>(rs, voff[s] | hmask);
+          for (int h = 0; h < HU; ++h) {
+            const int hh = ic.hbatch * HU + h;
+            const uint32_t hmask = hh < a.heads ? 0u : kOOB;
+            const __amdgpu_buffer_rsrc_t rs =
+                make_rsrc(base + (int64_t)p * a.plane_stride + (int64_t)hh * a.head_stride);
+#pragma unroll
+            for (int s = 0; s < S; ++s) x[p][h][s] = load_chunk<CHUNK>(rs, voff[s] | hmask);
+          }
         }
-        ic.next(nhb, a.planes, ngr);
+        ic.next(nhb, nplanes, ngr);
       };
-      auto consume = [&](const V(&x)[HU][S]) {
-        const uint64_t up = 2ull * (t0 + (uint64_t)(cc.group * rg)) * P + 1ull + (uint64_t)cc.plane * plane_term;
+      auto consume = [&](const V(&x)[PU][HU][S]) {
         const uint32_t mb = a.mbase[cc.cache];
 #pragma unroll
-        for (int h = 0; h < HU; ++h) {
-          uint64_t sh = 0;
+        for (int p = 0; p < PU; ++p) {
+          const uint64_t up = 2ull * (t0 + (uint64_t)(cc.group * rg)) * P + 1ull +
+                              (uint64_t)(cc.plane * PU + p) * plane_term;
 #pragma unroll
-          for (int s = 0; s < S; ++s) {
-            const uint64_t u = up + lt.urel[s];
-            const uint64_t xa = (uint64_t)x[h][s].x | ((uint64_t)x[h][s].y << 32);
-            if constexpr (CHUNK == 16) {
-              const uint64_t xb = (uint64_t)x[h][s].z | ((uint64_t)x[h][s].w << 32);
-              sh += (xa + xb) * u + (xb << 1);
-            } else {
-              sh += xa * u;
+          for (int h = 0; h < HU; ++h) {
+            uint64_t sh = 0;
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+              const uint64_t u = up + lt.urel[s];
+              const uint64_t xa = (uint64_t)x[p][h][s].x | ((uint64_t)x[p][h][s].y << 32);
+              if constexpr (CHUNK == 16) {
+                const uint64_t xb = (uint64_t)x[p][h][s].z | ((uint64_t)x[p][h][s].w << 32);
+                sh += (xa + xb) * u + (xb << 1);
+              } else {
+                sh += xa * u;
+              }
             }
+            acc += sh * (uint64_t)(mb + 2u * (uint32_t)(cc.hbatch * HU + h));
           }
-          acc += sh * (uint64_t)(mb + 2u * (uint32_t)(cc.hbatch * HU + h));
         }
-        cc.next(nhb, a.planes, ngr);
+        cc.next(nhb, nplanes, ngr);
       };
 
       if constexpr (PIPE) {
-        V A[HU][S], B[HU][S];
+        V A[PU][HU][S], B[PU][HU][S];
         issue(A);
         for (int ui = 0; ui < nunits; ui += 2) {
           if (ui + 1 < nunits) issue(B);
@@ -289,7 +299,7 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
         }
       } else {
         for (int ui = 0; ui < nunits; ++ui) {
-          V A[HU][S];
+          V A[PU][HU][S];
           issue(A);
           consume(A);
         }
@@ -322,37 +332,55 @@ __global__ __launch_bounds__(256) void reduce_kernel(const uint64_t* __restrict_
   }
 }
 
-template <int CHUNK, int S, bool PIPE>
+// Same sum, one wavefront per output: lanes stride over the partials, then
+// the wave reduces.  Used when each output has many partials.
+__global__ __launch_bounds__(256) void reduce_wave_kernel(const uint64_t* __restrict__ partials, int64_t stride,
+                                                          int32_t splits, const uint32_t* __restrict__ n_items,
+                                                          int64_t n_fixed, const PosRecord* __restrict__ recs,
+                                                          uint64_t* __restrict__ out, int32_t accumulate) {
+  const int64_t n = n_items ? (int64_t)*n_items : n_fixed;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t i = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; i < n; i += waves) {
+    uint64_t s = 0;
+    for (int32_t sp = lane; sp < splits; sp += kWave) s += partials[(int64_t)sp * stride + i];
+    s = wave_sum(s);
+    if (lane == 0) {
+      const int64_t o = recs ? recs[i].out_idx : i;
+      out[o] = accumulate ? out[o] + s : s;
+    }
+  }
+}
+
+template <int CHUNK, int S, int PU, bool PIPE>
 constexpr auto pick_kernel() {
-  return &blocks_kernel<CHUNK, S, (16 / S > 0 ? 16 / S : 1), PIPE>;
+  constexpr int hu = 16 / (S * PU) > 0 ? 16 / (S * PU) : 1;
+  return &blocks_kernel<CHUNK, S, hu, PU, PIPE>;
 }
 
 using BlocksFn = void (*)(const BlocksArgs);
 
-template <bool PIPE>
-BlocksFn blocks_fn_for(const BlocksShape& shp) {
-  if (shp.chunk == 16) {
-    switch (shp.slots) {
-      case 1: return pick_kernel<16, 1, PIPE>();
-      case 2: return pick_kernel<16, 2, PIPE>();
-      case 4: return pick_kernel<16, 4, PIPE>();
-      case 8: return pick_kernel<16, 8, PIPE>();
-      case 16: return pick_kernel<16, 16, PIPE>();
-    }
-  } else {
-    switch (shp.slots) {
-      case 1: return pick_kernel<8, 1, PIPE>();
-      case 2: return pick_kernel<8, 2, PIPE>();
-      case 4: return pick_kernel<8, 4, PIPE>();
-      case 8: return pick_kernel<8, 8, PIPE>();
-      case 16: return pick_kernel<8, 16, PIPE>();
-    }
+template <int CHUNK, int PU, bool PIPE>
+BlocksFn blocks_fn_slots(int slots) {
+  switch (slots) {
+    case 1: return pick_kernel<CHUNK, 1, PU, PIPE>();
+    case 2: return pick_kernel<CHUNK, 2, PU, PIPE>();
+    case 4: return pick_kernel<CHUNK, 4, PU, PIPE>();
+    case 8: return pick_kernel<CHUNK, 8, 1, PIPE>();
+    case 16: return pick_kernel<CHUNK, 16, 1, PIPE>();
   }
   return nullptr;
 }
 
+// Pipelined units may carry both planes (PU = 2); the unpipelined kernel and
+// wide lane tables (S >= 8) always take one plane per unit.
 BlocksFn blocks_fn(const BlocksShape& shp) {
-  return shp.pipelined ? blocks_fn_for<true>(shp) : blocks_fn_for<false>(shp);
+  if (shp.pipelined) {
+    if (shp.planes_per_unit == 2)
+      return shp.chunk == 16 ? blocks_fn_slots<16, 2, true>(shp.slots) : blocks_fn_slots<8, 2, true>(shp.slots);
+    return shp.chunk == 16 ? blocks_fn_slots<16, 1, true>(shp.slots) : blocks_fn_slots<8, 1, true>(shp.slots);
+  }
+  return shp.chunk == 16 ? blocks_fn_slots<16, 1, false>(shp.slots) : blocks_fn_slots<8, 1, false>(shp.slots);
 }
 
 int device_cus(int device) {
@@ -409,6 +437,14 @@ hipError_t launch_blocks(const BlocksArgs& a, const BlocksShape& shp, int grid, 
 hipError_t launch_reduce(const uint64_t* partials, int64_t stride, int32_t splits, const uint32_t* n_items,
                          int64_t n_fixed, const PosRecord* recs, uint64_t* out, int32_t accumulate,
                          hipStream_t stream) {
+  if (splits >= 64) {
+    int64_t grid = (stride + 3) / 4;
+    if (grid > 4096) grid = 4096;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(reduce_wave_kernel, dim3((unsigned)grid), dim3(256), 0, stream, partials, stride, splits,
+                       n_items, n_fixed, recs, out, accumulate);
+    return hipGetLastError();
+  }
   int64_t grid = (stride + 255) / 256;
   if (grid > 4096) grid = 4096;
   if (grid < 1) grid = 1;

@@ -88,6 +88,7 @@ struct BlocksShape {
   int rows_per_group;
   bool pipelined; // two unit buffers in flight, several caches per task
   int caches_per_task;
+  int planes_per_unit;  // 1, or 2 (K and V in one unit) when heads are few
 };
 
 // launchers (return hipSuccess or the first HIP error)
