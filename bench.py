@@ -186,6 +186,22 @@ def main(argv=None):
                                         "GB_per_s": shard_bytes / (sms * 1e-3) / 1e9,
                                         "main_pass_ms": smain / max(sc, 1),
                                         "main_pass_GB_per_s": shard_bytes / (smain / max(sc, 1) * 1e-3) / 1e9}
+    # offloaded-checksum check of every listed position: tag, compare, count
+    hashes = torch.randint(0, 256, (req.num_reqs * req.max_blocks, 32), dtype=torch.uint8, device=dev)
+    stored, _ = kvck.kvck_tag_checksums(out.view(-1), hashes, 0x1234, num_blocks_per_req=nb, stream=stream)
+    mism = torch.zeros(req.num_reqs * req.max_blocks, dtype=torch.uint8, device=dev)
+    cnt = torch.zeros(1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        kvck.kvck_tag_checksums(out.view(-1), hashes, 0x1234, num_blocks_per_req=nb, tagged=False, stored=stored,
+                                mismatch=mism, mismatch_count=cnt, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    extra["offload_check"] = {"positions": int(req.num_blocks.sum()), "us_per_call": e0.elapsed_time(e1) / args.steps * 1e3,
+                              "mismatches": int(cnt.item())}
+    del hashes, stored, mism
+
     if not args.no_states:
         # Mamba running-state rows: the hybrid workload's 24 Mamba layers
         from paged_kv_cache_kvck_amd import workloads as wl

@@ -199,6 +199,37 @@ kvck_status kvck_checksum_states(
 size_t kvck_states_workspace_bytes(int32_t num_layers, int32_t row_count, int32_t num_reqs);
 
 /*
+ * kvck_tag_checksums -- tags of offloaded checksums and the load-time check.
+ *
+ * The page's function block_checksum_tags: a block's tag is the first 8 bytes
+ * of its block hash read little-endian, XOR the group's fingerprint; the
+ * checksum offloaded with a block (one uint64, the page's BLOCK_CHECKSUM_BYTES)
+ * is XORed with its tag so that it only matches the block it was stored for.
+ * For every entry i (only listed positions i = r*max_blocks + k,
+ * k < num_blocks_per_req[r], when num_blocks_per_req is given):
+ *   t_i = checksums[i] ^ LE64(block_hashes + i*hash_stride) ^ fingerprint
+ *   tagged[i] = t_i                               (if tagged: the value to offload)
+ *   mismatch[i] = (t_i != stored[i])              (if stored: a load of offloaded KV)
+ *   *mismatch_count += number of mismatches       (if mismatch_count)
+ * Other entries are not written.  All pointers are device pointers;
+ * block_hashes must be 8-byte aligned with hash_stride a multiple of 8
+ * (vLLM block hashes are 32 bytes).  At least one of tagged / stored.
+ */
+kvck_status kvck_tag_checksums(
+    const uint64_t* checksums,             /* device [n] */
+    const uint8_t* block_hashes,           /* device [n][hash_stride] */
+    int64_t hash_stride,                   /* bytes, >= 8, multiple of 8 */
+    uint64_t fingerprint,
+    int64_t n,
+    const int32_t* num_blocks_per_req,     /* device [n/max_blocks], optional */
+    int32_t max_blocks,
+    uint64_t* tagged,                      /* device [n], optional */
+    const uint64_t* stored,                /* device [n], optional */
+    uint8_t* mismatch,                     /* device [n], optional, needs stored */
+    uint32_t* mismatch_count,              /* device, optional, needs stored; incremented */
+    kvck_stream_t stream);
+
+/*
  * Instrumentation (optional, process-wide).  While enabled, every
  * kvck_checksum_blocks / kvck_checksum_states call records one pair of HIP
  * events on its stream around its main pass -- the kernel launches that

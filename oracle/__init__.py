@@ -13,7 +13,10 @@ What it computes is defined on the vLLM API page
   m = 2 * (layer * H + head) + 1,  H = MAX_KV_HEADS_PER_LAYER   (item 2)
 * Mamba running-state rows, one slice per global row       (Mamba paragraph)
 
-Two independent implementations live here:
+``tags`` holds the offloaded-checksum tags (page function
+``block_checksum_tags``) and the load-time comparison.
+
+Two independent implementations of the checksum live here:
 
 ``kv_checksum``  numpy, vectorised per (position, cache); the oracle proper.
 ``brute``        pure-Python integers, one piece at a time; for tiny inputs,
@@ -41,3 +44,4 @@ from .kv_checksum import (  # noqa: F401
     checksum_states,
 )
 from . import brute  # noqa: F401
+from . import tags  # noqa: F401

@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     kvck_platform_supported,
     kvck_states_workspace_bytes,
     kvck_status_string,
+    kvck_tag_checksums,
     load_library,
     state_desc,
 )

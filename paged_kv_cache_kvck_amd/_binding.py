@@ -28,7 +28,8 @@ KVCK_FLAG_BAD_STATE_SLOT = 4
 
 # symbols include/kvck.h declares
 EXPORTS = ("kvck_checksum_blocks", "kvck_blocks_workspace_bytes", "kvck_checksum_states",
-           "kvck_states_workspace_bytes", "kvck_instrument", "kvck_instrument_read", "kvck_status_string",
+           "kvck_states_workspace_bytes", "kvck_tag_checksums", "kvck_instrument", "kvck_instrument_read",
+           "kvck_status_string",
            "kvck_platform_supported", "kvck_abi_version")
 
 
@@ -89,6 +90,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kvck_platform_supported.argtypes = []
     lib.kvck_abi_version.restype = i32
     lib.kvck_abi_version.argtypes = []
+    lib.kvck_tag_checksums.restype = i32
+    lib.kvck_tag_checksums.argtypes = [vp, vp, i64, ctypes.c_uint64, i64, vp, i32, vp, vp, vp, vp, vp]
     lib.kvck_instrument.restype = i32
     lib.kvck_instrument.argtypes = [i32]
     lib.kvck_instrument_read.restype = i32
@@ -323,3 +326,43 @@ def kvck_checksum_states(layer_states: Sequence[Sequence[torch.Tensor]], layer_n
         if flags:
             raise KvckDeviceError(flags)
     return out
+
+
+def kvck_tag_checksums(checksums: torch.Tensor, block_hashes: torch.Tensor, fingerprint: int,
+                       num_blocks_per_req: torch.Tensor | None = None, tagged: torch.Tensor | bool | None = True,
+                       stored: torch.Tensor | None = None, mismatch: torch.Tensor | bool | None = None,
+                       mismatch_count: torch.Tensor | None = None, stream=None):
+    """Tags of offloaded checksums (the page's block_checksum_tags) and the
+    load-time comparison; see include/kvck.h.
+
+    ``checksums``: uint64 tensor (e.g. the (num_reqs, max_blocks) output of
+    kvck_checksum_blocks); ``block_hashes``: uint8 (n, hash_bytes >= 8) tensor,
+    row i the hash of the block at entry i.  Returns (tagged, mismatch) --
+    each a tensor or None.
+    """
+    lib = load_library()
+    dev = checksums.device
+    n = checksums.numel()
+    if checksums.dtype not in (torch.uint64, torch.int64) or not checksums.is_contiguous():
+        raise ValueError("checksums must be a contiguous uint64 tensor")
+    if block_hashes.dtype != torch.uint8 or block_hashes.dim() != 2 or block_hashes.shape[0] != n \
+            or block_hashes.stride(1) != 1 or block_hashes.device != dev:
+        raise ValueError("block_hashes must be a uint8 (n, hash_bytes) tensor with contiguous rows")
+    max_blocks = 0
+    if num_blocks_per_req is not None:
+        _meta(num_blocks_per_req, torch.int32, "num_blocks_per_req", dev)
+        max_blocks = n // max(1, num_blocks_per_req.numel())
+    if tagged is True:
+        tagged = torch.zeros(n, dtype=torch.uint64, device=dev)
+    elif tagged is False:
+        tagged = None
+    if mismatch is True or (mismatch is None and stored is not None):
+        mismatch = torch.zeros(n, dtype=torch.uint8, device=dev)
+    elif mismatch is False:
+        mismatch = None
+    st = lib.kvck_tag_checksums(checksums.data_ptr(), block_hashes.data_ptr(), block_hashes.stride(0),
+                                ctypes.c_uint64(int(fingerprint) & ((1 << 64) - 1)), n, _ptr(num_blocks_per_req),
+                                max_blocks, _ptr(tagged), _ptr(stored), _ptr(mismatch), _ptr(mismatch_count),
+                                _stream_handle(stream, dev))
+    _check(st, "kvck_tag_checksums")
+    return tagged, mismatch

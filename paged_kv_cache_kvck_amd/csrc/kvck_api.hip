@@ -394,3 +394,24 @@ KVCK_EXPORT kvck_status kvck_checksum_states(const kvck_state_desc* states, int3
   }
   return KVCK_OK;
 }
+
+KVCK_EXPORT kvck_status kvck_tag_checksums(const uint64_t* checksums, const uint8_t* block_hashes, int64_t hash_stride,
+                                           uint64_t fingerprint, int64_t n, const int32_t* num_blocks_per_req,
+                                           int32_t max_blocks, uint64_t* tagged, const uint64_t* stored,
+                                           uint8_t* mismatch, uint32_t* mismatch_count, kvck_stream_t stream) {
+  if (n < 0) return KVCK_ERR_INVALID_ARGUMENT;
+  if (n == 0) return KVCK_OK;
+  if (!checksums || !block_hashes) return KVCK_ERR_INVALID_ARGUMENT;
+  if (!tagged && !stored) return KVCK_ERR_INVALID_ARGUMENT;       // nothing to do
+  if ((mismatch || mismatch_count) && !stored) return KVCK_ERR_INVALID_ARGUMENT;
+  if (hash_stride < 8) return KVCK_ERR_INVALID_ARGUMENT;
+  if (hash_stride % 8 != 0 || !aligned(block_hashes, 8)) return KVCK_ERR_MISALIGNED;
+  if (num_blocks_per_req && (max_blocks < 1 || n % max_blocks != 0)) return KVCK_ERR_INVALID_ARGUMENT;
+  int dev = 0;
+  const kvck_status ds = current_device(&dev);
+  if (ds != KVCK_OK) return ds;
+  if (launch_tags(checksums, block_hashes, hash_stride, fingerprint, n, num_blocks_per_req, max_blocks, tagged, stored,
+                  mismatch, mismatch_count, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return KVCK_ERR_HIP;
+  return KVCK_OK;
+}

@@ -102,6 +102,9 @@ hipError_t launch_reduce(const uint64_t* partials, int64_t stride, int32_t split
                          int64_t n_fixed, const PosRecord* recs, uint64_t* out, int32_t accumulate,
                          hipStream_t stream);
 hipError_t launch_states(const StatesArgs& a, int grid, hipStream_t stream);
+hipError_t launch_tags(const uint64_t* checksums, const uint8_t* hashes, int64_t hash_stride, uint64_t fingerprint,
+                       int64_t n, const int32_t* nbpr, int32_t max_blocks, uint64_t* tagged, const uint64_t* stored,
+                       uint8_t* mismatch, uint32_t* count, hipStream_t stream);
 int states_grid(int device, int64_t tasks);
 
 }  // namespace kvck

@@ -1,0 +1,62 @@
+// Offloaded-checksum tags and load-time comparison on gfx950.
+//
+// vLLM API page "vllm.distributed.kv_transfer.kv_checksum.checksum", function
+// block_checksum_tags: the tag of a block is the first 8 bytes of its hash,
+// read little-endian, XOR the group's fingerprint; an offloaded checksum is
+// XORed with it (one uint64 per block, BLOCK_CHECKSUM_BYTES), so it matches
+// only the block it was stored for.  Here, per listed position i:
+//   t_i = checksum_i ^ LE64(hash_i[0..8)) ^ fingerprint
+// is written (the value to offload) and/or compared with the stored value
+// (a load of offloaded KV), mismatches flagged per position and counted.
+#include "kvck_internal.h"
+
+namespace kvck {
+namespace {
+
+__global__ __launch_bounds__(256) void tags_kernel(const uint64_t* __restrict__ checksums,
+                                                   const uint8_t* __restrict__ hashes, int64_t hash_stride,
+                                                   uint64_t fingerprint, int64_t n, const int32_t* __restrict__ nbpr,
+                                                   int32_t max_blocks, uint64_t* __restrict__ tagged,
+                                                   const uint64_t* __restrict__ stored, uint8_t* __restrict__ mismatch,
+                                                   uint32_t* __restrict__ count) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < n; base += stride) {
+    const int64_t i = base + threadIdx.x;
+    bool live = i < n;
+    if (live && nbpr) {
+      const int64_t r = i / max_blocks;
+      live = (int32_t)(i - r * max_blocks) < nbpr[r];
+    }
+    bool bad = false;
+    if (live) {
+      // little-endian hosts and devices: a 64-bit load is the LE value of the 8 bytes
+      const uint64_t tag = *reinterpret_cast<const uint64_t*>(hashes + i * hash_stride) ^ fingerprint;
+      const uint64_t t = checksums[i] ^ tag;
+      if (tagged) tagged[i] = t;
+      if (stored) {
+        bad = t != stored[i];
+        if (mismatch) mismatch[i] = bad ? 1 : 0;
+      }
+    }
+    if (count) {
+      // one atomic per wavefront
+      const uint64_t votes = __ballot(bad);
+      if ((threadIdx.x & (kWave - 1)) == 0 && votes) atomicAdd(count, (uint32_t)__popcll(votes));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tags(const uint64_t* checksums, const uint8_t* hashes, int64_t hash_stride, uint64_t fingerprint,
+                       int64_t n, const int32_t* nbpr, int32_t max_blocks, uint64_t* tagged, const uint64_t* stored,
+                       uint8_t* mismatch, uint32_t* count, hipStream_t stream) {
+  int64_t grid = (n + 255) / 256;
+  if (grid > 8192) grid = 8192;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(tags_kernel, dim3((unsigned)grid), dim3(256), 0, stream, checksums, hashes, hash_stride,
+                     fingerprint, n, nbpr, max_blocks, tagged, stored, mismatch, count);
+  return hipGetLastError();
+}
+
+}  // namespace kvck

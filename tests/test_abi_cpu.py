@@ -25,7 +25,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = kvck.load_library()
     decl = header_functions()
-    assert len(decl) == 9
+    assert len(decl) == 10
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTS) == decl
@@ -141,3 +141,22 @@ def test_binding_argument_checks():
     with pytest.raises(ValueError):
         kvck.kvck_checksum_blocks(pools, "NHD", [0], bt, torch.zeros(1, dtype=torch.int32),
                                   torch.zeros(1, dtype=torch.int64), torch.zeros(1, dtype=torch.int64))
+
+
+def test_tags_rejects_before_launch():
+    lib = kvck.load_library()
+
+    def call(cs=FAKE, h=FAKE, stride=32, n=16, nbpr=None, mb=0, tagged=FAKE, stored=None, mm=None, cnt=None):
+        return lib.kvck_tag_checksums(cs, h, stride, 0, n, nbpr, mb, tagged, stored, mm, cnt, None)
+
+    assert call(n=0) == 0
+    assert call(n=-1) == -1
+    assert call(cs=0) == -1
+    assert call(tagged=None) == -1               # neither tagged nor stored
+    assert call(mm=FAKE) == -1                   # mismatch output without stored values
+    assert call(stride=4) == -1
+    assert call(stride=12) == -3
+    assert call(h=FAKE + 4) == -3
+    assert call(nbpr=FAKE, mb=5) == -1           # n not a multiple of max_blocks
+    if not torch.cuda.is_available():
+        assert call() == -6
