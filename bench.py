@@ -115,6 +115,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-shard", action="store_true", help="skip the TP-shard timing")
     ap.add_argument("--no-states", action="store_true", help="skip the Mamba-state timing")
+    ap.add_argument("--no-copy", action="store_true", help="skip the fused copy + checksum timing")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="after timing, run one plain device copy of this many GiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -201,6 +202,44 @@ def main(argv=None):
     extra["offload_check"] = {"positions": int(req.num_blocks.sum()), "us_per_call": e0.elapsed_time(e1) / args.steps * 1e3,
                               "mismatches": int(cnt.item())}
     del hashes, stored, mism
+
+    if not args.no_copy and w.layout == "HND":
+        # connector save / load fused with the checksum, on the first half of the requests
+        half = req.num_reqs // 2
+        hb_t, hn_t, hs_t, ht_t = bt[:half].contiguous(), nb[:half].contiguous(), sp[:half].contiguous(), nt[:half].contiguous()
+        entries = int(req.num_blocks[:half].sum())
+        per = kvck.kvck_staging_bytes(pools[0], w.layout, w.num_layers)
+        staging = torch.empty(entries * per, dtype=torch.uint8, device=dev)
+        cout = torch.zeros((half, req.max_blocks), dtype=torch.uint64, device=dev)
+        cws = torch.empty(kvck.kvck_blocks_workspace_bytes(w.num_layers, half, req.max_blocks), dtype=torch.uint8,
+                          device=dev)
+        moved = 0
+        for r in range(half):
+            lo = int(req.start_pos[r]) * req.block_size
+            hi = min(int(req.num_tokens[r]), (int(req.start_pos[r]) + int(req.num_blocks[r])) * req.block_size)
+            moved += max(0, hi - lo)
+        moved *= w.num_layers * w.heads_used * w.planes * w.head_size * 2
+        res = {"valid_bytes": moved, "bytes_moved": 2 * moved}
+        for name, direction in (("save", kvck.KVCK_COPY_SAVE), ("load", kvck.KVCK_COPY_LOAD)):
+            def cstep():
+                kvck.kvck_copy_checksum_blocks(direction, pools, w.layout, w.layer_numbers, hb_t, hn_t, hs_t, ht_t,
+                                               staging, out=cout, workspace=cws, stream=stream)
+            cstep()
+            torch.cuda.synchronize()
+            kvck.kvck_instrument_read()
+            e0.record(stream)
+            for _ in range(max(2, args.steps // 4)):
+                cstep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cms = e0.elapsed_time(e1) / max(2, args.steps // 4)
+            cmain, cc = kvck.kvck_instrument_read()
+            cmain /= max(cc, 1)
+            res[name] = {"ms_per_call": cms, "main_pass_ms": cmain,
+                         "read_plus_write_GB_per_s": 2 * moved / (cmain * 1e-3) / 1e9,
+                         "frac_of_hbm_peak": 2 * moved / (cmain * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        extra["fused_copy_half_batch"] = res
+        del staging
 
     if not args.no_states:
         # Mamba running-state rows: the hybrid workload's 24 Mamba layers

@@ -75,6 +75,12 @@ typedef enum kvck_status {
                                        or start_pos < 0; the request is skipped */
 #define KVCK_FLAG_BAD_STATE_SLOT 4u /* a Mamba slot id outside [0, num_slots);
                                        the request's value is 0 */
+#define KVCK_FLAG_STAGING_FULL 8u   /* a listed position past the staging capacity:
+                                       neither copied nor checksummed (value 0) */
+
+/* Directions of kvck_copy_checksum_blocks. */
+#define KVCK_COPY_SAVE 0 /* paged pool -> staging buffer */
+#define KVCK_COPY_LOAD 1 /* staging buffer -> paged pool */
 
 /* A hipStream_t; NULL is the null stream. */
 typedef void* kvck_stream_t;
@@ -197,6 +203,41 @@ kvck_status kvck_checksum_states(
     kvck_stream_t stream);
 
 size_t kvck_states_workspace_bytes(int32_t num_layers, int32_t row_count, int32_t num_reqs);
+
+/*
+ * kvck_copy_checksum_blocks -- a connector's save or load of paged K/V fused
+ * with the checksum: every valid row is read once and written once, and the
+ * checksums of kvck_checksum_blocks come out of the same pass (all its
+ * arguments mean the same; on a load the pool is written).
+ *
+ * Staging layout (device, owned by the caller): entries are the listed
+ * positions in request order -- entry e of request r's k-th listed position is
+ * sum_{r'<r} num_blocks_per_req[r'] + k -- and each entry holds one block
+ * image per cache, in cache order.  An image is [plane][head][slot][row_bytes]
+ * over planes x head_count x block_size rows (kvck_staging_bytes(...) bytes
+ * per entry); only the valid slots of the position are copied, in either
+ * direction, and the rest of the image and of the pool block is left as is.
+ * Entries past staging_positions are flagged KVCK_FLAG_STAGING_FULL and
+ * skipped.  A load needs the same layout, heads and request structure as the
+ * save that filled the staging buffer.
+ */
+kvck_status kvck_copy_checksum_blocks(
+    int32_t direction,                     /* KVCK_COPY_SAVE or KVCK_COPY_LOAD */
+    const kvck_kv_layout* layout,
+    void* const* cache_ptrs,               /* host [num_caches] of device pointers */
+    const int32_t* layer_numbers, const int32_t* global_head_base, int32_t num_caches,
+    int32_t head_begin, int32_t head_count,
+    const int32_t* block_table, int64_t block_table_row_stride,
+    const int32_t* num_blocks_per_req, const int64_t* start_pos, const int64_t* num_tokens,
+    int32_t num_reqs, int32_t max_blocks,
+    void* staging, int64_t staging_positions,  /* device */
+    uint64_t* out, int32_t accumulate,
+    void* workspace, size_t workspace_bytes,
+    uint32_t* error_flags,
+    kvck_stream_t stream);
+
+/* Staging bytes of one entry (listed position) for kvck_copy_checksum_blocks. */
+size_t kvck_staging_bytes(const kvck_kv_layout* layout, int32_t num_caches, int32_t head_count);
 
 /*
  * kvck_tag_checksums -- tags of offloaded checksums and the load-time check.

@@ -11,7 +11,10 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     KVCK_FLAG_BAD_BLOCK_ID,
     KVCK_FLAG_BAD_REQUEST,
+    KVCK_COPY_LOAD,
+    KVCK_COPY_SAVE,
     KVCK_FLAG_BAD_STATE_SLOT,
+    KVCK_FLAG_STAGING_FULL,
     KvckDeviceError,
     KvckError,
     kv_layout,
@@ -19,9 +22,11 @@ from ._binding import (  # noqa: F401
     kvck_blocks_workspace_bytes,
     kvck_checksum_blocks,
     kvck_checksum_states,
+    kvck_copy_checksum_blocks,
     kvck_instrument,
     kvck_instrument_read,
     kvck_platform_supported,
+    kvck_staging_bytes,
     kvck_states_workspace_bytes,
     kvck_status_string,
     kvck_tag_checksums,

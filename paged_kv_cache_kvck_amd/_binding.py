@@ -25,10 +25,14 @@ STATUS_NAMES = {
 KVCK_FLAG_BAD_BLOCK_ID = 1
 KVCK_FLAG_BAD_REQUEST = 2
 KVCK_FLAG_BAD_STATE_SLOT = 4
+KVCK_FLAG_STAGING_FULL = 8
+KVCK_COPY_SAVE = 0
+KVCK_COPY_LOAD = 1
 
 # symbols include/kvck.h declares
 EXPORTS = ("kvck_checksum_blocks", "kvck_blocks_workspace_bytes", "kvck_checksum_states",
-           "kvck_states_workspace_bytes", "kvck_tag_checksums", "kvck_instrument", "kvck_instrument_read",
+           "kvck_states_workspace_bytes", "kvck_copy_checksum_blocks", "kvck_staging_bytes", "kvck_tag_checksums",
+           "kvck_instrument", "kvck_instrument_read",
            "kvck_status_string",
            "kvck_platform_supported", "kvck_abi_version")
 
@@ -44,7 +48,8 @@ class KvckDeviceError(RuntimeError):
 
     def __init__(self, flags: int):
         self.flags = flags
-        names = [n for bit, n in ((1, "BAD_BLOCK_ID"), (2, "BAD_REQUEST"), (4, "BAD_STATE_SLOT")) if flags & bit]
+        names = [n for bit, n in ((1, "BAD_BLOCK_ID"), (2, "BAD_REQUEST"), (4, "BAD_STATE_SLOT"),
+                                  (8, "STAGING_FULL")) if flags & bit]
         super().__init__("device reported " + "|".join(names))
 
 
@@ -90,6 +95,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kvck_platform_supported.argtypes = []
     lib.kvck_abi_version.restype = i32
     lib.kvck_abi_version.argtypes = []
+    lib.kvck_copy_checksum_blocks.restype = i32
+    lib.kvck_copy_checksum_blocks.argtypes = [
+        i32, ctypes.POINTER(kvck_kv_layout), ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(i32), i32,
+        i32, i32, vp, i64, vp, vp, vp, i32, i32, vp, i64, vp, i32, vp, sz, vp, vp]
+    lib.kvck_staging_bytes.restype = sz
+    lib.kvck_staging_bytes.argtypes = [ctypes.POINTER(kvck_kv_layout), i32, i32]
     lib.kvck_tag_checksums.restype = i32
     lib.kvck_tag_checksums.argtypes = [vp, vp, i64, ctypes.c_uint64, i64, vp, i32, vp, vp, vp, vp, vp]
     lib.kvck_instrument.restype = i32
@@ -190,19 +201,8 @@ def _meta(t: torch.Tensor, dtype, name, device, n=None):
     return t
 
 
-def kvck_checksum_blocks(caches: Sequence[torch.Tensor], layout: str, layer_numbers: Sequence[int],
-                         block_table: torch.Tensor, num_blocks_per_req: torch.Tensor, start_pos: torch.Tensor,
-                         num_tokens: torch.Tensor, global_head_base=None, head_begin: int = 0,
-                         head_count: int | None = None, out: torch.Tensor | None = None, accumulate: bool = False,
-                         workspace: torch.Tensor | None = None, error_flags: torch.Tensor | None = None,
-                         stream=None, check: bool = False) -> torch.Tensor:
-    """Per block position checksums of paged K/V (see include/kvck.h).
-
-    Returns ``out``: uint64 (num_reqs, max_blocks) on the caches' device;
-    entries past a request's listed positions are left as they were.
-    ``check=True`` zeroes a flag word, synchronizes, and raises
-    ``KvckDeviceError`` if the kernels flagged a bad block id or request.
-    """
+def _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req, start_pos, num_tokens,
+                 global_head_base, head_begin, head_count, out, workspace, check, error_flags):
     lib = load_library()
     caches = list(caches)
     if not caches:
@@ -242,18 +242,76 @@ def kvck_checksum_blocks(caches: Sequence[torch.Tensor], layout: str, layer_numb
     ptrs = (ctypes.c_void_p * n)(*[c.data_ptr() for c in caches])
     layers = (ctypes.c_int32 * n)(*[int(x) for x in layer_numbers])
     bases = (ctypes.c_int32 * n)(*[int(x) for x in global_head_base])
-    st = lib.kvck_checksum_blocks(
-        ctypes.byref(L), ptrs, layers, bases, n, int(head_begin), int(head_count),
-        block_table.data_ptr(), block_table.stride(0), num_blocks_per_req.data_ptr(), start_pos.data_ptr(),
-        num_tokens.data_ptr(), R, max_blocks, out.data_ptr(), int(bool(accumulate)), workspace.data_ptr(),
-        workspace.numel() * workspace.element_size(), _ptr(error_flags), _stream_handle(stream, dev))
-    _check(st, "kvck_checksum_blocks")
+    return dict(lib=lib, dev=dev, L=L, n=n, head_count=head_count, R=R, max_blocks=max_blocks, out=out,
+                workspace=workspace, error_flags=error_flags, ptrs=ptrs, layers=layers, bases=bases)
+
+
+def _finish(a, check):
     if check:
-        torch.cuda.synchronize(dev)
-        flags = int(error_flags.item())
+        torch.cuda.synchronize(a["dev"])
+        flags = int(a["error_flags"].item())
         if flags:
             raise KvckDeviceError(flags)
-    return out
+    return a["out"]
+
+
+def kvck_checksum_blocks(caches: Sequence[torch.Tensor], layout: str, layer_numbers: Sequence[int],
+                         block_table: torch.Tensor, num_blocks_per_req: torch.Tensor, start_pos: torch.Tensor,
+                         num_tokens: torch.Tensor, global_head_base=None, head_begin: int = 0,
+                         head_count: int | None = None, out: torch.Tensor | None = None, accumulate: bool = False,
+                         workspace: torch.Tensor | None = None, error_flags: torch.Tensor | None = None,
+                         stream=None, check: bool = False) -> torch.Tensor:
+    """Per block position checksums of paged K/V (see include/kvck.h).
+
+    Returns ``out``: uint64 (num_reqs, max_blocks) on the caches' device;
+    entries past a request's listed positions are left as they were.
+    ``check=True`` zeroes a flag word, synchronizes, and raises
+    ``KvckDeviceError`` if the kernels flagged a bad block id or request.
+    """
+    a = _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req, start_pos, num_tokens,
+                     global_head_base, head_begin, head_count, out, workspace, check, error_flags)
+    ws = a["workspace"]
+    st = a["lib"].kvck_checksum_blocks(
+        ctypes.byref(a["L"]), a["ptrs"], a["layers"], a["bases"], a["n"], int(head_begin), int(a["head_count"]),
+        block_table.data_ptr(), block_table.stride(0), num_blocks_per_req.data_ptr(), start_pos.data_ptr(),
+        num_tokens.data_ptr(), a["R"], a["max_blocks"], a["out"].data_ptr(), int(bool(accumulate)), ws.data_ptr(),
+        ws.numel() * ws.element_size(), _ptr(a["error_flags"]), _stream_handle(stream, a["dev"]))
+    _check(st, "kvck_checksum_blocks")
+    return _finish(a, check)
+
+
+def kvck_staging_bytes(cache: torch.Tensor, layout: str, num_caches: int, head_count: int | None = None) -> int:
+    """Staging bytes per listed position for kvck_copy_checksum_blocks."""
+    L = kv_layout(cache, layout)
+    return int(load_library().kvck_staging_bytes(ctypes.byref(L), int(num_caches),
+                                                 int(L.num_heads if head_count is None else head_count)))
+
+
+def kvck_copy_checksum_blocks(direction: int, caches: Sequence[torch.Tensor], layout: str,
+                              layer_numbers: Sequence[int], block_table: torch.Tensor,
+                              num_blocks_per_req: torch.Tensor, start_pos: torch.Tensor, num_tokens: torch.Tensor,
+                              staging: torch.Tensor, global_head_base=None, head_begin: int = 0,
+                              head_count: int | None = None, out: torch.Tensor | None = None,
+                              accumulate: bool = False, workspace: torch.Tensor | None = None,
+                              error_flags: torch.Tensor | None = None, stream=None, check: bool = False):
+    """A connector save (KVCK_COPY_SAVE: pool -> staging) or load
+    (KVCK_COPY_LOAD: staging -> pool) fused with the checksum; see
+    include/kvck.h for the staging layout.  Returns the checksums."""
+    a = _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req, start_pos, num_tokens,
+                     global_head_base, head_begin, head_count, out, workspace, check, error_flags)
+    if staging.device != a["dev"] or not staging.is_contiguous():
+        raise ValueError("staging must be a contiguous tensor on the caches' device")
+    per = int(a["lib"].kvck_staging_bytes(ctypes.byref(a["L"]), a["n"], int(a["head_count"])))
+    positions = (staging.numel() * staging.element_size()) // per
+    ws = a["workspace"]
+    st = a["lib"].kvck_copy_checksum_blocks(
+        int(direction), ctypes.byref(a["L"]), a["ptrs"], a["layers"], a["bases"], a["n"], int(head_begin),
+        int(a["head_count"]), block_table.data_ptr(), block_table.stride(0), num_blocks_per_req.data_ptr(),
+        start_pos.data_ptr(), num_tokens.data_ptr(), a["R"], a["max_blocks"], staging.data_ptr(), positions,
+        a["out"].data_ptr(), int(bool(accumulate)), ws.data_ptr(), ws.numel() * ws.element_size(),
+        _ptr(a["error_flags"]), _stream_handle(stream, a["dev"]))
+    _check(st, "kvck_copy_checksum_blocks")
+    return _finish(a, check)
 
 
 def state_desc(state: torch.Tensor) -> kvck_state_desc:

@@ -74,7 +74,7 @@ constexpr int64_t kPipeMinTasksPerWave = 64;
 static_assert(kCachesPerLaunch % kPipeMaxCaches == 0, "launch groups must not straddle launches");
 
 void choose_schedule(BlocksShape* shp, int32_t num_caches, int64_t max_items, int64_t block_bytes, int planes,
-                     int heads, int cus) {
+                     int heads, int cus, bool copy) {
   const int64_t waves = (int64_t)cus * 8;  // resident waves of the pipelined kernel (2 per SIMD)
   int lpt = 1;
   while (lpt < kPipeMaxCaches && (int64_t)(2 * lpt) * block_bytes <= kPipeTaskBytes) lpt *= 2;
@@ -85,6 +85,7 @@ void choose_schedule(BlocksShape* shp, int32_t num_caches, int64_t max_items, in
     if (strcmp(force, "pipelined") == 0) pipe = true;
     if (strcmp(force, "simple") == 0) pipe = false;
   }
+  if (copy) pipe = true;  // the fused copy kernel always runs the pipelined structure
   if (pipe) {
     shp->pipelined = true;
     shp->caches_per_task = lpt;
@@ -176,15 +177,19 @@ KVCK_EXPORT size_t kvck_blocks_workspace_bytes(int32_t num_caches, int32_t num_r
   return BlocksWorkspace::make(num_caches, num_reqs, max_blocks).total;
 }
 
-KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const void* const* cache_ptrs,
-                                             const int32_t* layer_numbers, const int32_t* global_head_base,
-                                             int32_t num_caches, int32_t head_begin, int32_t head_count,
-                                             const int32_t* block_table, int64_t block_table_row_stride,
-                                             const int32_t* num_blocks_per_req, const int64_t* start_pos,
-                                             const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks,
-                                             uint64_t* out, int32_t accumulate, void* workspace,
-                                             size_t workspace_bytes, uint32_t* error_flags,
-                                             kvck_stream_t stream) {
+namespace {
+constexpr int kModeChecksum = -1;  // kvck_checksum_blocks; otherwise a KVCK_COPY_* direction
+
+// kvck_checksum_blocks and kvck_copy_checksum_blocks: validation, plan, main
+// pass (checksum only, or fused copy), second pass.
+kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* const* cache_ptrs,
+                        const int32_t* layer_numbers, const int32_t* global_head_base, int32_t num_caches,
+                        int32_t head_begin, int32_t head_count, const int32_t* block_table,
+                        int64_t block_table_row_stride, const int32_t* num_blocks_per_req, const int64_t* start_pos,
+                        const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks, uint64_t* out,
+                        int32_t accumulate, void* workspace, size_t workspace_bytes, uint32_t* error_flags,
+                        void* staging, int64_t staging_positions, kvck_stream_t stream) {
+  if (mode != kModeChecksum && mode != KVCK_COPY_SAVE && mode != KVCK_COPY_LOAD) return KVCK_ERR_INVALID_ARGUMENT;
   // ---- layout
   if (!layout || !cache_ptrs || !layer_numbers || !global_head_base) return KVCK_ERR_INVALID_ARGUMENT;
   const kvck_kv_layout L = *layout;
@@ -215,6 +220,7 @@ KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const
               (L.planes == 1 || L.plane_stride % chunk == 0) && (L.block_size == 1 || L.slot_stride % chunk == 0) &&
               (L.num_heads == 1 || L.head_stride % chunk == 0);
     for (int32_t i = 0; ok && i < num_caches; ++i) ok = aligned(cache_ptrs[i], chunk);
+    if (mode != kModeChecksum) ok = ok && aligned(staging, chunk);
     if (ok) break;
     if (chunk == 8) return KVCK_ERR_MISALIGNED;
     chunk = 8;
@@ -226,6 +232,12 @@ KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const
   const int64_t pieces = (int64_t)L.planes * L.row_bytes / 8;
   if (2 * (int64_t)shp.rows_per_group * pieces + 4 * (L.row_bytes / chunk) >= ((int64_t)1 << 32))
     return KVCK_ERR_UNSUPPORTED;
+  // ---- staging (fused copy)
+  const int64_t image_bytes = (int64_t)L.planes * head_count * L.block_size * L.row_bytes;
+  if (mode != kModeChecksum) {
+    if (!staging || staging_positions < 0) return KVCK_ERR_INVALID_ARGUMENT;
+    if ((int64_t)L.block_size * L.row_bytes >= ((int64_t)1 << 31)) return KVCK_ERR_UNSUPPORTED;
+  }
   // ---- workspace
   const BlocksWorkspace w = BlocksWorkspace::make(num_caches, num_reqs, max_blocks);
   if (!workspace || workspace_bytes < w.total || !aligned(workspace, (int64_t)kAlign)) return KVCK_ERR_WORKSPACE;
@@ -236,8 +248,8 @@ KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const
   hipStream_t st = static_cast<hipStream_t>(stream);
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  choose_schedule(&shp, num_caches, (int64_t)num_reqs * max_blocks,
-                  (int64_t)head_count * L.planes * L.block_size * L.row_bytes, L.planes, head_count, cus);
+  choose_schedule(&shp, num_caches, (int64_t)num_reqs * max_blocks, image_bytes, L.planes, head_count, cus,
+                  mode != kModeChecksum);
   const int32_t lpt = shp.caches_per_task;
   const int32_t total_groups = (num_caches + lpt - 1) / lpt;
 
@@ -278,8 +290,23 @@ KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const
       a.base[i] = static_cast<const uint8_t*>(cache_ptrs[c0 + i]) + (int64_t)head_begin * L.head_stride;
       a.mbase[i] = (uint32_t)(2 * ((int64_t)layer_numbers[c0 + i] * kH + global_head_base[c0 + i]) + 1);
     }
-    const int grid = blocks_grid(shp, dev, max_items * ((n + lpt - 1) / lpt));
-    if (launch_blocks(a, shp, grid, st) != hipSuccess) return KVCK_ERR_HIP;
+    if (mode == kModeChecksum) {
+      const int grid = blocks_grid(shp, dev, max_items * ((n + lpt - 1) / lpt));
+      if (launch_blocks(a, shp, grid, st) != hipSuccess) return KVCK_ERR_HIP;
+    } else {
+      CopyArgs ca;
+      memset(&ca, 0, sizeof(ca));
+      ca.b = a;
+      ca.staging = static_cast<uint8_t*>(staging);
+      ca.staging_positions = staging_positions;
+      ca.image_bytes = image_bytes;
+      ca.error_flags = error_flags;
+      ca.num_caches_total = num_caches;
+      ca.cache_offset = c0;
+      ca.block_size = L.block_size;
+      const int grid = copy_grid(shp, mode, dev, max_items * ((n + lpt - 1) / lpt));
+      if (launch_copy(ca, shp, mode, grid, st) != hipSuccess) return KVCK_ERR_HIP;
+    }
   }
   if (timed && hipEventRecord(ev1, st) != hipSuccess) return KVCK_ERR_HIP;
   if (total_groups > 1) {
@@ -287,6 +314,47 @@ KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const
       return KVCK_ERR_HIP;
   }
   return KVCK_OK;
+}
+}  // namespace
+
+KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const void* const* cache_ptrs,
+                                             const int32_t* layer_numbers, const int32_t* global_head_base,
+                                             int32_t num_caches, int32_t head_begin, int32_t head_count,
+                                             const int32_t* block_table, int64_t block_table_row_stride,
+                                             const int32_t* num_blocks_per_req, const int64_t* start_pos,
+                                             const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks,
+                                             uint64_t* out, int32_t accumulate, void* workspace,
+                                             size_t workspace_bytes, uint32_t* error_flags,
+                                             kvck_stream_t stream) {
+  return blocks_call(kModeChecksum, layout, cache_ptrs, layer_numbers, global_head_base, num_caches, head_begin,
+                     head_count, block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens,
+                     num_reqs, max_blocks, out, accumulate, workspace, workspace_bytes, error_flags, nullptr, 0,
+                     stream);
+}
+
+KVCK_EXPORT kvck_status kvck_copy_checksum_blocks(int32_t direction, const kvck_kv_layout* layout,
+                                                  void* const* cache_ptrs, const int32_t* layer_numbers,
+                                                  const int32_t* global_head_base, int32_t num_caches,
+                                                  int32_t head_begin, int32_t head_count,
+                                                  const int32_t* block_table, int64_t block_table_row_stride,
+                                                  const int32_t* num_blocks_per_req, const int64_t* start_pos,
+                                                  const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks,
+                                                  void* staging, int64_t staging_positions, uint64_t* out,
+                                                  int32_t accumulate, void* workspace, size_t workspace_bytes,
+                                                  uint32_t* error_flags, kvck_stream_t stream) {
+  if (direction != KVCK_COPY_SAVE && direction != KVCK_COPY_LOAD) return KVCK_ERR_INVALID_ARGUMENT;
+  return blocks_call(direction, layout, cache_ptrs, layer_numbers, global_head_base, num_caches, head_begin,
+                     head_count, block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens,
+                     num_reqs, max_blocks, out, accumulate, workspace, workspace_bytes, error_flags, staging,
+                     staging_positions, stream);
+}
+
+KVCK_EXPORT size_t kvck_staging_bytes(const kvck_kv_layout* layout, int32_t num_caches, int32_t head_count) {
+  if (!layout || num_caches < 1 || head_count < 1 || layout->planes < 1 || layout->block_size < 1 ||
+      layout->row_bytes < 1)
+    return 0;
+  return (size_t)layout->planes * (size_t)head_count * (size_t)layout->block_size * (size_t)layout->row_bytes *
+         (size_t)num_caches;
 }
 
 namespace {

@@ -1,0 +1,220 @@
+// Fused copy + checksum of paged K/V blocks on gfx950: a connector's save
+// (pool -> staging buffer) or load (staging buffer -> pool) that also yields
+// the block checksums of the vLLM API page
+// "vllm.distributed.kv_transfer.kv_checksum.checksum", from one read and one
+// write of every valid row.
+//
+// Staging layout: listed positions in request order (entry e of request r's
+// k-th listed position is sum_{r'<r} listed(r') + k), and per entry one block
+// image per cache of the call, in cache order; an image is
+//   [plane][head][slot][row_bytes]      (planes x head_count x block_size rows)
+// holding only the valid slots of the position (slots at or past num_tokens
+// are neither read nor written, on either side).
+//
+// The kernel is the pipelined main pass with a second lane table for the
+// staging side: unit i+1's loads are in flight while unit i is stored to the
+// other side and folded into the checksum.
+#include "kvck_device.h"
+
+namespace kvck {
+namespace {
+
+template <int CHUNK>
+__device__ __forceinline__ void store_chunk(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                            const typename ChunkType<CHUNK>::T& v) {
+  if constexpr (CHUNK == 16)
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kNonTemporal);
+  else
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kNonTemporal);
+}
+
+template <int CHUNK, int S, int HU, int PU, int DIR>
+__global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) {
+  using V = typename ChunkType<CHUNK>::T;
+  const BlocksArgs& a = ca.b;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  const int64_t n_items = (int64_t)*a.n_items;
+  const int lpt = a.caches_per_task;
+  const int ngroups = (a.num_caches + lpt - 1) / lpt;
+  const int64_t total = n_items * ngroups;
+  if (wave >= total) return;
+
+  LaneTable<S> lt;
+  lt.template init<CHUNK>(lane, a);
+  uint32_t ioff[S];  // staging-side offsets of the same chunks: rows are row_bytes apart
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int f = lane + kWave * s;
+    const int r = f / a.chunks_per_row;
+    ioff[s] = (uint32_t)((int64_t)r * a.row_bytes + (int64_t)(f - r * a.chunks_per_row) * CHUNK);
+  }
+  const uint64_t P = (uint64_t)a.pieces;
+  const int rg = a.rows_per_group;
+  const uint64_t plane_term = 2ull * (P / (uint64_t)a.planes);
+  const int nhb = (a.heads + HU - 1) / HU;
+  const int64_t img_head = (int64_t)ca.block_size * a.row_bytes;
+  const int64_t img_plane = img_head * a.heads;
+
+  for (int64_t task = wave; task < total; task += nwaves) {
+    const int64_t grp = task / n_items;
+    const int64_t item = task - grp * n_items;
+    const int c_begin = (int)grp * lpt;
+    const int c_end = min(a.num_caches, c_begin + lpt);
+    const PosRecord* rp = a.recs + item;
+    int32_t v = __builtin_amdgcn_readfirstlane(rp->valid);
+    const int32_t blk = __builtin_amdgcn_readfirstlane(rp->block);
+    const uint64_t t0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(rp->t0 >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)rp->t0);
+    const int64_t out_idx = rp->out_idx;
+    if (item >= ca.staging_positions) {
+      if (v > 0 && lane == 0 && ca.error_flags) atomicOr(ca.error_flags, KVCK_FLAG_STAGING_FULL);
+      v = 0;
+    }
+    uint64_t acc = 0;
+    if (v > 0) {
+      const int64_t blk_off = (int64_t)blk * a.block_stride;
+      uint8_t* const img0 = ca.staging + (item * ca.num_caches_total + ca.cache_offset) * ca.image_bytes;
+      const int ngr = (v + rg - 1) / rg;
+      const int nplanes = a.planes / PU;
+      const int nunits = ngr * nplanes * nhb * (c_end - c_begin);
+      UnitCursor ic{c_begin, 0, 0, 0}, cc{c_begin, 0, 0, 0};
+
+      // base of (cache, group, plane, head) on the pool side and on the staging side
+      auto pool_base = [&](const UnitCursor& u, int p, int hh) {
+        return a.base[u.cache] + blk_off + (int64_t)(u.group * rg) * a.slot_stride +
+               (int64_t)(u.plane * PU + p) * a.plane_stride + (int64_t)hh * a.head_stride;
+      };
+      auto img_base = [&](const UnitCursor& u, int p, int hh) {
+        return img0 + (int64_t)u.cache * ca.image_bytes + (int64_t)(u.plane * PU + p) * img_plane +
+               (int64_t)hh * img_head + (int64_t)(u.group * rg) * a.row_bytes;
+      };
+      auto issue = [&](V(&x)[PU][HU][S]) {
+        const int rows = min(rg, v - ic.group * rg);
+#pragma unroll
+        for (int p = 0; p < PU; ++p) {
+#pragma unroll
+          for (int h = 0; h < HU; ++h) {
+            const int hh = ic.hbatch * HU + h;
+            const uint32_t hmask = hh < a.heads ? 0u : kOOB;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(DIR == 0 ? pool_base(ic, p, hh) : img_base(ic, p, hh));
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+              x[p][h][s] = load_chunk<CHUNK>(rs, (lt.row[s] < rows ? (DIR == 0 ? lt.off[s] : ioff[s]) : kOOB) | hmask);
+          }
+        }
+        ic.next(nhb, nplanes, ngr);
+      };
+      auto store_consume = [&](const V(&x)[PU][HU][S]) {
+        const int rows = min(rg, v - cc.group * rg);
+        const uint32_t mb = a.mbase[cc.cache];
+#pragma unroll
+        for (int p = 0; p < PU; ++p) {
+          const uint64_t up = 2ull * (t0 + (uint64_t)(cc.group * rg)) * P + 1ull +
+                              (uint64_t)(cc.plane * PU + p) * plane_term;
+#pragma unroll
+          for (int h = 0; h < HU; ++h) {
+            const int hh = cc.hbatch * HU + h;
+            const uint32_t hmask = hh < a.heads ? 0u : kOOB;
+            const __amdgpu_buffer_rsrc_t rd = make_rsrc(DIR == 0 ? img_base(cc, p, hh) : pool_base(cc, p, hh));
+            uint64_t sh = 0;
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+              store_chunk<CHUNK>(rd, (lt.row[s] < rows ? (DIR == 0 ? ioff[s] : lt.off[s]) : kOOB) | hmask,
+                                 x[p][h][s]);
+              const uint64_t u = up + lt.urel[s];
+              const uint64_t xa = (uint64_t)x[p][h][s].x | ((uint64_t)x[p][h][s].y << 32);
+              if constexpr (CHUNK == 16) {
+                const uint64_t xb = (uint64_t)x[p][h][s].z | ((uint64_t)x[p][h][s].w << 32);
+                sh += (xa + xb) * u + (xb << 1);
+              } else {
+                sh += xa * u;
+              }
+            }
+            acc += sh * (uint64_t)(mb + 2u * (uint32_t)hh);
+          }
+        }
+        cc.next(nhb, nplanes, ngr);
+      };
+
+      V A[PU][HU][S], B[PU][HU][S];
+      issue(A);
+      for (int ui = 0; ui < nunits; ui += 2) {
+        if (ui + 1 < nunits) issue(B);
+        store_consume(A);
+        if (ui + 1 < nunits) {
+          if (ui + 2 < nunits) issue(A);
+          store_consume(B);
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      if (a.direct) {
+        uint64_t* o = a.out + out_idx;
+        *o = a.accumulate ? *o + acc : acc;
+      } else {
+        a.partials[(int64_t)(a.group_offset + grp) * a.max_items + item] = acc;
+      }
+    }
+  }
+}
+
+using CopyFn = void (*)(const CopyArgs);
+
+template <int CHUNK, int S, int PU, int DIR>
+constexpr CopyFn pick() {
+  constexpr int hu = 16 / (S * PU) > 0 ? 16 / (S * PU) : 1;
+  return &copy_kernel<CHUNK, S, hu, PU, DIR>;
+}
+
+template <int CHUNK, int PU, int DIR>
+CopyFn copy_fn_slots(int slots) {
+  switch (slots) {
+    case 1: return pick<CHUNK, 1, PU, DIR>();
+    case 2: return pick<CHUNK, 2, PU, DIR>();
+    case 4: return pick<CHUNK, 4, PU, DIR>();
+    case 8: return pick<CHUNK, 8, 1, DIR>();
+    case 16: return pick<CHUNK, 16, 1, DIR>();
+  }
+  return nullptr;
+}
+
+template <int DIR>
+CopyFn copy_fn_dir(const BlocksShape& shp) {
+  if (shp.planes_per_unit == 2)
+    return shp.chunk == 16 ? copy_fn_slots<16, 2, DIR>(shp.slots) : copy_fn_slots<8, 2, DIR>(shp.slots);
+  return shp.chunk == 16 ? copy_fn_slots<16, 1, DIR>(shp.slots) : copy_fn_slots<8, 1, DIR>(shp.slots);
+}
+
+CopyFn copy_fn(const BlocksShape& shp, int direction) {
+  return direction == KVCK_COPY_SAVE ? copy_fn_dir<0>(shp) : copy_fn_dir<1>(shp);
+}
+
+}  // namespace
+
+int copy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks) {
+  CopyFn fn = copy_fn(shp, direction);
+  int per_cu = 0;
+  if (!fn ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kBlockThreads, 0) !=
+          hipSuccess ||
+      per_cu <= 0)
+    per_cu = 1;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0) cus = 256;
+  const int64_t waves_per_block = kBlockThreads / kWave;
+  const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
+  const int64_t cap = (int64_t)per_cu * cus;
+  return (int)(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
+hipError_t launch_copy(const CopyArgs& a, const BlocksShape& shp, int direction, int grid, hipStream_t stream) {
+  CopyFn fn = copy_fn(shp, direction);
+  if (!fn) return hipErrorInvalidValue;
+  void* args[] = {const_cast<CopyArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(kBlockThreads), args, 0, stream);
+}
+
+}  // namespace kvck

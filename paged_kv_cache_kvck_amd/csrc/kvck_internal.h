@@ -63,6 +63,18 @@ struct BlocksArgs {
   uint32_t mbase[kCachesPerLaunch];          // 2*(layer*H + global_head_base) + 1
 };
 
+// Arguments of the fused copy + checksum kernel.
+struct CopyArgs {
+  BlocksArgs b;              // pool side, records, caches, outputs
+  uint8_t* staging;          // device: entries x caches x block images
+  int64_t staging_positions; // capacity in entries (listed positions)
+  int64_t image_bytes;       // planes * heads * block_size * row_bytes
+  uint32_t* error_flags;
+  int32_t num_caches_total;  // caches of the call (images per entry)
+  int32_t cache_offset;      // global index of this launch's first cache
+  int32_t block_size;
+};
+
 struct StatesArgs {
   int64_t slot_stride[KVCK_MAX_STATES_PER_LAYER];
   int64_t row_stride[KVCK_MAX_STATES_PER_LAYER];
@@ -102,6 +114,8 @@ hipError_t launch_reduce(const uint64_t* partials, int64_t stride, int32_t split
                          int64_t n_fixed, const PosRecord* recs, uint64_t* out, int32_t accumulate,
                          hipStream_t stream);
 hipError_t launch_states(const StatesArgs& a, int grid, hipStream_t stream);
+hipError_t launch_copy(const CopyArgs& a, const BlocksShape& shp, int direction, int grid, hipStream_t stream);
+int copy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks);
 hipError_t launch_tags(const uint64_t* checksums, const uint8_t* hashes, int64_t hash_stride, uint64_t fingerprint,
                        int64_t n, const int32_t* nbpr, int32_t max_blocks, uint64_t* tagged, const uint64_t* stored,
                        uint8_t* mismatch, uint32_t* count, hipStream_t stream);

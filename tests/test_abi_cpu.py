@@ -25,7 +25,7 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = kvck.load_library()
     decl = header_functions()
-    assert len(decl) == 10
+    assert len(decl) == 12
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTS) == decl

@@ -1,0 +1,136 @@
+"""Fused copy + checksum (connector save / load) on the GPU.
+
+Save: the checksums equal the oracle's and the staging buffer holds exactly
+the specified block images (valid slots only, request order, cache order,
+[plane][head][slot][row]); load: a pool paged on other block ids receives the
+same valid rows, and the checksums are the same (GPU)."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_kvck_amd as kvck
+from paged_kv_cache_kvck_amd import workloads as wl
+from gpu_helpers import DEV, log, req_tensors, to_device_bits, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, layout, elem, layers, heads, head_size, block_size, lengths, start, extra, head_begin, head_count
+    ("nhd_bf16", "NHD", "bf16", [0, 1, 2], 2, 64, 16, [50, 17, 33, 1], None, [0, 1, 0, 2], 0, None),
+    ("hnd_d128", "HND", "bf16", [3, 9], 8, 128, 16, [77, 130, 16], [1, 0, 0], None, 0, None),
+    ("hnd_shard", "HND", "bf16", [0, 1, 2, 3, 4], 8, 128, 16, [90, 40], None, None, 2, 2),
+    ("nhd_fp8_12h", "NHD", "fp8", [5], 12, 64, 16, [100, 31, 2], None, None, 0, None),
+    ("mla_bs64", "MLA", "bf16", [0, 1, 60], 1, 576, 64, [130, 64, 3], None, None, 0, None),
+    ("nhd_8byte_rows", "NHD", "bf16", [0, 3], 3, 4, 4, [13, 6], None, None, 0, None),
+    ("nhd_bs64_fp16", "NHD", "fp16", [0, 1], 12, 64, 64, [300, 65], None, None, 0, None),
+]
+
+
+def _row(pool, layout, plane, b, i, h):
+    if layout == "NHD":
+        return pool[plane, b, i, h]
+    if layout == "HND":
+        return pool[plane, b, h, i]
+    return pool[b, i]
+
+
+def _expected_images(pools, layout, req, head_begin, head_count, bs, row_bytes):
+    """uint8 [entries, caches, planes, heads, bs, row_bytes]: valid slots only, the rest 0."""
+    planes = 1 if layout == "MLA" else 2
+    listed = req.listed()
+    img = np.zeros((len(listed), len(pools), planes, head_count, bs, row_bytes), np.uint8)
+    for e, (r, k) in enumerate(listed):
+        pos = int(req.start_pos[r]) + k
+        v = min(bs, max(0, int(req.num_tokens[r]) - pos * bs))
+        b = int(req.block_table[r, k])
+        for c, p in enumerate(pools):
+            for pl in range(planes):
+                for hh in range(head_count):
+                    for i in range(v):
+                        img[e, c, pl, hh, i] = np.frombuffer(
+                            np.ascontiguousarray(_row(p, layout, pl, b, i, head_begin + hh)).tobytes(), np.uint8)
+    return img
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_copy_save_and_load(case):
+    name, layout, elem, layers, nh, d, bs, lengths, start, extra, hb, hc = case
+    log(f"[copy] {name}")
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    req, nb = wl.page_requests(rng, lengths, bs, start_pos=start, extra_blocks=extra, spare_frac=0.3)
+    shape = wl.pool_shape(layout, nb, bs, nh, d)
+    hp = [wl.host_random_bits(rng, shape, elem) for _ in layers]
+    pools = [to_device_bits(p) for p in hp]
+    n_heads = (nh - hb) if hc is None else hc
+    bases = [hb + 3] * len(layers)
+    bt, nbt, sp, nt = req_tensors(req)
+    per = kvck.kvck_staging_bytes(pools[0], layout, len(layers), n_heads)
+    n_entries = int(req.num_blocks.sum())
+    staging = torch.zeros(n_entries * per, dtype=torch.uint8, device=DEV)
+    got = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, pools, layout, layers, bt, nbt, sp, nt, staging,
+                                         global_head_base=bases, head_begin=hb, head_count=hc, check=True)
+    got = got.cpu().numpy()
+    want = oracle.checksum_blocks(hp, layout, layers, bases, req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens, head_begin=hb, head_count=n_heads)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k]), (r, k)
+    row_bytes = d * wl.ELEM_BYTES[elem]
+    exp = _expected_images(hp, layout, req, hb, n_heads, bs, row_bytes)
+    assert np.array_equal(staging.cpu().numpy().reshape(exp.shape), exp)
+
+    # load into a pool paged on a different permutation of block ids
+    req2, _ = wl.page_requests(np.random.default_rng(99), lengths, bs, pool_blocks=nb, start_pos=start,
+                               extra_blocks=extra)
+    dst_h = [np.zeros(shape, wl.HOST_BITS[elem]) for _ in layers]
+    dst = [to_device_bits(p) for p in dst_h]
+    bt2, nbt2, sp2, nt2 = req_tensors(req2)
+    got2 = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_LOAD, dst, layout, layers, bt2, nbt2, sp2, nt2, staging,
+                                          global_head_base=bases, head_begin=hb, head_count=hc, check=True)
+    got2 = got2.cpu().numpy()
+    for r, k in req.listed():
+        assert got2[r, k] == got[r, k], (r, k)
+    # the destination holds the source rows at the valid slots, zeros elsewhere
+    dst_back = [to_host_bits(t) for t in dst]
+    assert np.array_equal(_expected_images(dst_back, layout, req2, hb, n_heads, bs, row_bytes), exp)
+    again = kvck.kvck_checksum_blocks(dst, layout, layers, bt2, nbt2, sp2, nt2, global_head_base=bases,
+                                      head_begin=hb, head_count=hc, check=True).cpu().numpy()
+    for r, k in req.listed():
+        assert again[r, k] == got[r, k]
+
+
+def test_copy_staging_full_is_flagged():
+    log("[copy] staging full")
+    rng = np.random.default_rng(5)
+    req, nb = wl.page_requests(rng, [40, 40], 16, spare_frac=0.5)
+    pools = [to_device_bits(wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 16, 2, 64), "bf16"))]
+    bt, nbt, sp, nt = req_tensors(req)
+    per = kvck.kvck_staging_bytes(pools[0], "NHD", 1)
+    staging = torch.zeros(3 * per, dtype=torch.uint8, device=DEV)     # 6 listed positions, room for 3
+    with pytest.raises(kvck.KvckDeviceError) as ei:
+        kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, pools, "NHD", [0], bt, nbt, sp, nt, staging, check=True)
+    assert ei.value.flags & kvck.KVCK_FLAG_STAGING_FULL
+
+
+def test_copy_many_caches():
+    """More caches than one argument block: several launches, image offsets by global cache index."""
+    log("[copy] 70 caches")
+    rng = np.random.default_rng(6)
+    req, nb = wl.page_requests(rng, [40, 9], 16, spare_frac=0.5)
+    hp = [wl.host_random_bits(rng, wl.pool_shape("HND", nb, 16, 2, 16), "bf16") for _ in range(70)]
+    pools = [to_device_bits(p) for p in hp]
+    layers = list(range(70))
+    bt, nbt, sp, nt = req_tensors(req)
+    per = kvck.kvck_staging_bytes(pools[0], "HND", 70)
+    staging = torch.zeros(int(req.num_blocks.sum()) * per, dtype=torch.uint8, device=DEV)
+    got = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, pools, "HND", layers, bt, nbt, sp, nt, staging,
+                                         check=True).cpu().numpy()
+    want = oracle.checksum_blocks(hp, "HND", layers, [0] * 70, req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k])
+    exp = _expected_images(hp, "HND", req, 0, 2, 16, 32)
+    assert np.array_equal(staging.cpu().numpy().reshape(exp.shape), exp)
