@@ -5,17 +5,17 @@
  * The checksum is the one defined on the vLLM API page
  * "vllm.distributed.kv_transfer.kv_checksum.checksum" (module docstring):
  *
- *   item 1  A slice is the K and V of one layer and one KV head of a block,
- *           token by token, cut into little-endian 8-byte pieces x_j with
- *           j = t*P + p (t: token position in the request, p: piece within
- *           the token, P pieces per token):
- *               s = sum_j x_j * (2j + 1)                    mod 2^64
- *   item 2  A block position's checksum weighs every slice by an odd factor:
- *               c = sum_{layer, head} m * s                 mod 2^64
- *               m = 2 * (layer * H + global_head) + 1,  H = 65536
- *   Mamba   A Mamba group's block is the request's running state at position
- *           0; each global row of its states is one slice whose pieces are
- *           the 2- or 4-byte elements read unsigned.
+ *   item 1  For each (layer, KV head) of a block, the K bytes then the V bytes
+ *           of every token, in token order, form a slice; it is read as
+ *           little-endian uint64 pieces x_j, j = t*P + p for the p-th piece
+ *           of the token at request position t (P pieces per token), and
+ *               s(layer, head) = sum over j of x_j (2j + 1)        mod 2^64
+ *   item 2  The block position's checksum weighs each slice by an odd factor:
+ *               c = sum over (layer, head) of m s(layer, head)     mod 2^64
+ *               m = 2 (layer * 65536 + global head) + 1
+ *   Mamba   For a Mamba group the request's running state takes the place of
+ *           its blocks (position 0); each global row of the layer's states is
+ *           a slice, its pieces the 2- or 4-byte elements as unsigned ints.
  *
  * Conventions shared by every entry point:
  *  - Pointers marked "device" are HIP device pointers on the current device;
@@ -24,7 +24,7 @@
  *    owns every buffer.
  *  - Calls are asynchronous and ordered on `stream`.  Results are valid once
  *    the stream has reached the call; the cache bytes must not change until
- *    then (checksums are taken "when their KV is final").
+ *    then (a checksum only means something once the KV is complete).
  *  - A negative return value means the call launched nothing.  Errors found
  *    only on the device (a bad block id, a bad request entry, a bad state
  *    slot) are reported by OR-ing KVCK_FLAG_* bits into *error_flags (if not
@@ -45,8 +45,8 @@ extern "C" {
 
 #define KVCK_ABI_VERSION 1
 
-/* H of the slice factor; groups with more KV heads per layer (or Mamba rows)
- * are not checksummed (page attribute MAX_KV_HEADS_PER_LAYER = 1 << 16). */
+/* The page attribute MAX_KV_HEADS_PER_LAYER (2^16): H of the slice factor and
+ * a bound on a layer's KV heads (or Mamba rows); calls beyond it are refused. */
 #define KVCK_MAX_KV_HEADS_PER_LAYER 65536
 /* Largest accepted layer number: keeps every factor m below 2^32. */
 #define KVCK_MAX_LAYER_NUMBER 32767
@@ -97,15 +97,31 @@ typedef void* kvck_stream_t;
  * planes = 1, num_heads = 1.
  */
 typedef struct kvck_kv_layout {
-  int32_t planes;       /* 2: plane 0 = K, plane 1 = V;  1: one latent plane */
+  int32_t planes;       /* planes of a token's slice: 2 = K then V; 1 = one latent plane */
   int32_t block_size;   /* slots per block, >= 1 */
   int32_t num_heads;    /* KV heads held by the pool tensor, >= 1 */
   int32_t row_bytes;    /* head_size * element bytes; multiple of 8 */
   int64_t num_blocks;   /* blocks in the pool; valid ids are [0, num_blocks) */
-  int64_t plane_stride; /* bytes; ignored when planes == 1 */
+  int64_t plane_stride; /* bytes between the planes the call covers */
   int64_t block_stride; /* bytes */
   int64_t slot_stride;  /* bytes */
   int64_t head_stride;  /* bytes; ignored when num_heads == 1 */
+  /* Optional (0 = default).  A row stored as contiguous runs of chunk_bytes
+   * (a multiple of 8 dividing row_bytes), consecutive runs chunk_stride bytes
+   * apart -- e.g. the x-split K layout [num_blocks, num_heads, head_size/x,
+   * block_size, x] (page "[vLLM 源码解析] KV Cache", the reshape_and_cache
+   * section): chunk_bytes = x*element bytes, chunk_stride = block_size*x*
+   * element bytes, slot_stride = x*element bytes.  0: the row is contiguous. */
+  int32_t chunk_bytes;
+  int32_t reserved0;
+  int64_t chunk_stride;
+  /* Optional: the call covers planes plane_begin .. plane_begin+plane_count-1
+   * of the slice (plane_count 0 = all planes).  Pieces keep their numbering
+   * in the whole slice, so calls over K and over V (e.g. separate K and V
+   * tensors, each its own cache_ptrs) add up to the checksum of both; the
+   * cache pointers address the call's first plane. */
+  int32_t plane_begin;
+  int32_t plane_count;
 } kvck_kv_layout;
 
 /*
@@ -114,10 +130,10 @@ typedef struct kvck_kv_layout {
  * A token's slice bytes are its K row then its V row (planes == 2) or its
  * latent row (planes == 1); P = planes*row_bytes/8.  Request r lists
  * num_blocks_per_req[r] blocks, block_table[r*block_table_row_stride + k]
- * at block position start_pos[r] + k (the page's KVChecksumBlocks: "the
- * position of the first block and the ids of the blocks at consecutive
- * positions"); position pos holds tokens pos*block_size .. +block_size-1 of
- * the request, and slots at or past num_tokens[r] are not checksummed.
+ * at block position start_pos[r] + k (as the page's KVChecksumBlocks gives a
+ * start position and then one block id per following position); position pos
+ * holds tokens pos*block_size .. +block_size-1 of the request, and slots at
+ * or past num_tokens[r] are not checksummed.
  *
  * Caches: cache_ptrs[i] (host array of device pointers) is layer
  * layer_numbers[i]; the call covers its local heads head_begin ..
@@ -242,10 +258,10 @@ size_t kvck_staging_bytes(const kvck_kv_layout* layout, int32_t num_caches, int3
 /*
  * kvck_tag_checksums -- tags of offloaded checksums and the load-time check.
  *
- * The page's function block_checksum_tags: a block's tag is the first 8 bytes
- * of its block hash read little-endian, XOR the group's fingerprint; the
+ * The page's function block_checksum_tags: a block's tag is the little-endian
+ * value of its hash's leading 8 bytes, XOR the group's fingerprint; the
  * checksum offloaded with a block (one uint64, the page's BLOCK_CHECKSUM_BYTES)
- * is XORed with its tag so that it only matches the block it was stored for.
+ * is XORed with the tag, which ties it to that block hash and group of layers.
  * For every entry i (only listed positions i = r*max_blocks + k,
  * k < num_blocks_per_req[r], when num_blocks_per_req is given):
  *   t_i = checksums[i] ^ LE64(block_hashes + i*hash_stride) ^ fingerprint

@@ -8,10 +8,13 @@ share no code, headers, tables or helpers.
 What it computes is defined on the vLLM API page
 "vllm.distributed.kv_transfer.kv_checksum.checksum" (module docstring):
 
-* slice checksum  s = sum_j x_j * (2j + 1)  mod 2^64       (docstring item 1)
-* block checksum  c = sum_{layer, head} m * s  mod 2^64,
-  m = 2 * (layer * H + head) + 1,  H = MAX_KV_HEADS_PER_LAYER   (item 2)
-* Mamba running-state rows, one slice per global row       (Mamba paragraph)
+* slice checksum: the pieces x_j of one (layer, head) slice, each times the
+  odd weight 2j+1, summed modulo 2^64                          (docstring item 1)
+* block checksum: the slices' checksums s(L, h), each times the odd factor
+  m(L, h) = 2(L*H + h) + 1 with H = MAX_KV_HEADS_PER_LAYER, summed modulo
+  2^64                                                          (item 2)
+* Mamba running states: every global row of a layer's states is a slice
+                                                               (Mamba paragraph)
 
 ``tags`` holds the offloaded-checksum tags (page function
 ``block_checksum_tags``) and the load-time comparison.

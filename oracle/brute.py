@@ -29,6 +29,10 @@ def _row_bytes(cache, layout, plane, b, i, h) -> bytes:
         return cache[plane, b, i, h, :].tobytes()
     if layout == "HND":
         return cache[plane, b, h, i, :].tobytes()
+    if layout == "FI_NHD":
+        return cache[b, plane, i, h, :].tobytes()
+    if layout == "FI_HND":
+        return cache[b, plane, h, i, :].tobytes()
     if layout == "MLA":
         return cache[b, i, :].tobytes()
     raise ValueError(layout)
@@ -38,9 +42,9 @@ def position_checksum(caches, layout, layer_numbers, global_head_base, block_id,
                       num_tokens, head_begin=0, head_count=None) -> int:
     total = 0
     for cache, layer, g0 in zip(caches, layer_numbers, global_head_base):
-        if layout == "NHD":
+        if layout in ("NHD", "FI_NHD"):
             bs, nh, planes = cache.shape[2], cache.shape[3], (0, 1)
-        elif layout == "HND":
+        elif layout in ("HND", "FI_HND"):
             bs, nh, planes = cache.shape[3], cache.shape[2], (0, 1)
         else:
             bs, nh, planes = cache.shape[1], 1, (0,)

@@ -20,6 +20,9 @@ byte strides:
 ``"HND"``  (2, num_blocks, num_heads, block_size, head_size)  -- not on the
            pages; the head-major permutation of the same pool.
 ``"MLA"``  (num_blocks, block_size, head_size)  one latent plane, one head.
+``"FI_NHD"`` (num_blocks, 2, block_size, num_heads, head_size) and ``"FI_HND"``
+           (num_blocks, 2, num_heads, block_size, head_size): K and V kept
+           together inside each block.
 
 Readings of points the pages leave open:
 
@@ -36,23 +39,26 @@ from __future__ import annotations
 
 import numpy as np
 
-# "H in the slice factor; groups with more KV heads per layer are not
-# checksummed" -- page attribute MAX_KV_HEADS_PER_LAYER = 1 << 16.
+# Page attribute MAX_KV_HEADS_PER_LAYER (2^16): the H of the slice factor, a
+# fixed upper bound on KV heads per layer; a group above it gets no checksum.
 MAX_KV_HEADS_PER_LAYER = 1 << 16
 # Page attribute BLOCK_CHECKSUM_BYTES: one int64 per block.
 BLOCK_CHECKSUM_BYTES = 8
 
-LAYOUTS = ("NHD", "HND", "MLA")
+LAYOUTS = ("NHD", "HND", "MLA", "FI_NHD", "FI_HND")
 
 _U64 = np.uint64
 _MASK = (1 << 64) - 1
 
 
 def num_valid_tokens(position: int, block_size: int, num_tokens: int) -> int:
-    """How many of the first ``num_tokens`` tokens block ``position`` holds
-    (page helper ``num_valid_tokens``): the block covers tokens
-    [position*block_size, (position+1)*block_size)."""
-    return min(block_size, max(0, num_tokens - position * block_size))
+    """Slots of block ``position`` that hold one of the request's first
+    ``num_tokens`` tokens (page helper of the same name).  The block spans
+    tokens [first, first + block_size) with first = position*block_size; the
+    count is the length of that span's overlap with [0, num_tokens)."""
+    first = position * block_size
+    last = min(first + block_size, num_tokens)
+    return last - first if last > first else 0
 
 
 def slice_factor(layer: int, head: int) -> int:
@@ -61,9 +67,9 @@ def slice_factor(layer: int, head: int) -> int:
 
 
 def _block_size(cache: np.ndarray, layout: str) -> int:
-    if layout == "NHD":
+    if layout in ("NHD", "FI_NHD"):
         return cache.shape[2]
-    if layout == "HND":
+    if layout in ("HND", "FI_HND"):
         return cache.shape[3]
     if layout == "MLA":
         return cache.shape[1]
@@ -71,23 +77,31 @@ def _block_size(cache: np.ndarray, layout: str) -> int:
 
 
 def _num_heads(cache: np.ndarray, layout: str) -> int:
-    if layout == "NHD":
+    if layout in ("NHD", "FI_NHD"):
         return cache.shape[3]
-    if layout == "HND":
+    if layout in ("HND", "FI_HND"):
         return cache.shape[2]
     return 1
+
+
+def _num_blocks(cache: np.ndarray, layout: str) -> int:
+    return cache.shape[1] if layout in ("NHD", "HND") else cache.shape[0]
 
 
 def _token_rows(cache: np.ndarray, layout: str, b: int, v: int, h0: int, n: int) -> np.ndarray:
     """Bytes of the first ``v`` tokens of block ``b`` for local heads h0..h0+n-1.
 
     Returns uint8 (v, n, row_bytes): per token and head, the K row then the V
-    row ("the K and V of the block's tokens for that head. Laid out token by
-    token", module docstring item 1)."""
+    row -- a slice is the K and V of one head, token after token (module
+    docstring, item 1)."""
     if layout == "NHD":
         planes = [cache[p, b, :v, h0:h0 + n, :] for p in (0, 1)]
     elif layout == "HND":
         planes = [np.swapaxes(cache[p, b, h0:h0 + n, :v, :], 0, 1) for p in (0, 1)]
+    elif layout == "FI_NHD":
+        planes = [cache[b, p, :v, h0:h0 + n, :] for p in (0, 1)]
+    elif layout == "FI_HND":
+        planes = [np.swapaxes(cache[b, p, h0:h0 + n, :v, :], 0, 1) for p in (0, 1)]
     elif layout == "MLA":
         if (h0, n) != (0, 1):
             raise ValueError("an MLA cache has exactly one head")
@@ -118,7 +132,7 @@ def checksum_position(caches, layout, layer_numbers, global_head_base, block_id,
         v = num_valid_tokens(position, bs, num_tokens)
         if v == 0:
             continue
-        if not 0 <= block_id < cache.shape[1 if layout != "MLA" else 0]:
+        if not 0 <= block_id < _num_blocks(cache, layout):
             raise IndexError(f"block id {block_id} outside the pool")
         rows = _token_rows(cache, layout, block_id, v, head_begin, n)
         if rows.shape[2] % 8:
@@ -144,8 +158,8 @@ def checksum_blocks(caches, layout, layer_numbers, global_head_base, block_table
     """Per-position checksums of a batch of requests.
 
     Request r lists ``num_blocks[r]`` blocks, ``block_table[r, k]`` at block
-    position ``start_pos[r] + k`` (``KVChecksumBlocks.groups``: "the position
-    of the first block and the ids of the blocks at consecutive positions");
+    position ``start_pos[r] + k`` (``KVChecksumBlocks.groups`` gives a start
+    position, then one block id for each following position);
     slots at or past ``num_tokens[r]`` are not checksummed.
 
     Returns uint64 (num_reqs, block_table.shape[1]); positions a request does

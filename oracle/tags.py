@@ -2,11 +2,11 @@
 
 vLLM API page "vllm.distributed.kv_transfer.kv_checksum.checksum":
 
-* function ``block_checksum_tags(block_hashes, fingerprint)``: the uint64 an
-  offloaded block checksum is XORed with, so that it matches only the block it
-  was stored for -- the first 8 bytes of the block's hash read little-endian,
-  XOR the group's fingerprint;
-* attribute ``BLOCK_CHECKSUM_BYTES``: one int64 is stored per block;
+* function ``block_checksum_tags(block_hashes, fingerprint)``: a per-block
+  uint64 built from the block's hash (its leading 8 bytes as a little-endian
+  integer) and the group's fingerprint (XOR), used to bind an offloaded
+  checksum to the one block and group of layers it belongs to;
+* attribute ``BLOCK_CHECKSUM_BYTES``: 8 bytes are kept per offloaded block;
 * ``KVChecksumGroup.stored`` / ``KVChecksumScheduled.reqs_to_load``: a load of
   offloaded KV is checked against the checksums offloaded with it.
 
@@ -19,10 +19,18 @@ from __future__ import annotations
 import numpy as np
 
 
+def _le64(digest) -> int:
+    """Integer whose little-endian byte string is the digest's first 8 bytes."""
+    value = 0
+    for i, byte in enumerate(bytes(digest)[:8]):
+        value |= byte << (8 * i)
+    return value
+
+
 def block_checksum_tags(block_hashes, fingerprint: int) -> np.ndarray:
-    """uint64 tag per block: little-endian value of hash[:8] XOR fingerprint."""
-    tags = [int.from_bytes(bytes(h[:8]), "little") for h in block_hashes]
-    return np.array(tags, dtype=np.uint64) ^ np.uint64(fingerprint)
+    """One uint64 tag per block hash: _le64(hash) XOR fingerprint."""
+    fp = int(fingerprint) & ((1 << 64) - 1)
+    return np.array([_le64(h) ^ fp for h in block_hashes], dtype=np.uint64)
 
 
 def tag_checksums(checksums, block_hashes, fingerprint: int) -> np.ndarray:

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     KVCK_FLAG_STAGING_FULL,
     KvckDeviceError,
     KvckError,
+    LAYOUT_NAMES,
     kv_layout,
     kvck_abi_version,
     kvck_blocks_workspace_bytes,

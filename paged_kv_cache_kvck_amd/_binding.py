@@ -56,7 +56,9 @@ class KvckDeviceError(RuntimeError):
 class kvck_kv_layout(ctypes.Structure):
     _fields_ = [("planes", ctypes.c_int32), ("block_size", ctypes.c_int32), ("num_heads", ctypes.c_int32),
                 ("row_bytes", ctypes.c_int32), ("num_blocks", ctypes.c_int64), ("plane_stride", ctypes.c_int64),
-                ("block_stride", ctypes.c_int64), ("slot_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64)]
+                ("block_stride", ctypes.c_int64), ("slot_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("chunk_bytes", ctypes.c_int32), ("reserved0", ctypes.c_int32), ("chunk_stride", ctypes.c_int64),
+                ("plane_begin", ctypes.c_int32), ("plane_count", ctypes.c_int32)]
 
 
 class kvck_state_desc(ctypes.Structure):
@@ -161,35 +163,74 @@ def _stream_handle(stream, device) -> int | None:
 
 # ----------------------------------------------------------------- layouts
 
+# Pool tensor layouts the binding understands (semantic shapes):
+#   NHD      (2, num_blocks, block_size, num_heads, head_size)   K and V (vLLM flash-attention pool)
+#   HND      (2, num_blocks, num_heads, block_size, head_size)   K and V
+#   FI_NHD   (num_blocks, 2, block_size, num_heads, head_size)   K and V inside each block
+#   FI_HND   (num_blocks, 2, num_heads, block_size, head_size)
+#   MLA      (num_blocks, block_size, head_size)                 one latent plane
+#   K_NHD / V_NHD   (num_blocks, block_size, num_heads, head_size)   one plane of a K/V slice
+#   K_HND / V_HND   (num_blocks, num_heads, block_size, head_size)
+#   K_XSPLIT (num_blocks, num_heads, head_size/x, block_size, x)  x-split K plane
+LAYOUT_NAMES = ("NHD", "HND", "FI_NHD", "FI_HND", "MLA", "K_NHD", "V_NHD", "K_HND", "V_HND", "K_XSPLIT")
+
+
 def kv_layout(cache: torch.Tensor, layout: str) -> kvck_kv_layout:
-    """Byte layout of a pool tensor in semantic shape:
-    NHD (2, num_blocks, block_size, num_heads, head_size),
-    HND (2, num_blocks, num_heads, block_size, head_size),
-    MLA (num_blocks, block_size, head_size)."""
+    """Byte layout (kvck_kv_layout) of a pool tensor in one of LAYOUT_NAMES."""
     es = cache.element_size()
-    st = [s * es for s in cache.stride()]
+    st = [x * es for x in cache.stride()]
     sh = cache.shape
     if cache.stride(-1) != 1:
-        raise ValueError("the head_size dimension must be contiguous")
+        raise ValueError("the innermost dimension must be contiguous")
     L = kvck_kv_layout()
-    if layout == "NHD":
-        if cache.dim() != 5 or sh[0] != 2:
-            raise ValueError("NHD pools are (2, num_blocks, block_size, num_heads, head_size)")
-        L.planes, L.num_blocks, L.block_size, L.num_heads = 2, sh[1], sh[2], sh[3]
-        L.plane_stride, L.block_stride, L.slot_stride, L.head_stride = st[0], st[1], st[2], st[3]
-    elif layout == "HND":
-        if cache.dim() != 5 or sh[0] != 2:
-            raise ValueError("HND pools are (2, num_blocks, num_heads, block_size, head_size)")
-        L.planes, L.num_blocks, L.num_heads, L.block_size = 2, sh[1], sh[2], sh[3]
-        L.plane_stride, L.block_stride, L.head_stride, L.slot_stride = st[0], st[1], st[2], st[3]
+
+    def need(dims, what):
+        if cache.dim() != dims:
+            raise ValueError(f"{layout} pools are {what}")
+
+    if layout in ("NHD", "HND"):
+        need(5, "(2, num_blocks, ., ., head_size)")
+        if sh[0] != 2:
+            raise ValueError("the first dimension holds K and V")
+        L.planes, L.num_blocks, L.plane_stride, L.block_stride = 2, sh[1], st[0], st[1]
+        if layout == "NHD":
+            L.block_size, L.num_heads, L.slot_stride, L.head_stride = sh[2], sh[3], st[2], st[3]
+        else:
+            L.num_heads, L.block_size, L.head_stride, L.slot_stride = sh[2], sh[3], st[2], st[3]
+        L.row_bytes = sh[4] * es
+    elif layout in ("FI_NHD", "FI_HND"):
+        need(5, "(num_blocks, 2, ., ., head_size)")
+        if sh[1] != 2:
+            raise ValueError("the second dimension holds K and V")
+        L.planes, L.num_blocks, L.block_stride, L.plane_stride = 2, sh[0], st[0], st[1]
+        if layout == "FI_NHD":
+            L.block_size, L.num_heads, L.slot_stride, L.head_stride = sh[2], sh[3], st[2], st[3]
+        else:
+            L.num_heads, L.block_size, L.head_stride, L.slot_stride = sh[2], sh[3], st[2], st[3]
+        L.row_bytes = sh[4] * es
     elif layout == "MLA":
-        if cache.dim() != 3:
-            raise ValueError("MLA pools are (num_blocks, block_size, head_size)")
+        need(3, "(num_blocks, block_size, head_size)")
         L.planes, L.num_blocks, L.block_size, L.num_heads = 1, sh[0], sh[1], 1
         L.plane_stride, L.block_stride, L.slot_stride, L.head_stride = 0, st[0], st[1], 0
+        L.row_bytes = sh[2] * es
+    elif layout in ("K_NHD", "V_NHD", "K_HND", "V_HND"):
+        need(4, "(num_blocks, ., ., head_size)")
+        L.planes, L.plane_begin, L.plane_count = 2, (0 if layout[0] == "K" else 1), 1
+        L.num_blocks, L.block_stride = sh[0], st[0]
+        if layout.endswith("NHD"):
+            L.block_size, L.num_heads, L.slot_stride, L.head_stride = sh[1], sh[2], st[1], st[2]
+        else:
+            L.num_heads, L.block_size, L.head_stride, L.slot_stride = sh[1], sh[2], st[1], st[2]
+        L.row_bytes = sh[3] * es
+    elif layout == "K_XSPLIT":
+        need(5, "(num_blocks, num_heads, head_size/x, block_size, x)")
+        L.planes, L.plane_begin, L.plane_count = 2, 0, 1
+        L.num_blocks, L.num_heads, L.block_size = sh[0], sh[1], sh[3]
+        L.block_stride, L.head_stride, L.chunk_stride, L.slot_stride = st[0], st[1], st[2], st[3]
+        L.chunk_bytes = sh[4] * es
+        L.row_bytes = sh[2] * sh[4] * es
     else:
-        raise ValueError(f"unknown layout {layout!r}")
-    L.row_bytes = sh[-1] * es
+        raise ValueError(f"unknown layout {layout!r}; one of {LAYOUT_NAMES}")
     return L
 
 
@@ -202,13 +243,20 @@ def _meta(t: torch.Tensor, dtype, name, device, n=None):
 
 
 def _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req, start_pos, num_tokens,
-                 global_head_base, head_begin, head_count, out, workspace, check, error_flags):
+                 global_head_base, head_begin, head_count, out, workspace, check, error_flags, planes=None):
     lib = load_library()
     caches = list(caches)
     if not caches:
         raise ValueError("no caches")
     dev = caches[0].device
     L = kv_layout(caches[0], layout)
+    plane_off = 0
+    if planes is not None:
+        # a subset (begin, count) of the planes of a pool that holds all of them
+        if L.plane_count != 0 or L.planes != 2:
+            raise ValueError("planes= selects K or V of a pool holding both")
+        L.plane_begin, L.plane_count = int(planes[0]), int(planes[1])
+        plane_off = L.plane_begin * L.plane_stride
     for c in caches[1:]:
         if c.shape != caches[0].shape or c.stride() != caches[0].stride() or c.dtype != caches[0].dtype \
                 or c.device != dev:
@@ -239,7 +287,7 @@ def _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req,
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if check and error_flags is None:
         error_flags = torch.zeros(1, dtype=torch.int32, device=dev)
-    ptrs = (ctypes.c_void_p * n)(*[c.data_ptr() for c in caches])
+    ptrs = (ctypes.c_void_p * n)(*[c.data_ptr() + plane_off for c in caches])
     layers = (ctypes.c_int32 * n)(*[int(x) for x in layer_numbers])
     bases = (ctypes.c_int32 * n)(*[int(x) for x in global_head_base])
     return dict(lib=lib, dev=dev, L=L, n=n, head_count=head_count, R=R, max_blocks=max_blocks, out=out,
@@ -260,8 +308,12 @@ def kvck_checksum_blocks(caches: Sequence[torch.Tensor], layout: str, layer_numb
                          num_tokens: torch.Tensor, global_head_base=None, head_begin: int = 0,
                          head_count: int | None = None, out: torch.Tensor | None = None, accumulate: bool = False,
                          workspace: torch.Tensor | None = None, error_flags: torch.Tensor | None = None,
-                         stream=None, check: bool = False) -> torch.Tensor:
+                         stream=None, check: bool = False, planes: tuple | None = None) -> torch.Tensor:
     """Per block position checksums of paged K/V (see include/kvck.h).
+
+    ``layout`` is one of LAYOUT_NAMES; ``planes=(begin, count)`` restricts a
+    pool holding K and V to K (0, 1) or V (1, 1) -- partials over K and V add
+    up to the checksum of both.
 
     Returns ``out``: uint64 (num_reqs, max_blocks) on the caches' device;
     entries past a request's listed positions are left as they were.
@@ -269,7 +321,7 @@ def kvck_checksum_blocks(caches: Sequence[torch.Tensor], layout: str, layer_numb
     ``KvckDeviceError`` if the kernels flagged a bad block id or request.
     """
     a = _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req, start_pos, num_tokens,
-                     global_head_base, head_begin, head_count, out, workspace, check, error_flags)
+                     global_head_base, head_begin, head_count, out, workspace, check, error_flags, planes)
     ws = a["workspace"]
     st = a["lib"].kvck_checksum_blocks(
         ctypes.byref(a["L"]), a["ptrs"], a["layers"], a["bases"], a["n"], int(head_begin), int(a["head_count"]),
@@ -293,12 +345,13 @@ def kvck_copy_checksum_blocks(direction: int, caches: Sequence[torch.Tensor], la
                               staging: torch.Tensor, global_head_base=None, head_begin: int = 0,
                               head_count: int | None = None, out: torch.Tensor | None = None,
                               accumulate: bool = False, workspace: torch.Tensor | None = None,
-                              error_flags: torch.Tensor | None = None, stream=None, check: bool = False):
+                              error_flags: torch.Tensor | None = None, stream=None, check: bool = False,
+                              planes: tuple | None = None):
     """A connector save (KVCK_COPY_SAVE: pool -> staging) or load
     (KVCK_COPY_LOAD: staging -> pool) fused with the checksum; see
     include/kvck.h for the staging layout.  Returns the checksums."""
     a = _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req, start_pos, num_tokens,
-                     global_head_base, head_begin, head_count, out, workspace, check, error_flags)
+                     global_head_base, head_begin, head_count, out, workspace, check, error_flags, planes)
     if staging.device != a["dev"] or not staging.is_contiguous():
         raise ValueError("staging must be a contiguous tensor on the caches' device")
     per = int(a["lib"].kvck_staging_bytes(ctypes.byref(a["L"]), a["n"], int(a["head_count"])))

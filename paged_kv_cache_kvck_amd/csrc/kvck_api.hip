@@ -199,6 +199,14 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
     return KVCK_ERR_INVALID_ARGUMENT;
   if (L.row_bytes % 8 != 0) return KVCK_ERR_UNSUPPORTED;
   if (num_caches < 1 || num_caches > KVCK_MAX_CACHES) return KVCK_ERR_UNSUPPORTED;
+  // rows stored as runs (x-split layouts) and plane subsets
+  if (L.chunk_bytes < 0 || L.chunk_stride < 0 || L.plane_begin < 0 || L.plane_count < 0)
+    return KVCK_ERR_INVALID_ARGUMENT;
+  const int32_t run_bytes = L.chunk_bytes == 0 ? L.row_bytes : L.chunk_bytes;
+  if (run_bytes % 8 != 0 || L.row_bytes % run_bytes != 0) return KVCK_ERR_UNSUPPORTED;
+  const int32_t runs = L.row_bytes / run_bytes;
+  const int32_t planes_cov = L.plane_count == 0 ? L.planes - L.plane_begin : L.plane_count;
+  if (planes_cov < 1 || L.plane_begin + planes_cov > L.planes) return KVCK_ERR_INVALID_ARGUMENT;
   if (head_begin < 0 || head_count < 1 || (int64_t)head_begin + head_count > L.num_heads)
     return KVCK_ERR_INVALID_ARGUMENT;
   for (int32_t i = 0; i < num_caches; ++i) {
@@ -216,9 +224,9 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   // ---- alignment: 16-byte lane loads when everything allows, else 8-byte
   int chunk = 16;
   for (int pass = 0; pass < 2; ++pass) {
-    bool ok = L.row_bytes % chunk == 0 && L.block_stride % chunk == 0 &&
-              (L.planes == 1 || L.plane_stride % chunk == 0) && (L.block_size == 1 || L.slot_stride % chunk == 0) &&
-              (L.num_heads == 1 || L.head_stride % chunk == 0);
+    bool ok = run_bytes % chunk == 0 && L.block_stride % chunk == 0 &&
+              (planes_cov == 1 || L.plane_stride % chunk == 0) && (L.block_size == 1 || L.slot_stride % chunk == 0) &&
+              (L.num_heads == 1 || L.head_stride % chunk == 0) && (runs == 1 || L.chunk_stride % chunk == 0);
     for (int32_t i = 0; ok && i < num_caches; ++i) ok = aligned(cache_ptrs[i], chunk);
     if (mode != kModeChecksum) ok = ok && aligned(staging, chunk);
     if (ok) break;
@@ -228,12 +236,14 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   BlocksShape shp;
   if (!choose_shape(L.block_size, L.row_bytes, chunk, &shp)) return KVCK_ERR_UNSUPPORTED;
   // lane-table offsets and piece terms are 32-bit
-  if ((int64_t)shp.rows_per_group * L.slot_stride + L.row_bytes >= ((int64_t)1 << 31)) return KVCK_ERR_UNSUPPORTED;
+  if ((int64_t)shp.rows_per_group * L.slot_stride + (int64_t)(runs - 1) * L.chunk_stride + run_bytes >=
+      ((int64_t)1 << 31))
+    return KVCK_ERR_UNSUPPORTED;
   const int64_t pieces = (int64_t)L.planes * L.row_bytes / 8;
   if (2 * (int64_t)shp.rows_per_group * pieces + 4 * (L.row_bytes / chunk) >= ((int64_t)1 << 32))
     return KVCK_ERR_UNSUPPORTED;
   // ---- staging (fused copy)
-  const int64_t image_bytes = (int64_t)L.planes * head_count * L.block_size * L.row_bytes;
+  const int64_t image_bytes = (int64_t)planes_cov * head_count * L.block_size * L.row_bytes;
   if (mode != kModeChecksum) {
     if (!staging || staging_positions < 0) return KVCK_ERR_INVALID_ARGUMENT;
     if ((int64_t)L.block_size * L.row_bytes >= ((int64_t)1 << 31)) return KVCK_ERR_UNSUPPORTED;
@@ -248,7 +258,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-  choose_schedule(&shp, num_caches, (int64_t)num_reqs * max_blocks, image_bytes, L.planes, head_count, cus,
+  choose_schedule(&shp, num_caches, (int64_t)num_reqs * max_blocks, image_bytes, planes_cov, head_count, cus,
                   mode != kModeChecksum);
   const int32_t lpt = shp.caches_per_task;
   const int32_t total_groups = (num_caches + lpt - 1) / lpt;
@@ -270,7 +280,11 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   a.partials = reinterpret_cast<uint64_t*>(ws + w.partials_off);
   a.out = out;
   a.max_items = max_items;
-  a.planes = L.planes;
+  a.chunk_stride = L.chunk_stride;
+  a.piece_base = 2ull * (uint64_t)L.plane_begin * (uint64_t)(pieces / L.planes);
+  a.planes = planes_cov;
+  a.planes_total = L.planes;
+  a.chunks_per_run = run_bytes / chunk;
   a.heads = head_count;
   a.row_bytes = L.row_bytes;
   a.pieces = (int32_t)pieces;
@@ -353,7 +367,9 @@ KVCK_EXPORT size_t kvck_staging_bytes(const kvck_kv_layout* layout, int32_t num_
   if (!layout || num_caches < 1 || head_count < 1 || layout->planes < 1 || layout->block_size < 1 ||
       layout->row_bytes < 1)
     return 0;
-  return (size_t)layout->planes * (size_t)head_count * (size_t)layout->block_size * (size_t)layout->row_bytes *
+  const int32_t planes = layout->plane_count > 0 ? layout->plane_count : layout->planes - layout->plane_begin;
+  if (planes < 1) return 0;
+  return (size_t)planes * (size_t)head_count * (size_t)layout->block_size * (size_t)layout->row_bytes *
          (size_t)num_caches;
 }
 

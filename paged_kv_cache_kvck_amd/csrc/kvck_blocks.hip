@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
   lt.template init<CHUNK>(lane, a);
   const uint64_t P = (uint64_t)a.pieces;
   const int rg = a.rows_per_group;
-  const uint64_t plane_term = 2ull * (P / (uint64_t)a.planes);
+  const uint64_t plane_term = 2ull * (P / (uint64_t)a.planes_total);
   const int nhb = (a.heads + HU - 1) / HU;
 
   for (int64_t task = wave; task < total; task += nwaves) {
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
         const uint32_t mb = a.mbase[cc.cache];
 #pragma unroll
         for (int p = 0; p < PU; ++p) {
-          const uint64_t up = 2ull * (t0 + (uint64_t)(cc.group * rg)) * P + 1ull +
+          const uint64_t up = 2ull * (t0 + (uint64_t)(cc.group * rg)) * P + 1ull + a.piece_base +
                               (uint64_t)(cc.plane * PU + p) * plane_term;
 #pragma unroll
           for (int h = 0; h < HU; ++h) {

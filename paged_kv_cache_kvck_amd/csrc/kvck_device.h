@@ -60,7 +60,9 @@ struct LaneTable {
       const int r = f / a.chunks_per_row;
       const int c = f - r * a.chunks_per_row;
       row[s] = r < a.rows_per_group ? r : 0x7fffffff;
-      off[s] = (uint32_t)((int64_t)r * a.slot_stride + (int64_t)c * CHUNK);
+      const int run = c / a.chunks_per_run;
+      off[s] = (uint32_t)((int64_t)r * a.slot_stride + (int64_t)run * a.chunk_stride +
+                          (int64_t)(c - run * a.chunks_per_run) * CHUNK);
       urel[s] = (uint32_t)(2u * (uint32_t)r * (uint32_t)a.pieces + (uint32_t)(CHUNK / 4) * (uint32_t)c);
     }
   }

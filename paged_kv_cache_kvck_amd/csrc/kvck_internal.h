@@ -51,9 +51,13 @@ struct BlocksArgs {
   uint64_t* partials;        // [num_caches][max_items] when not direct
   uint64_t* out;
   int64_t max_items;
-  int32_t planes, heads, row_bytes, pieces;  // pieces = P per token
+  int64_t chunk_stride;                      // bytes between a row's contiguous runs
+  uint64_t piece_base;                       // 2 * (first covered plane) * pieces per plane
+  int32_t planes, heads, row_bytes, pieces;  // planes covered by the call; pieces = P per token
+  int32_t planes_total;                      // planes of the slice
   int32_t rows_per_group;                    // rows covered by one lane table
   int32_t chunks_per_row;
+  int32_t chunks_per_run;                    // lane chunks in one contiguous run of a row
   int32_t num_caches;                        // caches in this launch
   int32_t caches_per_task;                   // caches one task covers (a partial's group)
   int32_t group_offset;                      // partial row of this launch's first group

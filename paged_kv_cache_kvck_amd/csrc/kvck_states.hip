@@ -1,12 +1,14 @@
 // Mamba running-state checksums on gfx950.
 //
 // Mamba paragraph of the vLLM API page
-// "vllm.distributed.kv_transfer.kv_checksum.checksum": a Mamba group's block is
-// the request's running state at position 0, and a layer with a known TP split
-// has one slice per global row of its states, whose pieces are its 2- or 4-byte
-// elements read unsigned.  Slice g = row g of every state of the layer,
-// concatenated in state order, elements numbered e = 0, 1, ..:
-//   s = sum_e x_e (2e + 1),  c = sum_{layer, g} m s,  m = 2 (layer*65536 + g) + 1.
+// "vllm.distributed.kv_transfer.kv_checksum.checksum": for a Mamba group the
+// request's running state stands in for its blocks (position 0); when the
+// layer's TP split is known, each global row along that split is a slice, and
+// the pieces are the row's elements (2 or 4 bytes each) as unsigned integers.
+// Slice g = row g of every state of the layer, concatenated in state order,
+// elements numbered e = 0, 1, ..:
+//   s(g) = sum over e of x_e (2e + 1);  c = sum over (layer, g) of m s(g),
+//   m = 2 (layer*65536 + g) + 1, all modulo 2^64.
 //
 // Task = (layer, group of rows, request), one wavefront each.  Lanes stream the
 // row's 16-byte chunks; a chunk of 4-byte elements x0..x3 starting at element e

@@ -1,10 +1,10 @@
 // Offloaded-checksum tags and load-time comparison on gfx950.
 //
 // vLLM API page "vllm.distributed.kv_transfer.kv_checksum.checksum", function
-// block_checksum_tags: the tag of a block is the first 8 bytes of its hash,
-// read little-endian, XOR the group's fingerprint; an offloaded checksum is
-// XORed with it (one uint64 per block, BLOCK_CHECKSUM_BYTES), so it matches
-// only the block it was stored for.  Here, per listed position i:
+// block_checksum_tags: a block's tag is the little-endian value of its hash's
+// leading 8 bytes, XOR the group's fingerprint; XOR-ing an offloaded checksum
+// (one uint64 per block, BLOCK_CHECKSUM_BYTES) with it ties that checksum to
+// its own block hash and group of layers.  Here, per listed position i:
 //   t_i = checksum_i ^ LE64(hash_i[0..8)) ^ fingerprint
 // is written (the value to offload) and/or compared with the stored value
 // (a load of offloaded KV), mismatches flagged per position and counted.

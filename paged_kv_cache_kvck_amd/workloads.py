@@ -99,6 +99,10 @@ def pool_shape(layout: str, num_blocks: int, block_size: int, num_heads: int, he
         if num_heads != 1:
             raise ValueError("MLA pools hold one latent head")
         return (num_blocks, block_size, head_size)
+    if layout == "FI_NHD":
+        return (num_blocks, 2, block_size, num_heads, head_size)
+    if layout == "FI_HND":
+        return (num_blocks, 2, num_heads, block_size, head_size)
     raise ValueError(layout)
 
 

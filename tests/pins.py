@@ -86,6 +86,8 @@ def pin_brute(o, seed=11, cases=None):
         dict(layout="HND", elem="bf16", layers=(5,), nh=4, d=8, bs=4, lengths=(10, 4),
              head_begin=1, head_count=2, bases=(9,)),
         dict(layout="NHD", elem="fp32", layers=(1, 0), nh=2, d=4, bs=2, lengths=(5, 0, 2), extra=(0, 1, 1)),
+        dict(layout="FI_NHD", elem="bf16", layers=(2,), nh=3, d=8, bs=4, lengths=(9, 4)),
+        dict(layout="FI_HND", elem="fp16", layers=(0, 7), nh=2, d=8, bs=3, lengths=(7,), start=(1,)),
     ]
     for spec in specs:
         case, _ = make_case(rng, **spec)
@@ -211,8 +213,9 @@ def pin_linearity(o):
 # ------------------------------------------------------------------ invariants on the page
 
 def pin_additivity_block_size(o):
-    """Checksums of consecutive blocks add up to that of the tokens they hold,
-    so block sizes 16 and 64 agree on each request's sum."""
+    """Pieces are numbered from the request's first token, so per-block
+    checksums sum to a value that depends only on the tokens: paging the same
+    tokens at block size 16 or 64 gives the same per-request sums."""
     rng = np.random.default_rng(6)
     lengths = [130, 64, 17, 200]
     c16, r16 = make_case(rng, layout="NHD", layers=(0, 3), nh=2, d=8, bs=16, lengths=lengths)
@@ -233,6 +236,11 @@ def pin_layout_independence(o):
     ch["layout"] = "HND"
     ch["caches"] = [np.ascontiguousarray(p.transpose(0, 1, 3, 2, 4)) for p in cn["caches"]]
     assert np.array_equal(run_blocks(o, cn), run_blocks(o, ch))
+    # K and V kept together inside each block
+    cf = dict(cn, layout="FI_NHD", caches=[np.ascontiguousarray(p.transpose(1, 0, 2, 3, 4)) for p in cn["caches"]])
+    assert np.array_equal(run_blocks(o, cn), run_blocks(o, cf))
+    cg = dict(cn, layout="FI_HND", caches=[np.ascontiguousarray(p.transpose(1, 0, 3, 2, 4)) for p in cn["caches"]])
+    assert np.array_equal(run_blocks(o, cn), run_blocks(o, cg))
 
 
 def pin_tp_pp_partials(o):
@@ -285,8 +293,9 @@ def pin_exclusion(o):
 
 
 def pin_detection(o, exhaustive=False):
-    """Any single-piece change changes c (odd factors); swapped tokens, blocks,
-    heads or layers change c for random data (distinct factors)."""
+    """Changing one piece always changes c (its weight is odd, hence
+    invertible mod 2^64); exchanging two tokens, two blocks, two heads or two
+    layers changes c for random data (their weights differ)."""
     rng = np.random.default_rng(10)
     w = wl.tiny()
     pools = w.host_pools()

@@ -34,8 +34,8 @@ MUTATIONS = {
                            "m = _U64(2) * (_U64(0) * _U64(MAX_KV_HEADS_PER_LAYER) + heads)"),
     "local head numbering": ("heads = _U64(g0) + np.arange(n, dtype=_U64)", "heads = np.arange(n, dtype=_U64)"),
     "H = 1 << 15": ("MAX_KV_HEADS_PER_LAYER = 1 << 16", "MAX_KV_HEADS_PER_LAYER = 1 << 15"),
-    "num_valid_tokens off by one": ("return min(block_size, max(0, num_tokens - position * block_size))",
-                                    "return min(block_size, max(0, num_tokens + 1 - position * block_size))"),
+    "num_valid_tokens off by one": ("last = min(first + block_size, num_tokens)",
+                                    "last = min(first + block_size, num_tokens + 1)"),
     "no exclusion of slots": ("v = num_valid_tokens(position, bs, num_tokens)\n", "v = bs\n"),
     "Mamba elements numbered from 1": ("e = np.arange(x.size, dtype=_U64)", "e = np.arange(x.size, dtype=_U64) + _U64(1)"),
     "Mamba local row numbering": ("m = _U64(slice_factor(layer, g0 + g))", "m = _U64(slice_factor(layer, g))"),
