@@ -141,11 +141,14 @@ def main(argv=None):
     ws = torch.empty(kvck.kvck_blocks_workspace_bytes(w.num_layers, req.num_reqs, req.max_blocks),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
+    prepared = {}
 
     def step(head_begin=w.head_begin, head_count=w.head_count, bases=None):
-        kvck.kvck_checksum_blocks(pools, w.layout, w.layer_numbers, bt, nb, sp, nt, global_head_base=bases,
-                                  head_begin=head_begin, head_count=head_count, out=out, workspace=ws,
-                                  stream=stream)
+        key = (head_begin, head_count, None if bases is None else tuple(bases))
+        if key not in prepared:
+            prepared[key] = kvck.prepare_caches(pools, w.layout, w.layer_numbers, global_head_base=bases,
+                                                head_begin=head_begin, head_count=head_count)
+        kvck.kvck_checksum_blocks(prepared[key], None, None, bt, nb, sp, nt, out=out, workspace=ws, stream=stream)
 
     valid = w.valid_bytes()
     kvck.kvck_instrument(True)

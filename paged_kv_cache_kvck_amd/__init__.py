@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     KvckDeviceError,
     KvckError,
     LAYOUT_NAMES,
+    PreparedCaches,
     kv_layout,
     kvck_abi_version,
     kvck_blocks_workspace_bytes,
@@ -32,5 +33,6 @@ from ._binding import (  # noqa: F401
     kvck_status_string,
     kvck_tag_checksums,
     load_library,
+    prepare_caches,
     state_desc,
 )

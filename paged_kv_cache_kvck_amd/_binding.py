@@ -242,34 +242,62 @@ def _meta(t: torch.Tensor, dtype, name, device, n=None):
     return t
 
 
+class PreparedCaches:
+    """A set of pool tensors validated and marshalled once (layout, device
+    pointers, layer numbers, global head bases), for calls in a hot loop: pass
+    it as ``caches`` to kvck_checksum_blocks / kvck_copy_checksum_blocks.  It
+    keeps the tensors alive; their storage must not move between calls."""
+
+    def __init__(self, caches, layout, layer_numbers, global_head_base=None, head_begin: int = 0,
+                 head_count: int | None = None, planes: tuple | None = None):
+        caches = list(caches)
+        if not caches:
+            raise ValueError("no caches")
+        self.tensors = caches
+        self.device = caches[0].device
+        self.layout_name = layout
+        L = kv_layout(caches[0], layout)
+        plane_off = 0
+        if planes is not None:
+            # a subset (begin, count) of the planes of a pool that holds all of them
+            if L.plane_count != 0 or L.planes != 2:
+                raise ValueError("planes= selects K or V of a pool holding both")
+            L.plane_begin, L.plane_count = int(planes[0]), int(planes[1])
+            plane_off = L.plane_begin * L.plane_stride
+        ref = caches[0]
+        for c in caches[1:]:
+            if c.shape != ref.shape or c.stride() != ref.stride() or c.dtype != ref.dtype or c.device != ref.device:
+                raise ValueError("every cache of a call must share shape, strides, dtype and device")
+        n = len(caches)
+        if head_count is None:
+            head_count = L.num_heads - head_begin
+        if global_head_base is None:
+            global_head_base = [head_begin] * n
+        elif isinstance(global_head_base, int):
+            global_head_base = [global_head_base] * n
+        if len(layer_numbers) != n or len(global_head_base) != n:
+            raise ValueError("one layer number and one global head base per cache")
+        self.layout = L
+        self.n = n
+        self.head_begin = int(head_begin)
+        self.head_count = int(head_count)
+        self.ptrs = (ctypes.c_void_p * n)(*[c.data_ptr() + plane_off for c in caches])
+        self.layers = (ctypes.c_int32 * n)(*[int(x) for x in layer_numbers])
+        self.bases = (ctypes.c_int32 * n)(*[int(x) for x in global_head_base])
+
+
+def prepare_caches(caches, layout, layer_numbers, global_head_base=None, head_begin: int = 0,
+                   head_count: int | None = None, planes: tuple | None = None) -> PreparedCaches:
+    return PreparedCaches(caches, layout, layer_numbers, global_head_base, head_begin, head_count, planes)
+
+
 def _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req, start_pos, num_tokens,
                  global_head_base, head_begin, head_count, out, workspace, check, error_flags, planes=None):
     lib = load_library()
-    caches = list(caches)
-    if not caches:
-        raise ValueError("no caches")
-    dev = caches[0].device
-    L = kv_layout(caches[0], layout)
-    plane_off = 0
-    if planes is not None:
-        # a subset (begin, count) of the planes of a pool that holds all of them
-        if L.plane_count != 0 or L.planes != 2:
-            raise ValueError("planes= selects K or V of a pool holding both")
-        L.plane_begin, L.plane_count = int(planes[0]), int(planes[1])
-        plane_off = L.plane_begin * L.plane_stride
-    for c in caches[1:]:
-        if c.shape != caches[0].shape or c.stride() != caches[0].stride() or c.dtype != caches[0].dtype \
-                or c.device != dev:
-            raise ValueError("every cache of a call must share shape, strides, dtype and device")
-    n = len(caches)
-    if head_count is None:
-        head_count = L.num_heads - head_begin
-    if global_head_base is None:
-        global_head_base = [head_begin] * n
-    elif isinstance(global_head_base, int):
-        global_head_base = [global_head_base] * n
-    if len(layer_numbers) != n or len(global_head_base) != n:
-        raise ValueError("one layer number and one global head base per cache")
+    pc = caches if isinstance(caches, PreparedCaches) else PreparedCaches(
+        caches, layout, layer_numbers, global_head_base, head_begin, head_count, planes)
+    dev = pc.device
+    n = pc.n
     _meta(block_table, torch.int32, "block_table", dev)
     if block_table.dim() != 2 or block_table.stride(1) != 1:
         raise ValueError("block_table must be 2-D with contiguous rows")
@@ -287,11 +315,9 @@ def _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req,
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if check and error_flags is None:
         error_flags = torch.zeros(1, dtype=torch.int32, device=dev)
-    ptrs = (ctypes.c_void_p * n)(*[c.data_ptr() + plane_off for c in caches])
-    layers = (ctypes.c_int32 * n)(*[int(x) for x in layer_numbers])
-    bases = (ctypes.c_int32 * n)(*[int(x) for x in global_head_base])
-    return dict(lib=lib, dev=dev, L=L, n=n, head_count=head_count, R=R, max_blocks=max_blocks, out=out,
-                workspace=workspace, error_flags=error_flags, ptrs=ptrs, layers=layers, bases=bases)
+    return dict(lib=lib, dev=dev, L=pc.layout, n=n, head_begin=pc.head_begin, head_count=pc.head_count, R=R,
+                max_blocks=max_blocks, out=out, workspace=workspace, error_flags=error_flags, ptrs=pc.ptrs,
+                layers=pc.layers, bases=pc.bases)
 
 
 def _finish(a, check):
@@ -303,7 +329,7 @@ def _finish(a, check):
     return a["out"]
 
 
-def kvck_checksum_blocks(caches: Sequence[torch.Tensor], layout: str, layer_numbers: Sequence[int],
+def kvck_checksum_blocks(caches, layout: str | None, layer_numbers: Sequence[int] | None,
                          block_table: torch.Tensor, num_blocks_per_req: torch.Tensor, start_pos: torch.Tensor,
                          num_tokens: torch.Tensor, global_head_base=None, head_begin: int = 0,
                          head_count: int | None = None, out: torch.Tensor | None = None, accumulate: bool = False,
@@ -311,9 +337,11 @@ def kvck_checksum_blocks(caches: Sequence[torch.Tensor], layout: str, layer_numb
                          stream=None, check: bool = False, planes: tuple | None = None) -> torch.Tensor:
     """Per block position checksums of paged K/V (see include/kvck.h).
 
-    ``layout`` is one of LAYOUT_NAMES; ``planes=(begin, count)`` restricts a
-    pool holding K and V to K (0, 1) or V (1, 1) -- partials over K and V add
-    up to the checksum of both.
+    ``caches`` is a list of pool tensors or a PreparedCaches (then the
+    layout, layer, head and plane arguments are taken from it).  ``layout`` is
+    one of LAYOUT_NAMES; ``planes=(begin, count)`` restricts a pool holding K
+    and V to K (0, 1) or V (1, 1) -- partials over K and V add up to the
+    checksum of both.
 
     Returns ``out``: uint64 (num_reqs, max_blocks) on the caches' device;
     entries past a request's listed positions are left as they were.
@@ -324,7 +352,7 @@ def kvck_checksum_blocks(caches: Sequence[torch.Tensor], layout: str, layer_numb
                      global_head_base, head_begin, head_count, out, workspace, check, error_flags, planes)
     ws = a["workspace"]
     st = a["lib"].kvck_checksum_blocks(
-        ctypes.byref(a["L"]), a["ptrs"], a["layers"], a["bases"], a["n"], int(head_begin), int(a["head_count"]),
+        ctypes.byref(a["L"]), a["ptrs"], a["layers"], a["bases"], a["n"], a["head_begin"], a["head_count"],
         block_table.data_ptr(), block_table.stride(0), num_blocks_per_req.data_ptr(), start_pos.data_ptr(),
         num_tokens.data_ptr(), a["R"], a["max_blocks"], a["out"].data_ptr(), int(bool(accumulate)), ws.data_ptr(),
         ws.numel() * ws.element_size(), _ptr(a["error_flags"]), _stream_handle(stream, a["dev"]))
@@ -339,8 +367,8 @@ def kvck_staging_bytes(cache: torch.Tensor, layout: str, num_caches: int, head_c
                                                  int(L.num_heads if head_count is None else head_count)))
 
 
-def kvck_copy_checksum_blocks(direction: int, caches: Sequence[torch.Tensor], layout: str,
-                              layer_numbers: Sequence[int], block_table: torch.Tensor,
+def kvck_copy_checksum_blocks(direction: int, caches, layout: str | None,
+                              layer_numbers: Sequence[int] | None, block_table: torch.Tensor,
                               num_blocks_per_req: torch.Tensor, start_pos: torch.Tensor, num_tokens: torch.Tensor,
                               staging: torch.Tensor, global_head_base=None, head_begin: int = 0,
                               head_count: int | None = None, out: torch.Tensor | None = None,
@@ -358,8 +386,8 @@ def kvck_copy_checksum_blocks(direction: int, caches: Sequence[torch.Tensor], la
     positions = (staging.numel() * staging.element_size()) // per
     ws = a["workspace"]
     st = a["lib"].kvck_copy_checksum_blocks(
-        int(direction), ctypes.byref(a["L"]), a["ptrs"], a["layers"], a["bases"], a["n"], int(head_begin),
-        int(a["head_count"]), block_table.data_ptr(), block_table.stride(0), num_blocks_per_req.data_ptr(),
+        int(direction), ctypes.byref(a["L"]), a["ptrs"], a["layers"], a["bases"], a["n"], a["head_begin"],
+        a["head_count"], block_table.data_ptr(), block_table.stride(0), num_blocks_per_req.data_ptr(),
         start_pos.data_ptr(), num_tokens.data_ptr(), a["R"], a["max_blocks"], staging.data_ptr(), positions,
         a["out"].data_ptr(), int(bool(accumulate)), ws.data_ptr(), ws.numel() * ws.element_size(),
         _ptr(a["error_flags"]), _stream_handle(stream, a["dev"]))

@@ -256,8 +256,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   const kvck_status ds = current_device(&dev);
   if (ds != KVCK_OK) return ds;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  const int cus = device_cus(dev);
   choose_schedule(&shp, num_caches, (int64_t)num_reqs * max_blocks, image_bytes, planes_cov, head_count, cus,
                   mode != kModeChecksum);
   const int32_t lpt = shp.caches_per_task;

@@ -19,6 +19,10 @@
 //           (skipped when the call has one cache).  Addition mod 2^64 is
 //           associative and commutative, so results are bit-exact whatever
 //           the task order or launch shape.
+#include <atomic>
+#include <map>
+#include <mutex>
+
 #include "kvck_device.h"
 
 namespace kvck {
@@ -82,6 +86,58 @@ __global__ __launch_bounds__(256) void plan_fill_kernel(
   const int32_t k = (int32_t)(idx - (int64_t)r * max_blocks);
   const int32_t p0 = prefix[r];
   if (k >= prefix[r + 1] - p0) return;
+  const int64_t t0 = (start_pos[r] + k) * (int64_t)block_size;
+  const int64_t left = num_tokens[r] - t0;
+  int32_t v = left <= 0 ? 0 : (left >= block_size ? block_size : (int32_t)left);
+  const int32_t b = block_table[(int64_t)r * bt_stride + k];
+  if (v > 0 && (b < 0 || (int64_t)b >= num_blocks)) {
+    if (error_flags) atomicOr(error_flags, KVCK_FLAG_BAD_BLOCK_ID);
+    v = 0;
+  }
+  PosRecord rec;
+  rec.t0 = t0;
+  rec.out_idx = idx;
+  rec.block = b;
+  rec.valid = v;
+  rec.pad = 0;
+  recs[p0 + k] = rec;
+}
+
+// Both plan steps in one launch, for batches of at most 1024 requests: every
+// workgroup loads the clamped per-request counts into LDS and scans them
+// itself, then writes the records of its 256 (request, position) slots.
+__global__ __launch_bounds__(1024) void plan_small_kernel(
+    const int32_t* __restrict__ block_table, int64_t bt_stride, const int32_t* __restrict__ nbpr,
+    const int64_t* __restrict__ start_pos, const int64_t* __restrict__ num_tokens, int32_t num_reqs,
+    int32_t max_blocks, int32_t block_size, int64_t num_blocks, int64_t max_start, uint32_t* __restrict__ n_items,
+    PosRecord* __restrict__ recs, uint32_t* __restrict__ error_flags) {
+  __shared__ int32_t scan[1024];
+  const int tid = threadIdx.x;
+  int n = 0;
+  if (tid < num_reqs) {
+    n = nbpr[tid];
+    const int64_t s = start_pos[tid];
+    if (n < 0 || n > max_blocks || s < 0 || s > max_start) {
+      if (blockIdx.x == 0 && error_flags) atomicOr(error_flags, KVCK_FLAG_BAD_REQUEST);
+      n = 0;
+    }
+  }
+  scan[tid] = n;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int t = tid >= o ? scan[tid - o] : 0;
+    __syncthreads();
+    scan[tid] += t;
+    __syncthreads();
+  }
+  if (blockIdx.x == 0 && tid == 0) *n_items = (uint32_t)scan[1023];
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + tid;
+  if (idx >= (int64_t)num_reqs * max_blocks) return;
+  const int32_t r = (int32_t)(idx / max_blocks);
+  const int32_t k = (int32_t)(idx - (int64_t)r * max_blocks);
+  const int32_t end = scan[r];
+  const int32_t p0 = r > 0 ? scan[r - 1] : 0;
+  if (k >= end - p0) return;
   const int64_t t0 = (start_pos[r] + k) * (int64_t)block_size;
   const int64_t left = num_tokens[r] - t0;
   int32_t v = left <= 0 ? 0 : (left >= block_size ? block_size : (int32_t)left);
@@ -306,12 +362,38 @@ BlocksFn blocks_fn(const BlocksShape& shp) {
   return shp.chunk == 16 ? blocks_fn_slots<16, 1, false>(shp.slots) : blocks_fn_slots<8, 1, false>(shp.slots);
 }
 
+}  // namespace
+
 int device_cus(int device) {
+  static std::atomic<int> cached[64];
+  if (device >= 0 && device < 64) {
+    const int c = cached[device].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
     cus = 256;
+  if (device >= 0 && device < 64) cached[device].store(cus, std::memory_order_relaxed);
   return cus;
 }
+
+int kernel_occupancy(const void* fn, int device, int fallback) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    auto it = cache.find({fn, device});
+    if (it != cache.end()) return it->second;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kBlockThreads, 0) != hipSuccess || per_cu <= 0)
+    per_cu = fallback;
+  std::lock_guard<std::mutex> g(mu);
+  cache[{fn, device}] = per_cu;
+  return per_cu;
+}
+
+namespace {
 
 }  // namespace
 
@@ -325,11 +407,17 @@ hipError_t launch_plan(const int32_t* block_table, int64_t bt_stride, const int3
   int32_t* prefix = reinterpret_cast<int32_t*>(ws + w.prefix_off);
   PosRecord* recs = reinterpret_cast<PosRecord*>(ws + w.recs_off);
   const int64_t max_start = INT64_MAX / block_size - max_blocks;
+  const int64_t items = (int64_t)num_reqs * max_blocks;
+  if (num_reqs <= 1024) {
+    hipLaunchKernelGGL(plan_small_kernel, dim3((unsigned)((items + 1023) / 1024)), dim3(1024), 0, stream,
+                       block_table, bt_stride, nbpr, start_pos, num_tokens, num_reqs, max_blocks, block_size,
+                       num_blocks, max_start, n_items, recs, error_flags);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, nbpr, start_pos, num_reqs, max_blocks,
                      max_start, prefix, n_items, error_flags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t items = (int64_t)num_reqs * max_blocks;
   const int64_t grid = (items + 255) / 256;
   hipLaunchKernelGGL(plan_fill_kernel, dim3((unsigned)grid), dim3(256), 0, stream, block_table, bt_stride,
                      start_pos, num_tokens, num_reqs, max_blocks, block_size, num_blocks, prefix, recs,
@@ -339,11 +427,7 @@ hipError_t launch_plan(const int32_t* block_table, int64_t bt_stride, const int3
 
 int blocks_grid(const BlocksShape& shp, int device, int64_t max_tasks) {
   BlocksFn fn = blocks_fn(shp);
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kBlockThreads,
-                                                   0) != hipSuccess ||
-      per_cu <= 0)
-    per_cu = 2;
+  const int per_cu = kernel_occupancy(reinterpret_cast<const void*>(fn), device, 2);
   const int64_t waves_per_block = kBlockThreads / kWave;
   const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
   const int64_t cap = (int64_t)per_cu * device_cus(device);

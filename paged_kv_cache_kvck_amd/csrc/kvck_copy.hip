@@ -196,14 +196,8 @@ CopyFn copy_fn(const BlocksShape& shp, int direction) {
 
 int copy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks) {
   CopyFn fn = copy_fn(shp, direction);
-  int per_cu = 0;
-  if (!fn ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kBlockThreads, 0) !=
-          hipSuccess ||
-      per_cu <= 0)
-    per_cu = 1;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0) cus = 256;
+  const int per_cu = fn ? kernel_occupancy(reinterpret_cast<const void*>(fn), device, 1) : 1;
+  const int cus = device_cus(device);
   const int64_t waves_per_block = kBlockThreads / kWave;
   const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
   const int64_t cap = (int64_t)per_cu * cus;

@@ -124,5 +124,7 @@ hipError_t launch_tags(const uint64_t* checksums, const uint8_t* hashes, int64_t
                        int64_t n, const int32_t* nbpr, int32_t max_blocks, uint64_t* tagged, const uint64_t* stored,
                        uint8_t* mismatch, uint32_t* count, hipStream_t stream);
 int states_grid(int device, int64_t tasks);
+int device_cus(int device);                                   // cached per device
+int kernel_occupancy(const void* fn, int device, int fallback);  // workgroups per CU, cached
 
 }  // namespace kvck

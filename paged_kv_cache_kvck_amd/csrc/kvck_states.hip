@@ -108,14 +108,8 @@ __global__ __launch_bounds__(kBlockThreads) void states_kernel(const StatesArgs 
 }  // namespace
 
 int states_grid(int device, int64_t tasks) {
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&states_kernel),
-                                                   kBlockThreads, 0) != hipSuccess ||
-      per_cu <= 0)
-    per_cu = 2;
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || cus <= 0)
-    cus = 256;
+  const int per_cu = kernel_occupancy(reinterpret_cast<const void*>(&states_kernel), device, 2);
+  const int cus = device_cus(device);
   const int64_t need = (tasks + (kBlockThreads / kWave) - 1) / (kBlockThreads / kWave);
   const int64_t cap = (int64_t)per_cu * cus;
   return (int)(need < cap ? (need > 0 ? need : 1) : cap);

@@ -250,3 +250,19 @@ def test_states_small_parity():
     bad = torch.tensor([0, 9], dtype=torch.int32, device=DEV)
     with pytest.raises(kvck.KvckDeviceError):
         kvck.kvck_checksum_states(ds, layers, bad, check=True)
+
+
+def test_more_than_1024_requests(schedule):
+    """Batches above 1024 requests take the two-kernel plan (scan, then fill)."""
+    log("[1500 requests]")
+    rng = np.random.default_rng(14)
+    lengths = rng.integers(0, 41, size=1500)
+    req, nb = wl.page_requests(rng, lengths, 16, start_pos=None, extra_blocks=rng.integers(0, 2, size=1500),
+                               spare_frac=0.2)
+    hp = [wl.host_random_bits(rng, wl.pool_shape("HND", nb, 16, 2, 32), "bf16") for _ in range(3)]
+    got = gpu_blocks([to_device_bits(p) for p in hp], "HND", [0, 1, 2], req)
+    want = oracle.checksum_blocks(hp, "HND", [0, 1, 2], [0] * 3, req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k]), (r, k)
+    assert_unlisted_untouched(got, req)
