@@ -19,7 +19,6 @@ from __future__ import annotations
 
 import argparse
 import hashlib
-import glob
 import json
 import os
 import sys
@@ -29,10 +28,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
 
+# The sources that decide what the main-pass kernel reads: its own file, the
+# device helpers and argument structs it is built from, the host code that
+# picks its schedule, and the public header.
+MAIN_PASS_SOURCES = ("paged_kv_cache_kvck_amd/csrc/kvck_blocks.hip", "paged_kv_cache_kvck_amd/csrc/kvck_device.h",
+                     "paged_kv_cache_kvck_amd/csrc/kvck_internal.h", "paged_kv_cache_kvck_amd/csrc/kvck_api.hip",
+                     "include/kvck.h")
+
+
 def kernel_sources_sha() -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "paged_kv_cache_kvck_amd", "csrc", "*"))) + \
-            [os.path.join(ROOT, "include", "kvck.h")]:
+    for p in (os.path.join(ROOT, f) for f in MAIN_PASS_SOURCES):
         with open(p, "rb") as f:
             h.update(os.path.basename(p).encode())
             h.update(f.read())

@@ -4,8 +4,9 @@
 
 The library is a plain C-ABI shared object (include/kvck.h); the Python
 binding loads it with ctypes, so no torch C++ extension is involved.  The
-build also makes ``hbm_read_probe``, a plain streaming-read kernel that
-measures the HBM read bandwidth a trivial kernel reaches.
+build also makes ``hbm_read_probe``, which measures the HBM read bandwidth
+trivial read kernels reach: grid-stride streaming, and whole contiguous runs
+per wavefront in address or scrambled order (the shape of a paged cache).
 """
 
 from __future__ import annotations
