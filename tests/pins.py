@@ -166,6 +166,50 @@ def pin_all_ones(o):
     assert sum(factor(L, g) for L in (0, 1) for g in (0, 1)) == 262152
 
 
+def pin_large_numbers(o):
+    """Closed forms far from zero: a request whose listed blocks start past
+    token 2^32 (piece indices near 2^34) on the largest layer number with the
+    largest global head, whose slice factor m = 2(32767*65536 + 65535) + 1 is
+    2^32 - 1.  One nonzero piece gives x*m*(2j+1); all-ones pieces give
+    P^2 (t1^2 - t0^2) * sum of m, both mod 2^64."""
+    assert factor(32767, 65535) == (1 << 32) - 1
+    rng = np.random.default_rng(12)
+    far = (1 << 30) + 3
+    for layout in ("HND", "NHD", "MLA"):
+        d, bs = 8, 4
+        layers = (32767, 5)
+        case, req = make_case(rng, layout=layout, layers=layers, nh=1, d=d, bs=bs, lengths=(far * bs + 6, 9),
+                              start=(far, 0), zero=True, bases=(65535, 65535))
+        planes = 1 if layout == "MLA" else 2
+        P = planes * d * 2 // 8
+        # one nonzero piece in the far request
+        k = int(rng.integers(0, 2))
+        pos = far + k
+        v = min(bs, int(req.num_tokens[0]) - pos * bs)
+        i = int(rng.integers(0, v))
+        q = int(rng.integers(0, P))
+        x = int(rng.integers(1, 1 << 63)) * 2 + 1
+        plane, within = divmod(q, P // planes)
+        b = int(req.block_table[0, k])
+        row_u8(case["caches"][0], layout, plane, b, i, 0)[8 * within:8 * within + 8] = \
+            np.frombuffer(x.to_bytes(8, "little"), np.uint8)
+        t = pos * bs + i
+        assert t * P > 1 << 33
+        want = x * ((1 << 32) - 1) * (2 * (t * P + q) + 1) & M64
+        got = run_blocks(o, case)
+        for rr, kk in listed(case):
+            assert int(got[rr, kk]) == (want if (rr, kk) == (0, k) else 0), (layout, rr, kk)
+        # every piece 1
+        for pool in case["caches"]:
+            pool.view("<u8")[...] = 1
+        sum_m = factor(32767, 65535) + factor(5, 65535)
+        got = run_blocks(o, case)
+        for r, kk in listed(case):
+            t0 = (int(req.start_pos[r]) + kk) * bs
+            t1 = max(t0, min(int(req.num_tokens[r]), t0 + bs))
+            assert int(got[r, kk]) == P * P * (t1 * t1 - t0 * t0) * sum_m & M64, (layout, r, kk)
+
+
 def pin_byte_probe(o):
     """Byte->piece mapping: a single byte B at byte beta of token t's K (plane 0)
     or V (plane 1) row is piece q = plane * P/2 + beta // 8 with value
@@ -391,4 +435,4 @@ def pin_mamba(o):
 
 ALL_PINS = [pin_num_valid_tokens, pin_brute, pin_zero, pin_single_piece, pin_all_ones, pin_byte_probe,
             pin_linearity, pin_additivity_block_size, pin_layout_independence, pin_tp_pp_partials,
-            pin_exclusion, pin_detection, pin_mamba]
+            pin_exclusion, pin_detection, pin_mamba, pin_large_numbers]

@@ -266,3 +266,55 @@ def test_more_than_1024_requests(schedule):
     for r, k in req.listed():
         assert int(got[r, k]) == int(want[r, k]), (r, k)
     assert_unlisted_untouched(got, req)
+
+
+def test_largest_numbering(schedule):
+    """The largest numbering the method allows: layer 32767 with 65536 heads
+    per layer, so the slice factor m = 2(layer*65536 + head) + 1 reaches
+    2^32 - 1 (8-byte rows, block size 2)."""
+    log("[largest numbering]")
+    rng = np.random.default_rng(15)
+    req, nb = wl.page_requests(rng, [3, 4, 1], 2, extra_blocks=[0, 1, 0], spare_frac=0.5)
+    hp = [wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 2, 65536, 4), "bf16") for _ in range(2)]
+    layers = [32767, 1]
+    got = gpu_blocks([to_device_bits(p) for p in hp], "NHD", layers, req)
+    want = oracle.checksum_blocks(hp, "NHD", layers, [0, 0], req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k]), (r, k)
+    # the last two global heads of the largest layer alone, by head subset
+    got = gpu_blocks([to_device_bits(hp[0])], "NHD", [32767], req, bases=[65534], head_begin=65534, head_count=2)
+    want = oracle.checksum_blocks(hp[:1], "NHD", [32767], [65534], req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens, head_begin=65534, head_count=2)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k]), (r, k)
+
+
+@pytest.mark.parametrize("layout,elem,nh,d", [("HND", "bf16", 8, 128), ("NHD", "fp8", 12, 64), ("MLA", "bf16", 1, 576)])
+def test_piece_indices_beyond_32_bits(layout, elem, nh, d, schedule):
+    """Requests whose first listed block starts past token 2^31: piece indices
+    j = t*P + p exceed 2^32 (and 2^36 for MLA's P = 144)."""
+    log(f"[large piece indices] {layout} {elem}")
+    rng = np.random.default_rng(zlib.crc32(f"big{layout}{elem}".encode()))
+    bs = 16
+    start = [(1 << 27) + 1, (1 << 28) + 5, 7]
+    lengths = [(s + 2) * bs + 9 for s in start]        # three listed blocks each, the last partly valid
+    req, nb = wl.page_requests(rng, lengths, bs, start_pos=start, extra_blocks=[1, 0, 0], spare_frac=0.3)
+    hp = [wl.host_random_bits(rng, wl.pool_shape(layout, nb, bs, nh, d), elem) for _ in range(2)]
+    layers = [0, 9]
+    got = gpu_blocks([to_device_bits(p) for p in hp], layout, layers, req)
+    want = oracle.checksum_blocks(hp, layout, layers, [0, 0], req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k]), (r, k)
+    if layout == "HND":
+        # the fused save path numbers pieces the same way
+        bt, nbt, sp, nt = (torch.from_numpy(x).to(DEV) for x in (req.block_table, req.num_blocks, req.start_pos,
+                                                                    req.num_tokens))
+        pools = [to_device_bits(p) for p in hp]
+        per = kvck.kvck_staging_bytes(pools[0], layout, len(layers))
+        staging = torch.zeros(int(req.num_blocks.sum()) * per, dtype=torch.uint8, device=DEV)
+        cs = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, pools, layout, layers, bt, nbt, sp, nt, staging,
+                                            check=True).cpu().numpy()
+        for r, k in req.listed():
+            assert int(cs[r, k]) == int(want[r, k]), (r, k)

@@ -37,6 +37,11 @@ MUTATIONS = {
     "num_valid_tokens off by one": ("last = min(first + block_size, num_tokens)",
                                     "last = min(first + block_size, num_tokens + 1)"),
     "no exclusion of slots": ("v = num_valid_tokens(position, bs, num_tokens)\n", "v = bs\n"),
+    "token index kept in 32 bits": ("t = _U64(position * bs) + np.arange(v, dtype=_U64)",
+                                    "t = _U64((position * bs) & 0xFFFFFFFF) + np.arange(v, dtype=_U64)"),
+    "piece index kept in 32 bits": ("odd = _U64(2) * j + _U64(1)", "odd = _U64(2) * (j & _U64(0xFFFFFFFF)) + _U64(1)"),
+    "slice factor kept in 31 bits": ("c = c + (m * s).sum(dtype=_U64)",
+                                     "c = c + ((m & _U64(0x7FFFFFFF)) * s).sum(dtype=_U64)"),
     "Mamba elements numbered from 1": ("e = np.arange(x.size, dtype=_U64)", "e = np.arange(x.size, dtype=_U64) + _U64(1)"),
     "Mamba local row numbering": ("m = _U64(slice_factor(layer, g0 + g))", "m = _U64(slice_factor(layer, g))"),
     "Mamba states reversed": ("for st in states])", "for st in states[::-1]])"),
