@@ -3,8 +3,8 @@
 //
 //   paged_kv_cache_kvck_amd/hbm_read_probe [GiB]      (default 64)
 //
-// Two access shapes over one large buffer, nothing written unless an XOR of the
-// data hits a magic value:
+// Access shapes over one large buffer (the read shapes write nothing unless an
+// XOR of the data hits a magic value):
 //   * grid-stride: thread i reads 16-byte chunks i, i+T, i+2T, .. (T = total
 //     threads), U loads in flight, plain or non-temporal loads;
 //   * runs: each wavefront reads whole contiguous runs of R bytes (R = 8, 32 or
@@ -12,7 +12,9 @@
 //     non-temporal 1 KiB buffer loads per batch, the runs taken in address
 //     order or in a scrambled order (odd multiplier modulo a power of two: a
 //     permutation), which is the shape of a paged cache walked through a block
-//     table.  "pipelined" keeps a second batch in flight while the first is used.
+//     table.  "pipelined" keeps a second batch in flight while the first is used;
+//   * copy: one half of the buffer to the other (read + write), by a streaming
+//     kernel and by the runtime's device-to-device copy.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -101,6 +103,24 @@ __global__ __launch_bounds__(256) void runs_kernel(const uint8_t* __restrict__ p
   if (acc == kMagic) out[0] = acc;
 }
 
+// Streaming copy: thread i moves 16-byte chunks i, i+T, .. of src to dst with
+// U loads in flight; non-temporal loads and stores.  The ceiling for a kernel
+// that reads every byte once and writes it once (a fused copy).
+template <int U>
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                   size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + (U - 1) * stride < n; i += U * stride) {
+    u32x4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u) __builtin_nontemporal_store(x[u], dst + i + u * stride);
+  }
+  for (; i < n; i += stride) dst[i] = src[i];
+}
+
 struct Timer {
   hipEvent_t a, b;
   Timer() {
@@ -168,6 +188,17 @@ int main(int argc, char** argv) {
     std::printf("runs %2u KiB scrambled, pipelined grid=%6d : %8.1f GB/s\n", run_kib, cus * 2,
                 time_gbs([&] { runs_kernel<true, true><<<cus * 2, 256>>>(p, nruns, run, out); }, rb));
   }
+  // copies between the two halves of the buffer (bytes read + bytes written)
+  const size_t half = bytes / 2 / 16 * 16;
+  const u32x4* src = reinterpret_cast<const u32x4*>(p);
+  u32x4* dst = reinterpret_cast<u32x4*>(p + half);
+  for (int m : {4, 16}) {
+    const int grid = cus * m;
+    std::printf("copy kernel non-temporal U= 8 grid=%6d : %8.1f GB/s read+write\n", grid,
+                time_gbs([&] { copy_kernel<8><<<grid, 256>>>(src, dst, half / 16); }, 2.0 * half));
+  }
+  std::printf("hipMemcpyAsync device to device        : %8.1f GB/s read+write\n",
+              time_gbs([&] { CHECK(hipMemcpyAsync(dst, src, half, hipMemcpyDeviceToDevice, 0)); }, 2.0 * half));
   CHECK(hipFree(p));
   CHECK(hipFree(out));
   return 0;
