@@ -10,7 +10,7 @@
 //   s(g) = sum over e of x_e (2e + 1);  c = sum over (layer, g) of m s(g),
 //   m = 2 (layer*65536 + g) + 1, all modulo 2^64.
 //
-// Task = (layer, group of rows, request), one wavefront each.  Lanes stream the
+// Task = (request, layer, group of rows), one wavefront each.  Lanes stream the
 // row's 16-byte chunks; a chunk of 4-byte elements x0..x3 starting at element e
 // adds sum_i x_i (2(e+i) + 1); a chunk of 2-byte elements x0..x7 adds
 // u*X + 2*Y with u = 2e + 1, X = sum x_i, Y = sum i*x_i (both fit 32 bits).
@@ -56,8 +56,11 @@ __global__ __launch_bounds__(kBlockThreads) void states_kernel(const StatesArgs 
   const int64_t splits = (int64_t)a.num_layers * a.groups_per_layer;
   const int64_t total = splits * a.num_reqs;
   for (int64_t task = wave; task < total; task += nwaves) {
-    const int32_t split = (int32_t)(task / a.num_reqs);
-    const int32_t r = (int32_t)(task - (int64_t)split * a.num_reqs);
+    // request-major: the waves resident at once read whole slots' states (a
+    // slot's rows are contiguous) rather than the same rows of many slots,
+    // whose addresses lie a slot's size apart and crowd the same HBM channels
+    const int32_t r = (int32_t)(task / splits);
+    const int32_t split = (int32_t)(task - (int64_t)r * splits);
     const int32_t l = split / a.groups_per_layer;
     const int32_t grp = split - l * a.groups_per_layer;
     const int32_t slot = a.slot_ids[r];
