@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -165,18 +166,23 @@ def main(argv=None):
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         step()
+        marks[i].record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
+    per_step = [e0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)]
     main_ms, calls = kvck.kvck_instrument_read()
     main_avg = main_ms / max(calls, 1)
     achieved = valid / (main_avg * 1e-3) / 1e9
 
-    extra = {"valid_bytes_per_step": valid, "main_pass_ms": main_avg, "listed_positions": int(req.num_blocks.sum()),
+    extra = {"valid_bytes_per_step": valid, "main_pass_ms": main_avg,
+             "step_ms_median": statistics.median(per_step), "step_ms_min": min(per_step),
+             "listed_positions": int(req.num_blocks.sum()),
              "metadata_bytes_per_step": int(req.num_blocks.sum()) * (4 + 8 + 32) + req.num_reqs * 20}
     if not args.no_shard and w.layout == "HND" and w.num_heads == 8:
         # TP = 4 shard over heads {2, 3}, global numbering from 2
