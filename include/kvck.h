@@ -61,7 +61,9 @@ typedef enum kvck_status {
   KVCK_ERR_INVALID_ARGUMENT = -1, /* null pointer, negative size, bad stride */
   KVCK_ERR_UNSUPPORTED = -2,      /* > H heads/rows, layer > KVCK_MAX_LAYER_NUMBER,
                                      row bytes not a multiple of 8, element
-                                     width not 2 or 4, too many caches */
+                                     width not 2 or 4, too many caches, a
+                                     tensor whose strided byte extent reaches
+                                     2^50 (pool, state, staging, hashes) */
   KVCK_ERR_MISALIGNED = -3,       /* base pointer or stride not 8-byte aligned */
   KVCK_ERR_WORKSPACE = -4,        /* workspace missing or too small */
   KVCK_ERR_HIP = -5,              /* a HIP runtime call failed */
@@ -147,7 +149,8 @@ typedef struct kvck_kv_layout {
  *
  * Workspace: device, at least kvck_blocks_workspace_bytes(num_caches,
  * num_reqs, max_blocks) bytes, 256-byte aligned; its contents on entry are
- * ignored.
+ * ignored.  kvck_blocks_workspace_bytes returns 0 for arguments the entry
+ * points reject (num_caches < 1, negative sizes, num_reqs*max_blocks >= 2^31).
  *
  * Schedule: large batches (many tasks per resident wavefront) keep two load
  * batches in flight and give each task four layers; small ones use one layer
@@ -200,7 +203,8 @@ typedef struct kvck_state_desc {
  * state_ptrs holds num_layers*states_per_layer device pointers, layer-major
  * (state_ptrs[l*states_per_layer + i] is state i of layer l).
  * Workspace: device, kvck_states_workspace_bytes(num_layers, row_count,
- * num_reqs) bytes, 256-byte aligned.
+ * num_reqs) bytes, 256-byte aligned (that function returns 0 for arguments
+ * the entry point rejects).
  */
 kvck_status kvck_checksum_states(
     const kvck_state_desc* states, int32_t states_per_layer,  /* host [states_per_layer], 1..4 */
@@ -252,7 +256,8 @@ kvck_status kvck_copy_checksum_blocks(
     uint32_t* error_flags,
     kvck_stream_t stream);
 
-/* Staging bytes of one entry (listed position) for kvck_copy_checksum_blocks. */
+/* Staging bytes of one entry (listed position) for kvck_copy_checksum_blocks;
+ * 0 for an invalid layout or plane range, or a size of 2^50 bytes or more. */
 size_t kvck_staging_bytes(const kvck_kv_layout* layout, int32_t num_caches, int32_t head_count);
 
 /*

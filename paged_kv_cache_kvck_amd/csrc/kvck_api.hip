@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <initializer_list>
 #include <mutex>
 #include <vector>
 
@@ -17,6 +18,33 @@ namespace {
 constexpr int64_t kH = KVCK_MAX_KV_HEADS_PER_LAYER;
 
 bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)a) == 0; }
+
+// Largest byte extent of a tensor the kernels address (64-bit offsets with
+// room to spare; far beyond any device memory).
+constexpr int64_t kMaxExtent = (int64_t)1 << 50;
+
+struct Dim {
+  int64_t n, stride;  // extent along one axis, bytes between neighbours
+};
+
+// Byte extent of a strided tensor, sum of (n-1)*stride over its axes plus the
+// bytes of its last element; false when that overflows or reaches kMaxExtent.
+// Callers have checked n >= 0 and stride >= 0.
+bool extent_ok(std::initializer_list<Dim> dims, int64_t tail) {
+  int64_t total = tail;
+  for (const Dim& d : dims) {
+    if (d.n < 1) continue;
+    int64_t t = 0;
+    if (__builtin_mul_overflow(d.n - 1, d.stride, &t) || __builtin_add_overflow(total, t, &total)) return false;
+  }
+  return total < kMaxExtent;
+}
+
+// a * b * c < kMaxExtent for non-negative factors, without overflow
+bool product_ok(int64_t a, int64_t b, int64_t c) {
+  int64_t t = 0;
+  return !__builtin_mul_overflow(a, b, &t) && !__builtin_mul_overflow(t, c, &t) && t < kMaxExtent;
+}
 
 // gfx950 check of the current device, cached per device id.
 kvck_status current_device(int* dev_out) {
@@ -174,6 +202,7 @@ KVCK_EXPORT int32_t kvck_platform_supported(void) {
 
 KVCK_EXPORT size_t kvck_blocks_workspace_bytes(int32_t num_caches, int32_t num_reqs, int32_t max_blocks) {
   if (num_caches < 1 || num_reqs < 0 || max_blocks < 0) return 0;
+  if ((int64_t)num_reqs * max_blocks >= ((int64_t)1 << 31)) return 0;  // a batch the entry points reject
   return BlocksWorkspace::make(num_caches, num_reqs, max_blocks).total;
 }
 
@@ -206,7 +235,12 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   if (run_bytes % 8 != 0 || L.row_bytes % run_bytes != 0) return KVCK_ERR_UNSUPPORTED;
   const int32_t runs = L.row_bytes / run_bytes;
   const int32_t planes_cov = L.plane_count == 0 ? L.planes - L.plane_begin : L.plane_count;
-  if (planes_cov < 1 || L.plane_begin + planes_cov > L.planes) return KVCK_ERR_INVALID_ARGUMENT;
+  if (planes_cov < 1 || (int64_t)L.plane_begin + planes_cov > L.planes) return KVCK_ERR_INVALID_ARGUMENT;
+  // every byte the kernels may address lies within a 2^50-byte extent
+  if (!extent_ok({{L.planes, L.plane_stride}, {L.num_blocks, L.block_stride}, {L.block_size, L.slot_stride},
+                  {L.num_heads, L.head_stride}, {runs, L.chunk_stride}},
+                 run_bytes))
+    return KVCK_ERR_UNSUPPORTED;
   if (head_begin < 0 || head_count < 1 || (int64_t)head_begin + head_count > L.num_heads)
     return KVCK_ERR_INVALID_ARGUMENT;
   for (int32_t i = 0; i < num_caches; ++i) {
@@ -247,6 +281,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   if (mode != kModeChecksum) {
     if (!staging || staging_positions < 0) return KVCK_ERR_INVALID_ARGUMENT;
     if ((int64_t)L.block_size * L.row_bytes >= ((int64_t)1 << 31)) return KVCK_ERR_UNSUPPORTED;
+    if (!product_ok(staging_positions, num_caches, image_bytes)) return KVCK_ERR_UNSUPPORTED;
   }
   // ---- workspace
   const BlocksWorkspace w = BlocksWorkspace::make(num_caches, num_reqs, max_blocks);
@@ -363,23 +398,27 @@ KVCK_EXPORT kvck_status kvck_copy_checksum_blocks(int32_t direction, const kvck_
 }
 
 KVCK_EXPORT size_t kvck_staging_bytes(const kvck_kv_layout* layout, int32_t num_caches, int32_t head_count) {
-  if (!layout || num_caches < 1 || head_count < 1 || layout->planes < 1 || layout->block_size < 1 ||
-      layout->row_bytes < 1)
+  if (!layout || num_caches < 1 || head_count < 1 || (layout->planes != 1 && layout->planes != 2) ||
+      layout->block_size < 1 || layout->row_bytes < 1 || layout->plane_begin < 0 || layout->plane_count < 0)
     return 0;
-  const int32_t planes = layout->plane_count > 0 ? layout->plane_count : layout->planes - layout->plane_begin;
-  if (planes < 1) return 0;
-  return (size_t)planes * (size_t)head_count * (size_t)layout->block_size * (size_t)layout->row_bytes *
-         (size_t)num_caches;
+  const int64_t planes =
+      layout->plane_count > 0 ? layout->plane_count : (int64_t)layout->planes - layout->plane_begin;
+  if (planes < 1 || (int64_t)layout->plane_begin + planes > layout->planes) return 0;
+  const int64_t image = planes * head_count * (int64_t)layout->block_size;  // < 2^2 * 2^31 * 2^31
+  if (!product_ok(image, layout->row_bytes, num_caches)) return 0;
+  return (size_t)(image * layout->row_bytes * num_caches);
 }
 
 namespace {
 constexpr int32_t kRowsPerTask = 8;
-int32_t row_groups(int32_t row_count) { return (row_count + kRowsPerTask - 1) / kRowsPerTask; }
+int32_t row_groups(int32_t row_count) { return (int32_t)(((int64_t)row_count + kRowsPerTask - 1) / kRowsPerTask); }
 }  // namespace
 
 KVCK_EXPORT size_t kvck_states_workspace_bytes(int32_t num_layers, int32_t row_count, int32_t num_reqs) {
   if (num_layers < 1 || row_count < 1 || num_reqs < 0) return 0;
   const int64_t splits = (int64_t)num_layers * row_groups(row_count);
+  int64_t items = 0;  // a batch the entry point rejects
+  if (__builtin_mul_overflow(splits, (int64_t)num_reqs, &items) || items >= ((int64_t)1 << 40)) return 0;
   return kAlign + (splits > 1 ? align_up(sizeof(uint64_t) * (size_t)splits * (size_t)num_reqs) : 0);
 }
 
@@ -402,6 +441,8 @@ KVCK_EXPORT kvck_status kvck_checksum_states(const kvck_state_desc* states, int3
     if (d.elem_bytes != 2 && d.elem_bytes != 4) return KVCK_ERR_UNSUPPORTED;
     if (((int64_t)d.row_elems * d.elem_bytes) % 16 != 0) return KVCK_ERR_UNSUPPORTED;
     if (d.slot_stride % 16 != 0 || d.row_stride % 16 != 0) return KVCK_ERR_MISALIGNED;
+    if (!extent_ok({{num_slots, d.slot_stride}, {num_rows, d.row_stride}}, (int64_t)d.row_elems * d.elem_bytes))
+      return KVCK_ERR_UNSUPPORTED;
     elems += d.row_elems;
   }
   if (elems >= ((int64_t)1 << 31) - 8) return KVCK_ERR_UNSUPPORTED;
@@ -420,7 +461,9 @@ KVCK_EXPORT kvck_status kvck_checksum_states(const kvck_state_desc* states, int3
   if (!slot_ids || !out) return KVCK_ERR_INVALID_ARGUMENT;
   const int32_t groups = row_groups(row_count);
   const int64_t splits = (int64_t)num_layers * groups;
-  if (splits * num_reqs >= ((int64_t)1 << 40)) return KVCK_ERR_UNSUPPORTED;
+  int64_t items = 0;
+  if (__builtin_mul_overflow(splits, (int64_t)num_reqs, &items) || items >= ((int64_t)1 << 40))
+    return KVCK_ERR_UNSUPPORTED;
   const size_t need = kvck_states_workspace_bytes(num_layers, row_count, num_reqs);
   if (splits > 1 && (!workspace || workspace_bytes < need || !aligned(workspace, (int64_t)kAlign)))
     return KVCK_ERR_WORKSPACE;
@@ -489,6 +532,7 @@ KVCK_EXPORT kvck_status kvck_tag_checksums(const uint64_t* checksums, const uint
   if ((mismatch || mismatch_count) && !stored) return KVCK_ERR_INVALID_ARGUMENT;
   if (hash_stride < 8) return KVCK_ERR_INVALID_ARGUMENT;
   if (hash_stride % 8 != 0 || !aligned(block_hashes, 8)) return KVCK_ERR_MISALIGNED;
+  if (!extent_ok({{n, hash_stride}}, 8)) return KVCK_ERR_UNSUPPORTED;
   if (num_blocks_per_req && (max_blocks < 1 || n % max_blocks != 0)) return KVCK_ERR_INVALID_ARGUMENT;
   int dev = 0;
   const kvck_status ds = current_device(&dev);
