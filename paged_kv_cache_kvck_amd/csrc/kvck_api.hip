@@ -68,14 +68,16 @@ kvck_status current_device(int* dev_out) {
 }
 
 // Lane-table shape: the smallest S whose 64*S lane-chunks cover a whole block
-// row set of one (plane, head); larger row sets are split into equal groups.
+// row set of one (plane, head); larger row sets are split into groups of
+// equal size, each at most the rows one table of 16 slots holds.
 bool choose_shape(int32_t block_size, int32_t row_bytes, int chunk, BlocksShape* shp) {
   const int64_t cpr = row_bytes / chunk;
   const int64_t max_chunks = (int64_t)kWave * 16;
   if (cpr > max_chunks) return false;
-  const int64_t groups = ((int64_t)block_size * cpr + max_chunks - 1) / max_chunks;
-  const int64_t rg = (block_size + groups - 1) / groups;
-  const int64_t need = (rg * cpr + kWave - 1) / kWave;
+  const int64_t rg_max = max_chunks / cpr;
+  const int64_t groups = (block_size + rg_max - 1) / rg_max;
+  const int64_t rg = (block_size + groups - 1) / groups;  // <= rg_max
+  const int64_t need = (rg * cpr + kWave - 1) / kWave;    // <= 16
   int s = 1;
   while (s < need) s <<= 1;
   shp->chunk = chunk;
@@ -84,8 +86,14 @@ bool choose_shape(int32_t block_size, int32_t row_bytes, int chunk, BlocksShape*
   shp->pipelined = false;
   shp->caches_per_task = 1;
   shp->planes_per_unit = 1;
+  shp->merged = false;
   return true;
 }
+
+// Heads side by side in a slot (head_stride == row_bytes) are read as one row
+// per slot when one head's row is shorter than this: short rows would leave
+// each load instruction with many short segments.
+constexpr int32_t kMergeBelowRowBytes = 128;
 
 // Schedule: with many tasks per resident wave, keep two unit buffers in
 // flight and let one task cover several caches, so a wave's loads do not
@@ -108,11 +116,13 @@ void choose_schedule(BlocksShape* shp, int32_t num_caches, int64_t max_items, in
   while (lpt < kPipeMaxCaches && (int64_t)(2 * lpt) * block_bytes <= kPipeTaskBytes) lpt *= 2;
   const int64_t tasks = max_items * ((num_caches + lpt - 1) / lpt);
   bool pipe = shp->slots <= 4 && num_caches > 1 && tasks >= kPipeMinTasksPerWave * waves;
-  // KVCK_SCHEDULE=pipelined|simple overrides the choice (results are identical either way)
+  // KVCK_SCHEDULE=pipelined|simple overrides the choice (results are identical
+  // either way); merged rows always run the unpipelined kernel
   if (const char* force = getenv("KVCK_SCHEDULE")) {
     if (strcmp(force, "pipelined") == 0) pipe = true;
     if (strcmp(force, "simple") == 0) pipe = false;
   }
+  if (shp->merged && !copy) pipe = false;
   if (copy) pipe = true;  // the fused copy kernel always runs the pipelined structure
   if (pipe) {
     shp->pipelined = true;
@@ -267,10 +277,20 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
     if (chunk == 8) return KVCK_ERR_MISALIGNED;
     chunk = 8;
   }
+  // merged rows: the call's heads of one slot side by side, read as one row
+  const int64_t wide = (int64_t)head_count * L.row_bytes;
+  const bool can_merge = mode == kModeChecksum && runs == 1 && head_count > 1 && L.head_stride == L.row_bytes &&
+                         wide <= (int64_t)kWave * 16 * chunk;
+  bool merged = can_merge && L.row_bytes < kMergeBelowRowBytes;
+  // KVCK_MERGE_HEADS=0|1 overrides the choice where merging is possible (results are identical)
+  if (const char* force = getenv("KVCK_MERGE_HEADS")) merged = can_merge && force[0] == '1';
+  const int32_t lane_row_bytes = merged ? (int32_t)wide : L.row_bytes;
   BlocksShape shp;
-  if (!choose_shape(L.block_size, L.row_bytes, chunk, &shp)) return KVCK_ERR_UNSUPPORTED;
+  if (!choose_shape(L.block_size, lane_row_bytes, chunk, &shp)) return KVCK_ERR_UNSUPPORTED;
+  shp.merged = merged;
   // lane-table offsets and piece terms are 32-bit
-  if ((int64_t)shp.rows_per_group * L.slot_stride + (int64_t)(runs - 1) * L.chunk_stride + run_bytes >=
+  if ((int64_t)shp.rows_per_group * L.slot_stride + (int64_t)(runs - 1) * L.chunk_stride +
+          (merged ? lane_row_bytes : run_bytes) >=
       ((int64_t)1 << 31))
     return KVCK_ERR_UNSUPPORTED;
   const int64_t pieces = (int64_t)L.planes * L.row_bytes / 8;
@@ -318,12 +338,13 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   a.piece_base = 2ull * (uint64_t)L.plane_begin * (uint64_t)(pieces / L.planes);
   a.planes = planes_cov;
   a.planes_total = L.planes;
-  a.chunks_per_run = run_bytes / chunk;
-  a.heads = head_count;
+  a.chunks_per_run = (merged ? lane_row_bytes : run_bytes) / chunk;
+  a.heads = merged ? 1 : head_count;  // a merged row is one unit-level head
   a.row_bytes = L.row_bytes;
   a.pieces = (int32_t)pieces;
   a.rows_per_group = shp.rows_per_group;
-  a.chunks_per_row = L.row_bytes / chunk;
+  a.chunks_per_row = lane_row_bytes / chunk;
+  a.chunks_per_head = L.row_bytes / chunk;
   a.caches_per_task = lpt;
   a.direct = total_groups == 1;
   a.accumulate = accumulate != 0;

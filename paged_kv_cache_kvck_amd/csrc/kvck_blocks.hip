@@ -179,7 +179,11 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
 // PIPE = false: each unit's loads are issued, then consumed.
 // PIPE = true:  two unit buffers in ping-pong, so the loads of unit i+1 are in
 //               flight while unit i is consumed, across the caches of a task.
-template <int CHUNK, int S, int HU, int PU, bool PIPE>
+// MERGED:       pools whose heads sit side by side in a slot (NHD-like): a
+//               lane-table row is the slot's whole run of heads, so a load
+//               instruction covers contiguous bytes even when one head's row
+//               is short; each chunk carries its own head's factor m.
+template <int CHUNK, int S, int HU, int PU, bool PIPE, bool MERGED>
 __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs a) {
   using V = typename ChunkType<CHUNK>::T;
   const int lane = threadIdx.x & (kWave - 1);
@@ -193,6 +197,8 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
 
   LaneTable<S> lt;
   lt.template init<CHUNK>(lane, a);
+  uint32_t lhead[S];  // local head of each lane chunk (merged rows only)
+  if constexpr (MERGED) lt.heads(lane, a, lhead);
   const uint64_t P = (uint64_t)a.pieces;
   const int rg = a.rows_per_group;
   const uint64_t plane_term = 2ull * (P / (uint64_t)a.planes_total);
@@ -252,14 +258,19 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
             for (int s = 0; s < S; ++s) {
               const uint64_t u = up + lt.urel[s];
               const uint64_t xa = (uint64_t)x[p][h][s].x | ((uint64_t)x[p][h][s].y << 32);
+              uint64_t t;
               if constexpr (CHUNK == 16) {
                 const uint64_t xb = (uint64_t)x[p][h][s].z | ((uint64_t)x[p][h][s].w << 32);
-                sh += (xa + xb) * u + (xb << 1);
+                t = (xa + xb) * u + (xb << 1);
               } else {
-                sh += xa * u;
+                t = xa * u;
               }
+              if constexpr (MERGED)
+                acc += t * (uint64_t)(mb + 2u * lhead[s]);
+              else
+                sh += t;
             }
-            acc += sh * (uint64_t)(mb + 2u * (uint32_t)(cc.hbatch * HU + h));
+            if constexpr (!MERGED) acc += sh * (uint64_t)(mb + 2u * (uint32_t)(cc.hbatch * HU + h));
           }
         }
         cc.next(nhb, nplanes, ngr);
@@ -331,29 +342,33 @@ __global__ __launch_bounds__(256) void reduce_wave_kernel(const uint64_t* __rest
   }
 }
 
-template <int CHUNK, int S, int PU, bool PIPE>
+template <int CHUNK, int S, int PU, bool PIPE, bool MERGED>
 constexpr auto pick_kernel() {
-  constexpr int hu = 16 / (S * PU) > 0 ? 16 / (S * PU) : 1;
-  return &blocks_kernel<CHUNK, S, hu, PU, PIPE>;
+  constexpr int hu = MERGED ? 1 : (16 / (S * PU) > 0 ? 16 / (S * PU) : 1);
+  return &blocks_kernel<CHUNK, S, hu, PU, PIPE, MERGED>;
 }
 
 using BlocksFn = void (*)(const BlocksArgs);
 
-template <int CHUNK, int PU, bool PIPE>
+template <int CHUNK, int PU, bool PIPE, bool MERGED = false>
 BlocksFn blocks_fn_slots(int slots) {
   switch (slots) {
-    case 1: return pick_kernel<CHUNK, 1, PU, PIPE>();
-    case 2: return pick_kernel<CHUNK, 2, PU, PIPE>();
-    case 4: return pick_kernel<CHUNK, 4, PU, PIPE>();
-    case 8: return pick_kernel<CHUNK, 8, 1, PIPE>();
-    case 16: return pick_kernel<CHUNK, 16, 1, PIPE>();
+    case 1: return pick_kernel<CHUNK, 1, PU, PIPE, MERGED>();
+    case 2: return pick_kernel<CHUNK, 2, PU, PIPE, MERGED>();
+    case 4: return pick_kernel<CHUNK, 4, PU, PIPE, MERGED>();
+    case 8: return pick_kernel<CHUNK, 8, 1, PIPE, MERGED>();
+    case 16: return pick_kernel<CHUNK, 16, 1, PIPE, MERGED>();
   }
   return nullptr;
 }
 
 // Pipelined units may carry both planes (PU = 2); the unpipelined kernel and
-// wide lane tables (S >= 8) always take one plane per unit.
+// wide lane tables (S >= 8) always take one plane per unit.  Merged rows run
+// the unpipelined kernel.
 BlocksFn blocks_fn(const BlocksShape& shp) {
+  if (shp.merged)
+    return shp.chunk == 16 ? blocks_fn_slots<16, 1, false, true>(shp.slots)
+                           : blocks_fn_slots<8, 1, false, true>(shp.slots);
   if (shp.pipelined) {
     if (shp.planes_per_unit == 2)
       return shp.chunk == 16 ? blocks_fn_slots<16, 2, true>(shp.slots) : blocks_fn_slots<8, 2, true>(shp.slots);

@@ -63,7 +63,18 @@ struct LaneTable {
       const int run = c / a.chunks_per_run;
       off[s] = (uint32_t)((int64_t)r * a.slot_stride + (int64_t)run * a.chunk_stride +
                           (int64_t)(c - run * a.chunks_per_run) * CHUNK);
-      urel[s] = (uint32_t)(2u * (uint32_t)r * (uint32_t)a.pieces + (uint32_t)(CHUNK / 4) * (uint32_t)c);
+      // a merged row holds several heads' rows back to back: pieces count from its head's row
+      const int cin = c - (c / a.chunks_per_head) * a.chunks_per_head;
+      urel[s] = (uint32_t)(2u * (uint32_t)r * (uint32_t)a.pieces + (uint32_t)(CHUNK / 4) * (uint32_t)cin);
+    }
+  }
+  // Local head of each chunk in a merged row (0 when rows are single heads).
+  __device__ __forceinline__ void heads(int lane, const BlocksArgs& a, uint32_t (&h)[S]) const {
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+      const int f = lane + kWave * s;
+      const int c = f - (f / a.chunks_per_row) * a.chunks_per_row;
+      h[s] = (uint32_t)(c / a.chunks_per_head);
     }
   }
 };

@@ -57,6 +57,7 @@ struct BlocksArgs {
   int32_t planes_total;                      // planes of the slice
   int32_t rows_per_group;                    // rows covered by one lane table
   int32_t chunks_per_row;
+  int32_t chunks_per_head;                   // chunks of one head's row (< chunks_per_row: merged heads)
   int32_t chunks_per_run;                    // lane chunks in one contiguous run of a row
   int32_t num_caches;                        // caches in this launch
   int32_t caches_per_task;                   // caches one task covers (a partial's group)
@@ -105,6 +106,7 @@ struct BlocksShape {
   bool pipelined; // two unit buffers in flight, several caches per task
   int caches_per_task;
   int planes_per_unit;  // 1, or 2 (K and V in one unit) when heads are few
+  bool merged;          // a lane-table row is a slot's adjacent heads (NHD-like pools)
 };
 
 // launchers (return hipSuccess or the first HIP error)

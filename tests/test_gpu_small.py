@@ -318,3 +318,56 @@ def test_piece_indices_beyond_32_bits(layout, elem, nh, d, schedule):
                                             check=True).cpu().numpy()
         for r, k in req.listed():
             assert int(cs[r, k]) == int(want[r, k]), (r, k)
+
+
+MERGE_CASES = [
+    # name, layout, elem, heads, head_size, block_size, lengths, head_begin, head_count
+    ("nhd_fp8_d64", "NHD", "fp8", 12, 64, 16, [90, 7, 33], 0, None),
+    ("nhd_fp8_bs64", "NHD", "fp8", 12, 64, 64, [200, 64, 5], 0, None),
+    ("nhd_fp8_heads_3_8", "NHD", "fp8", 12, 64, 16, [50, 17], 3, 5),
+    ("nhd_bf16_d32", "NHD", "bf16", 4, 32, 16, [40, 16, 9], 1, 2),
+    ("nhd_fp16_d64", "NHD", "fp16", 12, 64, 16, [100, 31], 0, None),
+    ("nhd_bf16_d384_bs64", "NHD", "bf16", 2, 384, 64, [130, 64], 0, None),
+    ("fi_nhd_fp8", "FI_NHD", "fp8", 8, 64, 16, [77, 16], 2, 4),
+    ("nhd_fp32_d2_bs1", "NHD", "fp32", 6, 2, 1, [5, 2], 0, None),         # 8-byte rows, 8-byte chunks
+]
+
+
+@pytest.mark.parametrize("merge", ["0", "1"])
+@pytest.mark.parametrize("case", MERGE_CASES, ids=[c[0] for c in MERGE_CASES])
+def test_merged_heads_parity(case, merge, monkeypatch):
+    """Heads side by side in a slot read as one row per slot (KVCK_MERGE_HEADS=1)
+    or head by head (=0): both equal the oracle."""
+    name, layout, elem, nh, d, bs, lengths, hb, hc = case
+    monkeypatch.setenv("KVCK_MERGE_HEADS", merge)
+    log(f"[merged heads] {name} merge={merge}")
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    req, nb = wl.page_requests(rng, lengths, bs, start_pos=[1] + [0] * (len(lengths) - 1),
+                               extra_blocks=[0] * (len(lengths) - 1) + [1], spare_frac=0.3)
+    layers = [2, 5, 9]
+    hp = [wl.host_random_bits(rng, wl.pool_shape(layout, nb, bs, nh, d), elem) for _ in layers]
+    n = nh - hb if hc is None else hc
+    bases = [hb + 7 * i for i in range(len(layers))]
+    got = gpu_blocks([to_device_bits(p) for p in hp], layout, layers, req, bases=bases, head_begin=hb, head_count=hc)
+    want = oracle.checksum_blocks(hp, layout, layers, bases, req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens, head_begin=hb, head_count=n)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k]), (r, k)
+    assert_unlisted_untouched(got, req)
+
+
+@pytest.mark.parametrize("layout,elem,nh,d", [("HND", "bf16", 2, 384), ("NHD", "bf16", 2, 384), ("MLA", "fp8", 1, 1536)])
+def test_row_groups_fit_one_lane_table(layout, elem, nh, d, schedule, monkeypatch):
+    """Rows whose size does not divide a lane table's 16 KiB (768- and
+    1536-byte rows in 64-slot blocks) are split into row groups that fit."""
+    monkeypatch.setenv("KVCK_MERGE_HEADS", "0")
+    log(f"[row groups] {layout} {elem} d={d}")
+    rng = np.random.default_rng(zlib.crc32(f"rg{layout}{d}".encode()))
+    req, nb = wl.page_requests(rng, [150, 64, 3], 64, spare_frac=0.3)
+    layers = [0, 1]
+    hp = [wl.host_random_bits(rng, wl.pool_shape(layout, nb, 64, nh, d), elem) for _ in layers]
+    got = gpu_blocks([to_device_bits(p) for p in hp], layout, layers, req)
+    want = oracle.checksum_blocks(hp, layout, layers, [0, 0], req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k]), (r, k)
