@@ -87,6 +87,7 @@ bool choose_shape(int32_t block_size, int32_t row_bytes, int chunk, BlocksShape*
   shp->caches_per_task = 1;
   shp->planes_per_unit = 1;
   shp->merged = false;
+  shp->copy_buffers = 1;
   return true;
 }
 
@@ -123,6 +124,13 @@ void choose_schedule(BlocksShape* shp, int32_t num_caches, int64_t max_items, in
     if (strcmp(force, "simple") == 0) pipe = false;
   }
   if (shp->merged && !copy) pipe = false;
+  if (copy) {
+    // One unit buffer per wave: twice the resident waves of the ping-pong
+    // kernel, which keeps more stores in flight (same-box A/B: load 5.6 ->
+    // 5.9 TB/s read+write, save unchanged).  KVCK_COPY_BUFFERS=2 selects the
+    // ping-pong kernel (results are identical).
+    if (const char* b = getenv("KVCK_COPY_BUFFERS")) shp->copy_buffers = b[0] == '2' ? 2 : 1;
+  }
   if (copy) pipe = true;  // the fused copy kernel always runs the pipelined structure
   if (pipe) {
     shp->pipelined = true;

@@ -28,7 +28,7 @@ __device__ __forceinline__ void store_chunk(__amdgpu_buffer_rsrc_t r, uint32_t o
     __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kNonTemporal);
 }
 
-template <int CHUNK, int S, int HU, int PU, int DIR>
+template <int CHUNK, int S, int HU, int PU, int DIR, bool PIPE>
 __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) {
   using V = typename ChunkType<CHUNK>::T;
   const BlocksArgs& a = ca.b;
@@ -138,14 +138,22 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
         cc.next(nhb, nplanes, ngr);
       };
 
-      V A[PU][HU][S], B[PU][HU][S];
-      issue(A);
-      for (int ui = 0; ui < nunits; ui += 2) {
-        if (ui + 1 < nunits) issue(B);
-        store_consume(A);
-        if (ui + 1 < nunits) {
-          if (ui + 2 < nunits) issue(A);
-          store_consume(B);
+      if constexpr (PIPE) {
+        V A[PU][HU][S], B[PU][HU][S];
+        issue(A);
+        for (int ui = 0; ui < nunits; ui += 2) {
+          if (ui + 1 < nunits) issue(B);
+          store_consume(A);
+          if (ui + 1 < nunits) {
+            if (ui + 2 < nunits) issue(A);
+            store_consume(B);
+          }
+        }
+      } else {
+        for (int ui = 0; ui < nunits; ++ui) {
+          V A[PU][HU][S];
+          issue(A);
+          store_consume(A);
         }
       }
     }
@@ -164,28 +172,29 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
 using CopyFn = void (*)(const CopyArgs);
 
 template <int CHUNK, int S, int PU, int DIR>
-constexpr CopyFn pick() {
+CopyFn pick(bool pipe) {
   constexpr int hu = 16 / (S * PU) > 0 ? 16 / (S * PU) : 1;
-  return &copy_kernel<CHUNK, S, hu, PU, DIR>;
+  return pipe ? &copy_kernel<CHUNK, S, hu, PU, DIR, true> : &copy_kernel<CHUNK, S, hu, PU, DIR, false>;
 }
 
 template <int CHUNK, int PU, int DIR>
-CopyFn copy_fn_slots(int slots) {
+CopyFn copy_fn_slots(int slots, bool pipe) {
   switch (slots) {
-    case 1: return pick<CHUNK, 1, PU, DIR>();
-    case 2: return pick<CHUNK, 2, PU, DIR>();
-    case 4: return pick<CHUNK, 4, PU, DIR>();
-    case 8: return pick<CHUNK, 8, 1, DIR>();
-    case 16: return pick<CHUNK, 16, 1, DIR>();
+    case 1: return pick<CHUNK, 1, PU, DIR>(pipe);
+    case 2: return pick<CHUNK, 2, PU, DIR>(pipe);
+    case 4: return pick<CHUNK, 4, PU, DIR>(pipe);
+    case 8: return pick<CHUNK, 8, 1, DIR>(pipe);
+    case 16: return pick<CHUNK, 16, 1, DIR>(pipe);
   }
   return nullptr;
 }
 
 template <int DIR>
 CopyFn copy_fn_dir(const BlocksShape& shp) {
+  const bool pipe = shp.copy_buffers == 2;
   if (shp.planes_per_unit == 2)
-    return shp.chunk == 16 ? copy_fn_slots<16, 2, DIR>(shp.slots) : copy_fn_slots<8, 2, DIR>(shp.slots);
-  return shp.chunk == 16 ? copy_fn_slots<16, 1, DIR>(shp.slots) : copy_fn_slots<8, 1, DIR>(shp.slots);
+    return shp.chunk == 16 ? copy_fn_slots<16, 2, DIR>(shp.slots, pipe) : copy_fn_slots<8, 2, DIR>(shp.slots, pipe);
+  return shp.chunk == 16 ? copy_fn_slots<16, 1, DIR>(shp.slots, pipe) : copy_fn_slots<8, 1, DIR>(shp.slots, pipe);
 }
 
 CopyFn copy_fn(const BlocksShape& shp, int direction) {

@@ -107,6 +107,7 @@ struct BlocksShape {
   int caches_per_task;
   int planes_per_unit;  // 1, or 2 (K and V in one unit) when heads are few
   bool merged;          // a lane-table row is a slot's adjacent heads (NHD-like pools)
+  int copy_buffers;     // fused copy: 1 = one unit buffer (more resident waves), 2 = ping-pong
 };
 
 // launchers (return hipSuccess or the first HIP error)

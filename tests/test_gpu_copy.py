@@ -56,10 +56,17 @@ def _expected_images(pools, layout, req, head_begin, head_count, bs, row_bytes):
     return img
 
 
+@pytest.fixture(params=["1", "2"])
+def copy_buffers(request, monkeypatch):
+    """Run the test with one unit buffer per wave and with two (KVCK_COPY_BUFFERS)."""
+    monkeypatch.setenv("KVCK_COPY_BUFFERS", request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_copy_save_and_load(case):
+def test_copy_save_and_load(case, copy_buffers):
     name, layout, elem, layers, nh, d, bs, lengths, start, extra, hb, hc = case
-    log(f"[copy] {name}")
+    log(f"[copy] {name} buffers={copy_buffers}")
     rng = np.random.default_rng(zlib.crc32(name.encode()))
     req, nb = wl.page_requests(rng, lengths, bs, start_pos=start, extra_blocks=extra, spare_frac=0.3)
     shape = wl.pool_shape(layout, nb, bs, nh, d)
@@ -115,7 +122,7 @@ def test_copy_staging_full_is_flagged():
     assert ei.value.flags & kvck.KVCK_FLAG_STAGING_FULL
 
 
-def test_copy_many_caches():
+def test_copy_many_caches(copy_buffers):
     """More caches than one argument block: several launches, image offsets by global cache index."""
     log("[copy] 70 caches")
     rng = np.random.default_rng(6)
