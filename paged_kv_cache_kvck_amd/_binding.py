@@ -313,11 +313,27 @@ def _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req,
     need = int(lib.kvck_blocks_workspace_bytes(n, R, max_blocks))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    if check and error_flags is None:
-        error_flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    error_flags = _flag_word(error_flags, check, dev)
     return dict(lib=lib, dev=dev, L=pc.layout, n=n, head_begin=pc.head_begin, head_count=pc.head_count, R=R,
                 max_blocks=max_blocks, out=out, workspace=workspace, error_flags=error_flags, ptrs=pc.ptrs,
                 layers=pc.layers, bases=pc.bases)
+
+
+def _flag_word(error_flags, check, dev):
+    """The kernels' error word.  With check=True it is a fresh or cleared word,
+    and the device is synchronized after clearing it, so the clear lands before
+    the call's kernels whichever stream they run on."""
+    if error_flags is not None and (error_flags.dtype not in (torch.int32, torch.uint32)
+                                    or error_flags.numel() < 1 or error_flags.device != dev):
+        raise ValueError(f"error_flags must be a 32-bit tensor on {dev}")
+    if not check:
+        return error_flags
+    if error_flags is None:
+        error_flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    else:
+        error_flags.zero_()
+    torch.cuda.synchronize(dev)
+    return error_flags
 
 
 def _finish(a, check):
@@ -452,8 +468,7 @@ def kvck_checksum_states(layer_states: Sequence[Sequence[torch.Tensor]], layer_n
     need = int(lib.kvck_states_workspace_bytes(nl, row_count, R))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    if check and error_flags is None:
-        error_flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    error_flags = _flag_word(error_flags, check, dev)
     st = lib.kvck_checksum_states(
         descs, k, ptrs, layers, bases, nl, slots, rows, int(row_begin), int(row_count), slot_ids.data_ptr(), R,
         out.data_ptr(), int(bool(accumulate)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),

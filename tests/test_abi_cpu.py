@@ -141,6 +141,11 @@ def test_binding_argument_checks():
     with pytest.raises(ValueError):
         kvck.kvck_checksum_blocks(pools, "NHD", [0], bt, torch.zeros(1, dtype=torch.int32),
                                   torch.zeros(1, dtype=torch.int64), torch.zeros(1, dtype=torch.int64))
+    # the kernels' error word is one 32-bit value
+    with pytest.raises(ValueError):
+        kvck.kvck_checksum_blocks(pools, "NHD", [0], bt.to(torch.int32), torch.zeros(1, dtype=torch.int32),
+                                  torch.zeros(1, dtype=torch.int64), torch.zeros(1, dtype=torch.int64),
+                                  error_flags=torch.zeros(1, dtype=torch.int64))
 
 
 def test_tags_rejects_before_launch():

@@ -17,7 +17,7 @@ import oracle
 import paged_kv_cache_kvck_amd as kvck
 from paged_kv_cache_kvck_amd import workloads as wl
 from gpu_helpers import (DEV, SENTINEL, assert_match, assert_unlisted_untouched, gpu_blocks, log, oracle_at,
-                         to_device_bits)
+                         req_tensors, to_device_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -190,6 +190,11 @@ def test_bad_block_id_and_bad_request_flagged():
     past.block_table[0, 1] = -1
     got = gpu_blocks([pool], "NHD", [0], past)
     assert got[0, 1] == 0
+    # a caller's flag word holding a stale bit is cleared by check=True
+    bt, nbt, sp, nt = req_tensors(req)
+    stale = torch.full((1,), kvck.KVCK_FLAG_BAD_BLOCK_ID, dtype=torch.int32, device=DEV)
+    kvck.kvck_checksum_blocks([pool], "NHD", [0], bt, nbt, sp, nt, error_flags=stale, check=True)
+    assert int(stale.item()) == 0
 
 
 def test_host_rejects_before_launch():
