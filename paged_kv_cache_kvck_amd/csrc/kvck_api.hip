@@ -70,14 +70,14 @@ kvck_status current_device(int* dev_out) {
 // Lane-table shape: the smallest S whose 64*S lane-chunks cover a whole block
 // row set of one (plane, head); larger row sets are split into groups of
 // equal size, each at most the rows one table of 16 slots holds.
-bool choose_shape(int32_t block_size, int32_t row_bytes, int chunk, BlocksShape* shp) {
+bool choose_shape(int32_t block_size, int32_t row_bytes, int chunk, int max_slots, BlocksShape* shp) {
   const int64_t cpr = row_bytes / chunk;
-  const int64_t max_chunks = (int64_t)kWave * 16;
+  const int64_t max_chunks = (int64_t)kWave * max_slots;
   if (cpr > max_chunks) return false;
   const int64_t rg_max = max_chunks / cpr;
   const int64_t groups = (block_size + rg_max - 1) / rg_max;
   const int64_t rg = (block_size + groups - 1) / groups;  // <= rg_max
-  const int64_t need = (rg * cpr + kWave - 1) / kWave;    // <= 16
+  const int64_t need = (rg * cpr + kWave - 1) / kWave;    // <= max_slots
   int s = 1;
   while (s < need) s <<= 1;
   shp->chunk = chunk;
@@ -107,16 +107,24 @@ constexpr int32_t kMergeBelowRowBytes = 128;
 // unpipelined.
 constexpr int64_t kPipeTaskBytes = 256 * 1024;
 constexpr int kPipeMaxCaches = 16;
-constexpr int64_t kPipeMinTasksPerWave = 64;
+constexpr int64_t kPipeMinTasksPerWave = 16;
 static_assert(kCachesPerLaunch % kPipeMaxCaches == 0, "launch groups must not straddle launches");
 
-void choose_schedule(BlocksShape* shp, int32_t num_caches, int64_t max_items, int64_t block_bytes, int planes,
-                     int heads, int cus, bool copy) {
+// `narrow` (or null) is the same rows split into lane tables of at most 4
+// slots, the widest the pipelined kernel double-buffers: blocks whose rows
+// need 8 or 16 slots per lane can still be pipelined, in more row groups.
+void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_caches, int64_t max_items,
+                     int64_t block_bytes, int planes, int heads, int cus, bool copy) {
   const int64_t waves = (int64_t)cus * 8;  // resident waves of the pipelined kernel (2 per SIMD)
   int lpt = 1;
   while (lpt < kPipeMaxCaches && (int64_t)(2 * lpt) * block_bytes <= kPipeTaskBytes) lpt *= 2;
   const int64_t tasks = max_items * ((num_caches + lpt - 1) / lpt);
-  bool pipe = shp->slots <= 4 && num_caches > 1 && tasks >= kPipeMinTasksPerWave * waves;
+  // A pipelined unit holds 16/S head slots (K and V can share one when heads
+  // are few); with fewer heads than that its loads would be mostly masked.
+  auto fills = [&](int slots) { return (int64_t)heads * (planes == 2 ? 2 : 1) * slots >= 16; };
+  const BlocksShape* cand = shp->slots <= 4 ? shp : narrow;
+  const bool fits = cand != nullptr && fills(cand->slots);
+  bool pipe = fits && num_caches > 1 && tasks >= kPipeMinTasksPerWave * waves;
   // KVCK_SCHEDULE=pipelined|simple overrides the choice (results are identical
   // either way); merged rows always run the unpipelined kernel
   if (const char* force = getenv("KVCK_SCHEDULE")) {
@@ -132,6 +140,10 @@ void choose_schedule(BlocksShape* shp, int32_t num_caches, int64_t max_items, in
     if (const char* b = getenv("KVCK_COPY_BUFFERS")) shp->copy_buffers = b[0] == '2' ? 2 : 1;
   }
   if (copy) pipe = true;  // the fused copy kernel always runs the pipelined structure
+  if (pipe && !copy && shp->slots > 4 && narrow && fills(narrow->slots)) {
+    shp->slots = narrow->slots;
+    shp->rows_per_group = narrow->rows_per_group;
+  }
   if (pipe) {
     shp->pipelined = true;
     shp->caches_per_task = lpt;
@@ -293,9 +305,10 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   // KVCK_MERGE_HEADS=0|1 overrides the choice where merging is possible (results are identical)
   if (const char* force = getenv("KVCK_MERGE_HEADS")) merged = can_merge && force[0] == '1';
   const int32_t lane_row_bytes = merged ? (int32_t)wide : L.row_bytes;
-  BlocksShape shp;
-  if (!choose_shape(L.block_size, lane_row_bytes, chunk, &shp)) return KVCK_ERR_UNSUPPORTED;
+  BlocksShape shp, narrow;
+  if (!choose_shape(L.block_size, lane_row_bytes, chunk, 16, &shp)) return KVCK_ERR_UNSUPPORTED;
   shp.merged = merged;
+  const bool has_narrow = !merged && choose_shape(L.block_size, lane_row_bytes, chunk, 4, &narrow);
   // lane-table offsets and piece terms are 32-bit
   if ((int64_t)shp.rows_per_group * L.slot_stride + (int64_t)(runs - 1) * L.chunk_stride +
           (merged ? lane_row_bytes : run_bytes) >=
@@ -320,8 +333,8 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   if (ds != KVCK_OK) return ds;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int cus = device_cus(dev);
-  choose_schedule(&shp, num_caches, (int64_t)num_reqs * max_blocks, image_bytes, planes_cov, head_count, cus,
-                  mode != kModeChecksum);
+  choose_schedule(&shp, has_narrow ? &narrow : nullptr, num_caches, (int64_t)num_reqs * max_blocks, image_bytes,
+                  planes_cov, head_count, cus, mode != kModeChecksum);
   const int32_t lpt = shp.caches_per_task;
   const int32_t total_groups = (num_caches + lpt - 1) / lpt;
 
@@ -347,6 +360,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   a.planes = planes_cov;
   a.planes_total = L.planes;
   a.chunks_per_run = (merged ? lane_row_bytes : run_bytes) / chunk;
+  a.run_major = runs > 1 ? 1 : 0;
   a.heads = merged ? 1 : head_count;  // a merged row is one unit-level head
   a.row_bytes = L.row_bytes;
   a.pieces = (int32_t)pieces;

@@ -46,9 +46,8 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
   uint32_t ioff[S];  // staging-side offsets of the same chunks: rows are row_bytes apart
 #pragma unroll
   for (int s = 0; s < S; ++s) {
-    const int f = lane + kWave * s;
-    const int r = f / a.chunks_per_row;
-    ioff[s] = (uint32_t)((int64_t)r * a.row_bytes + (int64_t)(f - r * a.chunks_per_row) * CHUNK);
+    const LaneChunk q = lane_chunk(lane + kWave * s, a);
+    ioff[s] = (uint32_t)((int64_t)q.r * a.row_bytes + (int64_t)(q.run * a.chunks_per_run + q.cr) * CHUNK);
   }
   const uint64_t P = (uint64_t)a.pieces;
   const int rg = a.rows_per_group;

@@ -47,6 +47,31 @@ __device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
 }
 
 
+// Lane chunk f of a row group -> row r, run of the row, chunk cr of the run.
+// Rows in one piece are walked row by row (f = r * chunks_per_row + chunk).
+// Rows stored as several runs (the x-split K layout, whose runs of all slots
+// sit together) are walked in memory order, run by run and within a run slot
+// by slot, so a load instruction still covers contiguous bytes.  Either way
+// f < rows_per_group * chunks_per_row enumerates every (row, chunk) once.
+struct LaneChunk {
+  int r, run, cr;
+};
+__device__ __forceinline__ LaneChunk lane_chunk(int f, const BlocksArgs& a) {
+  LaneChunk q;
+  if (a.run_major) {
+    q.cr = f % a.chunks_per_run;
+    const int t = f / a.chunks_per_run;
+    q.r = t % a.rows_per_group;
+    q.run = t / a.rows_per_group;
+  } else {
+    q.r = f / a.chunks_per_row;
+    const int c = f - q.r * a.chunks_per_row;
+    q.run = c / a.chunks_per_run;
+    q.cr = c - q.run * a.chunks_per_run;
+  }
+  return q;
+}
+
 template <int S>
 struct LaneTable {
   int row[S];
@@ -57,24 +82,21 @@ struct LaneTable {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
       const int f = lane + kWave * s;
-      const int r = f / a.chunks_per_row;
-      const int c = f - r * a.chunks_per_row;
-      row[s] = r < a.rows_per_group ? r : 0x7fffffff;
-      const int run = c / a.chunks_per_run;
-      off[s] = (uint32_t)((int64_t)r * a.slot_stride + (int64_t)run * a.chunk_stride +
-                          (int64_t)(c - run * a.chunks_per_run) * CHUNK);
+      const LaneChunk q = lane_chunk(f, a);
+      const int c = q.run * a.chunks_per_run + q.cr;  // chunk of the row
+      row[s] = f < a.rows_per_group * a.chunks_per_row ? q.r : 0x7fffffff;
+      off[s] = (uint32_t)((int64_t)q.r * a.slot_stride + (int64_t)q.run * a.chunk_stride + (int64_t)q.cr * CHUNK);
       // a merged row holds several heads' rows back to back: pieces count from its head's row
       const int cin = c - (c / a.chunks_per_head) * a.chunks_per_head;
-      urel[s] = (uint32_t)(2u * (uint32_t)r * (uint32_t)a.pieces + (uint32_t)(CHUNK / 4) * (uint32_t)cin);
+      urel[s] = (uint32_t)(2u * (uint32_t)q.r * (uint32_t)a.pieces + (uint32_t)(CHUNK / 4) * (uint32_t)cin);
     }
   }
   // Local head of each chunk in a merged row (0 when rows are single heads).
   __device__ __forceinline__ void heads(int lane, const BlocksArgs& a, uint32_t (&h)[S]) const {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-      const int f = lane + kWave * s;
-      const int c = f - (f / a.chunks_per_row) * a.chunks_per_row;
-      h[s] = (uint32_t)(c / a.chunks_per_head);
+      const LaneChunk q = lane_chunk(lane + kWave * s, a);
+      h[s] = (uint32_t)((q.run * a.chunks_per_run + q.cr) / a.chunks_per_head);
     }
   }
 };

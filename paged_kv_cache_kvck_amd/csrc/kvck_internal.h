@@ -59,6 +59,7 @@ struct BlocksArgs {
   int32_t chunks_per_row;
   int32_t chunks_per_head;                   // chunks of one head's row (< chunks_per_row: merged heads)
   int32_t chunks_per_run;                    // lane chunks in one contiguous run of a row
+  int32_t run_major;                         // rows stored as several runs: lanes walk [run][row]
   int32_t num_caches;                        // caches in this launch
   int32_t caches_per_task;                   // caches one task covers (a partial's group)
   int32_t group_offset;                      // partial row of this launch's first group
