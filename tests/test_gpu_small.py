@@ -376,3 +376,47 @@ def test_row_groups_fit_one_lane_table(layout, elem, nh, d, schedule, monkeypatc
                                   req.num_tokens)
     for r, k in req.listed():
         assert int(got[r, k]) == int(want[r, k]), (r, k)
+
+
+def test_calls_from_several_host_threads():
+    """The library is thread-safe: host threads, each with its own stream,
+    workspace and output, calling at once on two layouts all get the
+    single-thread result."""
+    import threading
+    log("[threads]")
+    rng = np.random.default_rng(16)
+    req, nb = wl.page_requests(rng, list(rng.integers(1, 400, 24)), 16, spare_frac=0.1)
+    layouts = {"HND": [to_device_bits(wl.host_random_bits(rng, wl.pool_shape("HND", nb, 16, 8, 128), "bf16"))
+                       for _ in range(6)],
+               "NHD": [to_device_bits(wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 16, 12, 64), "fp8"))
+                       for _ in range(6)]}
+    want = {k: gpu_blocks(p, k, list(range(6)), req) for k, p in layouts.items()}
+    bt, nbt, sp, nt = req_tensors(req)
+    errors, results = [], {}
+
+    def worker(i):
+        try:
+            layout = "HND" if i % 2 == 0 else "NHD"
+            s = torch.cuda.Stream()
+            ws = torch.empty(kvck.kvck_blocks_workspace_bytes(6, req.num_reqs, req.max_blocks), dtype=torch.uint8,
+                             device=DEV)
+            out = torch.zeros((req.num_reqs, req.max_blocks), dtype=torch.uint64, device=DEV)
+            with torch.cuda.stream(s):
+                for _ in range(5):
+                    kvck.kvck_checksum_blocks(layouts[layout], layout, list(range(6)), bt, nbt, sp, nt, out=out,
+                                              workspace=ws, stream=s)
+            s.synchronize()
+            results[i] = (layout, out.cpu().numpy().view(np.uint64))
+        except Exception as e:  # reported below
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(6)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    assert len(results) == 6
+    for i, (layout, got) in results.items():
+        for r, k in req.listed():
+            assert got[r, k] == want[layout][r, k], (i, r, k)
