@@ -113,7 +113,14 @@ typedef struct kvck_kv_layout {
    * apart -- e.g. the x-split K layout [num_blocks, num_heads, head_size/x,
    * block_size, x] (page "[vLLM 源码解析] KV Cache", the reshape_and_cache
    * section): chunk_bytes = x*element bytes, chunk_stride = block_size*x*
-   * element bytes, slot_stride = x*element bytes.  0: the row is contiguous. */
+   * element bytes, slot_stride = x*element bytes.  0: the row is contiguous.
+   * chunk_bytes of 1, 2 or 4 (one element per run) describes an
+   * element-transposed plane [num_blocks, num_heads, head_size, block_size]
+   * (the V layout of ROCm's paged-attention kernels): chunk_stride =
+   * block_size*element bytes, slot_stride = chunk_bytes.  Such calls cover one
+   * plane (plane_count 1), need block_size*element bytes to be a multiple of
+   * 8, and are not accepted by kvck_copy_checksum_blocks
+   * (KVCK_ERR_UNSUPPORTED otherwise). */
   int32_t chunk_bytes;
   int32_t reserved0;
   int64_t chunk_stride;

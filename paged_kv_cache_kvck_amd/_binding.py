@@ -172,7 +172,10 @@ def _stream_handle(stream, device) -> int | None:
 #   K_NHD / V_NHD   (num_blocks, block_size, num_heads, head_size)   one plane of a K/V slice
 #   K_HND / V_HND   (num_blocks, num_heads, block_size, head_size)
 #   K_XSPLIT (num_blocks, num_heads, head_size/x, block_size, x)  x-split K plane
-LAYOUT_NAMES = ("NHD", "HND", "FI_NHD", "FI_HND", "MLA", "K_NHD", "V_NHD", "K_HND", "V_HND", "K_XSPLIT")
+#   K_TRANS / V_TRANS (num_blocks, num_heads, head_size, block_size)  element-transposed plane
+#            (V_TRANS with K_XSPLIT is the K/V cache of ROCm's paged-attention kernels)
+LAYOUT_NAMES = ("NHD", "HND", "FI_NHD", "FI_HND", "MLA", "K_NHD", "V_NHD", "K_HND", "V_HND", "K_XSPLIT",
+                "K_TRANS", "V_TRANS")
 
 
 def kv_layout(cache: torch.Tensor, layout: str) -> kvck_kv_layout:
@@ -229,6 +232,13 @@ def kv_layout(cache: torch.Tensor, layout: str) -> kvck_kv_layout:
         L.block_stride, L.head_stride, L.chunk_stride, L.slot_stride = st[0], st[1], st[2], st[3]
         L.chunk_bytes = sh[4] * es
         L.row_bytes = sh[2] * sh[4] * es
+    elif layout in ("K_TRANS", "V_TRANS"):
+        need(4, "(num_blocks, num_heads, head_size, block_size)")
+        L.planes, L.plane_begin, L.plane_count = 2, (0 if layout[0] == "K" else 1), 1
+        L.num_blocks, L.num_heads, L.block_size = sh[0], sh[1], sh[3]
+        L.block_stride, L.head_stride, L.chunk_stride, L.slot_stride = st[0], st[1], st[2], st[3]
+        L.chunk_bytes = es                    # a row is head_size one-element runs
+        L.row_bytes = sh[2] * es
     else:
         raise ValueError(f"unknown layout {layout!r}; one of {LAYOUT_NAMES}")
     return L

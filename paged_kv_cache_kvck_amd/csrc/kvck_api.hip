@@ -88,6 +88,8 @@ bool choose_shape(int32_t block_size, int32_t row_bytes, int chunk, int max_slot
   shp->planes_per_unit = 1;
   shp->merged = false;
   shp->copy_buffers = 1;
+  shp->transposed = false;
+  shp->elem_bytes = 0;
   return true;
 }
 
@@ -132,6 +134,7 @@ void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_ca
     if (strcmp(force, "simple") == 0) pipe = false;
   }
   if (shp->merged && !copy) pipe = false;
+  if (shp->transposed && shp->slots > 4) pipe = false;  // pipelined variants stop at 4 slots
   if (copy) {
     // One unit buffer per wave: twice the resident waves of the ping-pong
     // kernel, which keeps more stores in flight (same-box A/B: load 5.6 ->
@@ -262,10 +265,23 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   if (L.chunk_bytes < 0 || L.chunk_stride < 0 || L.plane_begin < 0 || L.plane_count < 0)
     return KVCK_ERR_INVALID_ARGUMENT;
   const int32_t run_bytes = L.chunk_bytes == 0 ? L.row_bytes : L.chunk_bytes;
-  if (run_bytes % 8 != 0 || L.row_bytes % run_bytes != 0) return KVCK_ERR_UNSUPPORTED;
+  // runs shorter than a piece: rows stored element by element (element-transposed
+  // planes); the elements of all slots of one index must sit side by side
+  const bool transposed = run_bytes < 8;
+  if (transposed) {
+    if ((run_bytes != 1 && run_bytes != 2 && run_bytes != 4) || L.slot_stride != run_bytes)
+      return KVCK_ERR_UNSUPPORTED;
+    if (mode != kModeChecksum) return KVCK_ERR_UNSUPPORTED;  // the fused copy takes rows of whole pieces
+    if (L.chunk_stride < (int64_t)L.block_size * run_bytes) return KVCK_ERR_INVALID_ARGUMENT;
+    // an element row of the block must hold whole 8-byte loads
+    if (((int64_t)L.block_size * run_bytes) % 8 != 0) return KVCK_ERR_UNSUPPORTED;
+  } else if (run_bytes % 8 != 0 || L.row_bytes % run_bytes != 0) {
+    return KVCK_ERR_UNSUPPORTED;
+  }
   const int32_t runs = L.row_bytes / run_bytes;
   const int32_t planes_cov = L.plane_count == 0 ? L.planes - L.plane_begin : L.plane_count;
   if (planes_cov < 1 || (int64_t)L.plane_begin + planes_cov > L.planes) return KVCK_ERR_INVALID_ARGUMENT;
+  if (transposed && planes_cov != 1) return KVCK_ERR_UNSUPPORTED;  // one plane per call
   // every byte the kernels may address lies within a 2^50-byte extent
   if (!extent_ok({{L.planes, L.plane_stride}, {L.num_blocks, L.block_stride}, {L.block_size, L.slot_stride},
                   {L.num_heads, L.head_stride}, {runs, L.chunk_stride}},
@@ -288,8 +304,10 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   // ---- alignment: 16-byte lane loads when everything allows, else 8-byte
   int chunk = 16;
   for (int pass = 0; pass < 2; ++pass) {
-    bool ok = run_bytes % chunk == 0 && L.block_stride % chunk == 0 &&
-              (planes_cov == 1 || L.plane_stride % chunk == 0) && (L.block_size == 1 || L.slot_stride % chunk == 0) &&
+    // transposed rows: a chunk holds one element index of chunk/run_bytes slots
+    const bool rows_ok = transposed ? ((int64_t)L.block_size * run_bytes) % chunk == 0
+                                    : run_bytes % chunk == 0 && (L.block_size == 1 || L.slot_stride % chunk == 0);
+    bool ok = rows_ok && L.block_stride % chunk == 0 && (planes_cov == 1 || L.plane_stride % chunk == 0) &&
               (L.num_heads == 1 || L.head_stride % chunk == 0) && (runs == 1 || L.chunk_stride % chunk == 0);
     for (int32_t i = 0; ok && i < num_caches; ++i) ok = aligned(cache_ptrs[i], chunk);
     if (mode != kModeChecksum) ok = ok && aligned(staging, chunk);
@@ -306,9 +324,35 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   if (const char* force = getenv("KVCK_MERGE_HEADS")) merged = can_merge && force[0] == '1';
   const int32_t lane_row_bytes = merged ? (int32_t)wide : L.row_bytes;
   BlocksShape shp, narrow;
-  if (!choose_shape(L.block_size, lane_row_bytes, chunk, 16, &shp)) return KVCK_ERR_UNSUPPORTED;
+  if (transposed) {
+    // lane table over element rows of one (block, head): chunk f is element row
+    // f / cpe, slots (f mod cpe) * chunk/run_bytes onward; rows split into groups
+    // of at most what 16 slots per lane hold
+    const int64_t cpe = (int64_t)L.block_size * run_bytes / chunk;
+    const int64_t max_chunks = (int64_t)kWave * 16;
+    if (cpe > max_chunks) return KVCK_ERR_UNSUPPORTED;
+    const int64_t D = L.row_bytes / run_bytes;
+    const int64_t rge_max = max_chunks / cpe;
+    const int64_t groups = (D + rge_max - 1) / rge_max;
+    const int64_t rge = (D + groups - 1) / groups;
+    const int64_t need = (rge * cpe + kWave - 1) / kWave;
+    int s = 1;
+    while (s < need) s <<= 1;
+    if (rge * L.chunk_stride + (int64_t)L.block_size * run_bytes >= ((int64_t)1 << 31)) return KVCK_ERR_UNSUPPORTED;
+    memset(&shp, 0, sizeof(shp));
+    shp.chunk = chunk;
+    shp.slots = s;
+    shp.rows_per_group = (int)rge;
+    shp.caches_per_task = 1;
+    shp.planes_per_unit = 1;
+    shp.copy_buffers = 1;
+    shp.transposed = true;
+    shp.elem_bytes = run_bytes;
+  } else if (!choose_shape(L.block_size, lane_row_bytes, chunk, 16, &shp)) {
+    return KVCK_ERR_UNSUPPORTED;
+  }
   shp.merged = merged;
-  const bool has_narrow = !merged && choose_shape(L.block_size, lane_row_bytes, chunk, 4, &narrow);
+  const bool has_narrow = !merged && !transposed && choose_shape(L.block_size, lane_row_bytes, chunk, 4, &narrow);
   // lane-table offsets and piece terms are 32-bit
   if ((int64_t)shp.rows_per_group * L.slot_stride + (int64_t)(runs - 1) * L.chunk_stride +
           (merged ? lane_row_bytes : run_bytes) >=
@@ -365,7 +409,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   a.row_bytes = L.row_bytes;
   a.pieces = (int32_t)pieces;
   a.rows_per_group = shp.rows_per_group;
-  a.chunks_per_row = lane_row_bytes / chunk;
+  a.chunks_per_row = transposed ? (int32_t)((int64_t)L.block_size * run_bytes / chunk) : lane_row_bytes / chunk;
   a.chunks_per_head = L.row_bytes / chunk;
   a.caches_per_task = lpt;
   a.direct = total_groups == 1;
@@ -381,7 +425,10 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
       a.base[i] = static_cast<const uint8_t*>(cache_ptrs[c0 + i]) + (int64_t)head_begin * L.head_stride;
       a.mbase[i] = (uint32_t)(2 * ((int64_t)layer_numbers[c0 + i] * kH + global_head_base[c0 + i]) + 1);
     }
-    if (mode == kModeChecksum) {
+    if (mode == kModeChecksum && transposed) {
+      const int grid = tblocks_grid(shp, dev, max_items * ((n + lpt - 1) / lpt));
+      if (launch_tblocks(a, shp, grid, st) != hipSuccess) return KVCK_ERR_HIP;
+    } else if (mode == kModeChecksum) {
       const int grid = blocks_grid(shp, dev, max_items * ((n + lpt - 1) / lpt));
       if (launch_blocks(a, shp, grid, st) != hipSuccess) return KVCK_ERR_HIP;
     } else {

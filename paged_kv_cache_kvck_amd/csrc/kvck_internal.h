@@ -109,6 +109,8 @@ struct BlocksShape {
   int planes_per_unit;  // 1, or 2 (K and V in one unit) when heads are few
   bool merged;          // a lane-table row is a slot's adjacent heads (NHD-like pools)
   int copy_buffers;     // fused copy: 1 = one unit buffer (more resident waves), 2 = ping-pong
+  bool transposed;      // rows stored element by element (elements of a row elem_stride apart)
+  int elem_bytes;       // element size of transposed rows (1, 2 or 4)
 };
 
 // launchers (return hipSuccess or the first HIP error)
@@ -122,6 +124,8 @@ hipError_t launch_reduce(const uint64_t* partials, int64_t stride, int32_t split
                          int64_t n_fixed, const PosRecord* recs, uint64_t* out, int32_t accumulate,
                          hipStream_t stream);
 hipError_t launch_states(const StatesArgs& a, int grid, hipStream_t stream);
+hipError_t launch_tblocks(const BlocksArgs& a, const BlocksShape& shp, int grid, hipStream_t stream);
+int tblocks_grid(const BlocksShape& shp, int device, int64_t max_tasks);
 hipError_t launch_copy(const CopyArgs& a, const BlocksShape& shp, int direction, int grid, hipStream_t stream);
 int copy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks);
 hipError_t launch_tags(const uint64_t* checksums, const uint8_t* hashes, int64_t hash_stride, uint64_t fingerprint,

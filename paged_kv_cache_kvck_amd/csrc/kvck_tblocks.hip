@@ -1,0 +1,267 @@
+// Block checksums of K/V planes stored element-transposed, on gfx950: element
+// d of slot i's row sits at d * elem_stride + i * ES, so one element index of
+// all the block's slots is contiguous (the V layout
+// [num_blocks, num_heads, head_size, block_size] of ROCm's paged-attention
+// kernels).  The checksum is the one of the vLLM API page
+// "vllm.distributed.kv_transfer.kv_checksum.checksum"; a token's row is still
+// its head_size elements in order, read as little-endian 8-byte pieces.
+//
+// No element gather is needed: a piece is the little-endian packing of
+// PER_PIECE = 8/ES consecutive elements, so for element d of token t
+//   x_q (2j + 1) = sum over its elements e_d * 2^(8 ES (d mod PER_PIECE)) * u,
+//   u = 2 (t P + pb + d / PER_PIECE) + 1      (pb: first piece of the plane),
+// and a 16-byte chunk holds element d of N = 16/ES consecutive slots t0+k, whose
+// terms sum to ((u0 E + 2 P K) << 8 ES (d mod PER_PIECE)) with
+// E = sum_k e_k, K = sum_k k e_k over the valid slots and u0 the u of slot t0.
+//
+// Task = (group of caches, listed position), one wavefront each, as in the
+// main pass; a unit is HU heads x S chunks per lane of one element-row group,
+// with the same out-of-range buffer offsets masking unused lanes and heads.
+// PIPE: two unit buffers in ping-pong, as in the main pass's pipelined kernel.
+#include "kvck_device.h"
+
+namespace kvck {
+namespace {
+
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// E and K of one chunk: sums of its elements and of k * element over the first
+// `valid` of its N = CHUNK/ES slots (elements read unsigned).  Each word is
+// masked to its valid elements, then 2-byte elements go through the packed
+// u16 dot product and 1-byte elements through the u8 one (E with weights 1,
+// K with weights k); sums stay below 2^32 (at most 16 elements of 16 bits).
+template <int ES, typename V>
+__device__ __forceinline__ void chunk_sums(const V& x, int valid, uint64_t& E, uint64_t& K) {
+  constexpr int WORDS = sizeof(V) / 4;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(&x);
+  if constexpr (ES == 4) {
+    uint64_t e = 0, k = 0;
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) {
+      const uint64_t v = i < valid ? (uint64_t)w[i] : 0ull;
+      e += v;
+      k += (uint64_t)i * v;
+    }
+    E = e;
+    K = k;
+  } else if constexpr (ES == 2) {
+    uint32_t e = 0, k = 0;
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) {
+      const int m = valid - 2 * i;  // valid elements of this word, clamped below
+      const uint32_t mask = m >= 2 ? 0xffffffffu : (m == 1 ? 0x0000ffffu : 0u);
+      const u16x2 v = __builtin_bit_cast(u16x2, w[i] & mask);
+      e = __builtin_amdgcn_udot2(v, u16x2{1, 1}, e, false);
+      k = __builtin_amdgcn_udot2(v, u16x2{(uint16_t)(2 * i), (uint16_t)(2 * i + 1)}, k, false);
+    }
+    E = e;
+    K = k;
+  } else {
+    uint32_t e = 0, k = 0;
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) {
+      const int m = valid - 4 * i;
+      const uint32_t mask = m >= 4 ? 0xffffffffu : (m <= 0 ? 0u : (1u << (8 * m)) - 1u);
+      const uint32_t v = w[i] & mask;
+      const uint32_t kw = (uint32_t)(4 * i) | ((uint32_t)(4 * i + 1) << 8) | ((uint32_t)(4 * i + 2) << 16) |
+                          ((uint32_t)(4 * i + 3) << 24);
+      e = __builtin_amdgcn_udot4(v, 0x01010101u, e, false);
+      k = __builtin_amdgcn_udot4(v, kw, k, false);
+    }
+    E = e;
+    K = k;
+  }
+}
+
+template <int CHUNK, int ES, int S, int HU, bool PIPE>
+__global__ __launch_bounds__(kBlockThreads) void tblocks_kernel(const BlocksArgs a) {
+  using V = typename ChunkType<CHUNK>::T;
+  constexpr int N = CHUNK / ES;        // slots per chunk
+  constexpr int PER_PIECE = 8 / ES;    // elements per 8-byte piece
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  const int64_t n_items = (int64_t)*a.n_items;
+  const int lpt = a.caches_per_task;
+  const int ngroups = (a.num_caches + lpt - 1) / lpt;
+  const int64_t total = n_items * ngroups;
+  if (wave >= total) return;
+
+  // lane table of one element-row group of a (block, head): chunk f = lane + 64 s
+  // holds element row f / cpe of the group, slots (f mod cpe) * N onward
+  const int cpe = a.chunks_per_row;
+  const int rge = a.rows_per_group;
+  int erow[S];
+  uint32_t off[S], slot0[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int f = lane + kWave * s;
+    const int r = f / cpe;
+    const int q = f - r * cpe;
+    erow[s] = f < rge * cpe ? r : 0x7fffffff;
+    off[s] = (uint32_t)((int64_t)r * a.chunk_stride + (int64_t)q * CHUNK);
+    slot0[s] = (uint32_t)(q * N);
+  }
+  const int D = a.row_bytes / ES;                 // elements per row
+  const int ngr = (D + rge - 1) / rge;            // element-row groups
+  const uint64_t P = (uint64_t)a.pieces;
+  const int nhb = (a.heads + HU - 1) / HU;
+
+  for (int64_t task = wave; task < total; task += nwaves) {
+    const int64_t grp = task / n_items;
+    const int64_t item = task - grp * n_items;
+    const int c_begin = (int)grp * lpt;
+    const int c_end = min(a.num_caches, c_begin + lpt);
+    const PosRecord* rp = a.recs + item;
+    const int32_t v = __builtin_amdgcn_readfirstlane(rp->valid);
+    const int32_t blk = __builtin_amdgcn_readfirstlane(rp->block);
+    const uint64_t t0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(rp->t0 >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)rp->t0);
+    const int64_t out_idx = rp->out_idx;
+    uint64_t acc = 0;
+    if (v > 0) {
+      const int64_t blk_off = (int64_t)blk * a.block_stride;
+      // valid slots of each lane chunk, and the chunk's u without the element's piece
+      int nvalid[S];
+      uint64_t ubase[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int left = v - (int)slot0[s];
+        nvalid[s] = left < 0 ? 0 : (left > N ? N : left);
+        ubase[s] = 2ull * (t0 + slot0[s]) * P + 1ull + a.piece_base;
+      }
+      // units: (cache, element-row group, head batch), cache-major
+      struct Cursor {
+        int cache, group, hbatch;
+        __device__ __forceinline__ void next(int nhb_, int ngr_) {
+          if (++hbatch == nhb_) {
+            hbatch = 0;
+            if (++group == ngr_) {
+              group = 0;
+              ++cache;
+            }
+          }
+        }
+      };
+      const int nunits = (c_end - c_begin) * ngr * nhb;
+      Cursor ic{c_begin, 0, 0}, cc{c_begin, 0, 0};
+      auto issue = [&](V(&x)[HU][S]) {
+        const int rows = min(rge, D - ic.group * rge);
+        const uint8_t* gbase = a.base[ic.cache] + blk_off + (int64_t)(ic.group * rge) * a.chunk_stride;
+#pragma unroll
+        for (int h = 0; h < HU; ++h) {
+          const int hh = ic.hbatch * HU + h;
+          const uint32_t hmask = hh < a.heads ? 0u : kOOB;
+          const __amdgpu_buffer_rsrc_t rs = make_rsrc(gbase + (int64_t)hh * a.head_stride);
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+            x[h][s] = load_chunk<CHUNK>(rs, (erow[s] < rows && nvalid[s] > 0 ? off[s] : kOOB) | hmask);
+        }
+        ic.next(nhb, ngr);
+      };
+      auto consume = [&](const V(&x)[HU][S]) {
+        const uint32_t mb = a.mbase[cc.cache];
+#pragma unroll
+        for (int h = 0; h < HU; ++h) {
+          uint64_t sh = 0;
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            // element index; masked lanes read zeros, so any d is harmless there
+            const uint32_t d = (uint32_t)(cc.group * rge) + (uint32_t)erow[s];
+            uint64_t E, K;
+            chunk_sums<ES>(x[h][s], nvalid[s], E, K);
+            const uint64_t u0 = ubase[s] + 2ull * (d / PER_PIECE);
+            sh += (u0 * E + 2ull * P * K) << (8 * ES * (d % PER_PIECE));
+          }
+          acc += sh * (uint64_t)(mb + 2u * (uint32_t)(cc.hbatch * HU + h));
+        }
+        cc.next(nhb, ngr);
+      };
+      if constexpr (PIPE) {
+        V A[HU][S], B[HU][S];
+        issue(A);
+        for (int ui = 0; ui < nunits; ui += 2) {
+          if (ui + 1 < nunits) issue(B);
+          consume(A);
+          if (ui + 1 < nunits) {
+            if (ui + 2 < nunits) issue(A);
+            consume(B);
+          }
+        }
+      } else {
+        for (int ui = 0; ui < nunits; ++ui) {
+          V A[HU][S];
+          issue(A);
+          consume(A);
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      if (a.direct) {
+        uint64_t* o = a.out + out_idx;
+        *o = a.accumulate ? *o + acc : acc;
+      } else {
+        a.partials[(int64_t)(a.group_offset + grp) * a.max_items + item] = acc;
+      }
+    }
+  }
+}
+
+using TFn = void (*)(const BlocksArgs);
+
+template <int CHUNK, int ES, int S, bool PIPE>
+constexpr TFn tpick() {
+  return &tblocks_kernel<CHUNK, ES, S, (16 / S > 0 ? 16 / S : 1), PIPE>;
+}
+
+// The pipelined kernel double-buffers lane tables of at most 4 slots.
+template <int CHUNK, int ES>
+TFn tfn_slots(int slots, bool pipe) {
+  switch (slots) {
+    case 1: return pipe ? tpick<CHUNK, ES, 1, true>() : tpick<CHUNK, ES, 1, false>();
+    case 2: return pipe ? tpick<CHUNK, ES, 2, true>() : tpick<CHUNK, ES, 2, false>();
+    case 4: return pipe ? tpick<CHUNK, ES, 4, true>() : tpick<CHUNK, ES, 4, false>();
+    case 8: return pipe ? nullptr : tpick<CHUNK, ES, 8, false>();
+    case 16: return pipe ? nullptr : tpick<CHUNK, ES, 16, false>();
+  }
+  return nullptr;
+}
+
+TFn tfn(const BlocksShape& shp) {
+  const bool pipe = shp.pipelined;
+  if (shp.chunk == 16) {
+    switch (shp.elem_bytes) {
+      case 1: return tfn_slots<16, 1>(shp.slots, pipe);
+      case 2: return tfn_slots<16, 2>(shp.slots, pipe);
+      case 4: return tfn_slots<16, 4>(shp.slots, pipe);
+    }
+  } else {
+    switch (shp.elem_bytes) {
+      case 1: return tfn_slots<8, 1>(shp.slots, pipe);
+      case 2: return tfn_slots<8, 2>(shp.slots, pipe);
+      case 4: return tfn_slots<8, 4>(shp.slots, pipe);
+    }
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+int tblocks_grid(const BlocksShape& shp, int device, int64_t max_tasks) {
+  TFn fn = tfn(shp);
+  const int per_cu = fn ? kernel_occupancy(reinterpret_cast<const void*>(fn), device, 2) : 1;
+  const int64_t waves_per_block = kBlockThreads / kWave;
+  const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
+  const int64_t cap = (int64_t)per_cu * device_cus(device);
+  return (int)(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
+hipError_t launch_tblocks(const BlocksArgs& a, const BlocksShape& shp, int grid, hipStream_t stream) {
+  TFn fn = tfn(shp);
+  if (!fn) return hipErrorInvalidValue;
+  void* args[] = {const_cast<BlocksArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(kBlockThreads), args, 0, stream);
+}
+
+}  // namespace kvck

@@ -134,6 +134,18 @@ void blocks_checks(bool have_device) {
   EXPECT_EQ(call([](BlocksCall& c) { c.L.chunk_bytes = 16, c.L.chunk_stride = kI64Max / 32 * 16; }),
             KVCK_ERR_UNSUPPORTED);
   EXPECT_EQ(call([](BlocksCall& c) { c.L.chunk_bytes = 24; }), KVCK_ERR_UNSUPPORTED);  // 256 % 24 != 0
+  // element-transposed planes (one-element runs): one plane per call, slots side by side
+  auto trans = [](BlocksCall& c) {
+    c.L.chunk_bytes = 2, c.L.chunk_stride = 16 * 2, c.L.slot_stride = 2, c.L.plane_begin = 1, c.L.plane_count = 1;
+    c.L.head_stride = 128 * 16 * 2, c.L.block_stride = 8 * 128 * 16 * 2;
+  };
+  if (!have_device) EXPECT_EQ(call([&](BlocksCall& c) { trans(c); }), KVCK_ERR_NO_DEVICE);
+  EXPECT_EQ(call([&](BlocksCall& c) { trans(c), c.L.chunk_stride = 16; }), KVCK_ERR_INVALID_ARGUMENT);
+  EXPECT_EQ(call([&](BlocksCall& c) { trans(c), c.L.slot_stride = 4; }), KVCK_ERR_UNSUPPORTED);
+  EXPECT_EQ(call([&](BlocksCall& c) { trans(c), c.L.plane_begin = 0, c.L.plane_count = 0; }), KVCK_ERR_UNSUPPORTED);
+  EXPECT_EQ(call([&](BlocksCall& c) { trans(c), c.L.block_size = 2, c.L.chunk_stride = 4; }), KVCK_ERR_UNSUPPORTED);
+  EXPECT_EQ(call([&](BlocksCall& c) { trans(c), c.L.chunk_bytes = 3; }), KVCK_ERR_UNSUPPORTED);
+  EXPECT_EQ(call([&](BlocksCall& c) { trans(c), c.direction = KVCK_COPY_SAVE; }), KVCK_ERR_UNSUPPORTED);
   // batch sizes
   EXPECT_EQ(call([](BlocksCall& c) { c.num_reqs = kI32Max, c.max_blocks = kI32Max, c.bt_stride = kI32Max; }),
             KVCK_ERR_UNSUPPORTED);

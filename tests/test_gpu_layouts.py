@@ -145,3 +145,70 @@ def test_copy_with_separate_k_and_x_split():
         for c in range(len(layers)):
             k_rows = hp[c][0, b].view(np.uint8).reshape(8, 16, 256)      # [head][slot][row bytes]
             assert np.array_equal(img[e, c, 0, :, :v], k_rows[:, :v])
+
+
+TRANS_CASES = [
+    # name, elem, heads, head_size, block_size, head_begin, head_count
+    ("bf16_d128_bs16", "bf16", 8, 128, 16, 0, None),
+    ("fp16_d64_bs32_heads", "fp16", 4, 64, 32, 1, 2),
+    ("fp8_d128_bs16", "fp8", 4, 128, 16, 0, None),
+    ("fp32_d32_bs8", "fp32", 2, 32, 8, 0, None),
+    ("bf16_d72_bs64", "bf16", 2, 72, 64, 0, None),
+    ("bf16_d128_bs4", "bf16", 3, 128, 4, 0, None),       # 8-byte chunks
+]
+
+
+@pytest.mark.parametrize("case", TRANS_CASES, ids=[c[0] for c in TRANS_CASES])
+def test_element_transposed_planes(case):
+    """Planes stored [num_blocks, num_heads, head_size, block_size] (one
+    element index of every slot together): K_TRANS + V_TRANS equals the
+    oracle on the HND pool holding the same tokens, and so does the pair of
+    ROCm's paged-attention cache, x-split K + transposed V."""
+    name, elem, nh, d, bs, hb, hc = case
+    log(f"[layouts] transposed {name}")
+    rng = np.random.default_rng(zlib.crc32(f"trans{name}".encode()))
+    req, nb = wl.page_requests(rng, [3 * bs + 5, bs, 7, 2 * bs], bs, start_pos=[0, 1, 0, 0],
+                               extra_blocks=[0, 0, 1, 0], spare_frac=0.3)
+    layers = [0, 3, 11]
+    hp = [wl.host_random_bits(rng, wl.pool_shape("HND", nb, bs, nh, d), elem) for _ in layers]
+    n = nh - hb if hc is None else hc
+    bases = [hb + 5 * i for i in range(len(layers))]
+    want = _oracle(hp, "HND", layers, req, bases=bases, hb=hb, hc=n)
+    kt = [to_device_bits(np.ascontiguousarray(p[0].transpose(0, 1, 3, 2))) for p in hp]
+    vt = [to_device_bits(np.ascontiguousarray(p[1].transpose(0, 1, 3, 2))) for p in hp]
+    kw = dict(global_head_base=bases, head_begin=hb, head_count=hc)
+    out = _call(kt, "K_TRANS", layers, req, **kw)
+    out = _call(vt, "V_TRANS", layers, req, out=out, accumulate=True, **kw).cpu().numpy()
+    for r, k in req.listed():
+        assert int(out[r, k]) == int(want[r, k]), (r, k)
+    es = wl.ELEM_BYTES[elem]
+    x = 16 // es
+    if d % x == 0:
+        kx = [to_device_bits(np.ascontiguousarray(p[0].reshape(nb, nh, bs, d // x, x).transpose(0, 1, 3, 2, 4)))
+              for p in hp]
+        out = _call(kx, "K_XSPLIT", layers, req, **kw)
+        out = _call(vt, "V_TRANS", layers, req, out=out, accumulate=True, **kw).cpu().numpy()
+        for r, k in req.listed():
+            assert int(out[r, k]) == int(want[r, k]), (r, k)
+
+
+def test_element_transposed_limits():
+    """What the element-transposed path rejects before any launch: a fused
+    copy, and blocks whose element rows are shorter than one 8-byte load."""
+    log("[layouts] transposed limits")
+    rng = np.random.default_rng(77)
+    req, nb = wl.page_requests(rng, [20], 2, spare_frac=0.5)
+    hp = wl.host_random_bits(rng, wl.pool_shape("HND", nb, 2, 2, 64), "bf16")
+    vt = [to_device_bits(np.ascontiguousarray(hp[1].transpose(0, 1, 3, 2)))]
+    with pytest.raises(kvck.KvckError) as ei:
+        _call(vt, "V_TRANS", [0], req)                  # 2 slots x 2 bytes: no 8-byte load fits
+    assert ei.value.status == -2
+    req, nb = wl.page_requests(rng, [40], 16, spare_frac=0.5)
+    hp = wl.host_random_bits(rng, wl.pool_shape("HND", nb, 16, 2, 64), "bf16")
+    vt = [to_device_bits(np.ascontiguousarray(hp[1].transpose(0, 1, 3, 2)))]
+    bt, nbt, sp, nt = req_tensors(req)
+    staging = torch.zeros(int(req.num_blocks.sum()) * kvck.kvck_staging_bytes(vt[0], "V_TRANS", 1), dtype=torch.uint8,
+                          device=DEV)
+    with pytest.raises(kvck.KvckError) as ei:
+        kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, vt, "V_TRANS", [0], bt, nbt, sp, nt, staging)
+    assert ei.value.status == -2
