@@ -104,9 +104,9 @@ constexpr int32_t kMergeBelowRowBytes = 128;
 // costs about one memory latency plus the reduction).  A task covers enough
 // caches to stream about kPipeTaskBytes of a full block, capped at
 // kPipeMaxCaches.  Small batches keep one cache per task and higher occupancy
-// (their run time is dominated by ramp-up and tail).  Wide lane tables (S > 4)
-// would need more than half the register file double-buffered and stay
-// unpipelined.
+// (their run time is dominated by ramp-up and tail).  Lane tables of more
+// than 4 slots would need more than half the register file double-buffered:
+// such blocks pipeline only in the narrow shape below (more row groups).
 constexpr int64_t kPipeTaskBytes = 256 * 1024;
 constexpr int kPipeMaxCaches = 16;
 constexpr int64_t kPipeMinTasksPerWave = 16;
