@@ -6,7 +6,9 @@ The library is a plain C-ABI shared object (include/kvck.h); the Python
 binding loads it with ctypes, so no torch C++ extension is involved.  The
 build also makes ``hbm_read_probe``, which measures the HBM read bandwidth
 trivial read kernels reach: grid-stride streaming, and whole contiguous runs
-per wavefront in address or scrambled order (the shape of a paged cache).
+per wavefront in address or scrambled order (the shape of a paged cache); and
+``kvck_demo``, a plain C program that uses the library through include/kvck.h
+alone (examples/kvck_demo.c).
 """
 
 from __future__ import annotations
@@ -22,6 +24,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libkvck.so")
 PROBE = os.path.join(PKG, "hbm_read_probe")
+DEMO = os.path.join(PKG, "kvck_demo")
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are kept out of every kernel (no FP32 math is used
@@ -62,6 +65,15 @@ def build(save_temps: str | None = None, verbose: bool = False) -> str:
     subprocess.run([hipcc(), *[f for f in HIP_FLAGS if f not in ("-shared", "-fPIC", "-fvisibility=hidden")],
                     os.path.join(PKG, "probe", "hbm_read_probe.hip"), "-o", probe_tmp], check=True)
     os.replace(probe_tmp, PROBE)
+    # a plain C consumer of the C ABI (gcc, C99): no Python or torch involved
+    demo_tmp = DEMO + ".tmp"
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    subprocess.run([shutil.which("gcc") or "gcc", "-std=c99", "-O2", "-Wall", "-Wextra",
+                    "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+                    os.path.join(PKG, "examples", "kvck_demo.c"), "-o", demo_tmp, "-L", PKG, "-lkvck",
+                    "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-Wl,-rpath,$ORIGIN",
+                    "-Wl,-rpath," + os.path.join(rocm, "lib")], check=True)
+    os.replace(demo_tmp, DEMO)
     return LIB
 
 

@@ -60,6 +60,21 @@ def blocks_for(num_tokens: int, block_size: int) -> int:
     return -(-int(num_tokens) // block_size)
 
 
+def splitmix64_bytes(seed: int, nbytes: int) -> np.ndarray:
+    """``nbytes`` bytes of the splitmix64 stream seeded with ``seed`` (the
+    published generator of Steele, Lea and Flood: the state advances by
+    0x9E3779B97F4A7C15 and each output is two xor-shift-multiply rounds of
+    it), each 64-bit output giving 8 bytes little-endian.  Programs outside
+    Python (the C example) draw the same bytes from their own copy."""
+    n = (nbytes + 7) // 8
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed) + np.arange(1, n + 1, dtype=np.uint64) * np.uint64(0x9E3779B97F4A7C15)
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+        z = z ^ (z >> np.uint64(31))
+    return z.astype("<u8").view(np.uint8)[:nbytes]
+
+
 def page_requests(rng: np.random.Generator, lengths, block_size: int, pool_blocks: int | None = None,
                   start_pos=None, extra_blocks=None, spare_frac: float = 0.05) -> tuple[Requests, int]:
     """Lay requests out on random, distinct, non-contiguous pool blocks.
