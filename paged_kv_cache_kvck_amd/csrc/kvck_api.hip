@@ -137,7 +137,7 @@ void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_ca
   if (shp->transposed && shp->slots > 4) pipe = false;  // pipelined variants stop at 4 slots
   if (copy) {
     // One unit buffer per wave: twice the resident waves of the ping-pong
-    // kernel, which keeps more stores in flight (same-box A/B: load 5.6 ->
+    // kernel, which keeps more stores in flight (A/B on one GPU: load 5.6 ->
     // 5.9 TB/s read+write, save unchanged).  KVCK_COPY_BUFFERS=2 selects the
     // ping-pong kernel (results are identical).
     if (const char* b = getenv("KVCK_COPY_BUFFERS")) shp->copy_buffers = b[0] == '2' ? 2 : 1;

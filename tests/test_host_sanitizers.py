@@ -6,7 +6,7 @@ code is compiled as usual and never run here), links them into the C driver
 called with arguments it must reject, including integers at the edges of
 their types, and with valid arguments that must report the missing device.
 Any out-of-bounds host access, signed overflow or other undefined behaviour
-aborts the driver.
+aborts the program.
 """
 
 import concurrent.futures as cf
