@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -37,12 +38,19 @@ MAIN_PASS_SOURCES = ("paged_kv_cache_kvck_amd/csrc/kvck_blocks.hip", "paged_kv_c
                      "include/kvck.h")
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and whitespace: what the compiler sees."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", "", text)
+
+
 def kernel_sources_sha() -> str:
     h = hashlib.sha256()
     for p in (os.path.join(ROOT, f) for f in MAIN_PASS_SOURCES):
-        with open(p, "rb") as f:
+        with open(p, encoding="utf-8") as f:
             h.update(os.path.basename(p).encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
