@@ -120,6 +120,50 @@ def cpu_baseline(pools, w, seconds, seed=0):
                       f"heads), numpy single-threaded, {elapsed:.1f} s of oracle time; host copies excluded"}
 
 
+def _oracle_worker(args):
+    """One process of the parallel CPU baseline: the oracle on host pools of
+    the workload's shapes (random bits), full blocks at random positions, for
+    about ``seconds``.  Uses numpy only; never touches the GPU."""
+    seed, seconds, layout, nb, bs, nh, d, elem, layers, bases, head_begin, head_count = args
+    import numpy as np
+    import oracle
+    from paged_kv_cache_kvck_amd import workloads as wl
+    rng = np.random.default_rng(seed)
+    pools = [wl.host_random_bits(rng, wl.pool_shape(layout, nb, bs, nh, d), elem) for _ in layers]
+    n = nh - head_begin if head_count is None else head_count
+    per_block = bs * n * 2 * d * wl.ELEM_BYTES[elem] * len(layers)
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        b, pos = int(rng.integers(0, nb)), int(rng.integers(0, 512))
+        oracle.kv_checksum.checksum_position(pools, layout, layers, bases, b, pos, (pos + 1) * bs, head_begin,
+                                             head_count)
+        done += 1
+    return done * per_block, time.perf_counter() - t0
+
+
+def cpu_baseline_parallel(w, seconds, workers):
+    """The oracle in ``workers`` fresh processes at once (spawned: numpy only),
+    each on its own host pools of the workload's shapes: aggregate GB/s."""
+    import multiprocessing as mp
+    args = [(1000 + i, seconds, w.layout, 64, w.req.block_size, w.num_heads, w.head_size, w.elem,
+             list(w.layer_numbers), list(w.bases), w.head_begin, w.head_count) for i in range(workers)]
+    pool = mp.get_context("spawn").Pool(workers)
+    try:
+        # bounded: workers that cannot start (no importable main module) would be respawned forever
+        res = pool.map_async(_oracle_worker, args).get(timeout=seconds + 120)
+    except Exception as e:  # timeout or a worker error: no parallel figure
+        print(f"[bench] parallel cpu baseline skipped: {e!r}", file=sys.stderr, flush=True)
+        return None
+    finally:
+        pool.terminate()
+        pool.join()
+    nbytes = sum(r[0] for r in res)
+    wall = max(r[1] for r in res)
+    return {"value": nbytes / wall / 1e9, "unit": "GB/s", "cores": workers,
+            "sample": f"{workers} processes x {seconds:.0f} s, each the oracle on its own host pools of the "
+                      f"workload's shapes (64 blocks per layer, random bits), full blocks at random positions"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +171,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="processes of the parallel CPU baseline (0: the host's CPUs, at most 16)")
+    ap.add_argument("--cpu-parallel-seconds", type=float, default=5.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-shard", action="store_true", help="skip the TP-shard timing")
     ap.add_argument("--no-states", action="store_true", help="skip the Mamba-state timing")
@@ -312,6 +359,9 @@ def main(argv=None):
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(pools, w, args.cpu_seconds)
         cpu["host_cpu"] = _cpu_model()
+        workers = args.cpu_workers or min(16, os.cpu_count() or 1)
+        print(f"[bench] cpu baseline, {workers} processes", file=sys.stderr, flush=True)
+        cpu["parallel"] = cpu_baseline_parallel(w, args.cpu_parallel_seconds, workers)
 
     line = {
         "metric": "checksummed KV GB/s (bit-exact vs CPU oracle)",
