@@ -1,0 +1,124 @@
+"""Seeded sweep of the fused copy + checksum (connector save / load) over small
+random configurations (GPU).
+
+Save: checksums equal the oracle's and the staging buffer holds exactly the
+valid rows of each listed position ([plane][head][slot][row] per cache, in
+request and cache order).  Load into a pool paged on other block ids: the
+valid rows land there, everything else stays zero, and the checksums repeat.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_kvck_amd as kvck
+from paged_kv_cache_kvck_amd import workloads as wl
+from gpu_helpers import DEV, log, req_tensors, to_device_bits, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = ["NHD", "HND", "FI_NHD", "FI_HND", "MLA"]
+
+
+def _case(i):
+    rng = np.random.default_rng(zlib.crc32(f"copysweep{i}".encode()))
+    layout = LAYOUTS[i % len(LAYOUTS)]
+    elem = ["fp8", "bf16", "fp32"][int(rng.integers(0, 3))]
+    es = wl.ELEM_BYTES[elem]
+    heads = 1 if layout == "MLA" else int(rng.integers(1, 9))
+    unit = 8 // es
+    d = unit * int(rng.integers(1, 40))
+    bs = int(rng.choice([1, 2, 3, 4, 8, 16, 32]))
+    layers = sorted(int(x) for x in rng.choice(100, size=int(rng.integers(1, 4)), replace=False))
+    n_req = int(rng.integers(1, 5))
+    lengths = [int(x) for x in rng.integers(0, 3 * bs + 20, size=n_req)]
+    start = [int(x) for x in rng.integers(0, 2, size=n_req)]
+    extra = [int(x) for x in rng.integers(0, 2, size=n_req)]
+    hb = int(rng.integers(0, heads))
+    hc = int(rng.integers(1, heads - hb + 1))
+    buffers = ["1", "2"][int(rng.integers(0, 2))]
+    return dict(i=i, layout=layout, elem=elem, heads=heads, d=d, bs=bs, layers=layers, lengths=lengths,
+                start=start, extra=extra, hb=hb, hc=hc, buffers=buffers)
+
+
+CASES = [_case(i) for i in range(40)]
+
+
+def _ids(c):
+    return f"{c['i']}-{c['layout']}-{c['elem']}-h{c['heads']}-d{c['d']}-bs{c['bs']}-b{c['buffers']}"
+
+
+def _rows(pool, layout, pl, b, v, hb, n):
+    """(n heads, v slots, row) of block b, plane pl."""
+    if layout == "NHD":
+        return np.swapaxes(pool[pl, b, :v, hb:hb + n], 0, 1)
+    if layout == "HND":
+        return pool[pl, b, hb:hb + n, :v]
+    if layout == "FI_NHD":
+        return np.swapaxes(pool[b, pl, :v, hb:hb + n], 0, 1)
+    if layout == "FI_HND":
+        return pool[b, pl, hb:hb + n, :v]
+    return pool[b, :v][None]
+
+
+def _images(pools, layout, req, hb, n, bs, row_bytes):
+    planes = 1 if layout == "MLA" else 2
+    listed = req.listed()
+    img = np.zeros((len(listed), len(pools), planes, n, bs, row_bytes), np.uint8)
+    for e, (r, k) in enumerate(listed):
+        v = min(bs, max(0, int(req.num_tokens[r]) - (int(req.start_pos[r]) + k) * bs))
+        if v == 0:
+            continue
+        b = int(req.block_table[r, k])
+        for c, p in enumerate(pools):
+            for pl in range(planes):
+                rows = np.ascontiguousarray(_rows(p, layout, pl, b, v, hb, n))
+                img[e, c, pl, :, :v] = rows.view(np.uint8).reshape(n, v, row_bytes)
+    return img
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+def test_copy_sweep_case(case, monkeypatch):
+    monkeypatch.setenv("KVCK_COPY_BUFFERS", case["buffers"])
+    log(f"[copy sweep] {_ids(case)} heads {case['hb']}+{case['hc']}")
+    rng = np.random.default_rng(2000 + case["i"])
+    layout, bs, nh, d, layers = case["layout"], case["bs"], case["heads"], case["d"], case["layers"]
+    hb, hc = case["hb"], case["hc"]
+    req, nb = wl.page_requests(rng, case["lengths"], bs, start_pos=case["start"], extra_blocks=case["extra"],
+                               spare_frac=0.3)
+    shape = wl.pool_shape(layout, nb, bs, nh, d)
+    hp = [wl.host_random_bits(rng, shape, case["elem"]) for _ in layers]
+    pools = [to_device_bits(p) for p in hp]
+    bases = [hb + 7] * len(layers)
+    bt, nbt, sp, nt = req_tensors(req)
+    per = kvck.kvck_staging_bytes(pools[0], layout, len(layers), hc)
+    staging = torch.zeros(max(1, int(req.num_blocks.sum())) * per, dtype=torch.uint8, device=DEV)
+    got = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, pools, layout, layers, bt, nbt, sp, nt, staging,
+                                         global_head_base=bases, head_begin=hb, head_count=hc,
+                                         check=True).cpu().numpy()
+    want = oracle.checksum_blocks(hp, layout, layers, bases, req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens, head_begin=hb, head_count=hc)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k]), ("save", r, k)
+    row_bytes = d * wl.ELEM_BYTES[case["elem"]]
+    exp = _images(hp, layout, req, hb, hc, bs, row_bytes)
+    n_img = exp.size
+    assert np.array_equal(staging.cpu().numpy()[:n_img].reshape(exp.shape), exp)
+
+    req2, _ = wl.page_requests(np.random.default_rng(3000 + case["i"]), case["lengths"], bs, pool_blocks=nb,
+                               start_pos=case["start"], extra_blocks=case["extra"])
+    dst = [to_device_bits(np.zeros(shape, wl.HOST_BITS[case["elem"]])) for _ in layers]
+    bt2, nbt2, sp2, nt2 = req_tensors(req2)
+    got2 = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_LOAD, dst, layout, layers, bt2, nbt2, sp2, nt2, staging,
+                                          global_head_base=bases, head_begin=hb, head_count=hc,
+                                          check=True).cpu().numpy()
+    for r, k in req.listed():
+        assert got2[r, k] == got[r, k], ("load", r, k)
+    back = [to_host_bits(t) for t in dst]
+    assert np.array_equal(_images(back, layout, req2, hb, hc, bs, row_bytes), exp)
+    # nothing but the loaded rows was written
+    total = sum(int(np.count_nonzero(b.view(np.uint8))) for b in back)
+    assert total == int(np.count_nonzero(exp))
