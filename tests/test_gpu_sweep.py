@@ -96,3 +96,45 @@ def test_sweep_case(case, monkeypatch):
         got = gpu_blocks([to_device_bits(p) for p in hp], layout, case["layers"], req, **kw)
     for r, kk in req.listed():
         assert int(got[r, kk]) == int(want[r, kk]), (r, kk)
+
+
+def _states_case(i):
+    rng = np.random.default_rng(zlib.crc32(f"states{i}".encode()))
+    nstates = int(rng.integers(1, 5))
+    rows = int(rng.integers(1, 40))
+    states = []
+    for _ in range(nstates):
+        elem = ["fp16", "fp32"][int(rng.integers(0, 2))]
+        per16 = 16 // wl.ELEM_BYTES[elem]                       # row bytes are whole 16-byte chunks
+        inner = per16 * int(rng.integers(1, 70))
+        states.append((elem, inner))
+    layers = sorted(int(x) for x in rng.choice(32768, size=int(rng.integers(1, 5)), replace=False))
+    slots = int(rng.integers(2, 12))
+    n_req = int(rng.integers(1, 8))
+    row_begin = int(rng.integers(0, rows))
+    row_count = int(rng.integers(1, rows - row_begin + 1))
+    base = int(rng.integers(0, 65536 - row_count))
+    return dict(i=i, states=states, rows=rows, layers=layers, slots=slots, n_req=n_req, row_begin=row_begin,
+                row_count=row_count, base=base)
+
+
+STATE_CASES = [_states_case(i) for i in range(40)]
+
+
+@pytest.mark.parametrize("case", STATE_CASES, ids=lambda c: f"{c['i']}-s{len(c['states'])}-r{c['rows']}")
+def test_states_sweep_case(case):
+    import torch
+    import paged_kv_cache_kvck_amd as kvck
+    from gpu_helpers import DEV
+    log(f"[states sweep] {case}")
+    rng = np.random.default_rng(4000 + case["i"])
+    hs = [[wl.host_random_bits(rng, (case["slots"], case["rows"], inner), elem) for elem, inner in case["states"]]
+          for _ in case["layers"]]
+    slot_ids = rng.integers(0, case["slots"], size=case["n_req"]).astype(np.int32)   # repeats allowed
+    bases = [case["base"]] * len(case["layers"])
+    got = kvck.kvck_checksum_states([[to_device_bits(a) for a in l] for l in hs], case["layers"],
+                                    torch.from_numpy(slot_ids).to(DEV), global_row_base=bases,
+                                    row_begin=case["row_begin"], row_count=case["row_count"], check=True)
+    want = oracle.checksum_states(hs, case["layers"], bases, slot_ids, row_begin=case["row_begin"],
+                                  row_count=case["row_count"])
+    assert np.array_equal(got.cpu().numpy(), want)
