@@ -81,9 +81,11 @@ def make_workload(name):
     raise SystemExit(f"unknown workload {name}")
 
 
-def cpu_baseline(pools, w, seconds, seed=0):
+def cpu_baseline(pools, w, seconds, gpu_out=None, seed=0):
     """The oracle, as it stands, on a bounded random sample of listed positions
-    (host copies of their blocks are made outside the timed region)."""
+    (host copies of their blocks are made outside the timed region).  Each
+    value it computes is also compared with ``gpu_out`` (the GPU's checksums of
+    the timed steps, uint64 [num_reqs, max_blocks]) when given."""
     import numpy as np
     import torch
     import oracle
@@ -92,7 +94,7 @@ def cpu_baseline(pools, w, seconds, seed=0):
     rng = np.random.default_rng(seed)
     allpos = w.req.listed()
     order = rng.permutation(len(allpos))
-    done, nbytes, elapsed, i = 0, 0, 0.0, 0
+    done, nbytes, elapsed, i, mismatches = 0, 0, 0.0, 0, 0
     row = w.heads_used * w.planes * w.head_size * wl.ELEM_BYTES[w.elem] * w.num_layers
     while elapsed < seconds and i < len(order):
         chunk = [allpos[j] for j in order[i:i + 32]]
@@ -105,19 +107,26 @@ def cpu_baseline(pools, w, seconds, seed=0):
             sub = p.index_select(0 if w.layout == "MLA" else 1, idx).contiguous()
             mini.append(sub.view(torch.int16).cpu().numpy().view(np.uint16))
         t0 = time.perf_counter()
-        for r, k in chunk:
-            oracle.kv_checksum.checksum_position(mini, w.layout, w.layer_numbers, w.bases,
-                                                 remap[int(w.req.block_table[r, k])], int(w.req.start_pos[r]) + k,
-                                                 int(w.req.num_tokens[r]), w.head_begin, w.head_count)
+        vals = [oracle.kv_checksum.checksum_position(mini, w.layout, w.layer_numbers, w.bases,
+                                                     remap[int(w.req.block_table[r, k])],
+                                                     int(w.req.start_pos[r]) + k, int(w.req.num_tokens[r]),
+                                                     w.head_begin, w.head_count) for r, k in chunk]
         elapsed += time.perf_counter() - t0
+        if gpu_out is not None:
+            mismatches += sum(int(gpu_out[r, k]) != v for (r, k), v in zip(chunk, vals))
         for r, k in chunk:
             pos = int(w.req.start_pos[r]) + k
             v = min(w.req.block_size, max(0, int(w.req.num_tokens[r]) - pos * w.req.block_size))
             nbytes += v * row
         done += len(chunk)
-    return {"value": nbytes / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} random listed positions of the same workload ({nbytes} valid bytes, all layers and "
-                      f"heads), numpy single-threaded, {elapsed:.1f} s of oracle time; host copies excluded"}
+    res = {"value": nbytes / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{done} random listed positions of the same workload ({nbytes} valid bytes, all layers and "
+                     f"heads), numpy single-threaded, {elapsed:.1f} s of oracle time; host copies excluded"}
+    if gpu_out is not None:
+        # the same positions of the timed GPU steps, compared bit for bit
+        res["gpu_checked_positions"] = done
+        res["gpu_mismatches"] = mismatches
+    return res
 
 
 def _oracle_worker(args):
@@ -233,6 +242,7 @@ def main(argv=None):
     per_step = [e0.elapsed_time(marks[0])] + [marks[i - 1].elapsed_time(marks[i]) for i in range(1, args.steps)]
     main_ms, calls = kvck.kvck_instrument_read()
     main_avg = main_ms / max(calls, 1)
+    out_main = out.cpu().numpy().view("uint64").copy()  # the timed steps' checksums, for the oracle check
     achieved = valid / (main_avg * 1e-3) / 1e9
 
     extra = {"valid_bytes_per_step": valid, "main_pass_ms": main_avg,
@@ -357,7 +367,7 @@ def main(argv=None):
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(pools, w, args.cpu_seconds)
+        cpu = cpu_baseline(pools, w, args.cpu_seconds, gpu_out=out_main)
         cpu["host_cpu"] = _cpu_model()
         workers = args.cpu_workers or min(16, os.cpu_count() or 1)
         print(f"[bench] cpu baseline, {workers} processes", file=sys.stderr, flush=True)
