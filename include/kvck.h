@@ -163,6 +163,11 @@ typedef struct kvck_kv_layout {
  * batches in flight and give each task four layers; small ones use one layer
  * per task at higher occupancy.  The environment variable KVCK_SCHEDULE =
  * "pipelined" or "simple" forces one of the two; results are bit-identical.
+ * Calls of at most 8192 (request slot, cache) pairs read the request arrays
+ * in the main pass itself (no separate planning launch; the smallest run as a
+ * single launch); KVCK_PLAN = "compact" turns this off, with identical
+ * results and error bits.  Either way block_table entries k < max_blocks of
+ * every row may be read, and only listed, valid ones are used.
  */
 kvck_status kvck_checksum_blocks(
     const kvck_kv_layout* layout,          /* host */

@@ -90,6 +90,7 @@ bool choose_shape(int32_t block_size, int32_t row_bytes, int chunk, int max_slot
   shp->copy_buffers = 1;
   shp->transposed = false;
   shp->elem_bytes = 0;
+  shp->dense = false;
   return true;
 }
 
@@ -115,8 +116,12 @@ static_assert(kCachesPerLaunch % kPipeMaxCaches == 0, "launch groups must not st
 // `narrow` (or null) is the same rows split into lane tables of at most 4
 // slots, the widest the pipelined kernel double-buffers: blocks whose rows
 // need 8 or 16 slots per lane can still be pipelined, in more row groups.
+//
+// A call planned in place (`dense`) whose caches all fit one task's byte
+// budget runs one pipelined task per position over every cache: a single
+// launch with no second pass, where latency rather than lane use counts.
 void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_caches, int64_t max_items,
-                     int64_t block_bytes, int planes, int heads, int cus, bool copy) {
+                     int64_t block_bytes, int planes, int heads, int cus, bool copy, bool dense) {
   const int64_t waves = (int64_t)cus * 8;  // resident waves of the pipelined kernel (2 per SIMD)
   int lpt = 1;
   while (lpt < kPipeMaxCaches && (int64_t)(2 * lpt) * block_bytes <= kPipeTaskBytes) lpt *= 2;
@@ -126,7 +131,8 @@ void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_ca
   auto fills = [&](int slots) { return (int64_t)heads * (planes == 2 ? 2 : 1) * slots >= 16; };
   const BlocksShape* cand = shp->slots <= 4 ? shp : narrow;
   const bool fits = cand != nullptr && fills(cand->slots);
-  bool pipe = fits && num_caches > 1 && tasks >= kPipeMinTasksPerWave * waves;
+  const bool one_task = dense && !copy && !shp->merged && cand != nullptr && num_caches <= lpt;
+  bool pipe = (fits && num_caches > 1 && tasks >= kPipeMinTasksPerWave * waves) || one_task;
   // KVCK_SCHEDULE=pipelined|simple overrides the choice (results are identical
   // either way); merged rows always run the unpipelined kernel
   if (const char* force = getenv("KVCK_SCHEDULE")) {
@@ -143,7 +149,7 @@ void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_ca
     if (const char* b = getenv("KVCK_COPY_BUFFERS")) shp->copy_buffers = b[0] == '2' ? 2 : 1;
   }
   if (copy) pipe = true;  // the fused copy kernel always runs the pipelined structure
-  if (pipe && !copy && shp->slots > 4 && narrow && fills(narrow->slots)) {
+  if (pipe && !copy && shp->slots > 4 && narrow && (fills(narrow->slots) || one_task)) {
     shp->slots = narrow->slots;
     shp->rows_per_group = narrow->rows_per_group;
   }
@@ -377,17 +383,27 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   if (ds != KVCK_OK) return ds;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int cus = device_cus(dev);
-  choose_schedule(&shp, has_narrow ? &narrow : nullptr, num_caches, (int64_t)num_reqs * max_blocks, image_bytes,
-                  planes_cov, head_count, cus, mode != kModeChecksum);
+  const int64_t max_items = (int64_t)num_reqs * max_blocks;
+  // Small checksum calls plan in place: one wave per (slot, cache group) task
+  // reads its request's entries itself, which saves the plan launch; larger
+  // ones list the positions first so no wave is spent on empty slots.
+  // KVCK_PLAN=compact plans every call (results are identical).
+  bool dense = mode == kModeChecksum && max_items * num_caches <= kDenseMaxTasks;
+  if (const char* force = getenv("KVCK_PLAN"))
+    if (strcmp(force, "compact") == 0) dense = false;
+  choose_schedule(&shp, has_narrow ? &narrow : nullptr, num_caches, max_items, image_bytes, planes_cov, head_count,
+                  cus, mode != kModeChecksum, dense);
+  shp.dense = dense;
   const int32_t lpt = shp.caches_per_task;
   const int32_t total_groups = (num_caches + lpt - 1) / lpt;
+  const int64_t max_start = INT64_MAX / L.block_size - max_blocks;  // keeps (start + k) * block_size exact
 
-  if (launch_plan(block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens, num_reqs,
-                  max_blocks, L.block_size, L.num_blocks, workspace, error_flags, st) != hipSuccess)
+  if (!dense && launch_plan(block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens,
+                            num_reqs, max_blocks, L.block_size, L.num_blocks, workspace, error_flags,
+                            st) != hipSuccess)
     return KVCK_ERR_HIP;
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const int64_t max_items = (int64_t)num_reqs * max_blocks;
   BlocksArgs a;
   memset(&a, 0, sizeof(a));
   a.plane_stride = L.plane_stride;
@@ -414,6 +430,16 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   a.caches_per_task = lpt;
   a.direct = total_groups == 1;
   a.accumulate = accumulate != 0;
+  a.max_blocks = max_blocks;
+  a.block_size = L.block_size;
+  a.bt_stride = block_table_row_stride;
+  a.num_blocks = L.num_blocks;
+  a.max_start = max_start;
+  a.block_table = block_table;
+  a.nbpr = num_blocks_per_req;
+  a.start_pos = start_pos;
+  a.num_tokens = num_tokens;
+  a.req_flags = error_flags;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
   const bool timed = instrument_pair(&ev0, &ev1);
   if (timed && hipEventRecord(ev0, st) != hipSuccess) return KVCK_ERR_HIP;
@@ -425,12 +451,12 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
       a.base[i] = static_cast<const uint8_t*>(cache_ptrs[c0 + i]) + (int64_t)head_begin * L.head_stride;
       a.mbase[i] = (uint32_t)(2 * ((int64_t)layer_numbers[c0 + i] * kH + global_head_base[c0 + i]) + 1);
     }
-    if (mode == kModeChecksum && transposed) {
-      const int grid = tblocks_grid(shp, dev, max_items * ((n + lpt - 1) / lpt));
-      if (launch_tblocks(a, shp, grid, st) != hipSuccess) return KVCK_ERR_HIP;
-    } else if (mode == kModeChecksum) {
-      const int grid = blocks_grid(shp, dev, max_items * ((n + lpt - 1) / lpt));
-      if (launch_blocks(a, shp, grid, st) != hipSuccess) return KVCK_ERR_HIP;
+    const int64_t tasks = max_items * ((n + lpt - 1) / lpt);
+    if (mode == kModeChecksum) {
+      const int grid = transposed ? tblocks_grid(shp, dev, tasks) : blocks_grid(shp, dev, tasks);
+      if (dense && (int64_t)grid * (kBlockThreads / kWave) < tasks) return KVCK_ERR_HIP;  // one wave per task
+      if ((transposed ? launch_tblocks(a, shp, grid, st) : launch_blocks(a, shp, grid, st)) != hipSuccess)
+        return KVCK_ERR_HIP;
     } else {
       CopyArgs ca;
       memset(&ca, 0, sizeof(ca));
@@ -442,14 +468,17 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
       ca.num_caches_total = num_caches;
       ca.cache_offset = c0;
       ca.block_size = L.block_size;
-      const int grid = copy_grid(shp, mode, dev, max_items * ((n + lpt - 1) / lpt));
+      const int grid = copy_grid(shp, mode, dev, tasks);
       if (launch_copy(ca, shp, mode, grid, st) != hipSuccess) return KVCK_ERR_HIP;
     }
   }
   if (timed && hipEventRecord(ev1, st) != hipSuccess) return KVCK_ERR_HIP;
   if (total_groups > 1) {
-    if (launch_reduce(a.partials, max_items, total_groups, a.n_items, 0, a.recs, out, a.accumulate, st) != hipSuccess)
-      return KVCK_ERR_HIP;
+    const hipError_t e = dense ? launch_reduce_dense(a.partials, max_items, total_groups, num_blocks_per_req,
+                                                     start_pos, max_blocks, max_start, out, a.accumulate, st)
+                               : launch_reduce(a.partials, max_items, total_groups, a.n_items, 0, a.recs, out,
+                                               a.accumulate, st);
+    if (e != hipSuccess) return KVCK_ERR_HIP;
   }
   return KVCK_OK;
 }

@@ -47,8 +47,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(const int32_t* __restri
     int n = 0;
     if (r < num_reqs) {
       n = nbpr[r];
-      const int64_t s = start_pos[r];
-      if (n < 0 || n > max_blocks || s < 0 || s > max_start) {
+      if (bad_request(n, start_pos[r], max_blocks, max_start)) {
         if (error_flags) atomicOr(error_flags, KVCK_FLAG_BAD_REQUEST);
         n = 0;
       }
@@ -87,8 +86,7 @@ __global__ __launch_bounds__(256) void plan_fill_kernel(
   const int32_t p0 = prefix[r];
   if (k >= prefix[r + 1] - p0) return;
   const int64_t t0 = (start_pos[r] + k) * (int64_t)block_size;
-  const int64_t left = num_tokens[r] - t0;
-  int32_t v = left <= 0 ? 0 : (left >= block_size ? block_size : (int32_t)left);
+  int32_t v = valid_slots(num_tokens[r], t0, block_size);
   const int32_t b = block_table[(int64_t)r * bt_stride + k];
   if (v > 0 && (b < 0 || (int64_t)b >= num_blocks)) {
     if (error_flags) atomicOr(error_flags, KVCK_FLAG_BAD_BLOCK_ID);
@@ -116,8 +114,7 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
   int n = 0;
   if (tid < num_reqs) {
     n = nbpr[tid];
-    const int64_t s = start_pos[tid];
-    if (n < 0 || n > max_blocks || s < 0 || s > max_start) {
+    if (bad_request(n, start_pos[tid], max_blocks, max_start)) {
       if (blockIdx.x == 0 && error_flags) atomicOr(error_flags, KVCK_FLAG_BAD_REQUEST);
       n = 0;
     }
@@ -139,8 +136,7 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
   const int32_t p0 = r > 0 ? scan[r - 1] : 0;
   if (k >= end - p0) return;
   const int64_t t0 = (start_pos[r] + k) * (int64_t)block_size;
-  const int64_t left = num_tokens[r] - t0;
-  int32_t v = left <= 0 ? 0 : (left >= block_size ? block_size : (int32_t)left);
+  int32_t v = valid_slots(num_tokens[r], t0, block_size);
   const int32_t b = block_table[(int64_t)r * bt_stride + k];
   if (v > 0 && (b < 0 || (int64_t)b >= num_blocks)) {
     if (error_flags) atomicOr(error_flags, KVCK_FLAG_BAD_BLOCK_ID);
@@ -183,13 +179,13 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
 //               lane-table row is the slot's whole run of heads, so a load
 //               instruction covers contiguous bytes even when one head's row
 //               is short; each chunk carries its own head's factor m.
-template <int CHUNK, int S, int HU, int PU, bool PIPE, bool MERGED>
+template <int CHUNK, int S, int HU, int PU, bool PIPE, bool MERGED, bool DENSE>
 __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs a) {
   using V = typename ChunkType<CHUNK>::T;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
-  const int64_t n_items = (int64_t)*a.n_items;
+  const int64_t n_items = DENSE ? a.max_items : (int64_t)*a.n_items;
   const int lpt = a.caches_per_task;
   const int ngroups = (a.num_caches + lpt - 1) / lpt;
   const int64_t total = n_items * ngroups;
@@ -209,13 +205,13 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
     const int64_t item = task - grp * n_items;
     const int c_begin = (int)grp * lpt;
     const int c_end = min(a.num_caches, c_begin + lpt);
-    const PosRecord* rp = a.recs + item;
-    // the record is the same for the whole wave
-    const int32_t v = __builtin_amdgcn_readfirstlane(rp->valid);
-    const int32_t blk = __builtin_amdgcn_readfirstlane(rp->block);
-    const uint64_t t0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(rp->t0 >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)rp->t0);
-    const int64_t out_idx = rp->out_idx;
+    const TaskRecord rec = task_record<DENSE>(a, item, a.group_offset + grp == 0, lane);
+    // Dense variants run one task per wave (their grid covers every task), so
+    // they leave the loop after it; only their slots can be unlisted.
+    if (!rec.listed) break;  // uniform
+    const int32_t v = rec.valid;
+    const int32_t blk = rec.block;
+    const uint64_t t0 = rec.t0;
     uint64_t acc = 0;
     if (v > 0) {
       const int64_t blk_off = (int64_t)blk * a.block_stride;
@@ -298,12 +294,13 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
     acc = wave_sum(acc);
     if (lane == 0) {
       if (a.direct) {
-        uint64_t* o = a.out + out_idx;
+        uint64_t* o = a.out + rec.out_idx;
         *o = a.accumulate ? *o + acc : acc;
       } else {
         a.partials[(int64_t)(a.group_offset + grp) * a.max_items + item] = acc;
       }
     }
+    if constexpr (DENSE) break;
   }
 }
 
@@ -342,39 +339,69 @@ __global__ __launch_bounds__(256) void reduce_wave_kernel(const uint64_t* __rest
   }
 }
 
-template <int CHUNK, int S, int PU, bool PIPE, bool MERGED>
+// Second pass of a call planned in place: one wavefront per (r, k) slot, the
+// partials of listed positions summed in split order (lanes stride over the
+// splits); other slots are left untouched.
+__global__ __launch_bounds__(256) void reduce_dense_kernel(const uint64_t* __restrict__ partials, int64_t stride,
+                                                           int32_t splits, const int32_t* __restrict__ nbpr,
+                                                           const int64_t* __restrict__ start_pos, int32_t max_blocks,
+                                                           int64_t max_start, uint64_t* __restrict__ out,
+                                                           int32_t accumulate) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+  for (int64_t i = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; i < stride; i += waves) {
+    const int32_t r = (int32_t)i / max_blocks;  // stride = num_reqs * max_blocks < 2^31
+    const int32_t k = (int32_t)i - r * max_blocks;
+    const int32_t n = nbpr[r];
+    if (bad_request(n, start_pos[r], max_blocks, max_start) || k >= n) continue;
+    uint64_t s = 0;
+    for (int32_t sp = lane; sp < splits; sp += kWave) s += partials[(int64_t)sp * stride + i];
+    s = wave_sum(s);
+    if (lane == 0) out[i] = accumulate ? out[i] + s : s;
+  }
+}
+
+template <int CHUNK, int S, int PU, bool PIPE, bool MERGED, bool DENSE>
 constexpr auto pick_kernel() {
   constexpr int hu = MERGED ? 1 : (16 / (S * PU) > 0 ? 16 / (S * PU) : 1);
-  return &blocks_kernel<CHUNK, S, hu, PU, PIPE, MERGED>;
+  return &blocks_kernel<CHUNK, S, hu, PU, PIPE, MERGED, DENSE>;
 }
 
 using BlocksFn = void (*)(const BlocksArgs);
 
-template <int CHUNK, int PU, bool PIPE, bool MERGED = false>
+template <int CHUNK, int PU, bool PIPE, bool MERGED, bool DENSE>
 BlocksFn blocks_fn_slots(int slots) {
   switch (slots) {
-    case 1: return pick_kernel<CHUNK, 1, PU, PIPE, MERGED>();
-    case 2: return pick_kernel<CHUNK, 2, PU, PIPE, MERGED>();
-    case 4: return pick_kernel<CHUNK, 4, PU, PIPE, MERGED>();
-    case 8: return pick_kernel<CHUNK, 8, 1, PIPE, MERGED>();
-    case 16: return pick_kernel<CHUNK, 16, 1, PIPE, MERGED>();
+    case 1: return pick_kernel<CHUNK, 1, PU, PIPE, MERGED, DENSE>();
+    case 2: return pick_kernel<CHUNK, 2, PU, PIPE, MERGED, DENSE>();
+    case 4: return pick_kernel<CHUNK, 4, PU, PIPE, MERGED, DENSE>();
+    case 8: return pick_kernel<CHUNK, 8, 1, PIPE, MERGED, DENSE>();
+    case 16: return pick_kernel<CHUNK, 16, 1, PIPE, MERGED, DENSE>();
   }
   return nullptr;
 }
 
-// Pipelined units may carry both planes (PU = 2); the unpipelined kernel and
-// wide lane tables (S >= 8) always take one plane per unit.  Merged rows run
-// the unpipelined kernel.
-BlocksFn blocks_fn(const BlocksShape& shp) {
+template <bool DENSE>
+BlocksFn blocks_fn_plan(const BlocksShape& shp) {
   if (shp.merged)
-    return shp.chunk == 16 ? blocks_fn_slots<16, 1, false, true>(shp.slots)
-                           : blocks_fn_slots<8, 1, false, true>(shp.slots);
+    return shp.chunk == 16 ? blocks_fn_slots<16, 1, false, true, DENSE>(shp.slots)
+                           : blocks_fn_slots<8, 1, false, true, DENSE>(shp.slots);
   if (shp.pipelined) {
     if (shp.planes_per_unit == 2)
-      return shp.chunk == 16 ? blocks_fn_slots<16, 2, true>(shp.slots) : blocks_fn_slots<8, 2, true>(shp.slots);
-    return shp.chunk == 16 ? blocks_fn_slots<16, 1, true>(shp.slots) : blocks_fn_slots<8, 1, true>(shp.slots);
+      return shp.chunk == 16 ? blocks_fn_slots<16, 2, true, false, DENSE>(shp.slots)
+                             : blocks_fn_slots<8, 2, true, false, DENSE>(shp.slots);
+    return shp.chunk == 16 ? blocks_fn_slots<16, 1, true, false, DENSE>(shp.slots)
+                           : blocks_fn_slots<8, 1, true, false, DENSE>(shp.slots);
   }
-  return shp.chunk == 16 ? blocks_fn_slots<16, 1, false>(shp.slots) : blocks_fn_slots<8, 1, false>(shp.slots);
+  return shp.chunk == 16 ? blocks_fn_slots<16, 1, false, false, DENSE>(shp.slots)
+                         : blocks_fn_slots<8, 1, false, false, DENSE>(shp.slots);
+}
+
+// Pipelined units may carry both planes (PU = 2); the unpipelined kernel and
+// wide lane tables (S >= 8) always take one plane per unit.  Merged rows run
+// the unpipelined kernel.  Every variant exists planned and planned in place.
+BlocksFn blocks_fn(const BlocksShape& shp) {
+  return shp.dense ? blocks_fn_plan<true>(shp) : blocks_fn_plan<false>(shp);
 }
 
 }  // namespace
@@ -446,6 +473,7 @@ int blocks_grid(const BlocksShape& shp, int device, int64_t max_tasks) {
   const int64_t waves_per_block = kBlockThreads / kWave;
   const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
   const int64_t cap = (int64_t)per_cu * device_cus(device);
+  if (shp.dense) return (int)(need > 0 ? need : 1);  // one task per wave (at most kDenseMaxTasks)
   return (int)(need < cap ? (need > 0 ? need : 1) : cap);
 }
 
@@ -472,6 +500,17 @@ hipError_t launch_reduce(const uint64_t* partials, int64_t stride, int32_t split
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream, partials, stride, splits, n_items,
                      n_fixed, recs, out, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_dense(const uint64_t* partials, int64_t stride, int32_t splits, const int32_t* nbpr,
+                               const int64_t* start_pos, int32_t max_blocks, int64_t max_start, uint64_t* out,
+                               int32_t accumulate, hipStream_t stream) {
+  int64_t grid = (stride + 3) / 4;
+  if (grid > 4096) grid = 4096;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(reduce_dense_kernel, dim3((unsigned)grid), dim3(256), 0, stream, partials, stride, splits, nbpr,
+                     start_pos, max_blocks, max_start, out, accumulate);
   return hipGetLastError();
 }
 

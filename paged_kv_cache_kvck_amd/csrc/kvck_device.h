@@ -101,6 +101,80 @@ struct LaneTable {
   }
 };
 
+// A request whose listed count is outside [0, max_blocks] or whose start
+// position is negative or so large that a token index would overflow lists
+// nothing (and is reported as a bad request).
+__device__ __forceinline__ bool bad_request(int32_t n, int64_t start, int32_t max_blocks, int64_t max_start) {
+  return n < 0 || n > max_blocks || start < 0 || start > max_start;
+}
+
+// Valid slots of the block at first token t0 (the page's num_valid_tokens).
+__device__ __forceinline__ int32_t valid_slots(int64_t num_tokens, int64_t t0, int32_t block_size) {
+  const int64_t left = num_tokens - t0;
+  return left <= 0 ? 0 : (left >= block_size ? block_size : (int32_t)left);
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// What a task needs of its position.  `listed` is false for dense slots past
+// a request's listed count (or of a bad request): such tasks write nothing.
+struct TaskRecord {
+  uint64_t t0;
+  int64_t out_idx;
+  int32_t block, valid;
+  bool listed;
+};
+
+// Record of task item `item`, uniform over the wave.  Planned calls read the
+// plan's compact list; dense calls derive it from the request arrays with the
+// plan's rules (bad requests list nothing, an id outside the pool in a block
+// with valid slots contributes 0), and `report` lets one task per slot raise
+// the error bits.  DENSE is a template parameter so that the planned kernels
+// keep none of the request pointers live.
+template <bool DENSE>
+__device__ __forceinline__ TaskRecord task_record(const BlocksArgs& a, int64_t item, bool report, int lane) {
+  TaskRecord t;
+  if constexpr (!DENSE) {
+    const PosRecord* rp = a.recs + item;
+    t.valid = __builtin_amdgcn_readfirstlane(rp->valid);
+    t.block = __builtin_amdgcn_readfirstlane(rp->block);
+    t.t0 = (uint64_t)uniform64(rp->t0);
+    t.out_idx = rp->out_idx;
+    t.listed = true;
+    return t;
+  }
+  const int32_t r = (int32_t)item / a.max_blocks;  // item < 2^31
+  const int32_t k = (int32_t)item - r * a.max_blocks;
+  // four independent loads; the table entry is in bounds for every k < max_blocks
+  const int32_t n = __builtin_amdgcn_readfirstlane(a.nbpr[r]);
+  const int64_t s = uniform64(a.start_pos[r]);
+  const int64_t ntok = uniform64(a.num_tokens[r]);
+  const int32_t b = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)r * a.bt_stride + k]);
+  t.out_idx = item;
+  t.block = b;
+  t.valid = 0;
+  t.t0 = 0;
+  t.listed = false;
+  if (bad_request(n, s, a.max_blocks, a.max_start)) {
+    if (report && k == 0 && lane == 0 && a.req_flags) atomicOr(a.req_flags, KVCK_FLAG_BAD_REQUEST);
+    return t;
+  }
+  if (k >= n) return t;
+  t.listed = true;
+  const int64_t t0 = (s + k) * (int64_t)a.block_size;
+  t.t0 = (uint64_t)t0;
+  t.valid = valid_slots(ntok, t0, a.block_size);
+  if (t.valid > 0 && (b < 0 || (int64_t)b >= a.num_blocks)) {
+    if (report && lane == 0 && a.req_flags) atomicOr(a.req_flags, KVCK_FLAG_BAD_BLOCK_ID);
+    t.valid = 0;
+  }
+  return t;
+}
+
 // Position of the next unit of a task: cache, row group, plane, head batch.
 struct UnitCursor {
   int cache, group, plane, hbatch;

@@ -15,6 +15,10 @@ constexpr int kBlockThreads = 256;          // 4 independent waves per workgroup
 constexpr int kCachesPerLaunch = 64;        // caches carried in one argument block
 constexpr int kLayersPerStatesLaunch = 32;  // Mamba layers carried in one argument block
 constexpr size_t kAlign = 256;
+// Checksum calls of at most this many (slot, cache) tasks plan in place: the
+// dense kernel variants run one task per wave, in grids of at most
+// kDenseMaxTasks / 4 workgroups.
+constexpr int64_t kDenseMaxTasks = 8192;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -67,6 +71,16 @@ struct BlocksArgs {
   int32_t accumulate;
   const uint8_t* base[kCachesPerLaunch];     // pool base + head_begin*head_stride
   uint32_t mbase[kCachesPerLaunch];          // 2*(layer*H + global_head_base) + 1
+  // Calls planned in place (the dense kernel variants): tasks index every
+  // (r, k) slot, item = r*max_blocks + k, and read the request arrays
+  // themselves; recs and n_items are then unused.
+  int32_t max_blocks, block_size;
+  int64_t bt_stride, num_blocks, max_start;
+  const int32_t* block_table;
+  const int32_t* nbpr;
+  const int64_t* start_pos;
+  const int64_t* num_tokens;
+  uint32_t* req_flags;                       // error word for bad requests and ids (may be null)
 };
 
 // Arguments of the fused copy + checksum kernel.
@@ -111,6 +125,7 @@ struct BlocksShape {
   int copy_buffers;     // fused copy: 1 = one unit buffer (more resident waves), 2 = ping-pong
   bool transposed;      // rows stored element by element (elements of a row elem_stride apart)
   int elem_bytes;       // element size of transposed rows (1, 2 or 4)
+  bool dense;           // planned in place: tasks read the request arrays (kernel variant)
 };
 
 // launchers (return hipSuccess or the first HIP error)
@@ -123,6 +138,9 @@ int blocks_grid(const BlocksShape& shp, int device, int64_t max_tasks);
 hipError_t launch_reduce(const uint64_t* partials, int64_t stride, int32_t splits, const uint32_t* n_items,
                          int64_t n_fixed, const PosRecord* recs, uint64_t* out, int32_t accumulate,
                          hipStream_t stream);
+hipError_t launch_reduce_dense(const uint64_t* partials, int64_t stride, int32_t splits, const int32_t* nbpr,
+                               const int64_t* start_pos, int32_t max_blocks, int64_t max_start, uint64_t* out,
+                               int32_t accumulate, hipStream_t stream);
 hipError_t launch_states(const StatesArgs& a, int grid, hipStream_t stream);
 hipError_t launch_tblocks(const BlocksArgs& a, const BlocksShape& shp, int grid, hipStream_t stream);
 int tblocks_grid(const BlocksShape& shp, int device, int64_t max_tasks);

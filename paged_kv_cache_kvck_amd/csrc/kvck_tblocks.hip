@@ -73,7 +73,7 @@ __device__ __forceinline__ void chunk_sums(const V& x, int valid, uint64_t& E, u
   }
 }
 
-template <int CHUNK, int ES, int S, int HU, bool PIPE>
+template <int CHUNK, int ES, int S, int HU, bool PIPE, bool DENSE>
 __global__ __launch_bounds__(kBlockThreads) void tblocks_kernel(const BlocksArgs a) {
   using V = typename ChunkType<CHUNK>::T;
   constexpr int N = CHUNK / ES;        // slots per chunk
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kBlockThreads) void tblocks_kernel(const BlocksArgs
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
-  const int64_t n_items = (int64_t)*a.n_items;
+  const int64_t n_items = DENSE ? a.max_items : (int64_t)*a.n_items;
   const int lpt = a.caches_per_task;
   const int ngroups = (a.num_caches + lpt - 1) / lpt;
   const int64_t total = n_items * ngroups;
@@ -112,12 +112,13 @@ __global__ __launch_bounds__(kBlockThreads) void tblocks_kernel(const BlocksArgs
     const int64_t item = task - grp * n_items;
     const int c_begin = (int)grp * lpt;
     const int c_end = min(a.num_caches, c_begin + lpt);
-    const PosRecord* rp = a.recs + item;
-    const int32_t v = __builtin_amdgcn_readfirstlane(rp->valid);
-    const int32_t blk = __builtin_amdgcn_readfirstlane(rp->block);
-    const uint64_t t0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(rp->t0 >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)rp->t0);
-    const int64_t out_idx = rp->out_idx;
+    const TaskRecord rec = task_record<DENSE>(a, item, a.group_offset + grp == 0, lane);
+    // Dense variants run one task per wave (their grid covers every task), so
+    // they leave the loop after it; only their slots can be unlisted.
+    if (!rec.listed) break;  // uniform
+    const int32_t v = rec.valid;
+    const int32_t blk = rec.block;
+    const uint64_t t0 = rec.t0;
     uint64_t acc = 0;
     if (v > 0) {
       const int64_t blk_off = (int64_t)blk * a.block_stride;
@@ -199,52 +200,57 @@ __global__ __launch_bounds__(kBlockThreads) void tblocks_kernel(const BlocksArgs
     acc = wave_sum(acc);
     if (lane == 0) {
       if (a.direct) {
-        uint64_t* o = a.out + out_idx;
+        uint64_t* o = a.out + rec.out_idx;
         *o = a.accumulate ? *o + acc : acc;
       } else {
         a.partials[(int64_t)(a.group_offset + grp) * a.max_items + item] = acc;
       }
     }
+    if constexpr (DENSE) break;
   }
 }
 
 using TFn = void (*)(const BlocksArgs);
 
-template <int CHUNK, int ES, int S, bool PIPE>
+template <int CHUNK, int ES, int S, bool PIPE, bool DENSE>
 constexpr TFn tpick() {
-  return &tblocks_kernel<CHUNK, ES, S, (16 / S > 0 ? 16 / S : 1), PIPE>;
+  return &tblocks_kernel<CHUNK, ES, S, (16 / S > 0 ? 16 / S : 1), PIPE, DENSE>;
 }
 
 // The pipelined kernel double-buffers lane tables of at most 4 slots.
-template <int CHUNK, int ES>
+template <int CHUNK, int ES, bool DENSE>
 TFn tfn_slots(int slots, bool pipe) {
   switch (slots) {
-    case 1: return pipe ? tpick<CHUNK, ES, 1, true>() : tpick<CHUNK, ES, 1, false>();
-    case 2: return pipe ? tpick<CHUNK, ES, 2, true>() : tpick<CHUNK, ES, 2, false>();
-    case 4: return pipe ? tpick<CHUNK, ES, 4, true>() : tpick<CHUNK, ES, 4, false>();
-    case 8: return pipe ? nullptr : tpick<CHUNK, ES, 8, false>();
-    case 16: return pipe ? nullptr : tpick<CHUNK, ES, 16, false>();
+    case 1: return pipe ? tpick<CHUNK, ES, 1, true, DENSE>() : tpick<CHUNK, ES, 1, false, DENSE>();
+    case 2: return pipe ? tpick<CHUNK, ES, 2, true, DENSE>() : tpick<CHUNK, ES, 2, false, DENSE>();
+    case 4: return pipe ? tpick<CHUNK, ES, 4, true, DENSE>() : tpick<CHUNK, ES, 4, false, DENSE>();
+    case 8: return pipe ? nullptr : tpick<CHUNK, ES, 8, false, DENSE>();
+    case 16: return pipe ? nullptr : tpick<CHUNK, ES, 16, false, DENSE>();
   }
   return nullptr;
 }
 
-TFn tfn(const BlocksShape& shp) {
+template <bool DENSE>
+TFn tfn_plan(const BlocksShape& shp) {
   const bool pipe = shp.pipelined;
   if (shp.chunk == 16) {
     switch (shp.elem_bytes) {
-      case 1: return tfn_slots<16, 1>(shp.slots, pipe);
-      case 2: return tfn_slots<16, 2>(shp.slots, pipe);
-      case 4: return tfn_slots<16, 4>(shp.slots, pipe);
+      case 1: return tfn_slots<16, 1, DENSE>(shp.slots, pipe);
+      case 2: return tfn_slots<16, 2, DENSE>(shp.slots, pipe);
+      case 4: return tfn_slots<16, 4, DENSE>(shp.slots, pipe);
     }
   } else {
     switch (shp.elem_bytes) {
-      case 1: return tfn_slots<8, 1>(shp.slots, pipe);
-      case 2: return tfn_slots<8, 2>(shp.slots, pipe);
-      case 4: return tfn_slots<8, 4>(shp.slots, pipe);
+      case 1: return tfn_slots<8, 1, DENSE>(shp.slots, pipe);
+      case 2: return tfn_slots<8, 2, DENSE>(shp.slots, pipe);
+      case 4: return tfn_slots<8, 4, DENSE>(shp.slots, pipe);
     }
   }
   return nullptr;
 }
+
+// Every variant exists planned and planned in place.
+TFn tfn(const BlocksShape& shp) { return shp.dense ? tfn_plan<true>(shp) : tfn_plan<false>(shp); }
 
 }  // namespace
 
@@ -254,6 +260,7 @@ int tblocks_grid(const BlocksShape& shp, int device, int64_t max_tasks) {
   const int64_t waves_per_block = kBlockThreads / kWave;
   const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
   const int64_t cap = (int64_t)per_cu * device_cus(device);
+  if (shp.dense) return (int)(need > 0 ? need : 1);  // one task per wave (at most kDenseMaxTasks)
   return (int)(need < cap ? (need > 0 ? need : 1) : cap);
 }
 

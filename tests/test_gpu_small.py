@@ -22,10 +22,17 @@ from gpu_helpers import (DEV, SENTINEL, assert_match, assert_unlisted_untouched,
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["simple", "pipelined"])
+@pytest.fixture(params=["auto", "simple", "pipelined", "auto-compact"])
 def schedule(request, monkeypatch):
-    """Run the test under both main-pass schedules (KVCK_SCHEDULE)."""
-    monkeypatch.setenv("KVCK_SCHEDULE", request.param)
+    """Run the test under the library's own choices, under each main-pass
+    schedule forced (KVCK_SCHEDULE), and with every call's positions listed by
+    the plan launch first (KVCK_PLAN=compact) instead of small calls planning in
+    place."""
+    sched, _, plan = request.param.partition("-")
+    if sched != "auto":
+        monkeypatch.setenv("KVCK_SCHEDULE", sched)
+    if plan:
+        monkeypatch.setenv("KVCK_PLAN", plan)
     return request.param
 
 
@@ -195,6 +202,65 @@ def test_bad_block_id_and_bad_request_flagged():
     stale = torch.full((1,), kvck.KVCK_FLAG_BAD_BLOCK_ID, dtype=torch.int32, device=DEV)
     kvck.kvck_checksum_blocks([pool], "NHD", [0], bt, nbt, sp, nt, error_flags=stale, check=True)
     assert int(stale.item()) == 0
+
+
+@pytest.mark.parametrize("layout,ncaches", [("NHD", 1), ("NHD", 3), ("HND", 2), ("MLA", 4), ("HND", 70),
+                                            ("V_TRANS", 2)])
+def test_plan_in_place_matches_listed_plan(layout, ncaches, monkeypatch):
+    """Small calls read the request arrays in the main pass (no plan launch);
+    the result, the entries left untouched and the error bits must be those of
+    the listed plan, with bad requests, bad ids and past-end ids mixed in."""
+    log(f"[plan in place] {layout} caches {ncaches}")
+    rng = np.random.default_rng(zlib.crc32(f"inplace{layout}{ncaches}".encode()))
+    bs, nh, d = 16, 3, 64
+    req, nb = wl.page_requests(rng, [40, 0, 70, 33, 16, 90], bs, start_pos=[0, 0, 1, 0, 2, 0],
+                               extra_blocks=[1, 0, 0, 2, 0, 1], spare_frac=0.4)
+    pool_layout = "HND" if layout == "V_TRANS" else layout
+    heads = 1 if layout == "MLA" else nh
+    hp = [wl.host_random_bits(rng, wl.pool_shape(pool_layout, nb, bs, heads, 576 if layout == "MLA" else d), "bf16")
+          for _ in range(ncaches)]
+    if layout == "V_TRANS":
+        dev_pools = [to_device_bits(np.ascontiguousarray(p[1].transpose(0, 1, 3, 2))) for p in hp]
+    else:
+        dev_pools = [to_device_bits(p) for p in hp]
+    layers = [3 * i + 1 for i in range(ncaches)]
+    bt = req.block_table.copy()
+    nbpr = req.num_blocks.copy()
+    sp = req.start_pos.copy()
+    bt[0, 1] = nb + 3                      # a listed block with valid slots: flagged, contributes 0
+    bt[3, int(nbpr[3]) - 1] = -7           # past the last token: never read, not an error
+    nbpr[4] = req.max_blocks + 1           # bad request: lists nothing
+    sp[5] = -1                             # bad request: lists nothing
+    results = {}
+    for plan in ("auto", "compact"):
+        if plan == "compact":
+            monkeypatch.setenv("KVCK_PLAN", "compact")
+        else:
+            monkeypatch.delenv("KVCK_PLAN", raising=False)
+        out = torch.full((req.num_reqs, req.max_blocks), SENTINEL, dtype=torch.int64, device=DEV).view(torch.uint64)
+        flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+        kvck.kvck_checksum_blocks(dev_pools, layout, layers, torch.from_numpy(bt).to(DEV),
+                                  torch.from_numpy(nbpr).to(DEV), torch.from_numpy(sp).to(DEV),
+                                  torch.from_numpy(req.num_tokens).to(DEV), out=out, error_flags=flags)
+        torch.cuda.synchronize()
+        results[plan] = (out.cpu().numpy().view(np.uint64).reshape(req.num_reqs, req.max_blocks).copy(),
+                         int(flags.item()))
+    assert np.array_equal(results["auto"][0], results["compact"][0])
+    assert results["auto"][1] == results["compact"][1] == kvck.KVCK_FLAG_BAD_BLOCK_ID | kvck.KVCK_FLAG_BAD_REQUEST
+    got = results["auto"][0]
+    # the oracle on the same requests with the bad ones listing nothing and the bad id's block zeroed
+    ok = wl.Requests(bs, req.num_tokens, np.where(sp < 0, 0, sp), np.where(np.arange(req.num_reqs) >= 4, 0, nbpr)
+                     .astype(np.int32), np.where(bt < 0, 0, np.where(bt >= nb, 0, bt)).astype(np.int32))
+    # a V-only call is the checksum of the pool with its K plane zeroed
+    ref = [np.concatenate([np.zeros_like(p[:1]), p[1:]]) for p in hp] if layout == "V_TRANS" else hp
+    want = oracle.checksum_blocks(ref, pool_layout, layers, [0] * ncaches, ok.block_table, ok.num_blocks,
+                                  ok.start_pos, ok.num_tokens)
+    for r, k in ok.listed():
+        exp = 0 if (r, k) == (0, 1) else int(want[r, k])
+        assert int(got[r, k]) == exp, (r, k)
+    for r in (4, 5):
+        assert np.all(got[r] == np.uint64(SENTINEL))
+    assert_unlisted_untouched(got, ok)
 
 
 def test_host_rejects_before_launch():

@@ -4,8 +4,9 @@ listed position (GPU).
 Each case draws a layout (NHD, HND, FlashInfer-style, MLA, x-split K + V,
 K + element-transposed V), an element type, head count and size, block size,
 layer numbers up to the largest allowed, requests with start offsets, past-end
-positions and empty requests, an optional head subset, and a forced schedule
-or merge setting -- the corners where lane-table shapes and schedules change.
+positions and empty requests, an optional head subset, a forced schedule or
+merge setting, and sometimes the listed plan in place of planning in place --
+the corners where lane-table shapes and schedules change.
 The cases are fixed by the seed, so a failure names a reproducible case.
 """
 
@@ -49,6 +50,8 @@ def _case(i):
     base = int(rng.integers(0, 65536 - heads))
     env = [{}, {"KVCK_SCHEDULE": "simple"}, {"KVCK_SCHEDULE": "pipelined"}, {"KVCK_MERGE_HEADS": "1"},
            {"KVCK_MERGE_HEADS": "0"}][int(rng.integers(0, 5))]
+    if rng.random() < 0.3:
+        env = dict(env, KVCK_PLAN="compact")   # positions listed by the plan launch, not planned in place
     return dict(i=i, layout=layout, elem=elem, heads=heads, d=d, bs=bs, layers=layers, lengths=lengths,
                 start=start, extra=extra, hb=hb, hc=hc, base=base, env=env)
 
