@@ -14,11 +14,13 @@ alone (examples/kvck_demo.c).
 from __future__ import annotations
 
 import argparse
+import concurrent.futures as cf
 import glob
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -47,24 +49,41 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(save_temps: str | None = None, verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           *sources(), "-o", tmp]
-    cwd = None
-    if save_temps:
-        os.makedirs(save_temps, exist_ok=True)
-        cmd.insert(1, "-save-temps")
-        cwd = save_temps
+def _run(cmd, verbose, cwd=None):
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True, cwd=cwd)
-    os.replace(tmp, LIB)
-    # the plain-read bandwidth probe the benchmark's roofline discussion refers to
-    probe_tmp = PROBE + ".tmp"
-    subprocess.run([hipcc(), *[f for f in HIP_FLAGS if f not in ("-shared", "-fPIC", "-fvisibility=hidden")],
-                    os.path.join(PKG, "probe", "hbm_read_probe.hip"), "-o", probe_tmp], check=True)
-    os.replace(probe_tmp, PROBE)
+
+
+def build(save_temps: str | None = None, verbose: bool = False) -> str:
+    """Compile every source to an object in parallel (the kernel variants make
+    single files slow), link libkvck.so, then the probe and the C demo."""
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
+    if save_temps:
+        os.makedirs(save_temps, exist_ok=True)
+    with tempfile.TemporaryDirectory(prefix="kvck_build_") as objdir:
+        jobs = []
+        for src in sources():
+            obj = os.path.join(objdir, os.path.basename(src) + ".o")
+            cmd = [hipcc(), *compile_flags, *inc, "-c", src, "-o", obj]
+            if save_temps:
+                cmd.insert(1, "-save-temps")
+            jobs.append((cmd, obj))
+        # the plain-read bandwidth probe the benchmark's roofline discussion refers to
+        probe_tmp = PROBE + ".tmp"
+        probe_cmd = [hipcc(), *[f for f in HIP_FLAGS if f not in ("-shared", "-fPIC", "-fvisibility=hidden")],
+                     os.path.join(PKG, "probe", "hbm_read_probe.hip"), "-o", probe_tmp]
+        workers = max(1, min(len(jobs) + 1, os.cpu_count() or 1, 8))
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            futs = [ex.submit(_run, cmd, verbose, save_temps) for cmd, _ in jobs]
+            futs.append(ex.submit(_run, probe_cmd, verbose))
+            for f in futs:
+                f.result()
+        tmp = LIB + ".tmp"
+        _run([hipcc(), *HIP_FLAGS, *[obj for _, obj in jobs], "-o", tmp], verbose)
+        os.replace(tmp, LIB)
+        os.replace(probe_tmp, PROBE)
     # a plain C consumer of the C ABI (gcc, C99): no Python or torch involved
     demo_tmp = DEMO + ".tmp"
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
