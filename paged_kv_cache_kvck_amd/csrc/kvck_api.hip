@@ -134,7 +134,7 @@ void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_ca
   const bool one_task = dense && !copy && !shp->merged && cand != nullptr && num_caches <= lpt;
   bool pipe = (fits && num_caches > 1 && tasks >= kPipeMinTasksPerWave * waves) || one_task;
   // KVCK_SCHEDULE=pipelined|simple overrides the choice (results are identical
-  // either way); merged rows always run the unpipelined kernel
+  // either way); merged rows always run the unpipelined checksum kernel
   if (const char* force = getenv("KVCK_SCHEDULE")) {
     if (strcmp(force, "pipelined") == 0) pipe = true;
     if (strcmp(force, "simple") == 0) pipe = false;
@@ -158,7 +158,7 @@ void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_ca
     shp->caches_per_task = lpt;
     // a unit holds 16/S head slots; with half of them or fewer used, carry K and V together
     const int hu = 16 / shp->slots;
-    if (planes == 2 && shp->slots <= 4 && 2 * heads <= hu) shp->planes_per_unit = 2;
+    if (planes == 2 && shp->slots <= 4 && 2 * heads <= hu && !shp->merged) shp->planes_per_unit = 2;
   }
 }
 
@@ -321,10 +321,13 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
     if (chunk == 8) return KVCK_ERR_MISALIGNED;
     chunk = 8;
   }
-  // merged rows: the call's heads of one slot side by side, read as one row
+  // merged rows: the call's heads of one slot side by side, read (and, for the
+  // fused copy, written on the pool side) as one row
   const int64_t wide = (int64_t)head_count * L.row_bytes;
-  const bool can_merge = mode == kModeChecksum && runs == 1 && head_count > 1 && L.head_stride == L.row_bytes &&
-                         wide <= (int64_t)kWave * 16 * chunk;
+  // (a merged copy's staging offsets are 32-bit across a plane's head images)
+  const bool can_merge = !transposed && runs == 1 && head_count > 1 && L.head_stride == L.row_bytes &&
+                         wide <= (int64_t)kWave * 16 * chunk &&
+                         (mode == kModeChecksum || (int64_t)L.block_size * wide < ((int64_t)1 << 31));
   bool merged = can_merge && L.row_bytes < kMergeBelowRowBytes;
   // KVCK_MERGE_HEADS=0|1 overrides the choice where merging is possible (results are identical)
   if (const char* force = getenv("KVCK_MERGE_HEADS")) merged = can_merge && force[0] == '1';

@@ -13,7 +13,10 @@
 //
 // The kernel is the pipelined main pass with a second lane table for the
 // staging side: unit i+1's loads are in flight while unit i is stored to the
-// other side and folded into the checksum.
+// other side and folded into the checksum.  MERGED: pools whose heads sit side
+// by side in a slot with short rows are walked as one row per slot (as in the
+// checksum pass), and each lane chunk's staging offset lands in its own head's
+// image rows.
 #include "kvck_device.h"
 
 namespace kvck {
@@ -28,7 +31,7 @@ __device__ __forceinline__ void store_chunk(__amdgpu_buffer_rsrc_t r, uint32_t o
     __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kNonTemporal);
 }
 
-template <int CHUNK, int S, int HU, int PU, int DIR, bool PIPE>
+template <int CHUNK, int S, int HU, int PU, int DIR, bool PIPE, bool MERGED>
 __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) {
   using V = typename ChunkType<CHUNK>::T;
   const BlocksArgs& a = ca.b;
@@ -43,18 +46,26 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
 
   LaneTable<S> lt;
   lt.template init<CHUNK>(lane, a);
+  uint32_t lhead[S];  // local head of each lane chunk (merged rows only)
+  if constexpr (MERGED) lt.heads(lane, a, lhead);
+  const int64_t img_head = (int64_t)ca.block_size * a.row_bytes;
+  const int64_t img_plane = ca.image_bytes / a.planes;  // head_count images of one plane
   uint32_t ioff[S];  // staging-side offsets of the same chunks: rows are row_bytes apart
 #pragma unroll
   for (int s = 0; s < S; ++s) {
     const LaneChunk q = lane_chunk(lane + kWave * s, a);
-    ioff[s] = (uint32_t)((int64_t)q.r * a.row_bytes + (int64_t)(q.run * a.chunks_per_run + q.cr) * CHUNK);
+    const int c = q.run * a.chunks_per_run + q.cr;  // chunk of the (merged) row
+    if constexpr (MERGED) {
+      const int cin = c - (int)lhead[s] * a.chunks_per_head;
+      ioff[s] = (uint32_t)((int64_t)lhead[s] * img_head + (int64_t)q.r * a.row_bytes + (int64_t)cin * CHUNK);
+    } else {
+      ioff[s] = (uint32_t)((int64_t)q.r * a.row_bytes + (int64_t)c * CHUNK);
+    }
   }
   const uint64_t P = (uint64_t)a.pieces;
   const int rg = a.rows_per_group;
   const uint64_t plane_term = 2ull * (P / (uint64_t)a.planes_total);
   const int nhb = (a.heads + HU - 1) / HU;
-  const int64_t img_head = (int64_t)ca.block_size * a.row_bytes;
-  const int64_t img_plane = img_head * a.heads;
 
   for (int64_t task = wave; task < total; task += nwaves) {
     const int64_t grp = task / n_items;
@@ -124,14 +135,19 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
                                  x[p][h][s]);
               const uint64_t u = up + lt.urel[s];
               const uint64_t xa = (uint64_t)x[p][h][s].x | ((uint64_t)x[p][h][s].y << 32);
+              uint64_t t;
               if constexpr (CHUNK == 16) {
                 const uint64_t xb = (uint64_t)x[p][h][s].z | ((uint64_t)x[p][h][s].w << 32);
-                sh += (xa + xb) * u + (xb << 1);
+                t = (xa + xb) * u + (xb << 1);
               } else {
-                sh += xa * u;
+                t = xa * u;
               }
+              if constexpr (MERGED)
+                acc += t * (uint64_t)(mb + 2u * lhead[s]);
+              else
+                sh += t;
             }
-            acc += sh * (uint64_t)(mb + 2u * (uint32_t)hh);
+            if constexpr (!MERGED) acc += sh * (uint64_t)(mb + 2u * (uint32_t)hh);
           }
         }
         cc.next(nhb, nplanes, ngr);
@@ -170,27 +186,31 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
 
 using CopyFn = void (*)(const CopyArgs);
 
-template <int CHUNK, int S, int PU, int DIR>
+template <int CHUNK, int S, int PU, int DIR, bool MERGED>
 CopyFn pick(bool pipe) {
-  constexpr int hu = 16 / (S * PU) > 0 ? 16 / (S * PU) : 1;
-  return pipe ? &copy_kernel<CHUNK, S, hu, PU, DIR, true> : &copy_kernel<CHUNK, S, hu, PU, DIR, false>;
+  constexpr int hu = MERGED ? 1 : (16 / (S * PU) > 0 ? 16 / (S * PU) : 1);
+  return pipe ? &copy_kernel<CHUNK, S, hu, PU, DIR, true, MERGED> : &copy_kernel<CHUNK, S, hu, PU, DIR, false, MERGED>;
 }
 
-template <int CHUNK, int PU, int DIR>
+template <int CHUNK, int PU, int DIR, bool MERGED = false>
 CopyFn copy_fn_slots(int slots, bool pipe) {
   switch (slots) {
-    case 1: return pick<CHUNK, 1, PU, DIR>(pipe);
-    case 2: return pick<CHUNK, 2, PU, DIR>(pipe);
-    case 4: return pick<CHUNK, 4, PU, DIR>(pipe);
-    case 8: return pick<CHUNK, 8, 1, DIR>(pipe);
-    case 16: return pick<CHUNK, 16, 1, DIR>(pipe);
+    case 1: return pick<CHUNK, 1, PU, DIR, MERGED>(pipe);
+    case 2: return pick<CHUNK, 2, PU, DIR, MERGED>(pipe);
+    case 4: return pick<CHUNK, 4, PU, DIR, MERGED>(pipe);
+    case 8: return pick<CHUNK, 8, 1, DIR, MERGED>(pipe);
+    case 16: return pick<CHUNK, 16, 1, DIR, MERGED>(pipe);
   }
   return nullptr;
 }
 
+// Merged rows take one plane per unit.
 template <int DIR>
 CopyFn copy_fn_dir(const BlocksShape& shp) {
   const bool pipe = shp.copy_buffers == 2;
+  if (shp.merged)
+    return shp.chunk == 16 ? copy_fn_slots<16, 1, DIR, true>(shp.slots, pipe)
+                           : copy_fn_slots<8, 1, DIR, true>(shp.slots, pipe);
   if (shp.planes_per_unit == 2)
     return shp.chunk == 16 ? copy_fn_slots<16, 2, DIR>(shp.slots, pipe) : copy_fn_slots<8, 2, DIR>(shp.slots, pipe);
   return shp.chunk == 16 ? copy_fn_slots<16, 1, DIR>(shp.slots, pipe) : copy_fn_slots<8, 1, DIR>(shp.slots, pipe);

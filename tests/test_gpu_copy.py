@@ -27,6 +27,7 @@ CASES = [
     ("mla_bs64", "MLA", "bf16", [0, 1, 60], 1, 576, 64, [130, 64, 3], None, None, 0, None),
     ("nhd_8byte_rows", "NHD", "bf16", [0, 3], 3, 4, 4, [13, 6], None, None, 0, None),
     ("nhd_bs64_fp16", "NHD", "fp16", [0, 1], 12, 64, 64, [300, 65], None, None, 0, None),
+    ("nhd_fp8_shard", "NHD", "fp8", [2, 7], 6, 32, 16, [60, 21], None, [0, 1], 1, 3),
 ]
 
 
@@ -56,10 +57,15 @@ def _expected_images(pools, layout, req, head_begin, head_count, bs, row_bytes):
     return img
 
 
-@pytest.fixture(params=["1", "2"])
+@pytest.fixture(params=["1", "2", "1-merge0", "2-merge1"])
 def copy_buffers(request, monkeypatch):
-    """Run the test with one unit buffer per wave and with two (KVCK_COPY_BUFFERS)."""
-    monkeypatch.setenv("KVCK_COPY_BUFFERS", request.param)
+    """Run the test with one unit buffer per wave and with two
+    (KVCK_COPY_BUFFERS), under the library's choice of reading a slot's heads as
+    one row, and with that choice forced off or on (KVCK_MERGE_HEADS)."""
+    buffers, _, merge = request.param.partition("-merge")
+    monkeypatch.setenv("KVCK_COPY_BUFFERS", buffers)
+    if merge:
+        monkeypatch.setenv("KVCK_MERGE_HEADS", merge)
     return request.param
 
 

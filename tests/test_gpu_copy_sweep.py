@@ -40,15 +40,17 @@ def _case(i):
     hb = int(rng.integers(0, heads))
     hc = int(rng.integers(1, heads - hb + 1))
     buffers = ["1", "2"][int(rng.integers(0, 2))]
+    merge = [None, "0", "1"][int(rng.integers(0, 3))]   # a slot's heads read as one row: auto, off, on
     return dict(i=i, layout=layout, elem=elem, heads=heads, d=d, bs=bs, layers=layers, lengths=lengths,
-                start=start, extra=extra, hb=hb, hc=hc, buffers=buffers)
+                start=start, extra=extra, hb=hb, hc=hc, buffers=buffers, merge=merge)
 
 
 CASES = [_case(i) for i in range(40)]
 
 
 def _ids(c):
-    return f"{c['i']}-{c['layout']}-{c['elem']}-h{c['heads']}-d{c['d']}-bs{c['bs']}-b{c['buffers']}"
+    return (f"{c['i']}-{c['layout']}-{c['elem']}-h{c['heads']}-d{c['d']}-bs{c['bs']}-b{c['buffers']}"
+            f"-m{c['merge'] or 'auto'}")
 
 
 def _rows(pool, layout, pl, b, v, hb, n):
@@ -83,6 +85,8 @@ def _images(pools, layout, req, hb, n, bs, row_bytes):
 @pytest.mark.parametrize("case", CASES, ids=_ids)
 def test_copy_sweep_case(case, monkeypatch):
     monkeypatch.setenv("KVCK_COPY_BUFFERS", case["buffers"])
+    if case["merge"] is not None:
+        monkeypatch.setenv("KVCK_MERGE_HEADS", case["merge"])
     log(f"[copy sweep] {_ids(case)} heads {case['hb']}+{case['hc']}")
     rng = np.random.default_rng(2000 + case["i"])
     layout, bs, nh, d, layers = case["layout"], case["bs"], case["heads"], case["d"], case["layers"]
