@@ -2,11 +2,14 @@
 text summaries kept under ``profiles/``.
 
     python -m paged_kv_cache_kvck_amd.rocpd_summary \\
-        --trace T.db [--fetch F.db --write W.db --copy-bytes N] \\
+        --trace T.db [--fetch F.db --write W.db --copy-bytes N] [--kernel NAME] \\
         --workload llama3_8b --main-calls 12 --command "..." --out-md profiles/X.md [--out-json profiles/Y.json]
 
+* ``--kernel``: the kernel summarized (a substring of its name; default the
+  main pass, ``blocks_kernel``); ``--valid-bytes`` are its algorithmic bytes
+  per launch.
 * ``--trace``: kernel-trace database; per-kernel calls / average / min / max
-  durations.  The first ``--main-calls`` dispatches of the main-pass kernel
+  durations.  The first ``--main-calls`` dispatches of the summarized kernel
   are the timed workload (warm-up + steps); later ones (e.g. the TP-shard
   run) are listed separately.
 * ``--fetch`` / ``--write``: ``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``
@@ -61,34 +64,44 @@ def main(argv=None):
     ap.add_argument("--command", required=True, help="the rocprofv3 commands that made the databases")
     ap.add_argument("--out-md", required=True)
     ap.add_argument("--out-json")
+    ap.add_argument("--kernel", default=MAIN, help="substring of the summarized kernel's name")
+    ap.add_argument("--copy-kernel", action="store_true",
+                    help="the kernel reads and writes --valid-bytes (fused copy): throughput counts both")
+    ap.add_argument("--later-label", default="later calls: TP-shard run",
+                    help="label of the kernel's dispatches after --main-calls")
+    ap.add_argument("--label", help="display name of the kernel (default: --kernel)")
     a = ap.parse_args(argv)
+    kernel = a.kernel
+    label = a.label or kernel
 
     rows = _kernels(a.trace)
     groups = {}
     main_durs = []
     for name, dur, _ in rows:
-        if MAIN in name:
+        if kernel in name:
             main_durs.append(dur)
             continue
         groups.setdefault(_short(name), []).append(dur)
-    lines = [f"# rocprofv3 summary: {MAIN} on the {a.workload} workload", "", "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
+    lines = [f"# rocprofv3 summary: {label} on the {a.workload} workload", "", "Commands (run from /tmp with TMPDIR=/tmp; R = repository root):", "",
              "```", a.command.strip(), "```", "", "## Kernel trace (`--kernel-trace --stats`)", "",
              "| kernel | calls | avg ms | min ms | max ms |", "|---|---|---|---|---|"]
     head = main_durs[:a.main_calls]
     rest = main_durs[a.main_calls:]
     n, avg, mn, mx = _stats(head)
-    lines.append(f"| {MAIN} (workload: warm-up + timed steps) | {n} | {avg:.4f} | {mn:.4f} | {mx:.4f} |")
+    lines.append(f"| {label} (workload: warm-up + timed steps) | {n} | {avg:.4f} | {mn:.4f} | {mx:.4f} |")
     if rest:
         n2, avg2, mn2, mx2 = _stats(rest)
-        lines.append(f"| {MAIN} (later calls: TP-shard run) | {n2} | {avg2:.4f} | {mn2:.4f} | {mx2:.4f} |")
+        lines.append(f"| {label} ({a.later_label}) | {n2} | {avg2:.4f} | {mn2:.4f} | {mx2:.4f} |")
     for k, d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
         n3, a3, m3, x3 = _stats(d)
         lines.append(f"| {k} | {n3} | {a3:.4f} | {m3:.4f} | {x3:.4f} |")
     timed = head[a.warmup:] or head
     t_avg = statistics.mean(timed) / 1e6
-    lines += ["", f"Main pass, timed calls only: average {t_avg:.4f} ms -> "
-                  f"{a.valid_bytes / (t_avg * 1e-3) / 1e9:.1f} GB/s of valid KV bytes "
-                  f"({a.valid_bytes} B per launch), {a.valid_bytes / (t_avg * 1e-3) / 8e12 * 100:.1f} % of 8 TB/s."]
+    moved = a.valid_bytes * (2 if a.copy_kernel else 1)
+    what = "bytes moved (valid bytes read + written)" if a.copy_kernel else "valid bytes"
+    lines += ["", f"{label}, timed calls only: average {t_avg:.4f} ms -> "
+                  f"{moved / (t_avg * 1e-3) / 1e9:.1f} GB/s of {what} "
+                  f"({moved} B per launch), {moved / (t_avg * 1e-3) / 8e12 * 100:.1f} % of 8 TB/s."]
     traffic = None
     if a.fetch and a.write and a.copy_bytes:
         res = {}
@@ -98,25 +111,26 @@ def main(argv=None):
             copy = [r[2] for r in ev if "copyBuffer" in r[0] and "kvck" not in r[0]]
             copy_kib = max(copy)
             factor = a.copy_bytes / (copy_kib * 1024.0)
-            main = [r[2] for r in ev if MAIN in r[0]]
+            main = [r[2] for r in ev if kernel in r[0]][:a.main_calls]
             kib = statistics.mean(main)
             res[which] = dict(counter=counter, copy_kib=copy_kib, factor=factor, main_kib=kib,
                               bytes=kib * 1024.0 * factor, launches=len(main))
         traffic = res["fetch"]["bytes"] + res["write"]["bytes"]
         lines += ["", "## HBM traffic (`--pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, separate runs)", "",
-                  "| counter | plain copy reads (KiB) | copy bytes | scale | main pass per launch (KiB) | scaled bytes |",
+                  f"| counter | plain copy reads (KiB) | copy bytes | scale | {label} per launch (KiB) | scaled bytes |",
                   "|---|---|---|---|---|---|"]
         for which in ("fetch", "write"):
             r = res[which]
             lines.append(f"| {r['counter']} | {r['copy_kib']:.0f} | {a.copy_bytes} | {r['factor']:.4f} | "
                          f"{r['main_kib']:.0f} | {r['bytes']:.4e} |")
-        lines += ["", f"HBM bytes per launch: {traffic:.4e}; algorithmic (valid KV) bytes {a.valid_bytes:.4e}; "
-                      f"fetched / algorithmic = {res['fetch']['bytes'] / a.valid_bytes:.4f}."]
+        lines += ["", f"HBM bytes per launch: {traffic:.4e}; algorithmic (valid) bytes read {a.valid_bytes:.4e}; "
+                      f"fetched / algorithmic = {res['fetch']['bytes'] / a.valid_bytes:.4f}; "
+                      f"written / algorithmic = {res['write']['bytes'] / a.valid_bytes:.4f}."]
         if a.out_json:
             sys.path.insert(0, ROOT)
             import bench
             with open(a.out_json, "w") as f:
-                json.dump({"workload": a.workload, "kernel": MAIN, "kernel_sources_sha256": bench.kernel_sources_sha(),
+                json.dump({"workload": a.workload, "kernel": kernel, "kernel_sources_sha256": bench.kernel_sources_sha(),
                            "fetch_bytes_per_launch": res["fetch"]["bytes"],
                            "write_bytes_per_launch": res["write"]["bytes"],
                            "fetch_scale": res["fetch"]["factor"], "write_scale": res["write"]["factor"],
