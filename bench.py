@@ -187,6 +187,7 @@ def main(argv=None):
     ap.add_argument("--no-shard", action="store_true", help="skip the TP-shard timing")
     ap.add_argument("--no-states", action="store_true", help="skip the Mamba-state timing")
     ap.add_argument("--no-copy", action="store_true", help="skip the fused copy + checksum timing")
+    ap.add_argument("--no-small", action="store_true", help="skip the tiny-call latency timing")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="after timing, run one plain device copy of this many GiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -353,6 +354,31 @@ def main(argv=None):
                                  "main_pass_GB_per_s": sb / (smain / max(sc, 1) * 1e-3) / 1e9}
         del states
     kvck.kvck_instrument(False)
+    if not args.no_small:
+        # the tiny configuration (one 50-token request on 4 blocks, 2 layers x 2 heads): latency-bound,
+        # so each call is timed on its own, event to event, with caches prepared as a hot loop would
+        from paged_kv_cache_kvck_amd import workloads as wl
+        tw = wl.tiny()
+        tpools = tw.device_pools()
+        tr = tw.req
+        tt = [torch.from_numpy(x).to(dev) for x in (tr.block_table, tr.num_blocks, tr.start_pos, tr.num_tokens)]
+        tout = torch.zeros((tr.num_reqs, tr.max_blocks), dtype=torch.uint64, device=dev)
+        tws = torch.empty(kvck.kvck_blocks_workspace_bytes(tw.num_layers, tr.num_reqs, tr.max_blocks),
+                          dtype=torch.uint8, device=dev)
+        tpc = kvck.prepare_caches(tpools, tw.layout, tw.layer_numbers)
+        lat = []
+        for i in range(60):
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            kvck.kvck_checksum_blocks(tpc, None, None, *tt, out=tout, workspace=tws, stream=stream)
+            t1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 10:
+                lat.append(t0.elapsed_time(t1) * 1e3)
+        extra["tiny_call_latency"] = {"workload": "2 layers x 2 KV heads x head 64 bf16, block 16, NHD, one 50-token "
+                                                  "request on 4 blocks (51,200 valid bytes)",
+                                      "us_median": statistics.median(lat), "us_min": min(lat), "calls": len(lat)}
+        del tpools, tpc
     if args.copy_calibration_gib > 0:
         n = int(args.copy_calibration_gib * (1 << 30))
         a = torch.empty(n, dtype=torch.uint8, device=dev)
