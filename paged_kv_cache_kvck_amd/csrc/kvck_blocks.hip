@@ -6,17 +6,19 @@
 //   c(position)    = sum_{layer, head} m s,  m = 2 (layer*65536 + global_head) + 1
 // all mod 2^64.
 //
-// Three launches per call, all on the caller's stream:
+// Up to three launches per call, all on the caller's stream:
 //   plan    request arrays -> compact list of listed positions (PosRecord):
 //           block id, first token t0 = pos*block_size, valid slots
 //           v = min(block_size, max(0, num_tokens - t0)) (page helper
 //           num_valid_tokens), output index.  Bad ids and requests are flagged.
-//   blocks  one wavefront per task (cache, position): streams the valid rows of
-//           the block's pages with 16-byte loads and accumulates
+//           Small calls skip it: their main pass (the DENSE variants) derives
+//           each task's record from the request arrays with the same rules.
+//   blocks  one wavefront per task (group of caches, position): streams the
+//           valid rows of the block's pages with 16-byte loads and accumulates
 //           sum over pieces of x * m * (2j + 1) in 64-bit registers, then
 //           reduces the 64 lanes and writes one uint64 per task.
-//   reduce  sums the per-cache partials of each position in a fixed order
-//           (skipped when the call has one cache).  Addition mod 2^64 is
+//   reduce  sums the per-group partials of each position in a fixed order
+//           (skipped when the call has one group).  Addition mod 2^64 is
 //           associative and commutative, so results are bit-exact whatever
 //           the task order or launch shape.
 #include <atomic>
@@ -179,6 +181,9 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
 //               lane-table row is the slot's whole run of heads, so a load
 //               instruction covers contiguous bytes even when one head's row
 //               is short; each chunk carries its own head's factor m.
+// DENSE:        a call planned in place: tasks index every (request, block
+//               slot) and each wave runs exactly one task (the grid covers them
+//               all), so no request pointer stays live across the unit loop.
 template <int CHUNK, int S, int HU, int PU, bool PIPE, bool MERGED, bool DENSE>
 __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs a) {
   using V = typename ChunkType<CHUNK>::T;

@@ -18,6 +18,7 @@
 // main pass; a unit is HU heads x S chunks per lane of one element-row group,
 // with the same out-of-range buffer offsets masking unused lanes and heads.
 // PIPE: two unit buffers in ping-pong, as in the main pass's pipelined kernel.
+// DENSE: planned in place, one task per wave, as in the main pass.
 #include "kvck_device.h"
 
 namespace kvck {
