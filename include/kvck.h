@@ -118,8 +118,8 @@ typedef struct kvck_kv_layout {
    * element-transposed plane [num_blocks, num_heads, head_size, block_size]
    * (the V layout of ROCm's paged-attention kernels): chunk_stride =
    * block_size*element bytes, slot_stride = chunk_bytes.  Such calls cover one
-   * plane (plane_count 1), need block_size*element bytes to be a multiple of
-   * 8, and are not accepted by kvck_copy_checksum_blocks
+   * plane (plane_count 1) and need block_size*element bytes to be a multiple
+   * of 8; kvck_copy_checksum_blocks also needs block_size <= 1024
    * (KVCK_ERR_UNSUPPORTED otherwise). */
   int32_t chunk_bytes;
   int32_t reserved0;
@@ -250,8 +250,10 @@ size_t kvck_states_workspace_bytes(int32_t num_layers, int32_t row_count, int32_
  * per entry); only the valid slots of the position are copied, in either
  * direction, and the rest of the image and of the pool block is left as is.
  * Entries past staging_positions are flagged KVCK_FLAG_STAGING_FULL and
- * skipped.  A load needs the same layout, heads and request structure as the
- * save that filled the staging buffer.
+ * skipped.  A load needs the same planes, heads and request structure as the
+ * save that filled the staging buffer; the image does not depend on the pool
+ * layout, so a block saved from one layout (say an element-transposed V plane)
+ * loads into another (an HND V plane).
  */
 kvck_status kvck_copy_checksum_blocks(
     int32_t direction,                     /* KVCK_COPY_SAVE or KVCK_COPY_LOAD */

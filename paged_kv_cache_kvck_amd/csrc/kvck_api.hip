@@ -277,7 +277,6 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   if (transposed) {
     if ((run_bytes != 1 && run_bytes != 2 && run_bytes != 4) || L.slot_stride != run_bytes)
       return KVCK_ERR_UNSUPPORTED;
-    if (mode != kModeChecksum) return KVCK_ERR_UNSUPPORTED;  // the fused copy takes rows of whole pieces
     if (L.chunk_stride < (int64_t)L.block_size * run_bytes) return KVCK_ERR_INVALID_ARGUMENT;
     // an element row of the block must hold whole 8-byte loads
     if (((int64_t)L.block_size * run_bytes) % 8 != 0) return KVCK_ERR_UNSUPPORTED;
@@ -311,7 +310,9 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   int chunk = 16;
   for (int pass = 0; pass < 2; ++pass) {
     // transposed rows: a chunk holds one element index of chunk/run_bytes slots
-    const bool rows_ok = transposed ? ((int64_t)L.block_size * run_bytes) % chunk == 0
+    // (and, for the fused copy, chunk/run_bytes elements of one staging row)
+    const bool rows_ok = transposed ? ((int64_t)L.block_size * run_bytes) % chunk == 0 &&
+                                          (mode == kModeChecksum || L.row_bytes % chunk == 0)
                                     : run_bytes % chunk == 0 && (L.block_size == 1 || L.slot_stride % chunk == 0);
     bool ok = rows_ok && L.block_stride % chunk == 0 && (planes_cov == 1 || L.plane_stride % chunk == 0) &&
               (L.num_heads == 1 || L.head_stride % chunk == 0) && (runs == 1 || L.chunk_stride % chunk == 0);
@@ -341,9 +342,12 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
     const int64_t max_chunks = (int64_t)kWave * 16;
     if (cpe > max_chunks) return KVCK_ERR_UNSUPPORTED;
     const int64_t D = L.row_bytes / run_bytes;
-    const int64_t rge_max = max_chunks / cpe;
+    // the fused copy transposes whole N x N tiles (N = chunk/run_bytes): groups of whole tile rows
+    const int64_t unit = mode == kModeChecksum ? 1 : chunk / run_bytes;
+    const int64_t rge_max = max_chunks / cpe / unit * unit;
+    if (rge_max < 1) return KVCK_ERR_UNSUPPORTED;
     const int64_t groups = (D + rge_max - 1) / rge_max;
-    const int64_t rge = (D + groups - 1) / groups;
+    const int64_t rge = ((D + groups - 1) / groups + unit - 1) / unit * unit;  // <= rge_max
     const int64_t need = (rge * cpe + kWave - 1) / kWave;
     int s = 1;
     while (s < need) s <<= 1;
@@ -471,8 +475,13 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
       ca.num_caches_total = num_caches;
       ca.cache_offset = c0;
       ca.block_size = L.block_size;
-      const int grid = copy_grid(shp, mode, dev, tasks);
-      if (launch_copy(ca, shp, mode, grid, st) != hipSuccess) return KVCK_ERR_HIP;
+      if (transposed) {
+        const int grid = tcopy_grid(shp, mode, dev, tasks);
+        if (launch_tcopy(ca, shp, mode, grid, st) != hipSuccess) return KVCK_ERR_HIP;
+      } else {
+        const int grid = copy_grid(shp, mode, dev, tasks);
+        if (launch_copy(ca, shp, mode, grid, st) != hipSuccess) return KVCK_ERR_HIP;
+      }
     }
   }
   if (timed && hipEventRecord(ev1, st) != hipSuccess) return KVCK_ERR_HIP;

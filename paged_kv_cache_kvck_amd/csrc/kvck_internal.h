@@ -146,6 +146,8 @@ hipError_t launch_tblocks(const BlocksArgs& a, const BlocksShape& shp, int grid,
 int tblocks_grid(const BlocksShape& shp, int device, int64_t max_tasks);
 hipError_t launch_copy(const CopyArgs& a, const BlocksShape& shp, int direction, int grid, hipStream_t stream);
 int copy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks);
+hipError_t launch_tcopy(const CopyArgs& a, const BlocksShape& shp, int direction, int grid, hipStream_t stream);
+int tcopy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks);
 hipError_t launch_tags(const uint64_t* checksums, const uint8_t* hashes, int64_t hash_stride, uint64_t fingerprint,
                        int64_t n, const int32_t* nbpr, int32_t max_blocks, uint64_t* tagged, const uint64_t* stored,
                        uint8_t* mismatch, uint32_t* count, hipStream_t stream);

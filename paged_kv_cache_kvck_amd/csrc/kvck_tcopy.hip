@@ -1,0 +1,311 @@
+// Fused copy + checksum of element-transposed K/V planes on gfx950: a
+// connector's save (pool -> staging) or load (staging -> pool) for planes
+// stored [num_blocks, num_heads, head_size, block_size] (ROCm's
+// paged-attention V layout), with the checksum of the vLLM API page
+// "vllm.distributed.kv_transfer.kv_checksum.checksum".
+//
+// The staging image is the same as for every other layout, [head][slot][row]
+// with a token's row its head_size elements in order, so a block saved from
+// one layout loads into another.  The pool holds the transpose of that image
+// per (block, head), so the copy transposes in registers: the image is cut
+// into N x N tiles of ES-byte elements (N = CHUNK / ES, the elements of one
+// 16- or 8-byte chunk), a tile is held by N consecutive lanes, one chunk each,
+// and a butterfly exchange between those lanes turns pool chunks (one element
+// index of N slots) into staging chunks (N elements of one slot) and back.
+// The checksum is taken on the pool-side form of each chunk, exactly as in the
+// element-transposed checksum pass.
+//
+// Valid slots only: a save reads pool chunks holding at least one valid slot
+// and stores the staging rows of valid slots; a load reads the staging rows of
+// valid slots and writes exactly their elements into the pool (a chunk that
+// straddles the last valid slot is written element by element).
+#include "kvck_tdevice.h"
+
+namespace kvck {
+namespace {
+
+// In-register transpose of an N x N tile (N = W * 4 / ES elements of ES bytes)
+// spread over N consecutive lanes, lane j holding row j in w[0..W): afterwards
+// lane j holds column j.  Stage d (a power of two below N) exchanges, between
+// lanes j and j ^ d, the elements whose index bit d differs from the lane's
+// bit d; after all stages element (j, e) sits at (e, j).
+template <int ES, int W>
+__device__ __forceinline__ void tile_transpose(uint32_t (&w)[W], int j) {
+  constexpr int EPD = 4 / ES;  // elements per 32-bit word
+  constexpr int N = W * EPD;
+#pragma unroll
+  for (int d = N / 2; d >= 1; d >>= 1) {
+    const bool hi = (j & d) != 0;
+    uint32_t p[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) p[i] = (uint32_t)__shfl_xor((int)w[i], d, kWave);
+    if (d >= EPD) {
+      // whole words: word i takes the partner's word i ^ dd where bit dd of i
+      // differs from the lane's bit
+      const int dd = d / EPD;
+      uint32_t n[W];
+#pragma unroll
+      for (int i = 0; i < W; ++i) n[i] = (((i & dd) != 0) != hi) ? p[i ^ dd] : w[i];
+#pragma unroll
+      for (int i = 0; i < W; ++i) w[i] = n[i];
+    } else {
+      // within words: blocks of d elements (8*ES*d bits) trade places
+      const int bits = 8 * ES * d;
+      const uint32_t lo = bits == 16 ? 0x0000ffffu : 0x00ff00ffu;  // blocks with element bit d clear
+#pragma unroll
+      for (int i = 0; i < W; ++i)
+        w[i] = hi ? (((p[i] >> bits) & lo) | (w[i] & ~lo)) : ((w[i] & lo) | ((p[i] & lo) << bits));
+    }
+  }
+}
+
+template <int CHUNK>
+__device__ __forceinline__ void store_chunk(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                            const typename ChunkType<CHUNK>::T& v) {
+  if constexpr (CHUNK == 16)
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kNonTemporal);
+  else
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kNonTemporal);
+}
+
+// Element k of a chunk (ES bytes, zero-extended).
+template <int ES, int W>
+__device__ __forceinline__ uint32_t element(const uint32_t (&w)[W], int k) {
+  constexpr int EPD = 4 / ES;
+  const uint32_t word = w[k / EPD];
+  return ES == 4 ? word : (word >> (8 * ES * (k % EPD))) & ((1u << (8 * ES)) - 1u);
+}
+
+template <int ES>
+__device__ __forceinline__ void store_element(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  if constexpr (ES == 4)
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kNonTemporal);
+  else if constexpr (ES == 2)
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)v, r, (int)off, 0, kNonTemporal);
+  else
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)v, r, (int)off, 0, kNonTemporal);
+}
+
+// DIR 0: save (pool -> staging); DIR 1: load (staging -> pool).
+template <int CHUNK, int ES, int S, int HU, int DIR>
+__global__ __launch_bounds__(kBlockThreads) void tcopy_kernel(const CopyArgs ca) {
+  using V = typename ChunkType<CHUNK>::T;
+  constexpr int N = CHUNK / ES;       // elements per chunk, either side
+  constexpr int W = CHUNK / 4;        // 32-bit words per chunk
+  constexpr int PER_PIECE = 8 / ES;   // elements per 8-byte piece
+  const BlocksArgs& a = ca.b;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  const int64_t n_items = (int64_t)*a.n_items;
+  const int lpt = a.caches_per_task;
+  const int ngroups = (a.num_caches + lpt - 1) / lpt;
+  const int64_t total = n_items * ngroups;
+  if (wave >= total) return;
+
+  // Tile table of one element-row group of a (block, head): lane chunk
+  // f = lane + 64 s is row j = f mod N of tile t = f / N, and tile t covers
+  // element rows [c N, c N + N) x slots [q N, q N + N).  Pool form: element
+  // row c N + j of slots q N.. (offset (c N + j) * chunk_stride + q * CHUNK);
+  // staging form: elements c N.. of slot q N + j (offset
+  // (q N + j) * row_bytes + c N ES).  Tiles are numbered along the side that
+  // is stored, so that a store instruction writes long runs: along staging
+  // rows for a save (c fastest), along pool element rows for a load (q fastest).
+  const int cpe = a.chunks_per_row;  // block_size / N
+  const int rge = a.rows_per_group;  // element rows per group, a multiple of N
+  const int ctiles = rge / N;        // tile rows of a group
+  const int j = lane % N;
+  uint32_t prow[S], crow[S], q0[S], poff[S], soff[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int f = lane + kWave * s;
+    const int t = f / N;
+    const int c = DIR == 0 ? t % ctiles : t / cpe;
+    const int q = DIR == 0 ? t / ctiles : t - c * cpe;
+    const bool in = f < rge * cpe;
+    prow[s] = in ? (uint32_t)(c * N + j) : 0x7fffffffu;  // pool-form element row (in the group)
+    crow[s] = in ? (uint32_t)(c * N) : 0x7fffffffu;      // staging-form first element (in the group)
+    q0[s] = (uint32_t)(q * N);                            // pool-form first slot
+    poff[s] = (uint32_t)((int64_t)(c * N + j) * a.chunk_stride + (int64_t)q * CHUNK);
+    soff[s] = (uint32_t)((int64_t)(q * N + j) * a.row_bytes + (int64_t)c * N * ES);
+  }
+  const int D = a.row_bytes / ES;
+  const int ngr = (D + rge - 1) / rge;
+  const uint64_t P = (uint64_t)a.pieces;
+  const int nhb = (a.heads + HU - 1) / HU;
+  const int64_t img_head = (int64_t)ca.block_size * a.row_bytes;
+
+  for (int64_t task = wave; task < total; task += nwaves) {
+    const int64_t grp = task / n_items;
+    const int64_t item = task - grp * n_items;
+    const int c_begin = (int)grp * lpt;
+    const int c_end = min(a.num_caches, c_begin + lpt);
+    const TaskRecord rec = task_record<false>(a, item, false, lane);
+    int32_t v = rec.valid;
+    const uint64_t t0 = rec.t0;
+    if (item >= ca.staging_positions) {
+      if (v > 0 && lane == 0 && ca.error_flags) atomicOr(ca.error_flags, KVCK_FLAG_STAGING_FULL);
+      v = 0;
+    }
+    uint64_t acc = 0;
+    if (v > 0) {
+      const int64_t blk_off = (int64_t)rec.block * a.block_stride;
+      uint8_t* const img0 = ca.staging + (item * ca.num_caches_total + ca.cache_offset) * ca.image_bytes;
+      // valid slots of each pool-form chunk and its u before the element's piece
+      int nvalid[S];
+      uint64_t ubase[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int left = v - (int)q0[s];
+        nvalid[s] = left < 0 ? 0 : (left > N ? N : left);
+        ubase[s] = 2ull * (t0 + q0[s]) * P + 1ull + a.piece_base;
+      }
+      const bool straddle = (v % N) != 0;  // some chunk holds the last valid slot and invalid ones
+      const int nunits = (c_end - c_begin) * ngr * nhb;
+      int cache = c_begin, group = 0, hbatch = 0;
+      for (int ui = 0; ui < nunits; ++ui) {
+        const int rows = min(rge, D - group * rge);
+        const uint8_t* pgroup = a.base[cache] + blk_off + (int64_t)(group * rge) * a.chunk_stride;
+        uint8_t* sgroup = img0 + (int64_t)cache * ca.image_bytes + (int64_t)(group * rge) * ES;
+        V x[HU][S];
+        // loads: pool chunks holding a valid slot (save) or staging rows of valid slots (load)
+#pragma unroll
+        for (int h = 0; h < HU; ++h) {
+          const int hh = hbatch * HU + h;
+          const uint32_t hmask = hh < a.heads ? 0u : kOOB;
+          if constexpr (DIR == 0) {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(pgroup + (int64_t)hh * a.head_stride);
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+              x[h][s] = load_chunk<CHUNK>(rs, ((int)prow[s] < rows && (int)q0[s] < v ? poff[s] : kOOB) | hmask);
+          } else {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(sgroup + (int64_t)hh * img_head);
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+              x[h][s] = load_chunk<CHUNK>(rs, ((int)crow[s] < rows && (int)(q0[s] + j) < v ? soff[s] : kOOB) | hmask);
+          }
+        }
+        const uint32_t mb = a.mbase[cache];
+#pragma unroll
+        for (int h = 0; h < HU; ++h) {
+          const int hh = hbatch * HU + h;
+          const uint32_t hmask = hh < a.heads ? 0u : kOOB;
+          const __amdgpu_buffer_rsrc_t rp = make_rsrc(pgroup + (int64_t)hh * a.head_stride);
+          const __amdgpu_buffer_rsrc_t rst = make_rsrc(sgroup + (int64_t)hh * img_head);
+          uint64_t sh = 0;
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            uint32_t w[W];
+#pragma unroll
+            for (int i = 0; i < W; ++i) w[i] = x[h][s][i];
+            if constexpr (DIR == 1) tile_transpose<ES, W>(w, j);  // staging rows -> pool form
+            // checksum of the pool-form chunk: element row d of slots q0.. (masked lanes hold zeros)
+            {
+              V xv;
+#pragma unroll
+              for (int i = 0; i < W; ++i) xv[i] = w[i];
+              uint64_t E, K;
+              chunk_sums<ES>(xv, nvalid[s], E, K);
+              const uint32_t d = (uint32_t)(group * rge) + prow[s];
+              const uint64_t u0 = ubase[s] + 2ull * (d / PER_PIECE);
+              sh += (u0 * E + 2ull * P * K) << (8 * ES * (d % PER_PIECE));
+            }
+            if constexpr (DIR == 0) {
+              tile_transpose<ES, W>(w, j);  // pool form -> staging rows
+              V y;
+#pragma unroll
+              for (int i = 0; i < W; ++i) y[i] = w[i];
+              store_chunk<CHUNK>(rst, ((int)crow[s] < rows && (int)(q0[s] + j) < v ? soff[s] : kOOB) | hmask, y);
+            } else {
+              V y;
+#pragma unroll
+              for (int i = 0; i < W; ++i) y[i] = w[i];
+              const bool row_ok = (int)prow[s] < rows;
+              store_chunk<CHUNK>(rp, (row_ok && nvalid[s] == N ? poff[s] : kOOB) | hmask, y);
+              if (straddle) {  // uniform: the chunk holding the last valid slot, element by element
+                const bool part = row_ok && nvalid[s] > 0 && nvalid[s] < N;
+#pragma unroll
+                for (int k = 0; k < N - 1; ++k)
+                  store_element<ES>(rp, (part && k < nvalid[s] ? poff[s] + (uint32_t)(k * ES) : kOOB) | hmask,
+                                    element<ES, W>(w, k));
+              }
+            }
+          }
+          acc += sh * (uint64_t)(mb + 2u * (uint32_t)hh);
+        }
+        if (++hbatch == nhb) {
+          hbatch = 0;
+          if (++group == ngr) {
+            group = 0;
+            ++cache;
+          }
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      if (a.direct) {
+        uint64_t* o = a.out + rec.out_idx;
+        *o = a.accumulate ? *o + acc : acc;
+      } else {
+        a.partials[(int64_t)(a.group_offset + grp) * a.max_items + item] = acc;
+      }
+    }
+  }
+}
+
+using TCopyFn = void (*)(const CopyArgs);
+
+template <int CHUNK, int ES, int DIR>
+TCopyFn tcopy_slots(int slots) {
+  switch (slots) {
+    case 1: return &tcopy_kernel<CHUNK, ES, 1, 8, DIR>;
+    case 2: return &tcopy_kernel<CHUNK, ES, 2, 4, DIR>;
+    case 4: return &tcopy_kernel<CHUNK, ES, 4, 2, DIR>;
+    case 8: return &tcopy_kernel<CHUNK, ES, 8, 1, DIR>;
+    case 16: return &tcopy_kernel<CHUNK, ES, 16, 1, DIR>;
+  }
+  return nullptr;
+}
+
+template <int DIR>
+TCopyFn tcopy_dir(const BlocksShape& shp) {
+  if (shp.chunk == 16) {
+    switch (shp.elem_bytes) {
+      case 1: return tcopy_slots<16, 1, DIR>(shp.slots);
+      case 2: return tcopy_slots<16, 2, DIR>(shp.slots);
+      case 4: return tcopy_slots<16, 4, DIR>(shp.slots);
+    }
+  } else {
+    switch (shp.elem_bytes) {
+      case 1: return tcopy_slots<8, 1, DIR>(shp.slots);
+      case 2: return tcopy_slots<8, 2, DIR>(shp.slots);
+      case 4: return tcopy_slots<8, 4, DIR>(shp.slots);
+    }
+  }
+  return nullptr;
+}
+
+TCopyFn tcopy_fn(const BlocksShape& shp, int direction) {
+  return direction == KVCK_COPY_SAVE ? tcopy_dir<0>(shp) : tcopy_dir<1>(shp);
+}
+
+}  // namespace
+
+int tcopy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks) {
+  TCopyFn fn = tcopy_fn(shp, direction);
+  const int per_cu = fn ? kernel_occupancy(reinterpret_cast<const void*>(fn), device, 1) : 1;
+  const int64_t waves_per_block = kBlockThreads / kWave;
+  const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
+  const int64_t cap = (int64_t)per_cu * device_cus(device);
+  return (int)(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
+hipError_t launch_tcopy(const CopyArgs& a, const BlocksShape& shp, int direction, int grid, hipStream_t stream) {
+  TCopyFn fn = tcopy_fn(shp, direction);
+  if (!fn) return hipErrorInvalidValue;
+  void* args[] = {const_cast<CopyArgs*>(&a)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(kBlockThreads), args, 0, stream);
+}
+
+}  // namespace kvck

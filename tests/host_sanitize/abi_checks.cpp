@@ -145,7 +145,14 @@ void blocks_checks(bool have_device) {
   EXPECT_EQ(call([&](BlocksCall& c) { trans(c), c.L.plane_begin = 0, c.L.plane_count = 0; }), KVCK_ERR_UNSUPPORTED);
   EXPECT_EQ(call([&](BlocksCall& c) { trans(c), c.L.block_size = 2, c.L.chunk_stride = 4; }), KVCK_ERR_UNSUPPORTED);
   EXPECT_EQ(call([&](BlocksCall& c) { trans(c), c.L.chunk_bytes = 3; }), KVCK_ERR_UNSUPPORTED);
-  EXPECT_EQ(call([&](BlocksCall& c) { trans(c), c.direction = KVCK_COPY_SAVE; }), KVCK_ERR_UNSUPPORTED);
+  // the fused copy transposes whole N x N tiles: a tile row must fit one lane table (block_size <= 1024)
+  if (!have_device) EXPECT_EQ(call([&](BlocksCall& c) { trans(c), c.direction = KVCK_COPY_SAVE; }), KVCK_ERR_NO_DEVICE);
+  auto big = [&](BlocksCall& c) {
+    trans(c), c.L.block_size = 2048, c.L.chunk_stride = 2048 * 2;
+    c.L.head_stride = 128 * 2048 * 2, c.L.block_stride = 8 * c.L.head_stride;
+  };
+  if (!have_device) EXPECT_EQ(call([&](BlocksCall& c) { big(c); }), KVCK_ERR_NO_DEVICE);
+  EXPECT_EQ(call([&](BlocksCall& c) { big(c), c.direction = KVCK_COPY_LOAD; }), KVCK_ERR_UNSUPPORTED);
   // batch sizes
   EXPECT_EQ(call([](BlocksCall& c) { c.num_reqs = kI32Max, c.max_blocks = kI32Max, c.bt_stride = kI32Max; }),
             KVCK_ERR_UNSUPPORTED);

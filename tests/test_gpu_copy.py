@@ -147,3 +147,70 @@ def test_copy_many_caches(copy_buffers):
         assert int(got[r, k]) == int(want[r, k])
     exp = _expected_images(hp, "HND", req, 0, 2, 16, 32)
     assert np.array_equal(staging.cpu().numpy().reshape(exp.shape), exp)
+
+
+TRANS_CASES = [
+    # name, elem, heads, head_size, block_size, lengths, start, head_begin, head_count
+    ("bf16_d128_bs16", "bf16", 4, 128, 16, [50, 17, 33, 16], [0, 1, 0, 0], 0, None),
+    ("fp8_d64_bs32", "fp8", 3, 64, 32, [70, 5, 64], None, 1, 2),
+    ("fp32_d32_bs8", "fp32", 2, 32, 8, [21, 9, 8], [0, 2, 0], 0, None),
+    ("bf16_d256_bs64", "bf16", 2, 256, 64, [130, 64, 3], None, 0, None),   # two element-row groups
+    ("bf16_d64_bs4", "bf16", 3, 64, 4, [13, 6, 4], None, 1, None),         # 8-byte chunks
+    ("fp8_d32_bs8", "fp8", 2, 32, 8, [20, 3, 9], [1, 0, 0], 0, None),       # 8-byte chunks of 8 slots
+    ("fp32_d8_bs2", "fp32", 5, 8, 2, [7, 2, 1], None, 2, 3),                 # 8-byte chunks of 2 slots
+]
+
+
+@pytest.mark.parametrize("case", TRANS_CASES, ids=[c[0] for c in TRANS_CASES])
+def test_copy_element_transposed_planes(case):
+    """Fused save / load of planes stored [num_blocks, num_heads, head_size,
+    block_size] (ROCm's V layout): the staging image and checksums equal those
+    of the same tokens saved from an HND V plane (and the oracle's), and a load
+    writes exactly the valid elements of a pool paged on other ids."""
+    name, elem, nh, d, bs, lengths, start, hb, hc = case
+    log(f"[copy] transposed {name}")
+    rng = np.random.default_rng(zlib.crc32(f"tcopy{name}".encode()))
+    req, nb = wl.page_requests(rng, lengths, bs, start_pos=start, extra_blocks=[1] * len(lengths), spare_frac=0.3)
+    layers = [0, 5, 9]
+    hp = [wl.host_random_bits(rng, wl.pool_shape("HND", nb, bs, nh, d), elem) for _ in layers]
+    n_heads = (nh - hb) if hc is None else hc
+    bases = [hb + 2 * i for i in range(len(layers))]
+    kw = dict(global_head_base=bases, head_begin=hb, head_count=hc, check=True)
+    vt = [to_device_bits(np.ascontiguousarray(p[1].transpose(0, 1, 3, 2))) for p in hp]
+    vh = [to_device_bits(np.ascontiguousarray(p[1])) for p in hp]
+    bt, nbt, sp, nt = req_tensors(req)
+    per = kvck.kvck_staging_bytes(vt[0], "V_TRANS", len(layers), n_heads)
+    assert per == kvck.kvck_staging_bytes(vh[0], "V_HND", len(layers), n_heads)
+    n_entries = int(req.num_blocks.sum())
+    st_t = torch.zeros(n_entries * per, dtype=torch.uint8, device=DEV)
+    st_h = torch.zeros(n_entries * per, dtype=torch.uint8, device=DEV)
+    got_t = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, vt, "V_TRANS", layers, bt, nbt, sp, nt, st_t,
+                                           **kw).cpu().numpy()
+    got_h = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, vh, "V_HND", layers, bt, nbt, sp, nt, st_h,
+                                           **kw).cpu().numpy()
+    # a V-only partial is the checksum of the pool with its K plane zeroed
+    ref = [np.concatenate([np.zeros_like(p[:1]), p[1:]]) for p in hp]
+    want = oracle.checksum_blocks(ref, "HND", layers, bases, req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens, head_begin=hb, head_count=n_heads)
+    for r, k in req.listed():
+        assert int(got_t[r, k]) == int(want[r, k]) == int(got_h[r, k]), (r, k)
+    row_bytes = d * wl.ELEM_BYTES[elem]
+    exp = _expected_images(hp, "HND", req, hb, n_heads, bs, row_bytes)[:, :, 1:2]   # the V plane's images
+    assert np.array_equal(st_t.cpu().numpy().reshape(exp.shape), exp)
+    assert np.array_equal(st_h.cpu().numpy(), st_t.cpu().numpy())
+
+    # load into an empty transposed pool paged on other ids
+    req2, _ = wl.page_requests(np.random.default_rng(7), lengths, bs, pool_blocks=nb, start_pos=start,
+                               extra_blocks=[1] * len(lengths))
+    dst = [torch.zeros_like(t) for t in vt]
+    bt2, nbt2, sp2, nt2 = req_tensors(req2)
+    got2 = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_LOAD, dst, "V_TRANS", layers, bt2, nbt2, sp2, nt2, st_t,
+                                          **kw).cpu().numpy()
+    for r, k in req.listed():
+        assert got2[r, k] == got_t[r, k], (r, k)
+    # back in HND form: the valid rows of every listed position, and nothing else written
+    back = [to_host_bits(t).transpose(0, 1, 3, 2) for t in dst]
+    back_hnd = [np.stack([np.zeros_like(b), b]) for b in back]
+    assert np.array_equal(_expected_images(back_hnd, "HND", req2, hb, n_heads, bs, row_bytes)[:, :, 1:2], exp)
+    assert sum(int(np.count_nonzero(np.ascontiguousarray(b).view(np.uint8))) for b in back) == int(np.count_nonzero(
+        _expected_images(back_hnd, "HND", req2, hb, n_heads, bs, row_bytes)))   # bytes on both sides

@@ -126,3 +126,66 @@ def test_copy_sweep_case(case, monkeypatch):
     # nothing but the loaded rows was written
     total = sum(int(np.count_nonzero(b.view(np.uint8))) for b in back)
     assert total == int(np.count_nonzero(exp))
+
+
+def _tcase(i):
+    rng = np.random.default_rng(zlib.crc32(f"tcopysweep{i}".encode()))
+    elem = ["fp8", "bf16", "fp32"][int(rng.integers(0, 3))]
+    es = wl.ELEM_BYTES[elem]
+    heads = int(rng.integers(1, 6))
+    d = (8 // es) * int(rng.integers(1, 33))                     # rows of whole 8-byte pieces
+    bs = int(rng.choice([b for b in (1, 2, 4, 8, 16, 32, 64) if (b * es) % 8 == 0]))
+    layers = sorted(int(x) for x in rng.choice(100, size=int(rng.integers(1, 4)), replace=False))
+    n_req = int(rng.integers(1, 5))
+    lengths = [int(x) for x in rng.integers(0, 3 * bs + 20, size=n_req)]
+    start = [int(x) for x in rng.integers(0, 2, size=n_req)]
+    hb = int(rng.integers(0, heads))
+    hc = int(rng.integers(1, heads - hb + 1))
+    return dict(i=i, elem=elem, heads=heads, d=d, bs=bs, layers=layers, lengths=lengths, start=start, hb=hb, hc=hc)
+
+
+TCASES = [_tcase(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("case", TCASES, ids=lambda c: f"{c['i']}-{c['elem']}-h{c['heads']}-d{c['d']}-bs{c['bs']}")
+def test_copy_sweep_element_transposed(case):
+    """Element-transposed V planes: save gives the V_HND save's staging bytes and checksums,
+    a load into a pool paged on other ids repeats them and writes only the valid elements."""
+    log(f"[copy sweep] transposed {case}")
+    rng = np.random.default_rng(5000 + case["i"])
+    bs, nh, d, hb, hc = case["bs"], case["heads"], case["d"], case["hb"], case["hc"]
+    req, nb = wl.page_requests(rng, case["lengths"], bs, start_pos=case["start"], spare_frac=0.3)
+    hp = [wl.host_random_bits(rng, wl.pool_shape("HND", nb, bs, nh, d), case["elem"]) for _ in case["layers"]]
+    vt = [to_device_bits(np.ascontiguousarray(p[1].transpose(0, 1, 3, 2))) for p in hp]
+    vh = [to_device_bits(np.ascontiguousarray(p[1])) for p in hp]
+    bases = [hb + 1] * len(hp)
+    kw = dict(global_head_base=bases, head_begin=hb, head_count=hc, check=True)
+    bt, nbt, sp, nt = req_tensors(req)
+    per = kvck.kvck_staging_bytes(vt[0], "V_TRANS", len(hp), hc)
+    n = max(1, int(req.num_blocks.sum()))
+    st_t = torch.zeros(n * per, dtype=torch.uint8, device=DEV)
+    st_h = torch.zeros(n * per, dtype=torch.uint8, device=DEV)
+    got_t = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, vt, "V_TRANS", case["layers"], bt, nbt, sp, nt,
+                                           st_t, **kw).cpu().numpy()
+    got_h = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, vh, "V_HND", case["layers"], bt, nbt, sp, nt,
+                                           st_h, **kw).cpu().numpy()
+    ref = [np.concatenate([np.zeros_like(p[:1]), p[1:]]) for p in hp]
+    want = oracle.checksum_blocks(ref, "HND", case["layers"], bases, req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens, head_begin=hb, head_count=hc)
+    for r, k in req.listed():
+        assert int(got_t[r, k]) == int(want[r, k]) == int(got_h[r, k]), (r, k)
+    assert np.array_equal(st_t.cpu().numpy(), st_h.cpu().numpy())
+    req2, _ = wl.page_requests(np.random.default_rng(6000 + case["i"]), case["lengths"], bs, pool_blocks=nb,
+                               start_pos=case["start"])
+    dst = [torch.zeros_like(t) for t in vt]
+    dsth = [torch.zeros_like(t) for t in vh]
+    bt2, nbt2, sp2, nt2 = req_tensors(req2)
+    got2 = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_LOAD, dst, "V_TRANS", case["layers"], bt2, nbt2, sp2, nt2,
+                                          st_t, **kw).cpu().numpy()
+    kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_LOAD, dsth, "V_HND", case["layers"], bt2, nbt2, sp2, nt2, st_h,
+                                   **kw)
+    for r, k in req.listed():
+        assert got2[r, k] == got_t[r, k], (r, k)
+    # the transposed pool holds exactly what the HND load wrote, element for element
+    for a, b in zip(dst, dsth):
+        assert np.array_equal(to_host_bits(a).transpose(0, 1, 3, 2), to_host_bits(b))

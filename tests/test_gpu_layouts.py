@@ -193,8 +193,10 @@ def test_element_transposed_planes(case):
 
 
 def test_element_transposed_limits():
-    """What the element-transposed path rejects before any launch: a fused
-    copy, and blocks whose element rows are shorter than one 8-byte load."""
+    """What the element-transposed path rejects before any launch: blocks whose
+    element rows are shorter than one 8-byte load, and, for the fused copy,
+    blocks of more than 1024 slots (a tile row of the in-register transpose
+    must fit one lane table)."""
     log("[layouts] transposed limits")
     rng = np.random.default_rng(77)
     req, nb = wl.page_requests(rng, [20], 2, spare_frac=0.5)
@@ -203,8 +205,8 @@ def test_element_transposed_limits():
     with pytest.raises(kvck.KvckError) as ei:
         _call(vt, "V_TRANS", [0], req)                  # 2 slots x 2 bytes: no 8-byte load fits
     assert ei.value.status == -2
-    req, nb = wl.page_requests(rng, [40], 16, spare_frac=0.5)
-    hp = wl.host_random_bits(rng, wl.pool_shape("HND", nb, 16, 2, 64), "bf16")
+    req, nb = wl.page_requests(rng, [3000], 2048, spare_frac=0.5)
+    hp = wl.host_random_bits(rng, wl.pool_shape("HND", nb, 2048, 1, 16), "bf16")
     vt = [to_device_bits(np.ascontiguousarray(hp[1].transpose(0, 1, 3, 2)))]
     bt, nbt, sp, nt = req_tensors(req)
     staging = torch.zeros(int(req.num_blocks.sum()) * kvck.kvck_staging_bytes(vt[0], "V_TRANS", 1), dtype=torch.uint8,
@@ -212,3 +214,9 @@ def test_element_transposed_limits():
     with pytest.raises(kvck.KvckError) as ei:
         kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, vt, "V_TRANS", [0], bt, nbt, sp, nt, staging)
     assert ei.value.status == -2
+    # the checksum of the same blocks is supported
+    got = _call(vt, "V_TRANS", [0], req).cpu().numpy()
+    ref = [np.concatenate([np.zeros_like(hp[:1]), hp[1:]])]
+    want = oracle.checksum_blocks(ref, "HND", [0], [0], req.block_table, req.num_blocks, req.start_pos, req.num_tokens)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k])
