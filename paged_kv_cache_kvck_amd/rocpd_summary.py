@@ -67,7 +67,7 @@ def main(argv=None):
     ap.add_argument("--kernel", default=MAIN, help="substring of the summarized kernel's name")
     ap.add_argument("--copy-kernel", action="store_true",
                     help="the kernel reads and writes --valid-bytes (fused copy): throughput counts both")
-    ap.add_argument("--later-label", default="later calls: TP-shard run",
+    ap.add_argument("--later-label", default="later calls",
                     help="label of the kernel's dispatches after --main-calls")
     ap.add_argument("--label", help="display name of the kernel (default: --kernel)")
     a = ap.parse_args(argv)
@@ -75,10 +75,16 @@ def main(argv=None):
     label = a.label or kernel
 
     rows = _kernels(a.trace)
+    # the workload's dispatches: the first kernel matching --kernel fixes the
+    # variant (template arguments); other variants (a TP-shard run, a small
+    # call) are listed on rows of their own
+    main_name = next((name for name, _, _ in rows if kernel in name), None)
+    if main_name is None:
+        raise SystemExit(f"no dispatch of {kernel!r} in {a.trace}")
     groups = {}
     main_durs = []
     for name, dur, _ in rows:
-        if kernel in name:
+        if name == main_name:
             main_durs.append(dur)
             continue
         groups.setdefault(_short(name), []).append(dur)
@@ -111,7 +117,10 @@ def main(argv=None):
             copy = [r[2] for r in ev if "copyBuffer" in r[0] and "kvck" not in r[0]]
             copy_kib = max(copy)
             factor = a.copy_bytes / (copy_kib * 1024.0)
-            main = [r[2] for r in ev if kernel in r[0]][:a.main_calls]
+            pmc_name = next(r[0] for r in ev if kernel in r[0])
+            if pmc_name != main_name:
+                raise SystemExit(f"{counter}: first {kernel!r} dispatch is {pmc_name!r}, not {main_name!r}")
+            main = [r[2] for r in ev if r[0] == main_name][:a.main_calls]
             kib = statistics.mean(main)
             res[which] = dict(counter=counter, copy_kib=copy_kib, factor=factor, main_kib=kib,
                               bytes=kib * 1024.0 * factor, launches=len(main))
