@@ -400,7 +400,7 @@ def main(argv=None):
         cpu["parallel"] = cpu_baseline_parallel(w, args.cpu_parallel_seconds, workers)
 
     line = {
-        "metric": "checksummed KV GB/s (bit-exact vs CPU oracle)",
+        "metric": "checksummed KV GB/s and % of MI355X HBM peak; bit-exact vs CPU oracle",
         "value": valid / (ms_step * 1e-3) / 1e9,
         "unit": "GB/s",
         "n_gpus": 1,
