@@ -246,7 +246,8 @@ def main(argv=None):
     out_main = out.cpu().numpy().view("uint64").copy()  # the timed steps' checksums, for the oracle check
     achieved = valid / (main_avg * 1e-3) / 1e9
 
-    extra = {"valid_bytes_per_step": valid, "main_pass_ms": main_avg,
+    extra = {"valid_bytes_per_step": valid, "pct_of_hbm_peak": valid / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS * 100,
+             "main_pass_ms": main_avg,
              "step_ms_median": statistics.median(per_step), "step_ms_min": min(per_step),
              "listed_positions": int(req.num_blocks.sum()),
              "metadata_bytes_per_step": int(req.num_blocks.sum()) * (4 + 8 + 32) + req.num_reqs * 20}
