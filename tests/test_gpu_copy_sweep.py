@@ -45,7 +45,7 @@ def _case(i):
                 start=start, extra=extra, hb=hb, hc=hc, buffers=buffers, merge=merge)
 
 
-CASES = [_case(i) for i in range(40)]
+CASES = [_case(i) for i in range(120)]
 
 
 def _ids(c):
@@ -144,7 +144,7 @@ def _tcase(i):
     return dict(i=i, elem=elem, heads=heads, d=d, bs=bs, layers=layers, lengths=lengths, start=start, hb=hb, hc=hc)
 
 
-TCASES = [_tcase(i) for i in range(24)]
+TCASES = [_tcase(i) for i in range(72)]
 
 
 @pytest.mark.parametrize("case", TCASES, ids=lambda c: f"{c['i']}-{c['elem']}-h{c['heads']}-d{c['d']}-bs{c['bs']}")

@@ -56,7 +56,7 @@ def _case(i):
                 start=start, extra=extra, hb=hb, hc=hc, base=base, env=env)
 
 
-CASES = [_case(i) for i in range(160)]
+CASES = [_case(i) for i in range(480)]
 
 
 def _ids(c):
@@ -121,7 +121,7 @@ def _states_case(i):
                 row_count=row_count, base=base)
 
 
-STATE_CASES = [_states_case(i) for i in range(40)]
+STATE_CASES = [_states_case(i) for i in range(120)]
 
 
 @pytest.mark.parametrize("case", STATE_CASES, ids=lambda c: f"{c['i']}-s{len(c['states'])}-r{c['rows']}")
