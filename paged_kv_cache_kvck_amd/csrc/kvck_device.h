@@ -39,11 +39,30 @@ __device__ __forceinline__ typename ChunkType<CHUNK>::T load_chunk(__amdgpu_buff
     return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kNonTemporal);
 }
 
-// Sum of a 64-bit value over the 64 lanes of a wavefront (every lane gets it).
+// A 64-bit value moved across lanes by one DPP control, as two 32-bit halves;
+// lanes of rows outside ROW_MASK get 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint64_t dpp_move(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROW_MASK, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROW_MASK, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Sum of a 64-bit value over the 64 lanes of a wavefront, mod 2^64 (every lane
+// gets it).  DPP steps, no LDS: pairs and quads (quad_perm), half-rows and
+// rows of 16 (row_half_mirror, row_mirror), then row 0 into row 1 and row 2
+// into row 3 (row_bcast:15), rows 0-1 into rows 2-3 (row_bcast:31); lane 63
+// ends with the total.  Halves move separately; every add carries in 64 bits.
 __device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += dpp_move<0xb1>(v);        // quad_perm [1,0,3,2]
+  v += dpp_move<0x4e>(v);        // quad_perm [2,3,0,1]
+  v += dpp_move<0x141>(v);       // row_half_mirror
+  v += dpp_move<0x140>(v);       // row_mirror
+  v += dpp_move<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_move<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, kWave - 1);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), kWave - 1);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 

@@ -14,21 +14,13 @@
 // row's 16-byte chunks; a chunk of 4-byte elements x0..x3 starting at element e
 // adds sum_i x_i (2(e+i) + 1); a chunk of 2-byte elements x0..x7 adds
 // u*X + 2*Y with u = 2e + 1, X = sum x_i, Y = sum i*x_i (both fit 32 bits).
-#include "kvck_internal.h"
+#include "kvck_device.h"
 
 namespace kvck {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ u32x4 load16(const uint8_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-
-__device__ __forceinline__ uint64_t wave_sum(uint64_t v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
 }
 
 __device__ __forceinline__ uint64_t chunk_u32(u32x4 x, uint32_t u) {
