@@ -91,6 +91,7 @@ bool choose_shape(int32_t block_size, int32_t row_bytes, int chunk, int max_slot
   shp->transposed = false;
   shp->elem_bytes = 0;
   shp->dense = false;
+  shp->lds_transpose = false;
   return true;
 }
 
@@ -339,11 +340,20 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
     // f / cpe, slots (f mod cpe) * chunk/run_bytes onward; rows split into groups
     // of at most what 16 slots per lane hold
     const int64_t cpe = (int64_t)L.block_size * run_bytes / chunk;
-    const int64_t max_chunks = (int64_t)kWave * 16;
-    if (cpe > max_chunks) return KVCK_ERR_UNSUPPORTED;
+    // The fused copy transposes through LDS when chunks are 16 bytes (both
+    // sides then move whole lines; same-box A/B against the register transpose:
+    // 7-80 % faster, most for large blocks), with lane tables of at most 8
+    // slots so a wave's LDS region stays within 8 KiB; 8-byte chunks (small
+    // blocks) transpose in registers.  KVCK_TCOPY=regs|lds forces either where
+    // possible (results are identical).
+    bool lds_transpose = mode != kModeChecksum && chunk == 16;
+    if (const char* t = getenv("KVCK_TCOPY")) lds_transpose = lds_transpose && strcmp(t, "regs") != 0;
     const int64_t D = L.row_bytes / run_bytes;
     // the fused copy transposes whole N x N tiles (N = chunk/run_bytes): groups of whole tile rows
     const int64_t unit = mode == kModeChecksum ? 1 : chunk / run_bytes;
+    if (lds_transpose && (int64_t)kWave * 8 / cpe / unit < 1) lds_transpose = false;  // a tile row too wide
+    const int64_t max_chunks = (int64_t)kWave * (lds_transpose ? 8 : 16);
+    if (cpe > max_chunks) return KVCK_ERR_UNSUPPORTED;
     const int64_t rge_max = max_chunks / cpe / unit * unit;
     if (rge_max < 1) return KVCK_ERR_UNSUPPORTED;
     const int64_t groups = (D + rge_max - 1) / rge_max;
@@ -361,6 +371,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
     shp.copy_buffers = 1;
     shp.transposed = true;
     shp.elem_bytes = run_bytes;
+    shp.lds_transpose = lds_transpose;
   } else if (!choose_shape(L.block_size, lane_row_bytes, chunk, 16, &shp)) {
     return KVCK_ERR_UNSUPPORTED;
   }
@@ -476,7 +487,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
       ca.cache_offset = c0;
       ca.block_size = L.block_size;
       if (transposed) {
-        const int grid = tcopy_grid(shp, mode, dev, tasks);
+        const int grid = tcopy_grid(shp, mode, dev, tasks, L.block_size);
         if (launch_tcopy(ca, shp, mode, grid, st) != hipSuccess) return KVCK_ERR_HIP;
       } else {
         const int grid = copy_grid(shp, mode, dev, tasks);

@@ -126,6 +126,7 @@ struct BlocksShape {
   bool transposed;      // rows stored element by element (elements of a row elem_stride apart)
   int elem_bytes;       // element size of transposed rows (1, 2 or 4)
   bool dense;           // planned in place: tasks read the request arrays (kernel variant)
+  bool lds_transpose;   // fused copy of transposed planes: transpose staged through LDS
 };
 
 // launchers (return hipSuccess or the first HIP error)
@@ -147,7 +148,7 @@ int tblocks_grid(const BlocksShape& shp, int device, int64_t max_tasks);
 hipError_t launch_copy(const CopyArgs& a, const BlocksShape& shp, int direction, int grid, hipStream_t stream);
 int copy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks);
 hipError_t launch_tcopy(const CopyArgs& a, const BlocksShape& shp, int direction, int grid, hipStream_t stream);
-int tcopy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks);
+int tcopy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks, int32_t block_size);
 hipError_t launch_tags(const uint64_t* checksums, const uint8_t* hashes, int64_t hash_stride, uint64_t fingerprint,
                        int64_t n, const int32_t* nbpr, int32_t max_blocks, uint64_t* tagged, const uint64_t* stored,
                        uint8_t* mismatch, uint32_t* count, hipStream_t stream);

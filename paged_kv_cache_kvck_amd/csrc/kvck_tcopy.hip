@@ -7,13 +7,17 @@
 // The staging image is the same as for every other layout, [head][slot][row]
 // with a token's row its head_size elements in order, so a block saved from
 // one layout loads into another.  The pool holds the transpose of that image
-// per (block, head), so the copy transposes in registers: the image is cut
-// into N x N tiles of ES-byte elements (N = CHUNK / ES, the elements of one
-// 16- or 8-byte chunk), a tile is held by N consecutive lanes, one chunk each,
-// and a butterfly exchange between those lanes turns pool chunks (one element
-// index of N slots) into staging chunks (N elements of one slot) and back.
-// The checksum is taken on the pool-side form of each chunk, exactly as in the
-// element-transposed checksum pass.
+// per (block, head), so the copy transposes it, in one of two ways:
+//  - tcopy_lds_kernel (16-byte chunks, the default): through a per-wave LDS
+//    region holding the image in staging form, so that both the pool side and
+//    the staging side move whole contiguous chunks;
+//  - tcopy_kernel (8-byte chunks, small blocks): in registers, the image cut
+//    into N x N tiles of ES-byte elements (N = CHUNK / ES, the elements of one
+//    chunk), a tile held by N consecutive lanes, one chunk each, and a
+//    butterfly exchange between those lanes turning pool chunks (one element
+//    index of N slots) into staging chunks (N elements of one slot) and back.
+// Either way the checksum is taken on the pool-side form of each chunk,
+// exactly as in the element-transposed checksum pass.
 //
 // Valid slots only: a save reads pool chunks holding at least one valid slot
 // and stores the staging rows of valid slots; a load reads the staging rows of
@@ -254,6 +258,218 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_kernel(const CopyArgs ca)
   }
 }
 
+// The same copy with the transpose staged through LDS, for larger blocks: the
+// register transpose leaves the side that is not stored touching one 16-byte
+// piece of each of many lines per instruction, which grows with block_size.
+// Here both sides move whole contiguous chunks: pool chunks in pool order
+// (element row by element row), staging chunks in staging order (slot by
+// slot), and each wave's LDS region holds the group's image in staging form,
+// [slot][element], a row of pitch bytes.  Pool chunks go in and out element
+// by element.  The 16-byte columns of slot s are XOR-swizzled by (s / N) mod
+// 2^k (2^k dividing the row's column count, at most 8), so the N slots of a
+// pool chunk and the 64 lanes of a staging access fall in different banks.
+template <int ES>
+__device__ __forceinline__ void lds_store_element(uint8_t* lds, uint32_t addr, uint32_t v) {
+  if constexpr (ES == 4)
+    *reinterpret_cast<uint32_t*>(lds + addr) = v;
+  else if constexpr (ES == 2)
+    *reinterpret_cast<uint16_t*>(lds + addr) = (uint16_t)v;
+  else
+    lds[addr] = (uint8_t)v;
+}
+
+template <int ES>
+__device__ __forceinline__ uint32_t lds_load_element(const uint8_t* lds, uint32_t addr) {
+  if constexpr (ES == 4)
+    return *reinterpret_cast<const uint32_t*>(lds + addr);
+  else if constexpr (ES == 2)
+    return *reinterpret_cast<const uint16_t*>(lds + addr);
+  else
+    return lds[addr];
+}
+
+extern __shared__ __attribute__((aligned(16))) uint8_t tcopy_lds[];
+
+// Bytes of one wave's LDS region: block_size rows of the group's elements,
+// rounded up to whole 16-byte columns.
+__host__ __device__ inline int64_t tcopy_lds_pitch(int32_t rows_per_group, int es) {
+  return ((int64_t)rows_per_group * es + 15) / 16 * 16;
+}
+
+// DIR 0: save (pool -> staging); DIR 1: load (staging -> pool).  16-byte chunks.
+template <int ES, int S, int DIR>
+__global__ __launch_bounds__(kBlockThreads) void tcopy_lds_kernel(const CopyArgs ca) {
+  using V = typename ChunkType<16>::T;
+  constexpr int N = 16 / ES;
+  constexpr int EPD = 4 / ES;
+  constexpr int PER_PIECE = 8 / ES;
+  const BlocksArgs& a = ca.b;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+  const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
+  const int64_t n_items = (int64_t)*a.n_items;
+  const int lpt = a.caches_per_task;
+  const int ngroups = (a.num_caches + lpt - 1) / lpt;
+  const int64_t total = n_items * ngroups;
+  if (wave >= total) return;
+
+  const int bs = ca.block_size;
+  const int cpe = a.chunks_per_row;  // pool chunks per element row: block_size / N
+  const int rge = a.rows_per_group;  // element rows per group, a multiple of N
+  const uint32_t pitch = (uint32_t)tcopy_lds_pitch(rge, ES);
+  const uint32_t cols = pitch / 16;
+  const uint32_t low = cols & (0u - cols);
+  const uint32_t kmask = (low < 8u ? low : 8u) - 1u;
+  uint8_t* const lds = tcopy_lds + (threadIdx.x / kWave) * (int64_t)bs * pitch;
+  const int cps = rge * ES / 16;     // staging chunks of a slot's row segment (full group)
+
+  // pool side: chunk f is element row d = f / cpe, slots q N.. (q = f mod cpe)
+  // staging side: chunk f is column c = f mod cps of slot sl = f / cps
+  int prow[S], srow[S], q0[S], scol[S];
+  uint32_t poff[S], soff[S], lpool[S], lstg[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const int f = lane + kWave * s;
+    const bool pin = f < rge * cpe;
+    const int d = f / cpe, q = f - (f / cpe) * cpe;
+    prow[s] = pin ? d : 0x7fffffff;
+    q0[s] = q * N;
+    poff[s] = (uint32_t)((int64_t)d * a.chunk_stride + (int64_t)q * 16);
+    const uint32_t dcol = (uint32_t)(d * ES);
+    lpool[s] = (uint32_t)(q * N) * pitch + ((((dcol >> 4) ^ ((uint32_t)q & kmask)) << 4) | (dcol & 15u));
+    const bool sin = f < bs * cps;
+    const int sl = f / cps, c = f - (f / cps) * cps;
+    srow[s] = sin ? sl : 0x7fffffff;
+    scol[s] = c;
+    soff[s] = (uint32_t)((int64_t)sl * a.row_bytes + (int64_t)c * 16);
+    lstg[s] = (uint32_t)sl * pitch + ((((uint32_t)c) ^ (((uint32_t)sl / N) & kmask)) << 4);
+  }
+  const int D = a.row_bytes / ES;
+  const int ngr = (D + rge - 1) / rge;
+  const uint64_t P = (uint64_t)a.pieces;
+  const int64_t img_head = (int64_t)bs * a.row_bytes;
+
+  for (int64_t task = wave; task < total; task += nwaves) {
+    const int64_t grp = task / n_items;
+    const int64_t item = task - grp * n_items;
+    const int c_begin = (int)grp * lpt;
+    const int c_end = min(a.num_caches, c_begin + lpt);
+    const TaskRecord rec = task_record<false>(a, item, false, lane);
+    int32_t v = rec.valid;
+    const uint64_t t0 = rec.t0;
+    if (item >= ca.staging_positions) {
+      if (v > 0 && lane == 0 && ca.error_flags) atomicOr(ca.error_flags, KVCK_FLAG_STAGING_FULL);
+      v = 0;
+    }
+    uint64_t acc = 0;
+    if (v > 0) {
+      const int64_t blk_off = (int64_t)rec.block * a.block_stride;
+      uint8_t* const img0 = ca.staging + (item * ca.num_caches_total + ca.cache_offset) * ca.image_bytes;
+      int nvalid[S];
+      uint64_t ubase[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int left = v - q0[s];
+        nvalid[s] = left < 0 ? 0 : (left > N ? N : left);
+        ubase[s] = 2ull * (t0 + (uint64_t)q0[s]) * P + 1ull + a.piece_base;
+      }
+      const bool straddle = (v % N) != 0;
+      const int nunits = (c_end - c_begin) * ngr * a.heads;
+      int cache = c_begin, group = 0, hh = 0;
+      for (int ui = 0; ui < nunits; ++ui) {
+        const int rows = min(rge, D - group * rge);
+        const int seg = rows * ES / 16;  // staging chunks of this group's row segment
+        const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.base[cache] + blk_off + (int64_t)(group * rge) * a.chunk_stride +
+                                                    (int64_t)hh * a.head_stride);
+        const __amdgpu_buffer_rsrc_t rst = make_rsrc(img0 + (int64_t)cache * ca.image_bytes +
+                                                     (int64_t)hh * img_head + (int64_t)(group * rge) * ES);
+        uint64_t sh = 0;
+        V x[S];
+        if constexpr (DIR == 0) {
+#pragma unroll
+          for (int s = 0; s < S; ++s) x[s] = load_chunk<16>(rp, prow[s] < rows && q0[s] < v ? poff[s] : kOOB);
+        } else {
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+            x[s] = load_chunk<16>(rst, srow[s] < v && scol[s] < seg ? soff[s] : kOOB);
+        }
+        if constexpr (DIR == 0) {
+          // checksum of each pool chunk, then its elements into the staging form
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            uint64_t E, K;
+            chunk_sums<ES>(x[s], nvalid[s], E, K);
+            const uint32_t d = (uint32_t)(group * rge) + (uint32_t)prow[s];
+            sh += ((ubase[s] + 2ull * (d / PER_PIECE)) * E + 2ull * P * K) << (8 * ES * (d % PER_PIECE));
+            if (prow[s] < rge) {
+#pragma unroll
+              for (int k = 0; k < N; ++k)
+                lds_store_element<ES>(lds, lpool[s] + (uint32_t)k * pitch,
+                                      ES == 4 ? x[s][k] : (x[s][k / EPD] >> (8 * ES * (k % EPD))));
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            V y = srow[s] < bs ? *reinterpret_cast<const V*>(lds + lstg[s]) : V(0);
+            store_chunk<16>(rst, srow[s] < v && scol[s] < seg ? soff[s] : kOOB, y);
+          }
+          __builtin_amdgcn_wave_barrier();
+        } else {
+          // staging rows into the staging form, then pool chunks gathered element by element
+#pragma unroll
+          for (int s = 0; s < S; ++s)
+            if (srow[s] < bs) *reinterpret_cast<V*>(lds + lstg[s]) = x[s];
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int s = 0; s < S; ++s) {
+            uint32_t w[4] = {0u, 0u, 0u, 0u};
+            if (prow[s] < rge) {
+#pragma unroll
+              for (int k = 0; k < N; ++k)
+                w[k / EPD] |= lds_load_element<ES>(lds, lpool[s] + (uint32_t)k * pitch) << (8 * ES * (k % EPD));
+            }
+            V xv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[i] = w[i];
+            uint64_t E, K;
+            chunk_sums<ES>(xv, nvalid[s], E, K);
+            const uint32_t d = (uint32_t)(group * rge) + (uint32_t)prow[s];
+            sh += ((ubase[s] + 2ull * (d / PER_PIECE)) * E + 2ull * P * K) << (8 * ES * (d % PER_PIECE));
+            const bool row_ok = prow[s] < rows;
+            store_chunk<16>(rp, row_ok && nvalid[s] == N ? poff[s] : kOOB, xv);
+            if (straddle) {  // uniform: the chunk holding the last valid slot, element by element
+              const bool part = row_ok && nvalid[s] > 0 && nvalid[s] < N;
+#pragma unroll
+              for (int k = 0; k < N - 1; ++k)
+                store_element<ES>(rp, part && k < nvalid[s] ? poff[s] + (uint32_t)(k * ES) : kOOB,
+                                  element<ES, 4>(w, k));
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
+        }
+        acc += sh * (uint64_t)(a.mbase[cache] + 2u * (uint32_t)hh);
+        if (++hh == a.heads) {
+          hh = 0;
+          if (++group == ngr) {
+            group = 0;
+            ++cache;
+          }
+        }
+      }
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) {
+      if (a.direct) {
+        uint64_t* o = a.out + rec.out_idx;
+        *o = a.accumulate ? *o + acc : acc;
+      } else {
+        a.partials[(int64_t)(a.group_offset + grp) * a.max_items + item] = acc;
+      }
+    }
+  }
+}
+
 using TCopyFn = void (*)(const CopyArgs);
 
 template <int CHUNK, int ES, int DIR>
@@ -268,8 +484,28 @@ TCopyFn tcopy_slots(int slots) {
   return nullptr;
 }
 
+template <int ES, int DIR>
+TCopyFn tcopy_lds_slots(int slots) {
+  switch (slots) {
+    case 1: return &tcopy_lds_kernel<ES, 1, DIR>;
+    case 2: return &tcopy_lds_kernel<ES, 2, DIR>;
+    case 4: return &tcopy_lds_kernel<ES, 4, DIR>;
+    case 8: return &tcopy_lds_kernel<ES, 8, DIR>;
+  }
+  return nullptr;
+}
+
 template <int DIR>
 TCopyFn tcopy_dir(const BlocksShape& shp) {
+  if (shp.lds_transpose) {
+    if (shp.chunk != 16) return nullptr;
+    switch (shp.elem_bytes) {
+      case 1: return tcopy_lds_slots<1, DIR>(shp.slots);
+      case 2: return tcopy_lds_slots<2, DIR>(shp.slots);
+      case 4: return tcopy_lds_slots<4, DIR>(shp.slots);
+    }
+    return nullptr;
+  }
   if (shp.chunk == 16) {
     switch (shp.elem_bytes) {
       case 1: return tcopy_slots<16, 1, DIR>(shp.slots);
@@ -290,11 +526,28 @@ TCopyFn tcopy_fn(const BlocksShape& shp, int direction) {
   return direction == KVCK_COPY_SAVE ? tcopy_dir<0>(shp) : tcopy_dir<1>(shp);
 }
 
+// Dynamic LDS of one workgroup of the LDS variant: a region per wave.
+size_t tcopy_lds_bytes(const BlocksShape& shp, int32_t block_size) {
+  return shp.lds_transpose ? (size_t)(kBlockThreads / kWave) * (size_t)block_size *
+                                 (size_t)tcopy_lds_pitch(shp.rows_per_group, shp.elem_bytes)
+                           : 0;
+}
+
 }  // namespace
 
-int tcopy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks) {
+int tcopy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks, int32_t block_size) {
   TCopyFn fn = tcopy_fn(shp, direction);
-  const int per_cu = fn ? kernel_occupancy(reinterpret_cast<const void*>(fn), device, 1) : 1;
+  int per_cu = fn ? kernel_occupancy(reinterpret_cast<const void*>(fn), device, 1) : 1;
+  const size_t lds = tcopy_lds_bytes(shp, block_size);
+  if (lds > 0) {
+    // the occupancy query counts no dynamic LDS: bound it by the CU's LDS
+    int per_cu_lds = 0;
+    if (hipDeviceGetAttribute(&per_cu_lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, device) != hipSuccess ||
+        per_cu_lds <= 0)
+      per_cu_lds = 64 * 1024;
+    const int by_lds = (int)((size_t)per_cu_lds / lds);
+    per_cu = by_lds < 1 ? 1 : (by_lds < per_cu ? by_lds : per_cu);
+  }
   const int64_t waves_per_block = kBlockThreads / kWave;
   const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
   const int64_t cap = (int64_t)per_cu * device_cus(device);
@@ -305,7 +558,8 @@ hipError_t launch_tcopy(const CopyArgs& a, const BlocksShape& shp, int direction
   TCopyFn fn = tcopy_fn(shp, direction);
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {const_cast<CopyArgs*>(&a)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(kBlockThreads), args, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(kBlockThreads), args,
+                         tcopy_lds_bytes(shp, a.block_size), stream);
 }
 
 }  // namespace kvck

@@ -158,17 +158,22 @@ TRANS_CASES = [
     ("bf16_d64_bs4", "bf16", 3, 64, 4, [13, 6, 4], None, 1, None),         # 8-byte chunks
     ("fp8_d32_bs8", "fp8", 2, 32, 8, [20, 3, 9], [1, 0, 0], 0, None),       # 8-byte chunks of 8 slots
     ("fp32_d8_bs2", "fp32", 5, 8, 2, [7, 2, 1], None, 2, 3),                 # 8-byte chunks of 2 slots
+    ("bf16_d576_bs128", "bf16", 1, 576, 128, [300, 128, 5], None, 0, None),  # several groups either way
+    ("fp8_d128_bs256", "fp8", 2, 128, 256, [600, 17], None, 1, 1),
 ]
 
 
+@pytest.mark.parametrize("transpose", ["auto", "regs", "lds"])
 @pytest.mark.parametrize("case", TRANS_CASES, ids=[c[0] for c in TRANS_CASES])
-def test_copy_element_transposed_planes(case):
+def test_copy_element_transposed_planes(case, transpose, monkeypatch):
     """Fused save / load of planes stored [num_blocks, num_heads, head_size,
     block_size] (ROCm's V layout): the staging image and checksums equal those
     of the same tokens saved from an HND V plane (and the oracle's), and a load
     writes exactly the valid elements of a pool paged on other ids."""
     name, elem, nh, d, bs, lengths, start, hb, hc = case
-    log(f"[copy] transposed {name}")
+    if transpose != "auto":
+        monkeypatch.setenv("KVCK_TCOPY", transpose)   # the transpose in registers or through LDS
+    log(f"[copy] transposed {name} {transpose}")
     rng = np.random.default_rng(zlib.crc32(f"tcopy{name}".encode()))
     req, nb = wl.page_requests(rng, lengths, bs, start_pos=start, extra_blocks=[1] * len(lengths), spare_frac=0.3)
     layers = [0, 5, 9]

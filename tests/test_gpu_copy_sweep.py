@@ -141,16 +141,21 @@ def _tcase(i):
     start = [int(x) for x in rng.integers(0, 2, size=n_req)]
     hb = int(rng.integers(0, heads))
     hc = int(rng.integers(1, heads - hb + 1))
-    return dict(i=i, elem=elem, heads=heads, d=d, bs=bs, layers=layers, lengths=lengths, start=start, hb=hb, hc=hc)
+    transpose = ["regs", "lds"][int(rng.integers(0, 2))]
+    return dict(i=i, elem=elem, heads=heads, d=d, bs=bs, layers=layers, lengths=lengths, start=start, hb=hb, hc=hc,
+                transpose=transpose)
 
 
 TCASES = [_tcase(i) for i in range(72)]
 
 
-@pytest.mark.parametrize("case", TCASES, ids=lambda c: f"{c['i']}-{c['elem']}-h{c['heads']}-d{c['d']}-bs{c['bs']}")
-def test_copy_sweep_element_transposed(case):
+@pytest.mark.parametrize("case", TCASES,
+                         ids=lambda c: f"{c['i']}-{c['elem']}-h{c['heads']}-d{c['d']}-bs{c['bs']}-{c['transpose']}")
+def test_copy_sweep_element_transposed(case, monkeypatch):
     """Element-transposed V planes: save gives the V_HND save's staging bytes and checksums,
-    a load into a pool paged on other ids repeats them and writes only the valid elements."""
+    a load into a pool paged on other ids repeats them and writes only the valid elements
+    (transpose in registers or through LDS)."""
+    monkeypatch.setenv("KVCK_TCOPY", case["transpose"])
     log(f"[copy sweep] transposed {case}")
     rng = np.random.default_rng(5000 + case["i"])
     bs, nh, d, hb, hc = case["bs"], case["heads"], case["d"], case["hb"], case["hc"]
