@@ -115,12 +115,20 @@ constexpr int64_t kPipeMinTasksPerWave = 16;
 static_assert(kCachesPerLaunch % kPipeMaxCaches == 0, "launch groups must not straddle launches");
 
 // `narrow` (or null) is the same rows split into lane tables of at most 4
-// slots, the widest the pipelined kernel double-buffers: blocks whose rows
-// need 8 or 16 slots per lane can still be pipelined, in more row groups.
+// slots (8 for merged rows), the widest the pipelined kernel double-buffers:
+// blocks whose rows need more slots per lane can still be pipelined, in more
+// row groups.
 //
 // A call planned in place (`dense`) whose caches all fit one task's byte
 // budget runs one pipelined task per position over every cache: a single
 // launch with no second pass, where latency rather than lane use counts.
+// KVCK_MERGED_PIPE=0 keeps merged rows on the unpipelined kernel (A/B switch;
+// results are identical).
+bool merged_pipe_off() {
+  const char* e = getenv("KVCK_MERGED_PIPE");
+  return e && e[0] == '0';
+}
+
 void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_caches, int64_t max_items,
                      int64_t block_bytes, int planes, int heads, int cus, bool copy, bool dense) {
   const int64_t waves = (int64_t)cus * 8;  // resident waves of the pipelined kernel (2 per SIMD)
@@ -130,18 +138,20 @@ void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_ca
   // A pipelined unit holds 16/S head slots (K and V can share one when heads
   // are few); with fewer heads than that its loads would be mostly masked.
   auto fills = [&](int slots) { return (int64_t)heads * (planes == 2 ? 2 : 1) * slots >= 16; };
-  const BlocksShape* cand = shp->slots <= 4 ? shp : narrow;
-  const bool fits = cand != nullptr && fills(cand->slots);
-  const bool one_task = dense && !copy && !shp->merged && cand != nullptr && num_caches <= lpt;
+  // Merged rows (a slot's heads as one row) fill their lanes by construction
+  // and pipeline with up to 8 slots per lane (one plane per unit).
+  const int max_pipe_slots = shp->merged ? 8 : 4;
+  const BlocksShape* cand = shp->slots <= max_pipe_slots ? shp : narrow;
+  const bool fits = cand != nullptr && (shp->merged || fills(cand->slots));
+  const bool one_task = dense && !copy && cand != nullptr && num_caches <= lpt;
   bool pipe = (fits && num_caches > 1 && tasks >= kPipeMinTasksPerWave * waves) || one_task;
   // KVCK_SCHEDULE=pipelined|simple overrides the choice (results are identical
-  // either way); merged rows always run the unpipelined checksum kernel
+  // either way)
   if (const char* force = getenv("KVCK_SCHEDULE")) {
     if (strcmp(force, "pipelined") == 0) pipe = true;
     if (strcmp(force, "simple") == 0) pipe = false;
   }
-  if (shp->merged && !copy) pipe = false;
-  if (shp->transposed && shp->slots > 4) pipe = false;  // pipelined variants stop at 4 slots
+  if (merged_pipe_off() && shp->merged && !copy) pipe = false;
   if (copy) {
     // One unit buffer per wave: twice the resident waves of the ping-pong
     // kernel, which keeps more stores in flight (A/B on one GPU: load 5.6 ->
@@ -150,10 +160,12 @@ void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_ca
     if (const char* b = getenv("KVCK_COPY_BUFFERS")) shp->copy_buffers = b[0] == '2' ? 2 : 1;
   }
   if (copy) pipe = true;  // the fused copy kernel always runs the pipelined structure
-  if (pipe && !copy && shp->slots > 4 && narrow && (fills(narrow->slots) || one_task)) {
+  if (pipe && !copy && shp->slots > max_pipe_slots && narrow && (shp->merged || fills(narrow->slots) || one_task)) {
     shp->slots = narrow->slots;
     shp->rows_per_group = narrow->rows_per_group;
   }
+  if (!copy && shp->merged && shp->slots > 8) pipe = false;      // merged pipelined variants stop at 8 slots
+  if (!copy && shp->transposed && shp->slots > 4) pipe = false;  // transposed ones at 4
   if (pipe) {
     shp->pipelined = true;
     shp->caches_per_task = lpt;
@@ -376,7 +388,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
     return KVCK_ERR_UNSUPPORTED;
   }
   shp.merged = merged;
-  const bool has_narrow = !merged && !transposed && choose_shape(L.block_size, lane_row_bytes, chunk, 4, &narrow);
+  const bool has_narrow = !transposed && choose_shape(L.block_size, lane_row_bytes, chunk, merged ? 8 : 4, &narrow);
   // lane-table offsets and piece terms are 32-bit
   if ((int64_t)shp.rows_per_group * L.slot_stride + (int64_t)(runs - 1) * L.chunk_stride +
           (merged ? lane_row_bytes : run_bytes) >=

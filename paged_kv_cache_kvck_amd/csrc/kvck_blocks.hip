@@ -388,9 +388,14 @@ BlocksFn blocks_fn_slots(int slots) {
 
 template <bool DENSE>
 BlocksFn blocks_fn_plan(const BlocksShape& shp) {
-  if (shp.merged)
+  if (shp.merged) {
+    if (shp.pipelined)  // lane tables of at most 8 slots (the host's rule)
+      return shp.slots > 8 ? nullptr
+                           : (shp.chunk == 16 ? blocks_fn_slots<16, 1, true, true, DENSE>(shp.slots)
+                                              : blocks_fn_slots<8, 1, true, true, DENSE>(shp.slots));
     return shp.chunk == 16 ? blocks_fn_slots<16, 1, false, true, DENSE>(shp.slots)
                            : blocks_fn_slots<8, 1, false, true, DENSE>(shp.slots);
+  }
   if (shp.pipelined) {
     if (shp.planes_per_unit == 2)
       return shp.chunk == 16 ? blocks_fn_slots<16, 2, true, false, DENSE>(shp.slots)
@@ -403,8 +408,9 @@ BlocksFn blocks_fn_plan(const BlocksShape& shp) {
 }
 
 // Pipelined units may carry both planes (PU = 2); the unpipelined kernel and
-// wide lane tables (S >= 8) always take one plane per unit.  Merged rows run
-// the unpipelined kernel.  Every variant exists planned and planned in place.
+// wide lane tables (S >= 8) always take one plane per unit.  Merged rows take
+// one plane per unit and pipeline with lane tables of up to 8 slots.  Every
+// variant exists planned and planned in place.
 BlocksFn blocks_fn(const BlocksShape& shp) {
   return shp.dense ? blocks_fn_plan<true>(shp) : blocks_fn_plan<false>(shp);
 }
