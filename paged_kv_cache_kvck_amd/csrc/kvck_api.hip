@@ -339,10 +339,12 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   // fused copy, written on the pool side) as one row
   const int64_t wide = (int64_t)head_count * L.row_bytes;
   // (a merged copy's staging offsets are 32-bit across a plane's head images)
-  const bool can_merge = !transposed && runs == 1 && head_count > 1 && L.head_stride == L.row_bytes &&
+  const bool can_merge = !transposed && runs == 1 && (head_count == 1 || L.head_stride == L.row_bytes) &&
                          wide <= (int64_t)kWave * 16 * chunk &&
                          (mode == kModeChecksum || (int64_t)L.block_size * wide < ((int64_t)1 << 31));
-  bool merged = can_merge && L.row_bytes < kMergeBelowRowBytes;
+  // (a single head, e.g. an MLA latent, is a merged row of one head: it then
+  // pipelines with one head per unit instead of a unit of mostly masked heads)
+  bool merged = can_merge && (L.row_bytes < kMergeBelowRowBytes || head_count == 1);
   // KVCK_MERGE_HEADS=0|1 overrides the choice where merging is possible (results are identical)
   if (const char* force = getenv("KVCK_MERGE_HEADS")) merged = can_merge && force[0] == '1';
   const int32_t lane_row_bytes = merged ? (int32_t)wide : L.row_bytes;
