@@ -219,3 +219,29 @@ def test_copy_element_transposed_planes(case, transpose, monkeypatch):
     assert np.array_equal(_expected_images(back_hnd, "HND", req2, hb, n_heads, bs, row_bytes)[:, :, 1:2], exp)
     assert sum(int(np.count_nonzero(np.ascontiguousarray(b).view(np.uint8))) for b in back) == int(np.count_nonzero(
         _expected_images(back_hnd, "HND", req2, hb, n_heads, bs, row_bytes)))   # bytes on both sides
+
+
+def test_copy_element_transposed_many_caches():
+    """Transposed V planes over more caches than one argument block (several launches):
+    the staging bytes and checksums equal those of the HND V planes holding the same tokens."""
+    log("[copy] transposed, 70 caches")
+    rng = np.random.default_rng(8)
+    req, nb = wl.page_requests(rng, [40, 9, 23], 16, spare_frac=0.5)
+    hp = [wl.host_random_bits(rng, wl.pool_shape("HND", nb, 16, 2, 64), "bf16") for _ in range(70)]
+    vt = [to_device_bits(np.ascontiguousarray(p[1].transpose(0, 1, 3, 2))) for p in hp]
+    vh = [to_device_bits(np.ascontiguousarray(p[1])) for p in hp]
+    layers = list(range(70))
+    bt, nbt, sp, nt = req_tensors(req)
+    per = kvck.kvck_staging_bytes(vt[0], "V_TRANS", 70)
+    st_t = torch.zeros(int(req.num_blocks.sum()) * per, dtype=torch.uint8, device=DEV)
+    st_h = torch.zeros_like(st_t)
+    got_t = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, vt, "V_TRANS", layers, bt, nbt, sp, nt, st_t,
+                                           check=True).cpu().numpy()
+    got_h = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, vh, "V_HND", layers, bt, nbt, sp, nt, st_h,
+                                           check=True).cpu().numpy()
+    assert np.array_equal(st_t.cpu().numpy(), st_h.cpu().numpy())
+    ref = [np.concatenate([np.zeros_like(p[:1]), p[1:]]) for p in hp]
+    want = oracle.checksum_blocks(ref, "HND", layers, [0] * 70, req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens)
+    for r, k in req.listed():
+        assert int(got_t[r, k]) == int(got_h[r, k]) == int(want[r, k]), (r, k)
