@@ -258,9 +258,10 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_kernel(const CopyArgs ca)
   }
 }
 
-// The same copy with the transpose staged through LDS, for larger blocks: the
-// register transpose leaves the side that is not stored touching one 16-byte
-// piece of each of many lines per instruction, which grows with block_size.
+// The same copy with the transpose staged through LDS (the choice whenever
+// chunks are 16 bytes): the register transpose leaves the side that is not
+// stored touching one 16-byte piece of each of many lines per instruction,
+// more of them as block_size grows.
 // Here both sides move whole contiguous chunks: pool chunks in pool order
 // (element row by element row), staging chunks in staging order (slot by
 // slot), and each wave's LDS region holds the group's image in staging form,
@@ -290,8 +291,8 @@ __device__ __forceinline__ uint32_t lds_load_element(const uint8_t* lds, uint32_
 
 extern __shared__ __attribute__((aligned(16))) uint8_t tcopy_lds[];
 
-// Bytes of one wave's LDS region: block_size rows of the group's elements,
-// rounded up to whole 16-byte columns.
+// Row pitch of a wave's LDS region (one row per slot, block_size rows): the
+// group's elements rounded up to whole 16-byte columns.
 __host__ __device__ inline int64_t tcopy_lds_pitch(int32_t rows_per_group, int es) {
   return ((int64_t)rows_per_group * es + 15) / 16 * 16;
 }
