@@ -168,6 +168,13 @@ typedef struct kvck_kv_layout {
  * single launch); KVCK_PLAN = "compact" turns this off, with identical
  * results and error bits.  Either way block_table entries k < max_blocks of
  * every row may be read, and only listed, valid ones are used.
+ *
+ * Other switches, read at each call, that change how the work is done but
+ * never the results: KVCK_MERGE_HEADS = "0" / "1" (read a slot's heads as one
+ * row: automatic for rows under 128 bytes and single heads), KVCK_MERGED_PIPE
+ * = "0" (merged rows unpipelined), KVCK_COPY_BUFFERS = "2" (fused copy with
+ * two load buffers per wave), KVCK_TCOPY = "regs" (fused copy of
+ * element-transposed planes transposed in registers instead of through LDS).
  */
 kvck_status kvck_checksum_blocks(
     const kvck_kv_layout* layout,          /* host */
