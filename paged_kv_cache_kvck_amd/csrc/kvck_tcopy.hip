@@ -266,9 +266,10 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_kernel(const CopyArgs ca)
 // (element row by element row), staging chunks in staging order (slot by
 // slot), and each wave's LDS region holds the group's image in staging form,
 // [slot][element], a row of pitch bytes.  Pool chunks go in and out element
-// by element.  The 16-byte columns of slot s are XOR-swizzled by (s / N) mod
-// 2^k (2^k dividing the row's column count, at most 8), so the N slots of a
-// pool chunk and the 64 lanes of a staging access fall in different banks.
+// by element.  The 16-byte columns of slot s are XOR-swizzled by
+// (s / N) * nd mod 2^k (nd: the columns one instruction's element rows span;
+// 2^k: the largest power of two dividing the row's column count), so the
+// slot groups one instruction writes or reads land in different banks.
 template <int ES>
 __device__ __forceinline__ void lds_store_element(uint8_t* lds, uint32_t addr, uint32_t v) {
   if constexpr (ES == 4)
@@ -319,8 +320,8 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_lds_kernel(const CopyArgs
   const int rge = a.rows_per_group;  // element rows per group, a multiple of N
   const uint32_t pitch = (uint32_t)tcopy_lds_pitch(rge, ES);
   const uint32_t cols = pitch / 16;
-  const uint32_t low = cols & (0u - cols);
-  const uint32_t kmask = (low < 8u ? low : 8u) - 1u;
+  const uint32_t kmask = (cols & (0u - cols)) - 1u;
+  const uint32_t nd = (uint32_t)max(1, kWave / cpe * ES / 16);  // columns of one instruction's element rows
   uint8_t* const lds = tcopy_lds + (threadIdx.x / kWave) * (int64_t)bs * pitch;
   const int cps = rge * ES / 16;     // staging chunks of a slot's row segment (full group)
 
@@ -337,13 +338,13 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_lds_kernel(const CopyArgs
     q0[s] = q * N;
     poff[s] = (uint32_t)((int64_t)d * a.chunk_stride + (int64_t)q * 16);
     const uint32_t dcol = (uint32_t)(d * ES);
-    lpool[s] = (uint32_t)(q * N) * pitch + ((((dcol >> 4) ^ ((uint32_t)q & kmask)) << 4) | (dcol & 15u));
+    lpool[s] = (uint32_t)(q * N) * pitch + ((((dcol >> 4) ^ (((uint32_t)q * nd) & kmask)) << 4) | (dcol & 15u));
     const bool sin = f < bs * cps;
     const int sl = f / cps, c = f - (f / cps) * cps;
     srow[s] = sin ? sl : 0x7fffffff;
     scol[s] = c;
     soff[s] = (uint32_t)((int64_t)sl * a.row_bytes + (int64_t)c * 16);
-    lstg[s] = (uint32_t)sl * pitch + ((((uint32_t)c) ^ (((uint32_t)sl / N) & kmask)) << 4);
+    lstg[s] = (uint32_t)sl * pitch + ((((uint32_t)c) ^ ((((uint32_t)sl / N) * nd) & kmask)) << 4);
   }
   const int D = a.row_bytes / ES;
   const int ngr = (D + rge - 1) / rge;
