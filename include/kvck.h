@@ -159,9 +159,10 @@ typedef struct kvck_kv_layout {
  * ignored.  kvck_blocks_workspace_bytes returns 0 for arguments the entry
  * points reject (num_caches < 1, negative sizes, num_reqs*max_blocks >= 2^31).
  *
- * Schedule: large batches (many tasks per resident wavefront) keep two load
- * batches in flight and give each task four layers; small ones use one layer
- * per task at higher occupancy.  The environment variable KVCK_SCHEDULE =
+ * Schedule: one workgroup of four wavefronts per compute unit.  Large
+ * batches (many tasks per resident wavefront) keep two load batches in flight
+ * per wavefront and give each task several layers; small ones use one layer
+ * per task.  The environment variable KVCK_SCHEDULE =
  * "pipelined" or "simple" forces one of the two; results are bit-identical.
  * Calls of at most 8192 (request slot, cache) pairs read the request arrays
  * in the main pass itself (no separate planning launch; the smallest run as a
@@ -174,7 +175,9 @@ typedef struct kvck_kv_layout {
  * row: automatic for rows under 128 bytes and single heads), KVCK_MERGED_PIPE
  * = "0" (merged rows unpipelined), KVCK_COPY_BUFFERS = "2" (fused copy with
  * two load buffers per wave), KVCK_TCOPY = "regs" (fused copy of
- * element-transposed planes transposed in registers instead of through LDS).
+ * element-transposed planes transposed in registers instead of through LDS),
+ * KVCK_GRID_PER_CU = n (workgroups per compute unit of every launch, up to
+ * what fits).
  */
 kvck_status kvck_checksum_blocks(
     const kvck_kv_layout* layout,          /* host */

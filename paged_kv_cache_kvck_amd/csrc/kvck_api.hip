@@ -111,7 +111,7 @@ constexpr int32_t kMergeBelowRowBytes = 128;
 // such blocks pipeline only in the narrow shape below (more row groups).
 constexpr int64_t kPipeTaskBytes = 256 * 1024;
 constexpr int kPipeMaxCaches = 16;
-constexpr int64_t kPipeMinTasksPerWave = 16;
+constexpr int64_t kPipeMinTasksPerWave = 32;
 static_assert(kCachesPerLaunch % kPipeMaxCaches == 0, "launch groups must not straddle launches");
 
 // `narrow` (or null) is the same rows split into lane tables of at most 4
@@ -131,7 +131,7 @@ bool merged_pipe_off() {
 
 void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_caches, int64_t max_items,
                      int64_t block_bytes, int planes, int heads, int cus, bool copy, bool dense) {
-  const int64_t waves = (int64_t)cus * 8;  // resident waves of the pipelined kernel (2 per SIMD)
+  const int64_t waves = (int64_t)cus * 4 * kMainWorkgroupsPerCU;  // resident waves of the main pass
   int lpt = 1;
   while (lpt < kPipeMaxCaches && (int64_t)(2 * lpt) * block_bytes <= kPipeTaskBytes) lpt *= 2;
   const int64_t tasks = max_items * ((num_caches + lpt - 1) / lpt);

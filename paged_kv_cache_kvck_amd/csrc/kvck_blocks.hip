@@ -188,9 +188,9 @@ template <int CHUNK, int S, int HU, int PU, bool PIPE, bool MERGED, bool DENSE>
 __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs a) {
   using V = typename ChunkType<CHUNK>::T;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+  const int64_t wave = wave_index();
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
-  const int64_t n_items = DENSE ? a.max_items : (int64_t)*a.n_items;
+  const int64_t n_items = DENSE ? a.max_items : (int64_t)read_const(a.n_items);
   const int lpt = a.caches_per_task;
   const int ngroups = (a.num_caches + lpt - 1) / lpt;
   const int64_t total = n_items * ngroups;
@@ -225,9 +225,10 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
       const int nunits = ngr * nplanes * nhb * (c_end - c_begin);
       UnitCursor ic{c_begin, 0, 0, 0}, cc{c_begin, 0, 0, 0};
 
-      auto issue = [&](V(&x)[PU][HU][S]) {
-        const int rows = min(rg, v - ic.group * rg);
-        const uint8_t* base = a.base[ic.cache] + blk_off + (int64_t)(ic.group * rg) * a.slot_stride +
+      // `live` false: a unit past the task's last one, every load out of range
+      auto issue = [&](V(&x)[PU][HU][S], bool live) {
+        const int rows = live ? min(rg, v - ic.group * rg) : 0;
+        const uint8_t* base = a.base[live ? ic.cache : c_begin] + blk_off + (int64_t)(ic.group * rg) * a.slot_stride +
                               (int64_t)(ic.plane * PU) * a.plane_stride;
         uint32_t voff[S];
 #pragma unroll
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
             for (int s = 0; s < S; ++s) x[p][h][s] = load_chunk<CHUNK>(rs, voff[s] | hmask);
           }
         }
-        ic.next(nhb, nplanes, ngr);
+        if (live) ic.next(nhb, nplanes, ngr);
       };
       auto consume = [&](const V(&x)[PU][HU][S]) {
         const uint32_t mb = a.mbase[cc.cache];
@@ -278,20 +279,26 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
       };
 
       if constexpr (PIPE) {
+        // Both buffers are issued at every step, past the task's last unit
+        // with every load out of range (zeros, no memory touched): with no
+        // branch around an issue, the waits before consuming one buffer count
+        // the other buffer's loads as still to come, and leave them in flight.
+        // order_after keeps a buffer's next loads after the last use of its
+        // data, so each buffer keeps its registers across steps.
         V A[PU][HU][S], B[PU][HU][S];
-        issue(A);
+        issue(A, true);
         for (int ui = 0; ui < nunits; ui += 2) {
-          if (ui + 1 < nunits) issue(B);
+          issue(B, ui + 1 < nunits);
           consume(A);
-          if (ui + 1 < nunits) {
-            if (ui + 2 < nunits) issue(A);
-            consume(B);
-          }
+          order_after(acc);
+          issue(A, ui + 2 < nunits);
+          if (ui + 1 < nunits) consume(B);
+          order_after(acc);
         }
       } else {
         for (int ui = 0; ui < nunits; ++ui) {
           V A[PU][HU][S];
-          issue(A);
+          issue(A, true);
           consume(A);
         }
       }
@@ -446,9 +453,16 @@ int kernel_occupancy(const void* fn, int device, int fallback) {
   return per_cu;
 }
 
-namespace {
-
-}  // namespace
+// Workgroups per CU a launch uses: `preferred`, at most what fits, or
+// KVCK_GRID_PER_CU=n where set (an A/B switch; results are identical).
+int workgroups_per_cu(int fits, int preferred) {
+  int n = preferred < fits ? preferred : fits;
+  if (const char* e = getenv("KVCK_GRID_PER_CU")) {
+    const int f = atoi(e);
+    if (f >= 1) n = f < fits ? f : fits;
+  }
+  return n < 1 ? 1 : n;
+}
 
 hipError_t launch_plan(const int32_t* block_table, int64_t bt_stride, const int32_t* nbpr,
                        const int64_t* start_pos, const int64_t* num_tokens, int32_t num_reqs,
@@ -480,7 +494,8 @@ hipError_t launch_plan(const int32_t* block_table, int64_t bt_stride, const int3
 
 int blocks_grid(const BlocksShape& shp, int device, int64_t max_tasks) {
   BlocksFn fn = blocks_fn(shp);
-  const int per_cu = kernel_occupancy(reinterpret_cast<const void*>(fn), device, 2);
+  const int fits = kernel_occupancy(reinterpret_cast<const void*>(fn), device, 2);
+  const int per_cu = workgroups_per_cu(fits, kMainWorkgroupsPerCU);
   const int64_t waves_per_block = kBlockThreads / kWave;
   const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
   const int64_t cap = (int64_t)per_cu * device_cus(device);

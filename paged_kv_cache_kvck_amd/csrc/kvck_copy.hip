@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
   using V = typename ChunkType<CHUNK>::T;
   const BlocksArgs& a = ca.b;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+  const int64_t wave = wave_index();
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
   const int64_t n_items = (int64_t)*a.n_items;
   const int lpt = a.caches_per_task;
@@ -72,12 +72,11 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
     const int64_t item = task - grp * n_items;
     const int c_begin = (int)grp * lpt;
     const int c_end = min(a.num_caches, c_begin + lpt);
-    const PosRecord* rp = a.recs + item;
-    int32_t v = __builtin_amdgcn_readfirstlane(rp->valid);
-    const int32_t blk = __builtin_amdgcn_readfirstlane(rp->block);
-    const uint64_t t0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(rp->t0 >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)rp->t0);
-    const int64_t out_idx = rp->out_idx;
+    const TaskRecord rec = task_record<false>(a, item, false, lane);
+    int32_t v = rec.valid;
+    const int32_t blk = rec.block;
+    const uint64_t t0 = rec.t0;
+    const int64_t out_idx = rec.out_idx;
     if (item >= ca.staging_positions) {
       if (v > 0 && lane == 0 && ca.error_flags) atomicOr(ca.error_flags, KVCK_FLAG_STAGING_FULL);
       v = 0;
@@ -100,21 +99,24 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
         return img0 + (int64_t)u.cache * ca.image_bytes + (int64_t)(u.plane * PU + p) * img_plane +
                (int64_t)hh * img_head + (int64_t)(u.group * rg) * a.row_bytes;
       };
-      auto issue = [&](V(&x)[PU][HU][S]) {
-        const int rows = min(rg, v - ic.group * rg);
+      // `live` false: a unit past the task's last one, every load out of range
+      auto issue = [&](V(&x)[PU][HU][S], bool live) {
+        const int rows = live ? min(rg, v - ic.group * rg) : 0;
+        UnitCursor u = ic;
+        if (!live) u.cache = c_begin;
 #pragma unroll
         for (int p = 0; p < PU; ++p) {
 #pragma unroll
           for (int h = 0; h < HU; ++h) {
-            const int hh = ic.hbatch * HU + h;
+            const int hh = u.hbatch * HU + h;
             const uint32_t hmask = hh < a.heads ? 0u : kOOB;
-            const __amdgpu_buffer_rsrc_t rs = make_rsrc(DIR == 0 ? pool_base(ic, p, hh) : img_base(ic, p, hh));
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(DIR == 0 ? pool_base(u, p, hh) : img_base(u, p, hh));
 #pragma unroll
             for (int s = 0; s < S; ++s)
               x[p][h][s] = load_chunk<CHUNK>(rs, (lt.row[s] < rows ? (DIR == 0 ? lt.off[s] : ioff[s]) : kOOB) | hmask);
           }
         }
-        ic.next(nhb, nplanes, ngr);
+        if (live) ic.next(nhb, nplanes, ngr);
       };
       auto store_consume = [&](const V(&x)[PU][HU][S]) {
         const int rows = min(rg, v - cc.group * rg);
@@ -154,20 +156,23 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
       };
 
       if constexpr (PIPE) {
+        // Both buffers are issued at every step (past the last unit with every
+        // load out of range) and order_after keeps a buffer's next loads after
+        // the last use of its data, as in the checksum kernel.
         V A[PU][HU][S], B[PU][HU][S];
-        issue(A);
+        issue(A, true);
         for (int ui = 0; ui < nunits; ui += 2) {
-          if (ui + 1 < nunits) issue(B);
+          issue(B, ui + 1 < nunits);
           store_consume(A);
-          if (ui + 1 < nunits) {
-            if (ui + 2 < nunits) issue(A);
-            store_consume(B);
-          }
+          order_after(acc);
+          issue(A, ui + 2 < nunits);
+          if (ui + 1 < nunits) store_consume(B);
+          order_after(acc);
         }
       } else {
         for (int ui = 0; ui < nunits; ++ui) {
           V A[PU][HU][S];
-          issue(A);
+          issue(A, true);
           store_consume(A);
         }
       }
@@ -224,7 +229,8 @@ CopyFn copy_fn(const BlocksShape& shp, int direction) {
 
 int copy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks) {
   CopyFn fn = copy_fn(shp, direction);
-  const int per_cu = fn ? kernel_occupancy(reinterpret_cast<const void*>(fn), device, 1) : 1;
+  const int fits = fn ? kernel_occupancy(reinterpret_cast<const void*>(fn), device, 1) : 1;
+  const int per_cu = workgroups_per_cu(fits, kAllThatFit);
   const int cus = device_cus(device);
   const int64_t waves_per_block = kBlockThreads / kWave;
   const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;

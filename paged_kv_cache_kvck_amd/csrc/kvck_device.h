@@ -39,6 +39,19 @@ __device__ __forceinline__ typename ChunkType<CHUNK>::T load_chunk(__amdgpu_buff
     return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kNonTemporal);
 }
 
+// Wavefront of the calling lane within its workgroup, and within the grid.
+// threadIdx.x / 64 is the same on every lane of a wavefront, but the compiler
+// cannot prove it; taken through readfirstlane it is a scalar, and so is all
+// that derives from it (task, cache, page address).  Without that, each
+// buffer load whose descriptor derives from it is wrapped in a loop that
+// compares the descriptor across lanes.
+__device__ __forceinline__ int wave_in_block() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
+__device__ __forceinline__ int64_t wave_index() {
+  return (int64_t)blockIdx.x * (kBlockThreads / kWave) + wave_in_block();
+}
+
 // A 64-bit value moved across lanes by one DPP control, as two 32-bit halves;
 // lanes of rows outside ROW_MASK get 0.
 template <int CTRL, int ROW_MASK = 0xf>
@@ -139,6 +152,22 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// An empty statement that reads v and may touch memory: v is complete before
+// it, and no load moves above it.  Placed between the last use of a load
+// buffer and its next loads, it keeps the two from overlapping, so a buffer
+// reloaded in a loop keeps its registers instead of being copied back (and
+// waited for) at every step.
+__device__ __forceinline__ void order_after(uint64_t v) { asm volatile("" ::"v"(v) : "memory"); }
+
+// Read-only inputs of a launch (the plan, the request arrays) read through
+// the constant address space: at a uniform address that is a scalar load,
+// counted apart from the vector loads of cache bytes, so waiting for a task's
+// record does not also wait for the cache loads still in flight.
+template <class T>
+__device__ __forceinline__ T read_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // What a task needs of its position.  `listed` is false for dense slots past
 // a request's listed count (or of a bad request): such tasks write nothing.
 struct TaskRecord {
@@ -159,20 +188,20 @@ __device__ __forceinline__ TaskRecord task_record(const BlocksArgs& a, int64_t i
   TaskRecord t;
   if constexpr (!DENSE) {
     const PosRecord* rp = a.recs + item;
-    t.valid = __builtin_amdgcn_readfirstlane(rp->valid);
-    t.block = __builtin_amdgcn_readfirstlane(rp->block);
-    t.t0 = (uint64_t)uniform64(rp->t0);
-    t.out_idx = rp->out_idx;
+    t.valid = __builtin_amdgcn_readfirstlane(read_const(&rp->valid));
+    t.block = __builtin_amdgcn_readfirstlane(read_const(&rp->block));
+    t.t0 = (uint64_t)uniform64(read_const(&rp->t0));
+    t.out_idx = read_const(&rp->out_idx);
     t.listed = true;
     return t;
   }
   const int32_t r = (int32_t)item / a.max_blocks;  // item < 2^31
   const int32_t k = (int32_t)item - r * a.max_blocks;
   // four independent loads; the table entry is in bounds for every k < max_blocks
-  const int32_t n = __builtin_amdgcn_readfirstlane(a.nbpr[r]);
-  const int64_t s = uniform64(a.start_pos[r]);
-  const int64_t ntok = uniform64(a.num_tokens[r]);
-  const int32_t b = __builtin_amdgcn_readfirstlane(a.block_table[(int64_t)r * a.bt_stride + k]);
+  const int32_t n = __builtin_amdgcn_readfirstlane(read_const(a.nbpr + r));
+  const int64_t s = uniform64(read_const(a.start_pos + r));
+  const int64_t ntok = uniform64(read_const(a.num_tokens + r));
+  const int32_t b = __builtin_amdgcn_readfirstlane(read_const(a.block_table + (int64_t)r * a.bt_stride + k));
   t.out_idx = item;
   t.block = b;
   t.valid = 0;

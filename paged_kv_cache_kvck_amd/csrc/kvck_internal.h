@@ -13,6 +13,13 @@ namespace kvck {
 constexpr int kWave = 64;
 constexpr int kBlockThreads = 256;          // 4 independent waves per workgroup
 constexpr int kCachesPerLaunch = 64;        // caches carried in one argument block
+// Workgroups per CU of a planned checksum main pass (fewer than fit): one
+// wave per SIMD, each with two units of loads in flight.  Against full
+// occupancy, interleaved on one GPU over every pool shape measured: never
+// slower, 1-1.5 points of 8 TB/s faster on the large pools; fewer streams
+// read faster once each one is double-buffered.
+constexpr int kMainWorkgroupsPerCU = 1;
+constexpr int kAllThatFit = 1 << 20;  // workgroups_per_cu: as many as fit
 constexpr int kLayersPerStatesLaunch = 32;  // Mamba layers carried in one argument block
 constexpr size_t kAlign = 256;
 // Checksum calls of at most this many (slot, cache) tasks plan in place: the
@@ -155,5 +162,6 @@ hipError_t launch_tags(const uint64_t* checksums, const uint8_t* hashes, int64_t
 int states_grid(int device, int64_t tasks);
 int device_cus(int device);                                   // cached per device
 int kernel_occupancy(const void* fn, int device, int fallback);  // workgroups per CU, cached
+int workgroups_per_cu(int fits, int preferred);                  // what a launch uses of `fits`
 
 }  // namespace kvck

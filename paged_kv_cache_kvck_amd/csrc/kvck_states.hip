@@ -103,7 +103,8 @@ __global__ __launch_bounds__(kBlockThreads) void states_kernel(const StatesArgs 
 }  // namespace
 
 int states_grid(int device, int64_t tasks) {
-  const int per_cu = kernel_occupancy(reinterpret_cast<const void*>(&states_kernel), device, 2);
+  const int fits = kernel_occupancy(reinterpret_cast<const void*>(&states_kernel), device, 2);
+  const int per_cu = workgroups_per_cu(fits, kAllThatFit);
   const int cus = device_cus(device);
   const int64_t need = (tasks + (kBlockThreads / kWave) - 1) / (kBlockThreads / kWave);
   const int64_t cap = (int64_t)per_cu * cus;

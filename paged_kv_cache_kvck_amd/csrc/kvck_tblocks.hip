@@ -30,7 +30,7 @@ __global__ __launch_bounds__(kBlockThreads) void tblocks_kernel(const BlocksArgs
   constexpr int N = CHUNK / ES;        // slots per chunk
   constexpr int PER_PIECE = 8 / ES;    // elements per 8-byte piece
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+  const int64_t wave = wave_index();
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
   const int64_t n_items = DENSE ? a.max_items : (int64_t)*a.n_items;
   const int lpt = a.caches_per_task;
@@ -97,9 +97,11 @@ __global__ __launch_bounds__(kBlockThreads) void tblocks_kernel(const BlocksArgs
       };
       const int nunits = (c_end - c_begin) * ngr * nhb;
       Cursor ic{c_begin, 0, 0}, cc{c_begin, 0, 0};
-      auto issue = [&](V(&x)[HU][S]) {
-        const int rows = min(rge, D - ic.group * rge);
-        const uint8_t* gbase = a.base[ic.cache] + blk_off + (int64_t)(ic.group * rge) * a.chunk_stride;
+      // `live` false: a unit past the task's last one, every load out of range
+      auto issue = [&](V(&x)[HU][S], bool live) {
+        const int rows = live ? min(rge, D - ic.group * rge) : 0;
+        const uint8_t* gbase =
+            a.base[live ? ic.cache : c_begin] + blk_off + (int64_t)(ic.group * rge) * a.chunk_stride;
 #pragma unroll
         for (int h = 0; h < HU; ++h) {
           const int hh = ic.hbatch * HU + h;
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(kBlockThreads) void tblocks_kernel(const BlocksArgs
           for (int s = 0; s < S; ++s)
             x[h][s] = load_chunk<CHUNK>(rs, (erow[s] < rows && nvalid[s] > 0 ? off[s] : kOOB) | hmask);
         }
-        ic.next(nhb, ngr);
+        if (live) ic.next(nhb, ngr);
       };
       auto consume = [&](const V(&x)[HU][S]) {
         const uint32_t mb = a.mbase[cc.cache];
@@ -130,20 +132,24 @@ __global__ __launch_bounds__(kBlockThreads) void tblocks_kernel(const BlocksArgs
         cc.next(nhb, ngr);
       };
       if constexpr (PIPE) {
+        // Both buffers are issued at every step (past the last unit with every
+        // load out of range) and order_after keeps a buffer's next loads after
+        // the last use of its data, as in the row-layout kernel: the waits for
+        // one buffer then leave the other's loads in flight.
         V A[HU][S], B[HU][S];
-        issue(A);
+        issue(A, true);
         for (int ui = 0; ui < nunits; ui += 2) {
-          if (ui + 1 < nunits) issue(B);
+          issue(B, ui + 1 < nunits);
           consume(A);
-          if (ui + 1 < nunits) {
-            if (ui + 2 < nunits) issue(A);
-            consume(B);
-          }
+          order_after(acc);
+          issue(A, ui + 2 < nunits);
+          if (ui + 1 < nunits) consume(B);
+          order_after(acc);
         }
       } else {
         for (int ui = 0; ui < nunits; ++ui) {
           V A[HU][S];
-          issue(A);
+          issue(A, true);
           consume(A);
         }
       }
@@ -207,7 +213,8 @@ TFn tfn(const BlocksShape& shp) { return shp.dense ? tfn_plan<true>(shp) : tfn_p
 
 int tblocks_grid(const BlocksShape& shp, int device, int64_t max_tasks) {
   TFn fn = tfn(shp);
-  const int per_cu = fn ? kernel_occupancy(reinterpret_cast<const void*>(fn), device, 2) : 1;
+  const int fits = fn ? kernel_occupancy(reinterpret_cast<const void*>(fn), device, 2) : 1;
+  const int per_cu = workgroups_per_cu(fits, kAllThatFit);
   const int64_t waves_per_block = kBlockThreads / kWave;
   const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
   const int64_t cap = (int64_t)per_cu * device_cus(device);

@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_kernel(const CopyArgs ca)
   constexpr int PER_PIECE = 8 / ES;   // elements per 8-byte piece
   const BlocksArgs& a = ca.b;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+  const int64_t wave = wave_index();
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
   const int64_t n_items = (int64_t)*a.n_items;
   const int lpt = a.caches_per_task;
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_lds_kernel(const CopyArgs
   constexpr int PER_PIECE = 8 / ES;
   const BlocksArgs& a = ca.b;
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t wave = (int64_t)blockIdx.x * (kBlockThreads / kWave) + (threadIdx.x / kWave);
+  const int64_t wave = wave_index();
   const int64_t nwaves = (int64_t)gridDim.x * (kBlockThreads / kWave);
   const int64_t n_items = (int64_t)*a.n_items;
   const int lpt = a.caches_per_task;
@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_lds_kernel(const CopyArgs
   const uint32_t cols = pitch / 16;
   const uint32_t kmask = (cols & (0u - cols)) - 1u;
   const uint32_t nd = (uint32_t)max(1, kWave / cpe * ES / 16);  // columns of one instruction's element rows
-  uint8_t* const lds = tcopy_lds + (threadIdx.x / kWave) * (int64_t)bs * pitch;
+  uint8_t* const lds = tcopy_lds + wave_in_block() * (int64_t)bs * pitch;
   const int cps = rge * ES / 16;     // staging chunks of a slot's row segment (full group)
 
   // pool side: chunk f is element row d = f / cpe, slots q N.. (q = f mod cpe)
@@ -550,6 +550,7 @@ int tcopy_grid(const BlocksShape& shp, int direction, int device, int64_t max_ta
     const int by_lds = (int)((size_t)per_cu_lds / lds);
     per_cu = by_lds < 1 ? 1 : (by_lds < per_cu ? by_lds : per_cu);
   }
+  per_cu = workgroups_per_cu(per_cu, kAllThatFit);
   const int64_t waves_per_block = kBlockThreads / kWave;
   const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
   const int64_t cap = (int64_t)per_cu * device_cus(device);
