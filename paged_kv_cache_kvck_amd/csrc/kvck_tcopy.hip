@@ -377,31 +377,58 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_lds_kernel(const CopyArgs
       }
       const bool straddle = (v % N) != 0;
       const int nunits = (c_end - c_begin) * ngr * a.heads;
-      int cache = c_begin, group = 0, hh = 0;
-      for (int ui = 0; ui < nunits; ++ui) {
-        const int rows = min(rge, D - group * rge);
-        const int seg = rows * ES / 16;  // staging chunks of this group's row segment
-        const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.base[cache] + blk_off + (int64_t)(group * rge) * a.chunk_stride +
-                                                    (int64_t)hh * a.head_stride);
-        const __amdgpu_buffer_rsrc_t rst = make_rsrc(img0 + (int64_t)cache * ca.image_bytes +
-                                                     (int64_t)hh * img_head + (int64_t)(group * rge) * ES);
-        uint64_t sh = 0;
-        V x[S];
+      // units: (cache, element-row group, head), cache-major
+      struct Cursor {
+        int cache, group, hh;
+        __device__ __forceinline__ void next(int heads, int ngr_) {
+          if (++hh == heads) {
+            hh = 0;
+            if (++group == ngr_) {
+              group = 0;
+              ++cache;
+            }
+          }
+        }
+      };
+      Cursor ic{c_begin, 0, 0}, cc{c_begin, 0, 0};
+      auto pool_rsrc = [&](const Cursor& u) {
+        return make_rsrc(a.base[u.cache] + blk_off + (int64_t)(u.group * rge) * a.chunk_stride +
+                         (int64_t)u.hh * a.head_stride);
+      };
+      auto stg_rsrc = [&](const Cursor& u) {
+        return make_rsrc(img0 + (int64_t)u.cache * ca.image_bytes + (int64_t)u.hh * img_head +
+                         (int64_t)(u.group * rge) * ES);
+      };
+      // `live` false: a unit past the task's last one, every load out of range
+      auto issue = [&](V(&x)[S], bool live) {
+        Cursor u = ic;
+        if (!live) u.cache = c_begin;
+        const int rows = live ? min(rge, D - u.group * rge) : 0;
         if constexpr (DIR == 0) {
+          const __amdgpu_buffer_rsrc_t rp = pool_rsrc(u);
 #pragma unroll
           for (int s = 0; s < S; ++s) x[s] = load_chunk<16>(rp, prow[s] < rows && q0[s] < v ? poff[s] : kOOB);
         } else {
+          const int seg = rows * ES / 16;  // staging chunks of this group's row segment
+          const __amdgpu_buffer_rsrc_t rst = stg_rsrc(u);
 #pragma unroll
-          for (int s = 0; s < S; ++s)
-            x[s] = load_chunk<16>(rst, srow[s] < v && scol[s] < seg ? soff[s] : kOOB);
+          for (int s = 0; s < S; ++s) x[s] = load_chunk<16>(rst, srow[s] < v && scol[s] < seg ? soff[s] : kOOB);
         }
+        if (live) ic.next(a.heads, ngr);
+      };
+      auto process = [&](const V(&x)[S]) {
+        const int rows = min(rge, D - cc.group * rge);
+        const int seg = rows * ES / 16;
+        const __amdgpu_buffer_rsrc_t rp = pool_rsrc(cc);
+        const __amdgpu_buffer_rsrc_t rst = stg_rsrc(cc);
+        uint64_t sh = 0;
         if constexpr (DIR == 0) {
           // checksum of each pool chunk, then its elements into the staging form
 #pragma unroll
           for (int s = 0; s < S; ++s) {
             uint64_t E, K;
             chunk_sums<ES>(x[s], nvalid[s], E, K);
-            const uint32_t d = (uint32_t)(group * rge) + (uint32_t)prow[s];
+            const uint32_t d = (uint32_t)(cc.group * rge) + (uint32_t)prow[s];
             sh += ((ubase[s] + 2ull * (d / PER_PIECE)) * E + 2ull * P * K) << (8 * ES * (d % PER_PIECE));
             if (prow[s] < rge) {
 #pragma unroll
@@ -436,7 +463,7 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_lds_kernel(const CopyArgs
             for (int i = 0; i < 4; ++i) xv[i] = w[i];
             uint64_t E, K;
             chunk_sums<ES>(xv, nvalid[s], E, K);
-            const uint32_t d = (uint32_t)(group * rge) + (uint32_t)prow[s];
+            const uint32_t d = (uint32_t)(cc.group * rge) + (uint32_t)prow[s];
             sh += ((ubase[s] + 2ull * (d / PER_PIECE)) * E + 2ull * P * K) << (8 * ES * (d % PER_PIECE));
             const bool row_ok = prow[s] < rows;
             store_chunk<16>(rp, row_ok && nvalid[s] == N ? poff[s] : kOOB, xv);
@@ -450,14 +477,22 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_lds_kernel(const CopyArgs
           }
           __builtin_amdgcn_wave_barrier();
         }
-        acc += sh * (uint64_t)(a.mbase[cache] + 2u * (uint32_t)hh);
-        if (++hh == a.heads) {
-          hh = 0;
-          if (++group == ngr) {
-            group = 0;
-            ++cache;
-          }
-        }
+        acc += sh * (uint64_t)(a.mbase[cc.cache] + 2u * (uint32_t)cc.hh);
+        cc.next(a.heads, ngr);
+      };
+      // Two unit buffers: the loads of the next unit are in flight while this
+      // one goes through LDS.  Both are issued at every step (past the last
+      // unit with every load out of range) and order_after keeps a buffer's
+      // reload after the last use of its data, as in the checksum kernel.
+      V A[S], B[S];
+      issue(A, true);
+      for (int ui = 0; ui < nunits; ui += 2) {
+        issue(B, ui + 1 < nunits);
+        process(A);
+        order_after(acc);
+        issue(A, ui + 2 < nunits);
+        if (ui + 1 < nunits) process(B);
+        order_after(acc);
       }
     }
     acc = wave_sum(acc);
