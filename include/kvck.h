@@ -64,7 +64,8 @@ typedef enum kvck_status {
                                      width not 2 or 4, too many caches, a
                                      tensor whose strided byte extent reaches
                                      2^50 (pool, state, staging, hashes) */
-  KVCK_ERR_MISALIGNED = -3,       /* base pointer or stride not 8-byte aligned */
+  KVCK_ERR_MISALIGNED = -3,       /* base pointer or stride not 8-byte aligned, or an array
+                                     not aligned to its element size */
   KVCK_ERR_WORKSPACE = -4,        /* workspace missing or too small */
   KVCK_ERR_HIP = -5,              /* a HIP runtime call failed */
   KVCK_ERR_NO_DEVICE = -6         /* no gfx950 device is current */

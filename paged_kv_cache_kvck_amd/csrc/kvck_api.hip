@@ -317,6 +317,10 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   if (num_reqs < 0 || max_blocks < 0) return KVCK_ERR_INVALID_ARGUMENT;
   if (num_reqs == 0 || max_blocks == 0) return KVCK_OK;
   if (!block_table || !num_blocks_per_req || !start_pos || !num_tokens || !out) return KVCK_ERR_INVALID_ARGUMENT;
+  // arrays aligned to their element size (small calls read the request arrays with scalar loads)
+  if (!aligned(block_table, 4) || !aligned(num_blocks_per_req, 4) || !aligned(start_pos, 8) ||
+      !aligned(num_tokens, 8) || !aligned(out, 8) || (error_flags && !aligned(error_flags, 4)))
+    return KVCK_ERR_MISALIGNED;
   if (block_table_row_stride < max_blocks) return KVCK_ERR_INVALID_ARGUMENT;
   if ((int64_t)num_reqs * max_blocks >= (int64_t)1 << 31) return KVCK_ERR_UNSUPPORTED;
   // ---- alignment: 16-byte lane loads when everything allows, else 8-byte

@@ -65,13 +65,14 @@ struct BlocksCall {
   int32_t direction = -1;  // -1: kvck_checksum_blocks; else kvck_copy_checksum_blocks
   void* staging = kFake;
   int64_t staging_positions = 64;
+  uintptr_t bt_off = 0, nb_off = 0, i64_off = 0;  // byte offsets of the request arrays (misalignment)
 
   int run() {
     const size_t need = ws_bytes ? ws_bytes
                                  : kvck_blocks_workspace_bytes((int32_t)ptrs.size(), num_reqs, max_blocks);
-    const auto* bt = static_cast<const int32_t*>(kFake);
-    const auto* nb = static_cast<const int32_t*>(kFake);
-    const auto* i64 = static_cast<const int64_t*>(kFake);
+    const auto* bt = static_cast<const int32_t*>(fake(bt_off));
+    const auto* nb = static_cast<const int32_t*>(fake(nb_off));
+    const auto* i64 = static_cast<const int64_t*>(fake(i64_off));
     if (direction < 0)
       return kvck_checksum_blocks(&L, ptrs.data(), layers.data(), bases.data(), (int32_t)ptrs.size(), head_begin,
                                   head_count, bt, bt_stride, nb, i64, i64, num_reqs, max_blocks,
@@ -106,6 +107,12 @@ void blocks_checks(bool have_device) {
   EXPECT_EQ(call([](BlocksCall& c) { c.ptrs[1] = nullptr; }), KVCK_ERR_INVALID_ARGUMENT);
   EXPECT_EQ(call([](BlocksCall& c) { c.out = nullptr; }), KVCK_ERR_INVALID_ARGUMENT);
   EXPECT_EQ(call([](BlocksCall& c) { c.bt_stride = 4; }), KVCK_ERR_INVALID_ARGUMENT);
+  // request arrays and out aligned to their element size
+  EXPECT_EQ(call([](BlocksCall& c) { c.bt_off = 2; }), KVCK_ERR_MISALIGNED);
+  EXPECT_EQ(call([](BlocksCall& c) { c.nb_off = 2; }), KVCK_ERR_MISALIGNED);
+  EXPECT_EQ(call([](BlocksCall& c) { c.i64_off = 4; }), KVCK_ERR_MISALIGNED);
+  EXPECT_EQ(call([](BlocksCall& c) { c.out = fake(4); }), KVCK_ERR_MISALIGNED);
+  EXPECT_EQ(call([](BlocksCall& c) { c.direction = KVCK_COPY_LOAD, c.bt_off = 1; }), KVCK_ERR_MISALIGNED);
   EXPECT_EQ(call([](BlocksCall& c) { c.ws_bytes = 64; }), KVCK_ERR_WORKSPACE);
   EXPECT_EQ(call([](BlocksCall& c) { c.ws = fake(8); }), KVCK_ERR_WORKSPACE);
   EXPECT_EQ(call([](BlocksCall& c) { c.ws = nullptr; }), KVCK_ERR_WORKSPACE);
