@@ -12,7 +12,8 @@
 //     non-temporal 1 KiB buffer loads per batch, the runs taken in address
 //     order or in a scrambled order (odd multiplier modulo a power of two: a
 //     permutation), which is the shape of a paged cache walked through a block
-//     table.  "pipelined" keeps a second batch in flight while the first is used;
+//     table.  "pipelined" keeps a second batch in flight while the first is used
+//     (one or two workgroups per CU);
 //   * copy: one half of the buffer to the other (read + write), by a streaming
 //     kernel and by the runtime's device-to-device copy.
 #include <hip/hip_runtime.h>
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(256) void runs_kernel(const uint8_t* __restrict__ p
   constexpr uint32_t kBatch = 16 * 1024;
   constexpr uint32_t kOutside = 0x80000000u;
   const uint32_t lane = threadIdx.x & 63u;
-  const uint64_t wave = (uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const uint64_t wave = (uint64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint64_t nwaves = (uint64_t)gridDim.x * 4;
   const int batches = (int)((run + kBatch - 1) / kBatch);
   uint32_t acc = 0;
@@ -84,14 +85,17 @@ __global__ __launch_bounds__(256) void runs_kernel(const uint8_t* __restrict__ p
       for (int i = 0; i < 16; ++i) acc ^= x[i].x ^ x[i].y ^ x[i].z ^ x[i].w;
     };
     if constexpr (PIPE) {
+      // both buffers issued at every step (batches past the run read nothing),
+      // the empty asm keeps a buffer's reload after its last use: the waits
+      // for one buffer leave the other's loads in flight
       issue(a, 0);
       for (int k = 0; k < batches; k += 2) {
-        if (k + 1 < batches) issue(b, k + 1);
+        issue(b, k + 1);
         use(a);
-        if (k + 1 < batches) {
-          if (k + 2 < batches) issue(a, k + 2);
-          use(b);
-        }
+        asm volatile("" ::"v"(acc) : "memory");
+        issue(a, k + 2);
+        use(b);
+        asm volatile("" ::"v"(acc) : "memory");
       }
     } else {
       for (int k = 0; k < batches; ++k) {
@@ -185,8 +189,9 @@ int main(int argc, char** argv) {
                 time_gbs([&] { runs_kernel<false, false><<<grid, 256>>>(p, nruns, run, out); }, rb));
     std::printf("runs %2u KiB scrambled            grid=%6d : %8.1f GB/s\n", run_kib, grid,
                 time_gbs([&] { runs_kernel<true, false><<<grid, 256>>>(p, nruns, run, out); }, rb));
-    std::printf("runs %2u KiB scrambled, pipelined grid=%6d : %8.1f GB/s\n", run_kib, cus * 2,
-                time_gbs([&] { runs_kernel<true, true><<<cus * 2, 256>>>(p, nruns, run, out); }, rb));
+    for (int per_cu : {1, 2})
+      std::printf("runs %2u KiB scrambled, pipelined grid=%6d : %8.1f GB/s\n", run_kib, cus * per_cu,
+                  time_gbs([&] { runs_kernel<true, true><<<cus * per_cu, 256>>>(p, nruns, run, out); }, rb));
   }
   // copies between the two halves of the buffer (bytes read + bytes written)
   const size_t half = bytes / 2 / 16 * 16;
