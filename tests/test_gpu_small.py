@@ -76,6 +76,42 @@ def test_parity_small(case, schedule):
     assert_unlisted_untouched(got, req)
 
 
+_GRID_CASE = {}
+
+
+def _grid_case():
+    """About 2,200 listed positions over 4 layers: with the listed plan, more
+    tasks than resident waves at any launch shape, so each wave runs several."""
+    if not _GRID_CASE:
+        rng = np.random.default_rng(77)
+        lengths = rng.integers(100, 601, size=100)
+        layers = [0, 3, 4, 9]
+        req, nb = wl.page_requests(rng, lengths, 16, spare_frac=0.1)
+        hpools = [wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 16, 12, 64), "fp16") for _ in layers]
+        want = oracle.checksum_blocks(hpools, "NHD", layers, [0] * len(layers), req.block_table, req.num_blocks,
+                                      req.start_pos, req.num_tokens)
+        _GRID_CASE.update(req=req, hpools=hpools, layers=layers, want=want)
+    return _GRID_CASE
+
+
+@pytest.mark.parametrize("grid", ["1", "2", "64"])
+@pytest.mark.parametrize("sched", ["simple", "pipelined"])
+def test_launch_shapes_match_oracle(grid, sched, monkeypatch):
+    """Results do not depend on the launch shape: one, two or as many
+    workgroups per CU as fit (KVCK_GRID_PER_CU), under either schedule, with
+    every wave striding over several tasks."""
+    monkeypatch.setenv("KVCK_GRID_PER_CU", grid)
+    monkeypatch.setenv("KVCK_SCHEDULE", sched)
+    monkeypatch.setenv("KVCK_PLAN", "compact")
+    log(f"[launch_shapes] grid {grid} {sched}")
+    c = _grid_case()
+    req = c["req"]
+    got = gpu_blocks([to_device_bits(p) for p in c["hpools"]], "NHD", c["layers"], req)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(c["want"][r, k]), (grid, sched, r, k)
+    assert_unlisted_untouched(got, req)
+
+
 def test_tiny_config_golden():
     """The tiny workload on the GPU equals the oracle's committed values."""
     import json
