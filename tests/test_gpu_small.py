@@ -112,6 +112,32 @@ def test_launch_shapes_match_oracle(grid, sched, monkeypatch):
     assert_unlisted_untouched(got, req)
 
 
+@pytest.mark.parametrize("plan", ["in place", "compact"])
+def test_block_table_view_of_wider_rows(plan, monkeypatch):
+    """A block table that is a column slice of a wider table (row stride >
+    max_blocks, the extra columns holding out-of-range ids) gives the oracle's
+    checksums, whether the call plans in place (the main pass reads the table
+    itself) or lists its positions first."""
+    if plan == "compact":
+        monkeypatch.setenv("KVCK_PLAN", "compact")
+    log(f"[block_table_view] {plan}")
+    req, hpools = _host_case(91, "HND", "bf16", [0, 2], 4, 64, 16, [70, 33, 1, 48], None)
+    wide = np.full((req.num_reqs, req.max_blocks + 5), 2**31 - 1, dtype=np.int32)
+    wide[:, :req.max_blocks] = req.block_table
+    bt = torch.from_numpy(wide).to(DEV)[:, :req.max_blocks]
+    assert bt.stride(0) == req.max_blocks + 5
+    _, nb, sp, nt = req_tensors(req)
+    dpools = [to_device_bits(p) for p in hpools]
+    out = torch.full((req.num_reqs, req.max_blocks), SENTINEL, dtype=torch.int64, device=DEV).view(torch.uint64)
+    kvck.kvck_checksum_blocks(dpools, "HND", [0, 2], bt, nb, sp, nt, out=out, check=True)
+    got = out.cpu().numpy().view(np.uint64).reshape(req.num_reqs, req.max_blocks)
+    want = oracle.checksum_blocks(hpools, "HND", [0, 2], [0, 0], req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k]), (plan, r, k)
+    assert_unlisted_untouched(got, req)
+
+
 def test_tiny_config_golden():
     """The tiny workload on the GPU equals the oracle's committed values."""
     import json
