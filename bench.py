@@ -188,6 +188,8 @@ def main(argv=None):
     ap.add_argument("--no-states", action="store_true", help="skip the Mamba-state timing")
     ap.add_argument("--no-copy", action="store_true", help="skip the fused copy + checksum timing")
     ap.add_argument("--no-small", action="store_true", help="skip the tiny-call latency timing")
+    ap.add_argument("--survey", action="store_true",
+                    help="after the headline, time the main pass of every other configuration (extra.survey)")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="after timing, run one plain device copy of this many GiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -400,6 +402,12 @@ def main(argv=None):
         print(f"[bench] cpu baseline, {workers} processes", file=sys.stderr, flush=True)
         cpu["parallel"] = cpu_baseline_parallel(w, args.cpu_parallel_seconds, workers)
 
+    if args.survey:
+        del pools
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        extra["survey"] = config_survey(dev)
+
     line = {
         "metric": "checksummed KV GB/s and % of MI355X HBM peak; bit-exact vs CPU oracle",
         "value": valid / (ms_step * 1e-3) / 1e9,
@@ -423,6 +431,108 @@ def main(argv=None):
     }
     print(json.dumps(line), flush=True)
     return 0
+
+
+def config_survey(dev, calls=10):
+    """Main-pass time of each other configuration (median of `calls` calls,
+    HIP events around the main pass), one after another in this process: the
+    GPT-2-shaped pool and its re-pagings (block 64, HND, fp8 bits at blocks 16
+    and 64), the 61-layer MLA latent at blocks 64 and 16, and the hybrid
+    model's attention group and Mamba states.  Rows are printed to stderr as
+    they finish."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_kvck_amd as kvck
+    from paged_kv_cache_kvck_amd import workloads as wl
+
+    rows = []
+
+    def timed(call):
+        kvck.kvck_instrument(True)
+        call()
+        call()
+        torch.cuda.synchronize()
+        kvck.kvck_instrument_read()
+        ts = []
+        for _ in range(calls):
+            call()
+            torch.cuda.synchronize()
+            ms, c = kvck.kvck_instrument_read()
+            ts.append(ms / c)
+        kvck.kvck_instrument(False)
+        return statistics.median(ts)
+
+    def report(name, valid, ms):
+        gbs = valid / (ms * 1e-3) / 1e9
+        rows.append({"config": name, "valid_bytes": valid, "main_pass_ms": ms, "GB_per_s": gbs,
+                     "pct_of_hbm_peak": gbs / HBM_PEAK_GBS * 100})
+        print(f"[survey] {name:52s} {valid / 1e9:7.2f} GB {ms:8.3f} ms {gbs:8.1f} GB/s "
+              f"{gbs / HBM_PEAK_GBS * 100:5.1f} %", file=sys.stderr, flush=True)
+
+    def blocks(name, pools, layout, layers, req, valid):
+        bt, nb, sp, nt = (torch.from_numpy(x).to(dev) for x in
+                          (req.block_table, req.num_blocks, req.start_pos, req.num_tokens))
+        out = torch.zeros((req.num_reqs, req.max_blocks), dtype=torch.uint64, device=dev)
+        ws = torch.empty(kvck.kvck_blocks_workspace_bytes(len(pools), req.num_reqs, req.max_blocks),
+                         dtype=torch.uint8, device=dev)
+        pc = kvck.prepare_caches(pools, layout, layers)
+        report(name, valid, timed(lambda: kvck.kvck_checksum_blocks(pc, None, None, bt, nb, sp, nt, out=out,
+                                                                    workspace=ws)))
+
+    def free():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    g = wl.gpt2()
+    p = g.device_pools()
+    blocks("gpt2 NHD fp16, block 16", p, "NHD", g.layer_numbers, g.req, g.valid_bytes())
+    r64, n64 = wl.page_requests(np.random.default_rng(40), g.req.num_tokens, 64, spare_frac=0.05)
+    p64 = [torch.zeros(wl.pool_shape("NHD", n64, 64, 12, 64), dtype=p[0].dtype, device=dev) for _ in p]
+    for s_, d_ in zip(p, p64):
+        wl.repage_torch(s_, "NHD", g.req, d_, "NHD", r64)
+    blocks("gpt2 tokens re-paged at block 64 (NHD)", p64, "NHD", g.layer_numbers, r64, g.valid_bytes())
+    del p64
+    free()
+    ph = [x.permute(0, 1, 3, 2, 4).contiguous() for x in p]
+    blocks("gpt2 pool as HND, block 16", ph, "HND", g.layer_numbers, g.req, g.valid_bytes())
+    del ph, p
+    free()
+    f = wl.gpt2(seed=41, elem="fp8")
+    f16 = f.device_pools()
+    blocks("fp8 bits 12 x 64 (64-byte rows) NHD, block 16", f16, "NHD", f.layer_numbers, f.req, f.valid_bytes())
+    rf64, nf64 = wl.page_requests(np.random.default_rng(42), f.req.num_tokens, 64, spare_frac=0.05)
+    f64 = [torch.zeros(wl.pool_shape("NHD", nf64, 64, 12, 64), dtype=torch.uint8, device=dev) for _ in f16]
+    for s_, d_ in zip(f16, f64):
+        wl.repage_torch(s_, "NHD", f.req, d_, "NHD", rf64)
+    blocks("fp8 bits NHD, block 64", f64, "NHD", f.layer_numbers, rf64, f.valid_bytes())
+    del f16, f64
+    free()
+    m = wl.mla()
+    m64 = m.device_pools()
+    blocks("MLA 61 x 576 bf16, block 64", m64, "MLA", m.layer_numbers, m.req, m.valid_bytes())
+    rm16, nm16 = wl.page_requests(np.random.default_rng(43), m.req.num_tokens, 16, spare_frac=0.05)
+    m16 = [torch.zeros((nm16, 16, 576), dtype=m64[0].dtype, device=dev) for _ in m64]
+    for s_, d_ in zip(m64, m16):
+        wl.repage_torch(s_, "MLA", m.req, d_, "MLA", rm16)
+    blocks("MLA, block 16", m16, "MLA", m.layer_numbers, rm16, m.valid_bytes())
+    del m64, m16
+    free()
+    attn, mamba = wl.hybrid()
+    pa = attn.device_pools()
+    blocks("hybrid attention group (24 x 8 x 128 bf16 HND)", pa, attn.layout, attn.layer_numbers, attn.req,
+           attn.valid_bytes())
+    del pa
+    free()
+    states = mamba.device_states()
+    sid = torch.from_numpy(mamba.slot_ids).to(dev)
+    sout = torch.zeros(len(mamba.slot_ids), dtype=torch.uint64, device=dev)
+    sws = torch.empty(max(256, kvck.kvck_states_workspace_bytes(len(mamba.layer_numbers), mamba.rows_used,
+                                                                len(mamba.slot_ids))), dtype=torch.uint8, device=dev)
+    report("hybrid Mamba states (24 layers x 128 requests)", mamba.valid_bytes(),
+           timed(lambda: kvck.kvck_checksum_states(states, mamba.layer_numbers, sid, out=sout, workspace=sws)))
+    del states
+    free()
+    return rows
 
 
 def _cpu_model():
