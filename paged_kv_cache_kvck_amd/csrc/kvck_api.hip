@@ -259,27 +259,22 @@ KVCK_EXPORT size_t kvck_blocks_workspace_bytes(int32_t num_caches, int32_t num_r
 }
 
 namespace {
-constexpr int kModeChecksum = -1;  // kvck_checksum_blocks; otherwise a KVCK_COPY_* direction
+// What the kernels need to know of a layout once it is checked.
+struct LayoutInfo {
+  int32_t run_bytes;  // bytes of one contiguous run of a row (the row itself unless x-split)
+  int32_t runs;       // runs per row
+  int32_t planes_cov; // planes the call covers
+  bool transposed;    // runs shorter than a piece: rows stored element by element
+};
 
-// kvck_checksum_blocks and kvck_copy_checksum_blocks: validation, plan, main
-// pass (checksum only, or fused copy), second pass.
-kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* const* cache_ptrs,
-                        const int32_t* layer_numbers, const int32_t* global_head_base, int32_t num_caches,
-                        int32_t head_begin, int32_t head_count, const int32_t* block_table,
-                        int64_t block_table_row_stride, const int32_t* num_blocks_per_req, const int64_t* start_pos,
-                        const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks, uint64_t* out,
-                        int32_t accumulate, void* workspace, size_t workspace_bytes, uint32_t* error_flags,
-                        void* staging, int64_t staging_positions, kvck_stream_t stream) {
-  if (mode != kModeChecksum && mode != KVCK_COPY_SAVE && mode != KVCK_COPY_LOAD) return KVCK_ERR_INVALID_ARGUMENT;
-  // ---- layout
-  if (!layout || !cache_ptrs || !layer_numbers || !global_head_base) return KVCK_ERR_INVALID_ARGUMENT;
-  const kvck_kv_layout L = *layout;
+// Layout checks of the blocks entry points: strides, runs, plane range and
+// the extent every addressed byte lies in.
+kvck_status check_layout(const kvck_kv_layout& L, LayoutInfo* li) {
   if (L.planes != 1 && L.planes != 2) return KVCK_ERR_INVALID_ARGUMENT;
   if (L.block_size < 1 || L.num_heads < 1 || L.row_bytes < 1 || L.num_blocks < 0) return KVCK_ERR_INVALID_ARGUMENT;
   if (L.plane_stride < 0 || L.block_stride < 0 || L.slot_stride < 0 || L.head_stride < 0)
     return KVCK_ERR_INVALID_ARGUMENT;
   if (L.row_bytes % 8 != 0) return KVCK_ERR_UNSUPPORTED;
-  if (num_caches < 1 || num_caches > KVCK_MAX_CACHES) return KVCK_ERR_UNSUPPORTED;
   // rows stored as runs (x-split layouts) and plane subsets
   if (L.chunk_bytes < 0 || L.chunk_stride < 0 || L.plane_begin < 0 || L.plane_count < 0)
     return KVCK_ERR_INVALID_ARGUMENT;
@@ -305,6 +300,34 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
                   {L.num_heads, L.head_stride}, {runs, L.chunk_stride}},
                  run_bytes))
     return KVCK_ERR_UNSUPPORTED;
+  li->run_bytes = run_bytes;
+  li->runs = runs;
+  li->planes_cov = planes_cov;
+  li->transposed = transposed;
+  return KVCK_OK;
+}
+
+constexpr int kModeChecksum = -1;  // kvck_checksum_blocks; otherwise a KVCK_COPY_* direction
+
+// kvck_checksum_blocks and kvck_copy_checksum_blocks: validation, plan, main
+// pass (checksum only, or fused copy), second pass.
+kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* const* cache_ptrs,
+                        const int32_t* layer_numbers, const int32_t* global_head_base, int32_t num_caches,
+                        int32_t head_begin, int32_t head_count, const int32_t* block_table,
+                        int64_t block_table_row_stride, const int32_t* num_blocks_per_req, const int64_t* start_pos,
+                        const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks, uint64_t* out,
+                        int32_t accumulate, void* workspace, size_t workspace_bytes, uint32_t* error_flags,
+                        void* staging, int64_t staging_positions, kvck_stream_t stream) {
+  if (mode != kModeChecksum && mode != KVCK_COPY_SAVE && mode != KVCK_COPY_LOAD) return KVCK_ERR_INVALID_ARGUMENT;
+  // ---- layout
+  if (!layout || !cache_ptrs || !layer_numbers || !global_head_base) return KVCK_ERR_INVALID_ARGUMENT;
+  if (num_caches < 1 || num_caches > KVCK_MAX_CACHES) return KVCK_ERR_UNSUPPORTED;
+  const kvck_kv_layout L = *layout;
+  LayoutInfo li;
+  const kvck_status ls = check_layout(L, &li);
+  if (ls != KVCK_OK) return ls;
+  const int32_t run_bytes = li.run_bytes, runs = li.runs, planes_cov = li.planes_cov;
+  const bool transposed = li.transposed;
   if (head_begin < 0 || head_count < 1 || (int64_t)head_begin + head_count > L.num_heads)
     return KVCK_ERR_INVALID_ARGUMENT;
   for (int32_t i = 0; i < num_caches; ++i) {
