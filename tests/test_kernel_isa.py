@@ -7,9 +7,10 @@ neither shows in a correctness test:
   compiler cannot prove uniform across the wavefront, it wraps the access in
   a loop that compares the descriptor lane by lane (``v_readfirstlane`` and a
   branch back to the same block);
-* in the double-buffered main pass, the waits before the arithmetic on one
-  buffer leave the other buffer's loads in flight: every ``s_waitcnt vmcnt(N)``
-  among the multiply-accumulates keeps N at least that buffer's load count.
+* in the double-buffered kernels, the waits before the use of one buffer leave
+  the other buffer's loads in flight: every ``s_waitcnt vmcnt(N)`` among the
+  multiply-accumulates (or the fused copy's stores) keeps N at least that
+  buffer's load count.
 
 The kernels are compiled to AMD assembly here, exactly as the library build
 does (same flags), and the assembly is read.
@@ -89,24 +90,34 @@ def test_no_buffer_access_in_a_per_lane_descriptor_loop():
     assert not found, found[:5]
 
 
-def _consume_waits(blocks, min_mads):
+def _consume_waits(blocks, marker):
+    """vmcnt of every wait in the blocks that use loaded data: those with at
+    least four `marker` instructions (multiply-accumulates, or the fused
+    copy's stores)."""
     waits = []
     for _, ins in blocks:
-        if sum(i.startswith("v_mad_u64_u32") for i in ins) >= min_mads:
+        if sum(i.startswith(marker) for i in ins) >= 4:
             waits += [int(m.group(1)) for i in ins for m in [re.match(r"s_waitcnt vmcnt\((\d+)\)", i)] if m]
     return waits
 
 
-@pytest.mark.parametrize("variant,other_buffer", [
-    # <chunk, slots, heads per unit, planes per unit, pipelined, merged, dense>
-    ("blocks_kernelILi16ELi4ELi4ELi1ELb1ELb0ELb0E", 16),   # HND bf16 head 128 (the 147 GB workload)
-    ("blocks_kernelILi16ELi4ELi2ELi2ELb1ELb0ELb0E", 16),   # its TP shard: K and V in one unit
-    ("blocks_kernelILi16ELi8ELi1ELi1ELb1ELb1ELb0E", 8),    # merged rows
+MAC, STORE = "v_mad_u64_u32", "buffer_store"
+
+
+@pytest.mark.parametrize("src,variant,marker,other_buffer", [
+    # blocks_kernel<chunk, slots, heads per unit, planes per unit, pipelined, merged, dense>
+    ("kvck_blocks.hip", "blocks_kernelILi16ELi4ELi4ELi1ELb1ELb0ELb0E", MAC, 16),  # HND bf16 head 128 (147 GB)
+    ("kvck_blocks.hip", "blocks_kernelILi16ELi4ELi2ELi2ELb1ELb0ELb0E", MAC, 16),  # its TP shard: K+V units
+    ("kvck_blocks.hip", "blocks_kernelILi16ELi8ELi1ELi1ELb1ELb1ELb0E", MAC, 8),   # merged rows
+    # tblocks_kernel<chunk, element bytes, slots, heads per unit, pipelined, dense>: a transposed bf16 plane
+    ("kvck_tblocks.hip", "tblocks_kernelILi16ELi2ELi4ELi4ELb1ELb0E", MAC, 16),
+    # copy_kernel<chunk, slots, heads per unit, planes per unit, direction, pipelined, merged>: ping-pong save
+    ("kvck_copy.hip", "copy_kernelILi16ELi4ELi4ELi1ELi0ELb1ELb0E", STORE, 16),
 ])
-def test_pipelined_waits_leave_the_other_buffer_in_flight(variant, other_buffer):
-    text = assembly()["kvck_blocks.hip"]
+def test_pipelined_waits_leave_the_other_buffer_in_flight(src, variant, marker, other_buffer):
+    text = assembly()[src]
     ks = {n: b for n, b in kernels(text).items() if variant in n}
     assert len(ks) == 1, list(ks)
-    waits = _consume_waits(next(iter(ks.values())), min_mads=4)
-    assert waits, "no multiply-accumulate block found"
+    waits = _consume_waits(next(iter(ks.values())), marker)
+    assert waits, "no block using loaded data found"
     assert min(waits) >= other_buffer, sorted(set(waits))
