@@ -160,10 +160,11 @@ typedef struct kvck_kv_layout {
  * ignored.  kvck_blocks_workspace_bytes returns 0 for arguments the entry
  * points reject (num_caches < 1, negative sizes, num_reqs*max_blocks >= 2^31).
  *
- * Schedule: one workgroup of four wavefronts per compute unit.  Large
- * batches (many tasks per resident wavefront) keep two load batches in flight
- * per wavefront and give each task several layers; small ones use one layer
- * per task.  The environment variable KVCK_SCHEDULE =
+ * Schedule: pools of rows run one workgroup of four wavefronts per compute
+ * unit (element-transposed planes: as many as fit).  Large batches (many
+ * tasks per resident wavefront) keep two load batches in flight per
+ * wavefront and give each task several layers; small ones use one layer per
+ * task.  The environment variable KVCK_SCHEDULE =
  * "pipelined" or "simple" forces one of the two; results are bit-identical.
  * Calls of at most 8192 (request slot, cache) pairs read the request arrays
  * in the main pass itself (no separate planning launch; the smallest run as a
