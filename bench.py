@@ -18,40 +18,18 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
-import re
 import statistics
 import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
-
-# The sources that decide what the main-pass kernel reads: its own file, the
-# device helpers and argument structs it is built from, the host code that
-# picks its schedule, and the public header.
-MAIN_PASS_SOURCES = ("paged_kv_cache_kvck_amd/csrc/kvck_blocks.hip", "paged_kv_cache_kvck_amd/csrc/kvck_device.h",
-                     "paged_kv_cache_kvck_amd/csrc/kvck_internal.h", "paged_kv_cache_kvck_amd/csrc/kvck_api.hip",
-                     "include/kvck.h")
-
-
-def _code_only(text: str) -> str:
-    """C/C++ source without comments and whitespace: what the compiler sees."""
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    return re.sub(r"\s+", "", text)
-
-
-def kernel_sources_sha() -> str:
-    h = hashlib.sha256()
-    for p in (os.path.join(ROOT, f) for f in MAIN_PASS_SOURCES):
-        with open(p, encoding="utf-8") as f:
-            h.update(os.path.basename(p).encode())
-            h.update(_code_only(f.read()).encode())
-    return h.hexdigest()
+from paged_kv_cache_kvck_amd.sources import code_only as _code_only, kernel_sources_sha  # noqa: E402
 
 
 def committed_traffic(workload: str):

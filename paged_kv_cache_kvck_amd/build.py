@@ -4,11 +4,8 @@
 
 The library is a plain C-ABI shared object (include/kvck.h); the Python
 binding loads it with ctypes, so no torch C++ extension is involved.  The
-build also makes ``hbm_read_probe``, which measures the HBM read bandwidth
-trivial read kernels reach: grid-stride streaming, and whole contiguous runs
-per wavefront in address or scrambled order (the shape of a paged cache); and
-``kvck_demo``, a plain C program that uses the library through include/kvck.h
-alone (examples/kvck_demo.c).
+build also makes ``kvck_demo``, a plain C program that uses the library
+through include/kvck.h alone (examples/kvck_demo.c).
 """
 
 from __future__ import annotations
@@ -25,7 +22,6 @@ import tempfile
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libkvck.so")
-PROBE = os.path.join(PKG, "hbm_read_probe")
 DEMO = os.path.join(PKG, "kvck_demo")
 ARCH = "gfx950"
 
@@ -57,7 +53,7 @@ def _run(cmd, verbose, cwd=None):
 
 def build(save_temps: str | None = None, verbose: bool = False) -> str:
     """Compile every source to an object in parallel (the kernel variants make
-    single files slow), link libkvck.so, then the probe and the C demo."""
+    single files slow), link libkvck.so, then the C demo."""
     compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
     inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
     if save_temps:
@@ -70,20 +66,14 @@ def build(save_temps: str | None = None, verbose: bool = False) -> str:
             if save_temps:
                 cmd.insert(1, "-save-temps")
             jobs.append((cmd, obj))
-        # the plain-read bandwidth probe the benchmark's roofline discussion refers to
-        probe_tmp = PROBE + ".tmp"
-        probe_cmd = [hipcc(), *[f for f in HIP_FLAGS if f not in ("-shared", "-fPIC", "-fvisibility=hidden")],
-                     os.path.join(PKG, "probe", "hbm_read_probe.hip"), "-o", probe_tmp]
-        workers = max(1, min(len(jobs) + 1, os.cpu_count() or 1, 8))
+        workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
         with cf.ThreadPoolExecutor(max_workers=workers) as ex:
             futs = [ex.submit(_run, cmd, verbose, save_temps) for cmd, _ in jobs]
-            futs.append(ex.submit(_run, probe_cmd, verbose))
             for f in futs:
                 f.result()
         tmp = LIB + ".tmp"
         _run([hipcc(), *HIP_FLAGS, *[obj for _, obj in jobs], "-o", tmp], verbose)
         os.replace(tmp, LIB)
-        os.replace(probe_tmp, PROBE)
     # a plain C consumer of the C ABI (gcc, C99): no Python or torch involved
     demo_tmp = DEMO + ".tmp"
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")

@@ -136,10 +136,9 @@ def main(argv=None):
                       f"fetched / algorithmic = {res['fetch']['bytes'] / a.valid_bytes:.4f}; "
                       f"written / algorithmic = {res['write']['bytes'] / a.valid_bytes:.4f}."]
         if a.out_json:
-            sys.path.insert(0, ROOT)
-            import bench
+            from paged_kv_cache_kvck_amd.sources import kernel_sources_sha
             with open(a.out_json, "w") as f:
-                json.dump({"workload": a.workload, "kernel": kernel, "kernel_sources_sha256": bench.kernel_sources_sha(),
+                json.dump({"workload": a.workload, "kernel": kernel, "kernel_sources_sha256": kernel_sources_sha(),
                            "fetch_bytes_per_launch": res["fetch"]["bytes"],
                            "write_bytes_per_launch": res["write"]["bytes"],
                            "fetch_scale": res["fetch"]["factor"], "write_scale": res["write"]["factor"],
