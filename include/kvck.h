@@ -43,13 +43,15 @@
 extern "C" {
 #endif
 
-#define KVCK_ABI_VERSION 1
+#define KVCK_ABI_VERSION 2
 
 /* The page attribute MAX_KV_HEADS_PER_LAYER (2^16): H of the slice factor and
  * a bound on a layer's KV heads (or Mamba rows); calls beyond it are refused. */
 #define KVCK_MAX_KV_HEADS_PER_LAYER 65536
-/* Largest accepted layer number: keeps every factor m below 2^32. */
-#define KVCK_MAX_LAYER_NUMBER 32767
+/* Largest accepted layer number: any non-negative int32.  The page numbers a
+ * layer by the number in its name, with no bound; the factor
+ * m = 2(layer*H + head) + 1 stays below 2^48 and is carried in 64 bits. */
+#define KVCK_MAX_LAYER_NUMBER 2147483647
 /* Caches (layers) per kvck_checksum_blocks call and Mamba layers per
  * kvck_checksum_states call. */
 #define KVCK_MAX_CACHES 4096
@@ -59,8 +61,7 @@ extern "C" {
 typedef enum kvck_status {
   KVCK_OK = 0,
   KVCK_ERR_INVALID_ARGUMENT = -1, /* null pointer, negative size, bad stride */
-  KVCK_ERR_UNSUPPORTED = -2,      /* > H heads/rows, layer > KVCK_MAX_LAYER_NUMBER,
-                                     row bytes not a multiple of 8, element
+  KVCK_ERR_UNSUPPORTED = -2,      /* > H heads/rows, row bytes not a multiple of 8, element
                                      width not 2 or 4, too many caches, a
                                      tensor whose strided byte extent reaches
                                      2^50 (pool, state, staging, hashes) */
@@ -254,6 +255,15 @@ size_t kvck_states_workspace_bytes(int32_t num_layers, int32_t row_count, int32_
  * checksums of kvck_checksum_blocks come out of the same pass (all its
  * arguments mean the same; on a load the pool is written).
  *
+ * The two directions are the worker-side connector calls of the page
+ * "Connector.md", section 2.1 (worker side): save_kv_layer, which after a
+ * layer's attention writes that layer's paged KV out to the connector's side,
+ * and start_load_kv, which before the model's forward pass writes KV held
+ * outside into vLLM's paged KV buffer.  The staging buffer stands for the
+ * connector's side; the checksum is the one of the checksum page above, taken
+ * on the bytes as they pass (a save is checksummed once the KV is final, a
+ * load once its data have arrived).
+ *
  * Staging layout (device, owned by the caller): entries are the listed
  * positions in request order -- entry e of request r's k-th listed position is
  * sum_{r'<r} num_blocks_per_req[r'] + k -- and each entry holds one block
@@ -299,9 +309,13 @@ size_t kvck_staging_bytes(const kvck_kv_layout* layout, int32_t num_caches, int3
  *   tagged[i] = t_i                               (if tagged: the value to offload)
  *   mismatch[i] = (t_i != stored[i])              (if stored: a load of offloaded KV)
  *   *mismatch_count += number of mismatches       (if mismatch_count)
- * Other entries are not written.  All pointers are device pointers;
- * block_hashes must be 8-byte aligned with hash_stride a multiple of 8
- * (vLLM block hashes are 32 bytes).  At least one of tagged / stored.
+ * Other entries are not written.  A request lists nothing when its count is
+ * outside [0, max_blocks] or, with start_pos given, its start position is
+ * negative or too large for block_size (the rule under which
+ * kvck_checksum_blocks skips a request and leaves its entries unwritten), so
+ * a rejected request is neither tagged nor compared.  All pointers are device
+ * pointers; block_hashes must be 8-byte aligned with hash_stride a multiple
+ * of 8 (vLLM block hashes are 32 bytes).  At least one of tagged / stored.
  */
 kvck_status kvck_tag_checksums(
     const uint64_t* checksums,             /* device [n] */
@@ -310,7 +324,9 @@ kvck_status kvck_tag_checksums(
     uint64_t fingerprint,
     int64_t n,
     const int32_t* num_blocks_per_req,     /* device [n/max_blocks], optional */
+    const int64_t* start_pos,              /* device [n/max_blocks], optional, needs num_blocks_per_req */
     int32_t max_blocks,
+    int32_t block_size,                    /* >= 1 when start_pos is given */
     uint64_t* tagged,                      /* device [n], optional */
     const uint64_t* stored,                /* device [n], optional */
     uint8_t* mismatch,                     /* device [n], optional, needs stored */
@@ -331,7 +347,10 @@ kvck_status kvck_instrument_read(double* total_ms, int64_t* calls);
 /* Human-readable name of a kvck_status value (static storage). */
 const char* kvck_status_string(int32_t status);
 
-/* 1 if the current HIP device is a gfx950 GPU, else 0. */
+/* Whether this platform can run the checksum kernels: 1 if the current HIP
+ * device is a gfx950 GPU, else 0.  The library's counterpart of the checksum
+ * page's helper kv_checksum_platform_supported (section "helper functions"),
+ * which gates the page's Triton kernel on CUDA-like or XPU platforms. */
 int32_t kvck_platform_supported(void);
 
 /* KVCK_ABI_VERSION of the loaded library. */

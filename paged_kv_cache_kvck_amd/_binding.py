@@ -104,7 +104,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kvck_staging_bytes.restype = sz
     lib.kvck_staging_bytes.argtypes = [ctypes.POINTER(kvck_kv_layout), i32, i32]
     lib.kvck_tag_checksums.restype = i32
-    lib.kvck_tag_checksums.argtypes = [vp, vp, i64, ctypes.c_uint64, i64, vp, i32, vp, vp, vp, vp, vp]
+    lib.kvck_tag_checksums.argtypes = [vp, vp, i64, ctypes.c_uint64, i64, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.kvck_instrument.restype = i32
     lib.kvck_instrument.argtypes = [i32]
     lib.kvck_instrument_read.restype = i32
@@ -155,10 +155,25 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
-def _stream_handle(stream, device) -> int | None:
+def _stream_handle(stream, device, allocated=()) -> int:
+    """The HIP stream a call's kernels run on: ``stream`` (a torch stream or a
+    raw hipStream_t), else the current stream.  The binding fills and allocates
+    on the current stream (a zeroed ``out``, the workspace, the flag word), so
+    when the call runs elsewhere its stream first waits for the current
+    stream's work, and the ``allocated`` tensors are recorded as in use on it:
+    the caching allocator then does not hand their memory out again before
+    the call's kernels are done."""
+    cur = torch.cuda.current_stream(device)
     if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        return cur.cuda_stream
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    if handle != cur.cuda_stream:
+        s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(handle, device=device)
+        s.wait_stream(cur)
+        for t in allocated:
+            if t is not None:
+                t.record_stream(s)
+    return handle
 
 
 # ----------------------------------------------------------------- layouts
@@ -315,18 +330,24 @@ def _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req,
     _meta(num_blocks_per_req, torch.int32, "num_blocks_per_req", dev, R)
     _meta(start_pos, torch.int64, "start_pos", dev, R)
     _meta(num_tokens, torch.int64, "num_tokens", dev, R)
+    allocated = []
     if out is None:
         out = torch.zeros((R, max_blocks), dtype=torch.uint64, device=dev)
+        allocated.append(out)
     elif out.dtype not in (torch.uint64, torch.int64) or out.device != dev or not out.is_contiguous() \
             or out.numel() < R * max_blocks:
         raise ValueError("out must be a contiguous uint64 tensor of num_reqs*max_blocks entries")
     need = int(lib.kvck_blocks_workspace_bytes(n, R, max_blocks))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        allocated.append(workspace)
+    fresh_flags = check and error_flags is None
     error_flags = _flag_word(error_flags, check, dev)
+    if fresh_flags:
+        allocated.append(error_flags)
     return dict(lib=lib, dev=dev, L=pc.layout, n=n, head_begin=pc.head_begin, head_count=pc.head_count, R=R,
                 max_blocks=max_blocks, out=out, workspace=workspace, error_flags=error_flags, ptrs=pc.ptrs,
-                layers=pc.layers, bases=pc.bases)
+                layers=pc.layers, bases=pc.bases, allocated=allocated)
 
 
 def _flag_word(error_flags, check, dev):
@@ -381,7 +402,7 @@ def kvck_checksum_blocks(caches, layout: str | None, layer_numbers: Sequence[int
         ctypes.byref(a["L"]), a["ptrs"], a["layers"], a["bases"], a["n"], a["head_begin"], a["head_count"],
         block_table.data_ptr(), block_table.stride(0), num_blocks_per_req.data_ptr(), start_pos.data_ptr(),
         num_tokens.data_ptr(), a["R"], a["max_blocks"], a["out"].data_ptr(), int(bool(accumulate)), ws.data_ptr(),
-        ws.numel() * ws.element_size(), _ptr(a["error_flags"]), _stream_handle(stream, a["dev"]))
+        ws.numel() * ws.element_size(), _ptr(a["error_flags"]), _stream_handle(stream, a["dev"], a["allocated"]))
     _check(st, "kvck_checksum_blocks")
     return _finish(a, check)
 
@@ -416,7 +437,7 @@ def kvck_copy_checksum_blocks(direction: int, caches, layout: str | None,
         a["head_count"], block_table.data_ptr(), block_table.stride(0), num_blocks_per_req.data_ptr(),
         start_pos.data_ptr(), num_tokens.data_ptr(), a["R"], a["max_blocks"], staging.data_ptr(), positions,
         a["out"].data_ptr(), int(bool(accumulate)), ws.data_ptr(), ws.numel() * ws.element_size(),
-        _ptr(a["error_flags"]), _stream_handle(stream, a["dev"]))
+        _ptr(a["error_flags"]), _stream_handle(stream, a["dev"], a["allocated"]))
     _check(st, "kvck_copy_checksum_blocks")
     return _finish(a, check)
 
@@ -469,8 +490,10 @@ def kvck_checksum_states(layer_states: Sequence[Sequence[torch.Tensor]], layer_n
     R = slot_ids.numel()
     if not slot_ids.is_contiguous():
         raise ValueError("slot_ids must be contiguous")
+    allocated = []
     if out is None:
         out = torch.zeros(R, dtype=torch.uint64, device=dev)
+        allocated.append(out)
     descs = (kvck_state_desc * k)(*[state_desc(s) for s in ref])
     ptrs = (ctypes.c_void_p * (nl * k))(*[s.data_ptr() for sts in layer_states for s in sts])
     layers = (ctypes.c_int32 * nl)(*[int(x) for x in layer_numbers])
@@ -478,11 +501,16 @@ def kvck_checksum_states(layer_states: Sequence[Sequence[torch.Tensor]], layer_n
     need = int(lib.kvck_states_workspace_bytes(nl, row_count, R))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    error_flags = _flag_word(error_flags, check, dev)
+        allocated.append(workspace)
+    if check and error_flags is None:
+        error_flags = _flag_word(None, True, dev)
+        allocated.append(error_flags)
+    else:
+        error_flags = _flag_word(error_flags, check, dev)
     st = lib.kvck_checksum_states(
         descs, k, ptrs, layers, bases, nl, slots, rows, int(row_begin), int(row_count), slot_ids.data_ptr(), R,
         out.data_ptr(), int(bool(accumulate)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        _ptr(error_flags), _stream_handle(stream, dev))
+        _ptr(error_flags), _stream_handle(stream, dev, allocated))
     _check(st, "kvck_checksum_states")
     if check:
         torch.cuda.synchronize(dev)
@@ -495,14 +523,17 @@ def kvck_checksum_states(layer_states: Sequence[Sequence[torch.Tensor]], layer_n
 def kvck_tag_checksums(checksums: torch.Tensor, block_hashes: torch.Tensor, fingerprint: int,
                        num_blocks_per_req: torch.Tensor | None = None, tagged: torch.Tensor | bool | None = True,
                        stored: torch.Tensor | None = None, mismatch: torch.Tensor | bool | None = None,
-                       mismatch_count: torch.Tensor | None = None, stream=None):
+                       mismatch_count: torch.Tensor | None = None, stream=None, start_pos: torch.Tensor | None = None,
+                       block_size: int = 0):
     """Tags of offloaded checksums (the page's block_checksum_tags) and the
     load-time comparison; see include/kvck.h.
 
     ``checksums``: uint64 tensor (e.g. the (num_reqs, max_blocks) output of
     kvck_checksum_blocks); ``block_hashes``: uint8 (n, hash_bytes >= 8) tensor,
-    row i the hash of the block at entry i.  Returns (tagged, mismatch) --
-    each a tensor or None.
+    row i the hash of the block at entry i.  With ``num_blocks_per_req`` only
+    listed positions are touched; ``start_pos`` and ``block_size`` (those of
+    the checksum call) also skip requests that call rejected.  Returns
+    (tagged, mismatch) -- each a tensor or None.
     """
     lib = load_library()
     dev = checksums.device
@@ -516,17 +547,24 @@ def kvck_tag_checksums(checksums: torch.Tensor, block_hashes: torch.Tensor, fing
     if num_blocks_per_req is not None:
         _meta(num_blocks_per_req, torch.int32, "num_blocks_per_req", dev)
         max_blocks = n // max(1, num_blocks_per_req.numel())
+        if start_pos is not None:
+            _meta(start_pos, torch.int64, "start_pos", dev, num_blocks_per_req.numel())
+    elif start_pos is not None:
+        raise ValueError("start_pos needs num_blocks_per_req")
+    allocated = []
     if tagged is True:
         tagged = torch.zeros(n, dtype=torch.uint64, device=dev)
+        allocated.append(tagged)
     elif tagged is False:
         tagged = None
     if mismatch is True or (mismatch is None and stored is not None):
         mismatch = torch.zeros(n, dtype=torch.uint8, device=dev)
+        allocated.append(mismatch)
     elif mismatch is False:
         mismatch = None
     st = lib.kvck_tag_checksums(checksums.data_ptr(), block_hashes.data_ptr(), block_hashes.stride(0),
                                 ctypes.c_uint64(int(fingerprint) & ((1 << 64) - 1)), n, _ptr(num_blocks_per_req),
-                                max_blocks, _ptr(tagged), _ptr(stored), _ptr(mismatch), _ptr(mismatch_count),
-                                _stream_handle(stream, dev))
+                                _ptr(start_pos), max_blocks, int(block_size), _ptr(tagged), _ptr(stored),
+                                _ptr(mismatch), _ptr(mismatch_count), _stream_handle(stream, dev, allocated))
     _check(st, "kvck_tag_checksums")
     return tagged, mismatch

@@ -19,6 +19,7 @@ constexpr int64_t kH = KVCK_MAX_KV_HEADS_PER_LAYER;
 
 bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)a) == 0; }
 
+
 // Largest byte extent of a tensor the kernels address (64-bit offsets with
 // room to spare; far beyond any device memory).
 constexpr int64_t kMaxExtent = (int64_t)1 << 50;
@@ -333,7 +334,6 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   for (int32_t i = 0; i < num_caches; ++i) {
     if (!cache_ptrs[i]) return KVCK_ERR_INVALID_ARGUMENT;
     if (layer_numbers[i] < 0 || global_head_base[i] < 0) return KVCK_ERR_INVALID_ARGUMENT;
-    if (layer_numbers[i] > KVCK_MAX_LAYER_NUMBER) return KVCK_ERR_UNSUPPORTED;
     if ((int64_t)global_head_base[i] + head_count > kH) return KVCK_ERR_UNSUPPORTED;
   }
   // ---- requests
@@ -456,7 +456,6 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   const int32_t lpt = shp.caches_per_task;
   const int32_t total_groups = (num_caches + lpt - 1) / lpt;
   const int64_t max_start = INT64_MAX / L.block_size - max_blocks;  // keeps (start + k) * block_size exact
-
   if (!dense && launch_plan(block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens,
                             num_reqs, max_blocks, L.block_size, L.num_blocks, workspace, error_flags,
                             st) != hipSuccess)
@@ -508,7 +507,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
     a.group_offset = c0 / lpt;
     for (int32_t i = 0; i < n; ++i) {
       a.base[i] = static_cast<const uint8_t*>(cache_ptrs[c0 + i]) + (int64_t)head_begin * L.head_stride;
-      a.mbase[i] = (uint32_t)(2 * ((int64_t)layer_numbers[c0 + i] * kH + global_head_base[c0 + i]) + 1);
+      a.mbase[i] = (uint64_t)(2 * ((int64_t)layer_numbers[c0 + i] * kH + global_head_base[c0 + i]) + 1);
     }
     const int64_t tasks = max_items * ((n + lpt - 1) / lpt);
     if (mode == kModeChecksum) {
@@ -631,7 +630,6 @@ KVCK_EXPORT kvck_status kvck_checksum_states(const kvck_state_desc* states, int3
   if (elems >= ((int64_t)1 << 31) - 8) return KVCK_ERR_UNSUPPORTED;
   for (int32_t l = 0; l < num_layers; ++l) {
     if (layer_numbers[l] < 0 || global_row_base[l] < 0) return KVCK_ERR_INVALID_ARGUMENT;
-    if (layer_numbers[l] > KVCK_MAX_LAYER_NUMBER) return KVCK_ERR_UNSUPPORTED;
     if ((int64_t)global_row_base[l] + row_count > kH) return KVCK_ERR_UNSUPPORTED;
     for (int32_t i = 0; i < states_per_layer; ++i) {
       const void* p = state_ptrs[(int64_t)l * states_per_layer + i];
@@ -690,7 +688,7 @@ KVCK_EXPORT kvck_status kvck_checksum_states(const kvck_state_desc* states, int3
     for (int32_t l = 0; l < n; ++l) {
       for (int32_t i = 0; i < states_per_layer; ++i)
         a.ptr[l][i] = static_cast<const uint8_t*>(state_ptrs[(int64_t)(l0 + l) * states_per_layer + i]);
-      a.mbase[l] = (uint32_t)(2 * ((int64_t)layer_numbers[l0 + l] * kH + global_row_base[l0 + l]) + 1);
+      a.mbase[l] = (uint64_t)(2 * ((int64_t)layer_numbers[l0 + l] * kH + global_row_base[l0 + l]) + 1);
     }
     const int grid = states_grid(dev, (int64_t)n * groups * num_reqs);
     if (launch_states(a, grid, st) != hipSuccess) return KVCK_ERR_HIP;
@@ -706,8 +704,9 @@ KVCK_EXPORT kvck_status kvck_checksum_states(const kvck_state_desc* states, int3
 
 KVCK_EXPORT kvck_status kvck_tag_checksums(const uint64_t* checksums, const uint8_t* block_hashes, int64_t hash_stride,
                                            uint64_t fingerprint, int64_t n, const int32_t* num_blocks_per_req,
-                                           int32_t max_blocks, uint64_t* tagged, const uint64_t* stored,
-                                           uint8_t* mismatch, uint32_t* mismatch_count, kvck_stream_t stream) {
+                                           const int64_t* start_pos, int32_t max_blocks, int32_t block_size,
+                                           uint64_t* tagged, const uint64_t* stored, uint8_t* mismatch,
+                                           uint32_t* mismatch_count, kvck_stream_t stream) {
   if (n < 0) return KVCK_ERR_INVALID_ARGUMENT;
   if (n == 0) return KVCK_OK;
   if (!checksums || !block_hashes) return KVCK_ERR_INVALID_ARGUMENT;
@@ -717,11 +716,16 @@ KVCK_EXPORT kvck_status kvck_tag_checksums(const uint64_t* checksums, const uint
   if (hash_stride % 8 != 0 || !aligned(block_hashes, 8)) return KVCK_ERR_MISALIGNED;
   if (!extent_ok({{n, hash_stride}}, 8)) return KVCK_ERR_UNSUPPORTED;
   if (num_blocks_per_req && (max_blocks < 1 || n % max_blocks != 0)) return KVCK_ERR_INVALID_ARGUMENT;
+  if (start_pos && (!num_blocks_per_req || block_size < 1)) return KVCK_ERR_INVALID_ARGUMENT;
+  if ((num_blocks_per_req && !aligned(num_blocks_per_req, 4)) || (start_pos && !aligned(start_pos, 8)))
+    return KVCK_ERR_MISALIGNED;
+  // the start positions kvck_checksum_blocks accepts: (start + k) * block_size stays exact
+  const int64_t max_start = start_pos ? INT64_MAX / block_size - max_blocks : INT64_MAX;
   int dev = 0;
   const kvck_status ds = current_device(&dev);
   if (ds != KVCK_OK) return ds;
-  if (launch_tags(checksums, block_hashes, hash_stride, fingerprint, n, num_blocks_per_req, max_blocks, tagged, stored,
-                  mismatch, mismatch_count, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (launch_tags(checksums, block_hashes, hash_stride, fingerprint, n, num_blocks_per_req, start_pos, max_blocks,
+                  max_start, tagged, stored, mismatch, mismatch_count, static_cast<hipStream_t>(stream)) != hipSuccess)
     return KVCK_ERR_HIP;
   return KVCK_OK;
 }

@@ -8,9 +8,10 @@
 //
 // Up to three launches per call, all on the caller's stream:
 //   plan    request arrays -> compact list of listed positions (PosRecord):
-//           block id, first token t0 = pos*block_size, valid slots
-//           v = min(block_size, max(0, num_tokens - t0)) (page helper
-//           num_valid_tokens), output index.  Bad ids and requests are flagged.
+//           block id, first token t0 = pos*block_size, valid slots v (the
+//           block's slots whose token lies below num_tokens, as the page's
+//           helper num_valid_tokens counts them), output index.  Bad ids and
+//           requests are flagged.
 //           Small calls skip it: their main pass (the DENSE variants) derives
 //           each task's record from the request arrays with the same rules.
 //   blocks  one wavefront per task (group of caches, position): streams the
@@ -248,14 +249,17 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
         if (live) ic.next(nhb, nplanes, ngr);
       };
       auto consume = [&](const V(&x)[PU][HU][S]) {
-        const uint32_t mb = a.mbase[cc.cache];
+        const uint64_t mb = a.mbase[cc.cache];
 #pragma unroll
         for (int p = 0; p < PU; ++p) {
           const uint64_t up = 2ull * (t0 + (uint64_t)(cc.group * rg)) * P + 1ull + a.piece_base +
                               (uint64_t)(cc.plane * PU + p) * plane_term;
 #pragma unroll
           for (int h = 0; h < HU; ++h) {
-            uint64_t sh = 0;
+            // sh: sum of the unit's terms; sl (merged rows): the same weighted by
+            // each chunk's local head, so that sum_s t_s (mb + 2 head_s) costs one
+            // 64-bit multiply per unit: mb * sh + 2 sl
+            uint64_t sh = 0, sl = 0;
 #pragma unroll
             for (int s = 0; s < S; ++s) {
               const uint64_t u = up + lt.urel[s];
@@ -267,12 +271,13 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
               } else {
                 t = xa * u;
               }
-              if constexpr (MERGED)
-                acc += t * (uint64_t)(mb + 2u * lhead[s]);
-              else
-                sh += t;
+              sh += t;
+              if constexpr (MERGED) sl += t * (uint64_t)lhead[s];
             }
-            if constexpr (!MERGED) acc += sh * (uint64_t)(mb + 2u * (uint32_t)(cc.hbatch * HU + h));
+            if constexpr (MERGED)
+              acc += sh * mb + (sl << 1);
+            else
+              acc += sh * (mb + 2ull * (uint64_t)(cc.hbatch * HU + h));
           }
         }
         cc.next(nhb, nplanes, ngr);

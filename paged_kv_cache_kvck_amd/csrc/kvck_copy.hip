@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
       };
       auto store_consume = [&](const V(&x)[PU][HU][S]) {
         const int rows = min(rg, v - cc.group * rg);
-        const uint32_t mb = a.mbase[cc.cache];
+        const uint64_t mb = a.mbase[cc.cache];
 #pragma unroll
         for (int p = 0; p < PU; ++p) {
           const uint64_t up = 2ull * (t0 + (uint64_t)(cc.group * rg)) * P + 1ull + a.piece_base +
@@ -130,7 +130,8 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
             const int hh = cc.hbatch * HU + h;
             const uint32_t hmask = hh < a.heads ? 0u : kOOB;
             const __amdgpu_buffer_rsrc_t rd = make_rsrc(DIR == 0 ? img_base(cc, p, hh) : pool_base(cc, p, hh));
-            uint64_t sh = 0;
+            // as in the checksum kernel: mb * sh + 2 sl for merged rows
+            uint64_t sh = 0, sl = 0;
 #pragma unroll
             for (int s = 0; s < S; ++s) {
               store_chunk<CHUNK>(rd, (lt.row[s] < rows ? (DIR == 0 ? ioff[s] : lt.off[s]) : kOOB) | hmask,
@@ -144,12 +145,13 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
               } else {
                 t = xa * u;
               }
-              if constexpr (MERGED)
-                acc += t * (uint64_t)(mb + 2u * lhead[s]);
-              else
-                sh += t;
+              sh += t;
+              if constexpr (MERGED) sl += t * (uint64_t)lhead[s];
             }
-            if constexpr (!MERGED) acc += sh * (uint64_t)(mb + 2u * (uint32_t)hh);
+            if constexpr (MERGED)
+              acc += sh * mb + (sl << 1);
+            else
+              acc += sh * (mb + 2ull * (uint64_t)hh);
           }
         }
         cc.next(nhb, nplanes, ngr);

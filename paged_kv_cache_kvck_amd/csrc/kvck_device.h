@@ -140,10 +140,13 @@ __device__ __forceinline__ bool bad_request(int32_t n, int64_t start, int32_t ma
   return n < 0 || n > max_blocks || start < 0 || start > max_start;
 }
 
-// Valid slots of the block at first token t0 (the page's num_valid_tokens).
+// Valid slots of the block whose first token is t0 (what the page's helper
+// num_valid_tokens counts): the length of the overlap of its token span
+// [t0, t0 + block_size) with the request's tokens [0, num_tokens).  Callers
+// keep t0 <= INT64_MAX - block_size.
 __device__ __forceinline__ int32_t valid_slots(int64_t num_tokens, int64_t t0, int32_t block_size) {
-  const int64_t left = num_tokens - t0;
-  return left <= 0 ? 0 : (left >= block_size ? block_size : (int32_t)left);
+  const int64_t end = num_tokens < t0 + block_size ? num_tokens : t0 + block_size;
+  return end > t0 ? (int32_t)(end - t0) : 0;
 }
 
 __device__ __forceinline__ int64_t uniform64(int64_t x) {

@@ -77,7 +77,7 @@ struct BlocksArgs {
   int32_t direct;                            // write out[] directly (one group overall)
   int32_t accumulate;
   const uint8_t* base[kCachesPerLaunch];     // pool base + head_begin*head_stride
-  uint32_t mbase[kCachesPerLaunch];          // 2*(layer*H + global_head_base) + 1
+  uint64_t mbase[kCachesPerLaunch];          // 2*(layer*H + global_head_base) + 1 (< 2^48)
   // Calls planned in place (the dense kernel variants): tasks index every
   // (r, k) slot, item = r*max_blocks + k, and read the request arrays
   // themselves; recs and n_items are then unused.
@@ -117,7 +117,7 @@ struct StatesArgs {
   int32_t split_offset;  // split index of this launch's first (layer, group)
   int32_t direct, accumulate;
   const uint8_t* ptr[kLayersPerStatesLaunch][KVCK_MAX_STATES_PER_LAYER];
-  uint32_t mbase[kLayersPerStatesLaunch];  // 2*(layer*H + global_row_base) + 1
+  uint64_t mbase[kLayersPerStatesLaunch];  // 2*(layer*H + global_row_base) + 1 (< 2^48)
 };
 
 // Kernel shape chosen on the host for one kvck_checksum_blocks call.
@@ -157,8 +157,9 @@ int copy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tas
 hipError_t launch_tcopy(const CopyArgs& a, const BlocksShape& shp, int direction, int grid, hipStream_t stream);
 int tcopy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks, int32_t block_size);
 hipError_t launch_tags(const uint64_t* checksums, const uint8_t* hashes, int64_t hash_stride, uint64_t fingerprint,
-                       int64_t n, const int32_t* nbpr, int32_t max_blocks, uint64_t* tagged, const uint64_t* stored,
-                       uint8_t* mismatch, uint32_t* count, hipStream_t stream);
+                       int64_t n, const int32_t* nbpr, const int64_t* start_pos, int32_t max_blocks,
+                       int64_t max_start, uint64_t* tagged, const uint64_t* stored, uint8_t* mismatch,
+                       uint32_t* count, hipStream_t stream);
 int states_grid(int device, int64_t tasks);
 int device_cus(int device);                                   // cached per device
 int kernel_occupancy(const void* fn, int device, int fallback);  // workgroups per CU, cached

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kBlockThreads) void states_kernel(const StatesArgs 
             }
           }
         }
-        acc += s * (uint64_t)(a.mbase[l] + 2u * (uint32_t)g);
+        acc += s * (a.mbase[l] + 2ull * (uint64_t)g);
       }
     }
     acc = wave_sum(acc);

@@ -8,7 +8,7 @@
 //   t_i = checksum_i ^ LE64(hash_i[0..8)) ^ fingerprint
 // is written (the value to offload) and/or compared with the stored value
 // (a load of offloaded KV), mismatches flagged per position and counted.
-#include "kvck_internal.h"
+#include "kvck_device.h"
 
 namespace kvck {
 namespace {
@@ -16,7 +16,8 @@ namespace {
 __global__ __launch_bounds__(256) void tags_kernel(const uint64_t* __restrict__ checksums,
                                                    const uint8_t* __restrict__ hashes, int64_t hash_stride,
                                                    uint64_t fingerprint, int64_t n, const int32_t* __restrict__ nbpr,
-                                                   int32_t max_blocks, uint64_t* __restrict__ tagged,
+                                                   const int64_t* __restrict__ start_pos, int32_t max_blocks,
+                                                   int64_t max_start, uint64_t* __restrict__ tagged,
                                                    const uint64_t* __restrict__ stored, uint8_t* __restrict__ mismatch,
                                                    uint32_t* __restrict__ count) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -24,8 +25,12 @@ __global__ __launch_bounds__(256) void tags_kernel(const uint64_t* __restrict__ 
     const int64_t i = base + threadIdx.x;
     bool live = i < n;
     if (live && nbpr) {
+      // the checksum pass's rule: a bad request lists nothing (its entries
+      // were never written, so they are neither tagged nor compared)
       const int64_t r = i / max_blocks;
-      live = (int32_t)(i - r * max_blocks) < nbpr[r];
+      const int32_t nr = nbpr[r];
+      live = !bad_request(nr, start_pos ? start_pos[r] : 0, max_blocks, max_start) &&
+             (int32_t)(i - r * max_blocks) < nr;
     }
     bool bad = false;
     if (live) {
@@ -49,13 +54,14 @@ __global__ __launch_bounds__(256) void tags_kernel(const uint64_t* __restrict__ 
 }  // namespace
 
 hipError_t launch_tags(const uint64_t* checksums, const uint8_t* hashes, int64_t hash_stride, uint64_t fingerprint,
-                       int64_t n, const int32_t* nbpr, int32_t max_blocks, uint64_t* tagged, const uint64_t* stored,
-                       uint8_t* mismatch, uint32_t* count, hipStream_t stream) {
+                       int64_t n, const int32_t* nbpr, const int64_t* start_pos, int32_t max_blocks,
+                       int64_t max_start, uint64_t* tagged, const uint64_t* stored, uint8_t* mismatch,
+                       uint32_t* count, hipStream_t stream) {
   int64_t grid = (n + 255) / 256;
   if (grid > 8192) grid = 8192;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(tags_kernel, dim3((unsigned)grid), dim3(256), 0, stream, checksums, hashes, hash_stride,
-                     fingerprint, n, nbpr, max_blocks, tagged, stored, mismatch, count);
+                     fingerprint, n, nbpr, start_pos, max_blocks, max_start, tagged, stored, mismatch, count);
   return hipGetLastError();
 }
 

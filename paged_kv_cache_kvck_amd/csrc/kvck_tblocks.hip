@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kBlockThreads) void tblocks_kernel(const BlocksArgs
         if (live) ic.next(nhb, ngr);
       };
       auto consume = [&](const V(&x)[HU][S]) {
-        const uint32_t mb = a.mbase[cc.cache];
+        const uint64_t mb = a.mbase[cc.cache];
 #pragma unroll
         for (int h = 0; h < HU; ++h) {
           uint64_t sh = 0;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kBlockThreads) void tblocks_kernel(const BlocksArgs
             const uint64_t u0 = ubase[s] + 2ull * (d / PER_PIECE);
             sh += (u0 * E + 2ull * P * K) << (8 * ES * (d % PER_PIECE));
           }
-          acc += sh * (uint64_t)(mb + 2u * (uint32_t)(cc.hbatch * HU + h));
+          acc += sh * (mb + 2ull * (uint64_t)(cc.hbatch * HU + h));
         }
         cc.next(nhb, ngr);
       };

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_kernel(const CopyArgs ca)
               x[h][s] = load_chunk<CHUNK>(rs, ((int)crow[s] < rows && (int)(q0[s] + j) < v ? soff[s] : kOOB) | hmask);
           }
         }
-        const uint32_t mb = a.mbase[cache];
+        const uint64_t mb = a.mbase[cache];
 #pragma unroll
         for (int h = 0; h < HU; ++h) {
           const int hh = hbatch * HU + h;
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_kernel(const CopyArgs ca)
               }
             }
           }
-          acc += sh * (uint64_t)(mb + 2u * (uint32_t)hh);
+          acc += sh * (mb + 2ull * (uint64_t)hh);
         }
         if (++hbatch == nhb) {
           hbatch = 0;
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(kBlockThreads) void tcopy_lds_kernel(const CopyArgs
           }
           __builtin_amdgcn_wave_barrier();
         }
-        acc += sh * (uint64_t)(a.mbase[cc.cache] + 2u * (uint32_t)cc.hh);
+        acc += sh * (a.mbase[cc.cache] + 2ull * (uint64_t)cc.hh);
         cc.next(a.heads, ngr);
       };
       // Two unit buffers: the loads of the next unit are in flight while this

@@ -102,7 +102,7 @@ void blocks_checks(bool have_device) {
   EXPECT_EQ(call([](BlocksCall& c) { c.head_begin = kI32Max, c.head_count = kI32Max; }), KVCK_ERR_INVALID_ARGUMENT);
   EXPECT_EQ(call([](BlocksCall& c) { c.bases = {0, 65535}; }), KVCK_ERR_UNSUPPORTED);
   EXPECT_EQ(call([](BlocksCall& c) { c.bases = {0, kI32Max}; }), KVCK_ERR_UNSUPPORTED);
-  EXPECT_EQ(call([](BlocksCall& c) { c.layers = {0, 40000}; }), KVCK_ERR_UNSUPPORTED);
+  if (!have_device) EXPECT_EQ(call([](BlocksCall& c) { c.layers = {40000, kI32Max}; }), KVCK_ERR_NO_DEVICE);
   EXPECT_EQ(call([](BlocksCall& c) { c.layers = {0, -1}; }), KVCK_ERR_INVALID_ARGUMENT);
   EXPECT_EQ(call([](BlocksCall& c) { c.ptrs[1] = nullptr; }), KVCK_ERR_INVALID_ARGUMENT);
   EXPECT_EQ(call([](BlocksCall& c) { c.out = nullptr; }), KVCK_ERR_INVALID_ARGUMENT);
@@ -259,7 +259,7 @@ void tags_checks(bool have_device) {
   auto call = [](const void* cs, const void* h, int64_t stride, int64_t n, const void* nbpr, int32_t mb,
                  void* tagged, const void* stored, void* mm) {
     return kvck_tag_checksums(static_cast<const uint64_t*>(cs), static_cast<const uint8_t*>(h), stride, 0x1234, n,
-                              static_cast<const int32_t*>(nbpr), mb, static_cast<uint64_t*>(tagged),
+                              static_cast<const int32_t*>(nbpr), nullptr, mb, 0, static_cast<uint64_t*>(tagged),
                               static_cast<const uint64_t*>(stored), static_cast<uint8_t*>(mm), nullptr, nullptr);
   };
   EXPECT_EQ(call(kFake, kFake, 32, 0, nullptr, 0, kFake, nullptr, nullptr), KVCK_OK);
@@ -277,7 +277,7 @@ void tags_checks(bool have_device) {
 }
 
 void misc_checks() {
-  EXPECT_EQ(kvck_abi_version(), 1);
+  EXPECT_EQ(kvck_abi_version(), 2);
   const int32_t codes[] = {KVCK_OK,           KVCK_ERR_INVALID_ARGUMENT, KVCK_ERR_UNSUPPORTED, KVCK_ERR_MISALIGNED,
                            KVCK_ERR_WORKSPACE, KVCK_ERR_HIP,             KVCK_ERR_NO_DEVICE,   7,
                            -1000,             kI32Max};

@@ -168,16 +168,22 @@ def pin_all_ones(o):
 
 def pin_large_numbers(o):
     """Closed forms far from zero: a request whose listed blocks start past
-    token 2^32 (piece indices near 2^34) on the largest layer number with the
-    largest global head, whose slice factor m = 2(32767*65536 + 65535) + 1 is
-    2^32 - 1.  One nonzero piece gives x*m*(2j+1); all-ones pieces give
+    token 2^32 (piece indices near 2^34), with the largest global head, on
+    layer 32767 (slice factor m = 2(32767*65536 + 65535) + 1 = 2^32 - 1, the
+    largest that fits 32 bits), layer 2^20 (m just above 2^37) and layer
+    2^31 - 1 (the largest int32 layer number; m = 2^48 - 1).  The page bounds
+    the head number (H) but not the layer number, which is the number in the
+    layer's name.  One nonzero piece gives x*m*(2j+1); all-ones pieces give
     P^2 (t1^2 - t0^2) * sum of m, both mod 2^64."""
     assert factor(32767, 65535) == (1 << 32) - 1
+    assert factor((1 << 31) - 1, 65535) == (1 << 48) - 1
+    assert factor(1 << 20, 65535) == (1 << 37) + (1 << 17) - 1
     rng = np.random.default_rng(12)
     far = (1 << 30) + 3
-    for layout in ("HND", "NHD", "MLA"):
+    for layout, big in (("HND", 32767), ("NHD", 32767), ("MLA", 32767), ("NHD", 1 << 20), ("HND", (1 << 31) - 1),
+                        ("MLA", (1 << 31) - 1)):
         d, bs = 8, 4
-        layers = (32767, 5)
+        layers = (big, 5)
         case, req = make_case(rng, layout=layout, layers=layers, nh=1, d=d, bs=bs, lengths=(far * bs + 6, 9),
                               start=(far, 0), zero=True, bases=(65535, 65535))
         planes = 1 if layout == "MLA" else 2
@@ -195,14 +201,14 @@ def pin_large_numbers(o):
             np.frombuffer(x.to_bytes(8, "little"), np.uint8)
         t = pos * bs + i
         assert t * P > 1 << 33
-        want = x * ((1 << 32) - 1) * (2 * (t * P + q) + 1) & M64
+        want = x * factor(big, 65535) * (2 * (t * P + q) + 1) & M64
         got = run_blocks(o, case)
         for rr, kk in listed(case):
             assert int(got[rr, kk]) == (want if (rr, kk) == (0, k) else 0), (layout, rr, kk)
         # every piece 1
         for pool in case["caches"]:
             pool.view("<u8")[...] = 1
-        sum_m = factor(32767, 65535) + factor(5, 65535)
+        sum_m = factor(big, 65535) + factor(5, 65535)
         got = run_blocks(o, case)
         for r, kk in listed(case):
             t0 = (int(req.start_pos[r]) + kk) * bs

@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTS) == decl
-    assert kvck.kvck_abi_version() == 1
+    assert kvck.kvck_abi_version() == 2
     assert kvck.kvck_status_string(-4) == "KVCK_ERR_WORKSPACE"
     assert kvck.kvck_status_string(7) == "KVCK_UNKNOWN_STATUS"
 
@@ -74,7 +74,6 @@ def _call(L=None, ncaches=2, layers=(0, 1), bases=(0, 0), head_begin=0, head_cou
     (dict(head_count=0), -1),
     (dict(head_begin=7, head_count=2), -1),
     (dict(bases=(0, 65535)), -2),                    # more than MAX_KV_HEADS_PER_LAYER heads
-    (dict(layers=(0, 40000)), -2),                   # layer number too large for a 32-bit factor
     (dict(layers=(0, -1)), -1),
     (dict(ptr=0), -1),
     (dict(out=0), -1),
@@ -95,6 +94,8 @@ def test_blocks_zero_requests_is_a_no_op():
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU answer")
 def test_valid_call_without_gpu_reports_no_device():
     assert _call() == -6
+    # any non-negative int32 layer number passes validation (64-bit slice factors)
+    assert _call(layers=(40000, 2**31 - 1)) == -6
     assert kvck.kvck_platform_supported() is False
 
 
@@ -151,8 +152,9 @@ def test_binding_argument_checks():
 def test_tags_rejects_before_launch():
     lib = kvck.load_library()
 
-    def call(cs=FAKE, h=FAKE, stride=32, n=16, nbpr=None, mb=0, tagged=FAKE, stored=None, mm=None, cnt=None):
-        return lib.kvck_tag_checksums(cs, h, stride, 0, n, nbpr, mb, tagged, stored, mm, cnt, None)
+    def call(cs=FAKE, h=FAKE, stride=32, n=16, nbpr=None, mb=0, tagged=FAKE, stored=None, mm=None, cnt=None,
+             sp=None, bs=0):
+        return lib.kvck_tag_checksums(cs, h, stride, 0, n, nbpr, sp, mb, bs, tagged, stored, mm, cnt, None)
 
     assert call(n=0) == 0
     assert call(n=-1) == -1
@@ -163,5 +165,9 @@ def test_tags_rejects_before_launch():
     assert call(stride=12) == -3
     assert call(h=FAKE + 4) == -3
     assert call(nbpr=FAKE, mb=5) == -1           # n not a multiple of max_blocks
+    assert call(sp=FAKE, bs=16) == -1            # start positions without counts
+    assert call(nbpr=FAKE, mb=4, sp=FAKE) == -1  # start positions without a block size
+    assert call(nbpr=FAKE + 2, mb=4) == -3       # counts not 4-byte aligned
+    assert call(nbpr=FAKE, mb=4, sp=FAKE + 4, bs=16) == -3
     if not torch.cuda.is_available():
         assert call() == -6

@@ -106,6 +106,9 @@ def test_invariance_set():
     cf64 = gpu_blocks(f64, "NHD", f.layer_numbers, rf64)
     assert np.array_equal(_req_sums(cf16, f.req), _req_sums(cf64, rf64))
     assert_match(cf16, oracle_at(f16, "NHD", f.layer_numbers, f.req, sample_positions(f.req, 40, seed=6)), "fp8")
+    # block size 64 position by position too (the sums above cannot place an error)
+    assert_match(cf64, oracle_at(f64, "NHD", f.layer_numbers, rf64, sample_positions(rf64, 40, seed=9)), "fp8 bs64")
+    assert_unlisted_untouched(cf64, rf64)
     del f16, f64
     _free()
     # (iv) MLA: 61 layers x one latent head of 576 bf16, block sizes 64 and 16
@@ -120,6 +123,8 @@ def test_invariance_set():
         wl.repage_torch(s, "MLA", m.req, d, "MLA", rm16)
     cm16 = gpu_blocks(m16, "MLA", m.layer_numbers, rm16)
     assert np.array_equal(_req_sums(cm64, m.req), _req_sums(cm16, rm16))
+    assert_match(cm16, oracle_at(m16, "MLA", m.layer_numbers, rm16, sample_positions(rm16, 40, seed=10)), "mla16")
+    assert_unlisted_untouched(cm16, rm16)
     del m64, m16
     _free()
 

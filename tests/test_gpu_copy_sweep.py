@@ -32,7 +32,7 @@ def _case(i):
     unit = 8 // es
     d = unit * int(rng.integers(1, 40))
     bs = int(rng.choice([1, 2, 3, 4, 8, 16, 32]))
-    layers = sorted(int(x) for x in rng.choice(100, size=int(rng.integers(1, 4)), replace=False))
+    layers = sorted(int(x) << (int(x) % 17) for x in rng.choice(100, size=int(rng.integers(1, 4)), replace=False))
     n_req = int(rng.integers(1, 5))
     lengths = [int(x) for x in rng.integers(0, 3 * bs + 20, size=n_req)]
     start = [int(x) for x in rng.integers(0, 2, size=n_req)]
@@ -135,7 +135,7 @@ def _tcase(i):
     heads = int(rng.integers(1, 6))
     d = (8 // es) * int(rng.integers(1, 33))                     # rows of whole 8-byte pieces
     bs = int(rng.choice([b for b in (1, 2, 4, 8, 16, 32, 64) if (b * es) % 8 == 0]))
-    layers = sorted(int(x) for x in rng.choice(100, size=int(rng.integers(1, 4)), replace=False))
+    layers = sorted(int(x) << (int(x) % 17) for x in rng.choice(100, size=int(rng.integers(1, 4)), replace=False))
     n_req = int(rng.integers(1, 5))
     lengths = [int(x) for x in rng.integers(0, 3 * bs + 20, size=n_req)]
     start = [int(x) for x in rng.integers(0, 2, size=n_req)]

@@ -17,7 +17,7 @@ import oracle
 import paged_kv_cache_kvck_amd as kvck
 from paged_kv_cache_kvck_amd import workloads as wl
 from gpu_helpers import (DEV, SENTINEL, assert_match, assert_unlisted_untouched, gpu_blocks, log, oracle_at,
-                         req_tensors, to_device_bits)
+                         req_tensors, to_device_bits, to_host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -334,8 +334,13 @@ def test_host_rejects_before_launch():
         gpu_blocks([pool], "NHD", [0], req, bases=[65535])
     assert ei.value.status == -2
     with pytest.raises(kvck.KvckError) as ei:
-        gpu_blocks([pool], "NHD", [40000], req)
-    assert ei.value.status == -2
+        gpu_blocks([pool], "NHD", [-1], req)
+    assert ei.value.status == -1
+    # a layer number past 16 bits is valid (the page bounds heads, not layers)
+    got = gpu_blocks([pool], "NHD", [40000], req)
+    want = oracle.checksum_blocks([to_host_bits(pool)], "NHD", [40000], [0], req.block_table, req.num_blocks,
+                                  req.start_pos, req.num_tokens)
+    assert np.array_equal(got[0, :int(req.num_blocks[0])], want[0, :int(req.num_blocks[0])])
     with pytest.raises(kvck.KvckError) as ei:
         gpu_blocks([pool], "NHD", [0], req, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
     assert ei.value.status == -4
@@ -363,6 +368,41 @@ def test_determinism_and_streams():
         finally:
             del os.environ["KVCK_SCHEDULE"]
         assert np.array_equal(a, e), sched
+
+
+def test_calls_on_another_stream_wait_for_the_current_one():
+    """A call given stream=s without entering torch.cuda.stream(s): the pool
+    is rewritten on the current stream just before (behind a long kernel),
+    and out, workspace and flag word are allocated and cleared there by the
+    binding; the call on s must still see all of it (s waits for the current
+    stream) and its buffers must not be handed out again while s uses them."""
+    log("[side stream]")
+    rng = np.random.default_rng(19)
+    req, nb = wl.page_requests(rng, list(rng.integers(1, 900, 30)), 16, spare_frac=0.1)
+    host = [wl.host_random_bits(rng, wl.pool_shape("HND", nb, 16, 8, 128), "bf16") for _ in range(4)]
+    pools = [to_device_bits(p) for p in host]
+    layers = [0, 1, 2, 3]
+    want = gpu_blocks(pools, "HND", layers, req)
+    bt, nbt, sp, nt = req_tensors(req)
+    saved = pools[0].clone()
+    busy = torch.zeros(64 << 20, dtype=torch.float32, device=DEV)
+    hs = [[wl.host_random_bits(rng, (5, 4, 16), "fp32")] for _ in range(2)]
+    states = [[to_device_bits(a) for a in l] for l in hs]
+    sids = torch.tensor([4, 0, 2], dtype=torch.int32, device=DEV)
+    want_states = oracle.checksum_states(hs, [1, 3], [0, 0], sids.cpu().numpy())
+    s = torch.cuda.Stream()
+    for i in range(3):
+        pools[0].zero_()
+        for _ in range(20):
+            busy.add_(1.0)             # keeps the current stream busy
+        pools[0].copy_(saved)          # the final cache bytes, written on the current stream
+        got = kvck.kvck_checksum_blocks(pools, "HND", layers, bt, nbt, sp, nt, stream=s, check=(i == 2))
+        gs = kvck.kvck_checksum_states(states, [1, 3], sids, stream=s)
+        torch.cuda.synchronize()
+        got = got.cpu().numpy().view(np.uint64)
+        for r, k in req.listed():
+            assert got[r, k] == want[r, k], (i, r, k)
+        assert np.array_equal(gs.cpu().numpy().view(np.uint64), want_states), i
 
 
 def test_states_small_parity():
@@ -421,6 +461,50 @@ def test_largest_numbering(schedule):
                                   req.num_tokens, head_begin=65534, head_count=2)
     for r, k in req.listed():
         assert int(got[r, k]) == int(want[r, k]), (r, k)
+
+
+BIG_LAYERS = [(1 << 31) - 1, 1 << 20, 40000, 3]
+
+
+@pytest.mark.parametrize("layout,elem,nh,d", [("HND", "bf16", 8, 128), ("NHD", "fp8", 12, 64), ("NHD", "fp16", 4, 64),
+                                              ("MLA", "bf16", 1, 576)])
+def test_layer_numbers_beyond_16_bits(layout, elem, nh, d, schedule):
+    """Layer numbers are not bounded by the page (the number in the layer's
+    name): at layer 2^31 - 1 the factor m = 2(layer*65536 + head) + 1 nears
+    2^48.  Separate heads (HND), merged heads (fp8 NHD, 64-byte rows) and a
+    single latent head (MLA), and the fused save of the same pools."""
+    log(f"[large layer numbers] {layout} {elem}")
+    rng = np.random.default_rng(zlib.crc32(f"layers{layout}{elem}".encode()))
+    req, nb = wl.page_requests(rng, list(rng.integers(1, 300, 9)), 16, extra_blocks=[1] + [0] * 8, spare_frac=0.3)
+    hp = [wl.host_random_bits(rng, wl.pool_shape(layout, nb, 16, nh, d), elem) for _ in BIG_LAYERS]
+    pools = [to_device_bits(p) for p in hp]
+    bases = [nh * 7] * len(BIG_LAYERS)
+    got = gpu_blocks(pools, layout, BIG_LAYERS, req, bases=bases)
+    want = oracle.checksum_blocks(hp, layout, BIG_LAYERS, bases, req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k]), (r, k)
+    bt, nbt, sp, nt = req_tensors(req)
+    staging = torch.empty(int(req.num_blocks.sum()) * kvck.kvck_staging_bytes(pools[0], layout, len(pools)),
+                          dtype=torch.uint8, device=DEV)
+    saved = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, pools, layout, BIG_LAYERS, bt, nbt, sp, nt, staging,
+                                           global_head_base=bases, check=True).cpu().numpy().view(np.uint64)
+    for r, k in req.listed():
+        assert int(saved[r, k]) == int(want[r, k]), (r, k)
+
+
+def test_states_layer_numbers_beyond_16_bits():
+    """Mamba states on layers up to 2^31 - 1."""
+    log("[large layer numbers] states")
+    rng = np.random.default_rng(17)
+    layers = [(1 << 31) - 1, 1 << 20, 1]
+    hs = [[wl.host_random_bits(rng, (6, 4, 8, 4), "fp32"), wl.host_random_bits(rng, (6, 4, 16), "fp16")]
+          for _ in layers]
+    slots = np.array([5, 0, 3], dtype=np.int32)
+    got = kvck.kvck_checksum_states([[to_device_bits(a) for a in l] for l in hs], layers,
+                                    torch.from_numpy(slots).to(DEV), global_row_base=9, check=True)
+    want = oracle.checksum_states(hs, layers, [9] * 3, slots)
+    assert np.array_equal(got.cpu().numpy().view(np.uint64), want)
 
 
 @pytest.mark.parametrize("layout,elem,nh,d", [("HND", "bf16", 8, 128), ("NHD", "fp8", 12, 64), ("MLA", "bf16", 1, 576)])
@@ -529,6 +613,7 @@ def test_calls_from_several_host_threads():
             ws = torch.empty(kvck.kvck_blocks_workspace_bytes(6, req.num_reqs, req.max_blocks), dtype=torch.uint8,
                              device=DEV)
             out = torch.zeros((req.num_reqs, req.max_blocks), dtype=torch.uint64, device=DEV)
+            s.wait_stream(torch.cuda.current_stream())  # the zero fill above runs on this thread's current stream
             with torch.cuda.stream(s):
                 for _ in range(5):
                     kvck.kvck_checksum_blocks(layouts[layout], layout, list(range(6)), bt, nbt, sp, nt, out=out,

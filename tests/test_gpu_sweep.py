@@ -24,6 +24,13 @@ pytestmark = pytest.mark.gpu
 LAYOUTS = ["NHD", "HND", "FI_NHD", "FI_HND", "MLA", "XSPLIT_PAIR", "TRANS_PAIR"]
 
 
+
+def _spread(x):
+    """A drawn layer number x < 2^15 moved up by 0..16 bits (x mod 17), so the
+    cases cover layer numbers up to 2^31 - 1 (64-bit slice factors) without
+    changing the random stream that draws the rest of each case."""
+    return int(x) << (int(x) % 17)
+
 def _case(i):
     rng = np.random.default_rng(zlib.crc32(f"sweep{i}".encode()))
     layout = LAYOUTS[i % len(LAYOUTS)]
@@ -38,7 +45,7 @@ def _case(i):
         bs_choices = [b for b in bs_choices if (b * es) % 8 == 0]
     bs = int(rng.choice(bs_choices))
     n_layers = int(rng.integers(1, 5))
-    layers = sorted(int(x) for x in rng.choice(32768, size=n_layers, replace=False))
+    layers = sorted(_spread(x) for x in rng.choice(32768, size=n_layers, replace=False))
     n_req = int(rng.integers(1, 6))
     lengths = [int(x) for x in rng.integers(0, 4 * bs + 40, size=n_req)]
     start = [int(x) for x in rng.integers(0, 3, size=n_req)]
@@ -111,7 +118,7 @@ def _states_case(i):
         per16 = 16 // wl.ELEM_BYTES[elem]                       # row bytes are whole 16-byte chunks
         inner = per16 * int(rng.integers(1, 70))
         states.append((elem, inner))
-    layers = sorted(int(x) for x in rng.choice(32768, size=int(rng.integers(1, 5)), replace=False))
+    layers = sorted(_spread(x) for x in rng.choice(32768, size=int(rng.integers(1, 5)), replace=False))
     slots = int(rng.integers(2, 12))
     n_req = int(rng.integers(1, 8))
     row_begin = int(rng.integers(0, rows))

@@ -87,3 +87,46 @@ def test_offload_round_trip():
     assert check(ct, hashes_t=wrong)[0] == 1
     n_listed = int(req.num_blocks.sum())
     assert check(ct, fingerprint=fp + 1)[0] == n_listed
+
+
+def test_rejected_requests_are_not_tagged():
+    """A request the checksum call rejects (count outside [0, max_blocks],
+    negative start position) leaves its entries unwritten there, so the tags
+    call lists nothing for it either: no tag written, no comparison made, no
+    mismatch counted -- whatever stale values its entries hold."""
+    log("[tags] rejected requests")
+    rng = np.random.default_rng(22)
+    req, nb = wl.page_requests(rng, [60, 40, 90, 20], 16, spare_frac=0.2)
+    R, M = req.num_reqs, req.max_blocks
+    counts = req.num_blocks.copy()
+    counts[1] = M + 1          # too many listed blocks
+    counts[3] = -2             # negative count
+    start = req.start_pos.copy()
+    start[2] = -1              # negative start position
+    nbt = torch.from_numpy(counts).to(DEV)
+    spt = torch.from_numpy(start).to(DEV)
+    stale = rng.integers(0, 2**63, size=R * M, dtype=np.int64)
+    ct = torch.from_numpy(stale).to(DEV).view(torch.uint64)
+    ht = torch.from_numpy(_hashes(rng, R * M)).to(DEV)
+    sentinel = np.uint64(0x5A5A5A5A5A5A5A5A)
+    tagged = torch.full((R * M,), int(sentinel.view(np.int64)), dtype=torch.int64, device=DEV).view(torch.uint64)
+    kvck.kvck_tag_checksums(ct, ht, 77, num_blocks_per_req=nbt, start_pos=spt, block_size=16, tagged=tagged)
+    # stored values that match nothing: every listed entry of a good request mismatches
+    stored = torch.zeros(R * M, dtype=torch.int64, device=DEV).view(torch.uint64)
+    cnt = torch.zeros(1, dtype=torch.int32, device=DEV)
+    _, mm = kvck.kvck_tag_checksums(ct, ht, 77, num_blocks_per_req=nbt, start_pos=spt, block_size=16, tagged=False,
+                                    stored=stored, mismatch_count=cnt)
+    torch.cuda.synchronize()
+    t = tagged.cpu().numpy().reshape(R, M)
+    want = oracle.tags.tag_checksums(stale.view(np.uint64), [bytes(r) for r in ht.cpu().numpy()], 77).reshape(R, M)
+    good = [0]
+    assert int(cnt.item()) == sum(int(counts[r]) for r in good)
+    for r in range(R):
+        listed = int(counts[r]) if r in good else 0
+        assert np.array_equal(t[r, :listed], want[r, :listed]), r
+        assert np.all(t[r, listed:] == sentinel), r
+    # without start positions only the count rule applies: request 2 is listed again
+    cnt.zero_()
+    kvck.kvck_tag_checksums(ct, ht, 77, num_blocks_per_req=nbt, tagged=False, stored=stored, mismatch_count=cnt)
+    torch.cuda.synchronize()
+    assert int(cnt.item()) == int(counts[0]) + int(counts[2])

@@ -42,6 +42,10 @@ MUTATIONS = {
     "piece index kept in 32 bits": ("odd = _U64(2) * j + _U64(1)", "odd = _U64(2) * (j & _U64(0xFFFFFFFF)) + _U64(1)"),
     "slice factor kept in 31 bits": ("c = c + (m * s).sum(dtype=_U64)",
                                      "c = c + ((m & _U64(0x7FFFFFFF)) * s).sum(dtype=_U64)"),
+    "slice factor kept in 32 bits": ("c = c + (m * s).sum(dtype=_U64)",
+                                     "c = c + ((m & _U64(0xFFFFFFFF)) * s).sum(dtype=_U64)"),
+    "layer number kept in 16 bits": ("m = _U64(2) * (_U64(layer) * _U64(MAX_KV_HEADS_PER_LAYER) + heads)",
+                                     "m = _U64(2) * (_U64(layer & 0xFFFF) * _U64(MAX_KV_HEADS_PER_LAYER) + heads)"),
     "Mamba elements numbered from 1": ("e = np.arange(x.size, dtype=_U64)", "e = np.arange(x.size, dtype=_U64) + _U64(1)"),
     "Mamba local row numbering": ("m = _U64(slice_factor(layer, g0 + g))", "m = _U64(slice_factor(layer, g))"),
     "Mamba states reversed": ("for st in states])", "for st in states[::-1]])"),
