@@ -69,7 +69,9 @@ typedef enum kvck_status {
                                      not aligned to its element size */
   KVCK_ERR_WORKSPACE = -4,        /* workspace missing or too small */
   KVCK_ERR_HIP = -5,              /* a HIP runtime call failed */
-  KVCK_ERR_NO_DEVICE = -6         /* no gfx950 device is current */
+  KVCK_ERR_NO_DEVICE = -6,        /* no gfx950 device is current */
+  KVCK_ERR_SCRATCH = -7           /* an allocation-free call needs more than
+                                     KVCK_SCRATCH_BYTES of scratch */
 } kvck_status;
 
 /* Bits OR-ed into *error_flags by the kernels. */
@@ -202,6 +204,37 @@ kvck_status kvck_checksum_blocks(
     kvck_stream_t stream);
 
 size_t kvck_blocks_workspace_bytes(int32_t num_caches, int32_t num_reqs, int32_t max_blocks);
+
+/*
+ * kvck_checksum_blocks_noalloc -- kvck_checksum_blocks for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments and results, without
+ * the workspace.  In its place the call uses a scratch array of
+ * KVCK_SCRATCH_BYTES that the library holds on each device it runs on, from
+ * the first such call until the process ends.  The call allocates nothing
+ * and records no events (instrumentation does not time it).
+ *
+ * It needs the plan's position records (32 bytes per num_reqs*max_blocks
+ * slot, plus a few KiB) and, when its caches form more than one task group
+ * (one group covers one to sixteen caches, whichever the schedule picks), 8
+ * bytes per slot and group; a call that would need more than
+ * KVCK_SCRATCH_BYTES returns KVCK_ERR_SCRATCH and launches nothing.  Any call
+ * with kvck_blocks_workspace_bytes(num_caches, num_reqs, max_blocks) <=
+ * KVCK_SCRATCH_BYTES fits.  Nothing in the scratch has to start at any
+ * value: every call writes what it later reads.
+ *
+ * All such calls on one device share its scratch array, so calls that
+ * overlap on one device -- on different streams, or from different host
+ * threads without ordering them on one stream -- race and give wrong
+ * results; calls ordered on one stream do not.
+ */
+#define KVCK_SCRATCH_BYTES (32u << 20)
+kvck_status kvck_checksum_blocks_noalloc(
+    const kvck_kv_layout* layout, const void* const* cache_ptrs, const int32_t* layer_numbers,
+    const int32_t* global_head_base, int32_t num_caches, int32_t head_begin, int32_t head_count,
+    const int32_t* block_table, int64_t block_table_row_stride, const int32_t* num_blocks_per_req,
+    const int64_t* start_pos, const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks,
+    uint64_t* out, int32_t accumulate, uint32_t* error_flags, kvck_stream_t stream);
 
 /*
  * Shape of one Mamba state, shared by every Mamba layer of a call.  A state

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     KVCK_COPY_SAVE,
     KVCK_FLAG_BAD_STATE_SLOT,
     KVCK_FLAG_STAGING_FULL,
+    KVCK_SCRATCH_BYTES,
     KvckDeviceError,
     KvckError,
     LAYOUT_NAMES,
@@ -23,6 +24,7 @@ from ._binding import (  # noqa: F401
     kvck_abi_version,
     kvck_blocks_workspace_bytes,
     kvck_checksum_blocks,
+    kvck_checksum_blocks_noalloc,
     kvck_checksum_states,
     kvck_copy_checksum_blocks,
     kvck_instrument,

@@ -20,8 +20,9 @@ LIB_PATH = os.environ.get("KVCK_LIB", os.path.join(_PKG, "libkvck.so"))
 KVCK_OK = 0
 STATUS_NAMES = {
     0: "KVCK_OK", -1: "KVCK_ERR_INVALID_ARGUMENT", -2: "KVCK_ERR_UNSUPPORTED", -3: "KVCK_ERR_MISALIGNED",
-    -4: "KVCK_ERR_WORKSPACE", -5: "KVCK_ERR_HIP", -6: "KVCK_ERR_NO_DEVICE",
+    -4: "KVCK_ERR_WORKSPACE", -5: "KVCK_ERR_HIP", -6: "KVCK_ERR_NO_DEVICE", -7: "KVCK_ERR_SCRATCH",
 }
+KVCK_SCRATCH_BYTES = 32 << 20
 KVCK_FLAG_BAD_BLOCK_ID = 1
 KVCK_FLAG_BAD_REQUEST = 2
 KVCK_FLAG_BAD_STATE_SLOT = 4
@@ -30,7 +31,8 @@ KVCK_COPY_SAVE = 0
 KVCK_COPY_LOAD = 1
 
 # symbols include/kvck.h declares
-EXPORTS = ("kvck_checksum_blocks", "kvck_blocks_workspace_bytes", "kvck_checksum_states",
+EXPORTS = ("kvck_checksum_blocks", "kvck_blocks_workspace_bytes", "kvck_checksum_blocks_noalloc",
+           "kvck_checksum_states",
            "kvck_states_workspace_bytes", "kvck_copy_checksum_blocks", "kvck_staging_bytes", "kvck_tag_checksums",
            "kvck_instrument", "kvck_instrument_read",
            "kvck_status_string",
@@ -83,6 +85,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kvck_checksum_blocks.argtypes = [
         ctypes.POINTER(kvck_kv_layout), ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(i32), i32,
         i32, i32, vp, i64, vp, vp, vp, i32, i32, vp, i32, vp, sz, vp, vp]
+    lib.kvck_checksum_blocks_noalloc.restype = i32
+    lib.kvck_checksum_blocks_noalloc.argtypes = [
+        ctypes.POINTER(kvck_kv_layout), ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(i32), i32,
+        i32, i32, vp, i64, vp, vp, vp, i32, i32, vp, i32, vp, vp]
     lib.kvck_blocks_workspace_bytes.restype = sz
     lib.kvck_blocks_workspace_bytes.argtypes = [i32, i32, i32]
     lib.kvck_checksum_states.restype = i32
@@ -405,6 +411,41 @@ def kvck_checksum_blocks(caches, layout: str | None, layer_numbers: Sequence[int
         ws.numel() * ws.element_size(), _ptr(a["error_flags"]), _stream_handle(stream, a["dev"], a["allocated"]))
     _check(st, "kvck_checksum_blocks")
     return _finish(a, check)
+
+
+def kvck_checksum_blocks_noalloc(caches, layout: str | None, layer_numbers: Sequence[int] | None,
+                                 block_table: torch.Tensor, num_blocks_per_req: torch.Tensor, start_pos: torch.Tensor,
+                                 num_tokens: torch.Tensor, out: torch.Tensor, global_head_base=None,
+                                 head_begin: int = 0, head_count: int | None = None, accumulate: bool = False,
+                                 error_flags: torch.Tensor | None = None, stream=None,
+                                 planes: tuple | None = None) -> torch.Tensor:
+    """kvck_checksum_blocks without a workspace: the library's per-device
+    scratch array (KVCK_SCRATCH_BYTES) takes its place, and the call itself
+    allocates nothing (see include/kvck.h).  ``out`` is required, so that
+    this wrapper allocates nothing either.  Calls that overlap on one device
+    share that scratch and race; calls ordered on one stream do not."""
+    lib = load_library()
+    pc = caches if isinstance(caches, PreparedCaches) else PreparedCaches(
+        caches, layout, layer_numbers, global_head_base, head_begin, head_count, planes)
+    dev = pc.device
+    _meta(block_table, torch.int32, "block_table", dev)
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be 2-D with contiguous rows")
+    R, max_blocks = block_table.shape
+    _meta(num_blocks_per_req, torch.int32, "num_blocks_per_req", dev, R)
+    _meta(start_pos, torch.int64, "start_pos", dev, R)
+    _meta(num_tokens, torch.int64, "num_tokens", dev, R)
+    if not isinstance(out, torch.Tensor) or out.dtype not in (torch.uint64, torch.int64) or out.device != dev \
+            or not out.is_contiguous() or out.numel() < R * max_blocks:
+        raise ValueError("out must be a contiguous uint64 tensor of num_reqs*max_blocks entries")
+    error_flags = _flag_word(error_flags, False, dev)
+    st = lib.kvck_checksum_blocks_noalloc(
+        ctypes.byref(pc.layout), pc.ptrs, pc.layers, pc.bases, pc.n, pc.head_begin, pc.head_count,
+        block_table.data_ptr(), block_table.stride(0), num_blocks_per_req.data_ptr(), start_pos.data_ptr(),
+        num_tokens.data_ptr(), R, max_blocks, out.data_ptr(), int(bool(accumulate)), _ptr(error_flags),
+        _stream_handle(stream, dev))
+    _check(st, "kvck_checksum_blocks_noalloc")
+    return out
 
 
 def kvck_staging_bytes(cache: torch.Tensor, layout: str, num_caches: int, head_count: int | None = None) -> int:

@@ -19,6 +19,27 @@ constexpr int64_t kH = KVCK_MAX_KV_HEADS_PER_LAYER;
 
 bool aligned(const void* p, int64_t a) { return (reinterpret_cast<uintptr_t>(p) % (uintptr_t)a) == 0; }
 
+// Scratch of kvck_checksum_blocks_noalloc: one copy per device, held from the
+// module's load until the process ends.  In host code `scratch` names a host
+// stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that address is passed to kernels.
+static __device__ __align__(256) uint8_t scratch[KVCK_SCRATCH_BYTES];
+
+// Device address of `scratch` on device `dev` (current), or null if the
+// runtime cannot give it.
+void* scratch_address(int dev) {
+  static std::mutex mu;
+  static void* addr[64];
+  std::lock_guard<std::mutex> g(mu);
+  if (dev < 0 || dev >= 64) return nullptr;
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
 
 // Largest byte extent of a tensor the kernels address (64-bit offsets with
 // room to spare; far beyond any device memory).
@@ -244,6 +265,7 @@ KVCK_EXPORT const char* kvck_status_string(int32_t status) {
     case KVCK_ERR_WORKSPACE: return "KVCK_ERR_WORKSPACE";
     case KVCK_ERR_HIP: return "KVCK_ERR_HIP";
     case KVCK_ERR_NO_DEVICE: return "KVCK_ERR_NO_DEVICE";
+    case KVCK_ERR_SCRATCH: return "KVCK_ERR_SCRATCH";
   }
   return "KVCK_UNKNOWN_STATUS";
 }
@@ -318,8 +340,9 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
                         int64_t block_table_row_stride, const int32_t* num_blocks_per_req, const int64_t* start_pos,
                         const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks, uint64_t* out,
                         int32_t accumulate, void* workspace, size_t workspace_bytes, uint32_t* error_flags,
-                        void* staging, int64_t staging_positions, kvck_stream_t stream) {
+                        void* staging, int64_t staging_positions, kvck_stream_t stream, bool use_scratch = false) {
   if (mode != kModeChecksum && mode != KVCK_COPY_SAVE && mode != KVCK_COPY_LOAD) return KVCK_ERR_INVALID_ARGUMENT;
+  if (use_scratch && mode != kModeChecksum) return KVCK_ERR_INVALID_ARGUMENT;
   // ---- layout
   if (!layout || !cache_ptrs || !layer_numbers || !global_head_base) return KVCK_ERR_INVALID_ARGUMENT;
   if (num_caches < 1 || num_caches > KVCK_MAX_CACHES) return KVCK_ERR_UNSUPPORTED;
@@ -433,9 +456,13 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
     if ((int64_t)L.block_size * L.row_bytes >= ((int64_t)1 << 31)) return KVCK_ERR_UNSUPPORTED;
     if (!product_ok(staging_positions, num_caches, image_bytes)) return KVCK_ERR_UNSUPPORTED;
   }
-  // ---- workspace
+  // ---- workspace (or, allocation-free, the library's scratch: at least the records must fit)
   const BlocksWorkspace w = BlocksWorkspace::make(num_caches, num_reqs, max_blocks);
-  if (!workspace || workspace_bytes < w.total || !aligned(workspace, (int64_t)kAlign)) return KVCK_ERR_WORKSPACE;
+  if (use_scratch) {
+    if (w.partials_off > (size_t)KVCK_SCRATCH_BYTES) return KVCK_ERR_SCRATCH;
+  } else if (!workspace || workspace_bytes < w.total || !aligned(workspace, (int64_t)kAlign)) {
+    return KVCK_ERR_WORKSPACE;
+  }
 
   int dev = 0;
   const kvck_status ds = current_device(&dev);
@@ -456,6 +483,16 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   const int32_t lpt = shp.caches_per_task;
   const int32_t total_groups = (num_caches + lpt - 1) / lpt;
   const int64_t max_start = INT64_MAX / L.block_size - max_blocks;  // keeps (start + k) * block_size exact
+  if (use_scratch) {
+    // records, then partials of the task groups the schedule forms (none for one group)
+    const size_t need = w.partials_off + (total_groups > 1 ? align_up(sizeof(uint64_t) * (size_t)max_items *
+                                                                       (size_t)total_groups)
+                                                           : 0);
+    if (need > (size_t)KVCK_SCRATCH_BYTES) return KVCK_ERR_SCRATCH;
+    workspace = scratch_address(dev);
+    if (!workspace) return KVCK_ERR_HIP;
+  }
+
   if (!dense && launch_plan(block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens,
                             num_reqs, max_blocks, L.block_size, L.num_blocks, workspace, error_flags,
                             st) != hipSuccess)
@@ -499,7 +536,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   a.num_tokens = num_tokens;
   a.req_flags = error_flags;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
-  const bool timed = instrument_pair(&ev0, &ev1);
+  const bool timed = !use_scratch && instrument_pair(&ev0, &ev1);  // (an allocation-free call creates no events)
   if (timed && hipEventRecord(ev0, st) != hipSuccess) return KVCK_ERR_HIP;
   for (int32_t c0 = 0; c0 < num_caches; c0 += kCachesPerLaunch) {
     const int32_t n = num_caches - c0 < kCachesPerLaunch ? num_caches - c0 : kCachesPerLaunch;
@@ -560,6 +597,18 @@ KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const
                      head_count, block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens,
                      num_reqs, max_blocks, out, accumulate, workspace, workspace_bytes, error_flags, nullptr, 0,
                      stream);
+}
+
+KVCK_EXPORT kvck_status kvck_checksum_blocks_noalloc(
+    const kvck_kv_layout* layout, const void* const* cache_ptrs, const int32_t* layer_numbers,
+    const int32_t* global_head_base, int32_t num_caches, int32_t head_begin, int32_t head_count,
+    const int32_t* block_table, int64_t block_table_row_stride, const int32_t* num_blocks_per_req,
+    const int64_t* start_pos, const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks, uint64_t* out,
+    int32_t accumulate, uint32_t* error_flags, kvck_stream_t stream) {
+  return blocks_call(kModeChecksum, layout, cache_ptrs, layer_numbers, global_head_base, num_caches, head_begin,
+                     head_count, block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens,
+                     num_reqs, max_blocks, out, accumulate, nullptr, 0, error_flags, nullptr, 0, stream,
+                     /*use_scratch=*/true);
 }
 
 KVCK_EXPORT kvck_status kvck_copy_checksum_blocks(int32_t direction, const kvck_kv_layout* layout,

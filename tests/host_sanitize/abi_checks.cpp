@@ -62,7 +62,7 @@ struct BlocksCall {
   void* out = kFake;
   void* ws = kFake;
   size_t ws_bytes = 0;  // 0: the size kvck_blocks_workspace_bytes gives
-  int32_t direction = -1;  // -1: kvck_checksum_blocks; else kvck_copy_checksum_blocks
+  int32_t direction = -1;  // -1: kvck_checksum_blocks; -2: kvck_checksum_blocks_noalloc; else the fused copy
   void* staging = kFake;
   int64_t staging_positions = 64;
   uintptr_t bt_off = 0, nb_off = 0, i64_off = 0;  // byte offsets of the request arrays (misalignment)
@@ -73,6 +73,10 @@ struct BlocksCall {
     const auto* bt = static_cast<const int32_t*>(fake(bt_off));
     const auto* nb = static_cast<const int32_t*>(fake(nb_off));
     const auto* i64 = static_cast<const int64_t*>(fake(i64_off));
+    if (direction == -2)
+      return kvck_checksum_blocks_noalloc(&L, ptrs.data(), layers.data(), bases.data(), (int32_t)ptrs.size(),
+                                          head_begin, head_count, bt, bt_stride, nb, i64, i64, num_reqs, max_blocks,
+                                          static_cast<uint64_t*>(out), 0, nullptr, nullptr);
     if (direction < 0)
       return kvck_checksum_blocks(&L, ptrs.data(), layers.data(), bases.data(), (int32_t)ptrs.size(), head_begin,
                                   head_count, bt, bt_stride, nb, i64, i64, num_reqs, max_blocks,
@@ -276,11 +280,30 @@ void tags_checks(bool have_device) {
   if (!have_device) EXPECT_EQ(call(kFake, kFake, 32, 16, nullptr, 0, kFake, nullptr, nullptr), KVCK_ERR_NO_DEVICE);
 }
 
+void noalloc_checks(bool have_device) {
+  auto call = [](auto&& edit) {
+    BlocksCall c;
+    c.direction = -2;
+    edit(c);
+    return c.run();
+  };
+  EXPECT_EQ(call([](BlocksCall& c) { c.num_reqs = 0; }), KVCK_OK);
+  EXPECT_EQ(call([](BlocksCall& c) { c.out = nullptr; }), KVCK_ERR_INVALID_ARGUMENT);
+  EXPECT_EQ(call([](BlocksCall& c) { c.layers = {0, -1}; }), KVCK_ERR_INVALID_ARGUMENT);
+  EXPECT_EQ(call([](BlocksCall& c) { c.bt_off = 2; }), KVCK_ERR_MISALIGNED);
+  // position records alone past the scratch: 32 bytes per request slot
+  EXPECT_EQ(call([](BlocksCall& c) { c.num_reqs = 1100, c.max_blocks = 1024, c.bt_stride = 1024; }),
+            KVCK_ERR_SCRATCH);
+  EXPECT_EQ(call([](BlocksCall& c) { c.num_reqs = kI32Max, c.max_blocks = kI32Max, c.bt_stride = kI32Max; }),
+            KVCK_ERR_UNSUPPORTED);
+  if (!have_device) EXPECT_EQ(call([](BlocksCall&) {}), KVCK_ERR_NO_DEVICE);
+}
+
 void misc_checks() {
   EXPECT_EQ(kvck_abi_version(), 2);
   const int32_t codes[] = {KVCK_OK,           KVCK_ERR_INVALID_ARGUMENT, KVCK_ERR_UNSUPPORTED, KVCK_ERR_MISALIGNED,
-                           KVCK_ERR_WORKSPACE, KVCK_ERR_HIP,             KVCK_ERR_NO_DEVICE,   7,
-                           -1000,             kI32Max};
+                           KVCK_ERR_WORKSPACE, KVCK_ERR_HIP,             KVCK_ERR_NO_DEVICE,   KVCK_ERR_SCRATCH,
+                           7,                 -1000,                     kI32Max};
   for (int32_t c : codes) EXPECT_EQ(kvck_status_string(c) != nullptr && kvck_status_string(c)[0] == 'K', 1);
   EXPECT_EQ(std::strcmp(kvck_status_string(KVCK_ERR_WORKSPACE), "KVCK_ERR_WORKSPACE"), 0);
   double ms = -1.0;
@@ -297,6 +320,7 @@ void misc_checks() {
 int main() {
   const bool have_device = kvck_platform_supported() != 0;
   blocks_checks(have_device);
+  noalloc_checks(have_device);
   states_checks(have_device);
   tags_checks(have_device);
   misc_checks();

@@ -25,12 +25,13 @@ def header_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = kvck.load_library()
     decl = header_functions()
-    assert len(decl) == 12
+    assert len(decl) == 13
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTS) == decl
     assert kvck.kvck_abi_version() == 2
     assert kvck.kvck_status_string(-4) == "KVCK_ERR_WORKSPACE"
+    assert kvck.kvck_status_string(-7) == "KVCK_ERR_SCRATCH"
     assert kvck.kvck_status_string(7) == "KVCK_UNKNOWN_STATUS"
 
 
@@ -169,5 +170,28 @@ def test_tags_rejects_before_launch():
     assert call(nbpr=FAKE, mb=4, sp=FAKE) == -1  # start positions without a block size
     assert call(nbpr=FAKE + 2, mb=4) == -3       # counts not 4-byte aligned
     assert call(nbpr=FAKE, mb=4, sp=FAKE + 4, bs=16) == -3
+    if not torch.cuda.is_available():
+        assert call() == -6
+
+
+def test_noalloc_rejects_before_launch():
+    """The allocation-free variant validates like kvck_checksum_blocks and
+    refuses, before any device call, a batch whose position records alone
+    exceed the scratch array (32 bytes per request slot)."""
+    lib = kvck.load_library()
+    L = _layout()
+
+    def call(num_reqs=4, max_blocks=8, out=FAKE, layers=(0, 1)):
+        ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+        ly = (ctypes.c_int32 * 2)(*layers)
+        bs = (ctypes.c_int32 * 2)(0, 0)
+        return lib.kvck_checksum_blocks_noalloc(ctypes.byref(L), ptrs, ly, bs, 2, 0, 8, FAKE, max_blocks, FAKE, FAKE,
+                                                FAKE, num_reqs, max_blocks, out, 0, None, None)
+
+    assert call(num_reqs=0) == 0
+    assert call(out=0) == -1
+    assert call(layers=(0, -1)) == -1
+    slots = B.KVCK_SCRATCH_BYTES // 32 + 1024
+    assert call(num_reqs=slots // 1024, max_blocks=1024) == -7
     if not torch.cuda.is_available():
         assert call() == -6
