@@ -7,12 +7,21 @@ values, block 16, HND pool, 256 requests of 512..8192 tokens): plan, main
 pass over every valid K/V byte, second pass.  Inputs are resident in HBM
 before timing starts.
 
-    python bench.py [--steps K] [--warmup W] [--workload llama3_8b|gpt2|hybrid_attn]
+    python bench.py [--steps K] [--warmup W] [--only NAME[,NAME..]]
 
 Prints one JSON line: throughput in checksummed KV GB/s (valid cache bytes /
 step time), the roofline of the main pass (its own HIP events on its stream,
-via the library's instrumentation), and the CPU oracle's rate on a bounded
-sample of the same workload.
+via the library's instrumentation), the CPU oracle's rate on a bounded sample
+of the same workload -- one process, then one process per host CPU over
+layer subsets of the same bytes, whose partial sums must add up to the
+one-process values -- and in ``extra.configs`` one row per other
+configuration of the checksum (GPT-2-shaped pool and its re-pagings, fp8,
+MLA, the hybrid model's attention and Mamba groups, the TP-shard run): its
+main-pass time and fraction of HBM peak, and its values checked against the
+oracle at sampled positions.
+
+``--only`` runs just the named configuration rows (one of CONFIG_NAMES) and
+prints them; a profiler run of one kernel variant uses it.
 """
 
 from __future__ import annotations
@@ -22,6 +31,7 @@ import json
 import os
 import statistics
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -29,12 +39,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
-from paged_kv_cache_kvck_amd.sources import code_only as _code_only, kernel_sources_sha  # noqa: E402
+HEADLINE_DESC = ("llama3-8b-shaped paged KV cache: 32 layers x 8 KV heads x head 128 bf16 normal(0,1), block 16, "
+                 "HND, 256 requests of 512-8192 tokens")
 
 
 def committed_traffic(workload: str):
     """HBM bytes per launch of the main pass from the committed rocprofv3
     counter summary, or None when the kernel sources changed since."""
+    from paged_kv_cache_kvck_amd.sources import kernel_sources_sha
     p = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(p):
         return None
@@ -48,22 +60,93 @@ def committed_traffic(workload: str):
 def make_workload(name):
     from paged_kv_cache_kvck_amd import workloads as wl
     if name == "llama3_8b":
-        return wl.llama3_8b(), ("llama3-8b-shaped paged KV cache: 32 layers x 8 KV heads x head 128 bf16 "
-                                "normal(0,1), block 16, HND, 256 requests of 512-8192 tokens")
-    if name == "gpt2":
-        return wl.gpt2(), ("gpt2-shaped paged KV cache: 12 layers x 12 KV heads x head 64 fp16 random bits, "
-                           "block 16, NHD pool (2,18545,16,12,64) per layer, 64 requests of 128-2048 tokens")
-    if name == "hybrid_attn":
-        return wl.hybrid()[0], ("hybrid model attention group: 24 layers x 8 KV heads x head 128 bf16, block 16, "
-                                "HND, 128 requests of 512-8192 tokens")
+        return wl.llama3_8b(), HEADLINE_DESC
     raise SystemExit(f"unknown workload {name}")
 
 
-def cpu_baseline(pools, w, seconds, gpu_out=None, seed=0):
-    """The oracle, as it stands, on a bounded random sample of listed positions
-    (host copies of their blocks are made outside the timed region).  Each
-    value it computes is also compared with ``gpu_out`` (the GPU's checksums of
-    the timed steps, uint64 [num_reqs, max_blocks]) when given."""
+# ----------------------------------------------------------------- oracle checks
+
+def _host_bits(t):
+    """Raw bits of a device tensor as an unsigned numpy array of its shape."""
+    import numpy as np
+    import torch
+    es = t.element_size()
+    dt = {1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[es]
+    npdt = {1: np.uint8, 2: np.uint16, 4: np.uint32, 8: np.uint64}[es]
+    return t.contiguous().view(dt).cpu().numpy().view(npdt)
+
+
+def _block_axis(layout):
+    return 0 if layout == "MLA" else 1
+
+
+def sample_positions(req, n, seed):
+    """``n`` random listed positions plus every request's last one (its
+    partly valid tail), as (r, k) pairs."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    allpos = req.listed()
+    pick = [allpos[i] for i in rng.choice(len(allpos), min(n, len(allpos)), replace=False)]
+    pick += [(r, int(req.num_blocks[r]) - 1) for r in range(req.num_reqs) if req.num_blocks[r] > 0]
+    return sorted(set(pick))
+
+
+def oracle_check(pools, layout, layers, bases, req, got, positions, head_begin=0, head_count=None):
+    """The oracle's checksums of ``positions`` (computed from host copies of
+    just the blocks they name) against the GPU's ``got`` [num_reqs,
+    max_blocks]: (positions checked, mismatches)."""
+    import torch
+    import oracle
+    mismatches = 0
+    for i in range(0, len(positions), 64):
+        chunk = positions[i:i + 64]
+        ids = sorted({int(req.block_table[r, k]) for r, k in chunk})
+        remap = {b: n for n, b in enumerate(ids)}
+        idx = torch.tensor(ids, dtype=torch.int64, device=pools[0].device)
+        mini = [_host_bits(p.index_select(_block_axis(layout), idx)) for p in pools]
+        for r, k in chunk:
+            v = oracle.kv_checksum.checksum_position(mini, layout, layers, bases, remap[int(req.block_table[r, k])],
+                                                     int(req.start_pos[r]) + k, int(req.num_tokens[r]), head_begin,
+                                                     head_count)
+            mismatches += int(got[r, k]) != v
+    return len(positions), mismatches
+
+
+# ----------------------------------------------------------------- CPU baseline
+
+def _layer_worker(args):
+    """One process of the parallel oracle leg: the oracle over this worker's
+    subset of layers for every position of a chunk, reading the chunk's
+    blocks from the memory-mapped host copy.  numpy only; never touches the
+    GPU.  Returns (partial checksums, seconds of oracle time)."""
+    path, layout, layer_idx, layers, bases, items, head_begin, head_count = args
+    import numpy as np
+    import oracle
+    arr = np.load(path, mmap_mode="r")
+    caches = [arr[i] for i in layer_idx]
+    t0 = time.perf_counter()
+    vals = [oracle.kv_checksum.checksum_position(caches, layout, [layers[i] for i in layer_idx],
+                                                 [bases[i] for i in layer_idx], b, pos, ntok, head_begin, head_count)
+            for b, pos, ntok in items]
+    dt = time.perf_counter() - t0
+    del caches, arr
+    return vals, dt
+
+
+def cpu_baseline(pools, w, seconds, gpu_out, workers, chunk=512, seed=0):
+    """The oracle, as it stands, on a bounded random sample of listed
+    positions of the workload, in chunks: each chunk's blocks (all layers) are
+    copied to a host file in /dev/shm (outside the timed regions); then
+
+    * one process computes every position of the chunk (``value``, cores 1),
+      each compared with the GPU's checksum of the timed steps;
+    * ``workers`` processes at once each compute the same positions over their
+      own subset of the layers -- a PP-style split of the same bytes -- and the
+      partials, added mod 2^64, must equal the one-process values
+      (``parallel``: wall time around the workers, dispatch included).
+
+    Stops once the one-process leg has run ``seconds``."""
+    import multiprocessing as mp
     import numpy as np
     import torch
     import oracle
@@ -72,84 +155,263 @@ def cpu_baseline(pools, w, seconds, gpu_out=None, seed=0):
     rng = np.random.default_rng(seed)
     allpos = w.req.listed()
     order = rng.permutation(len(allpos))
-    done, nbytes, elapsed, i, mismatches = 0, 0, 0.0, 0, 0
-    row = w.heads_used * w.planes * w.head_size * wl.ELEM_BYTES[w.elem] * w.num_layers
-    while elapsed < seconds and i < len(order):
-        chunk = [allpos[j] for j in order[i:i + 32]]
-        i += 32
-        ids = sorted({int(w.req.block_table[r, k]) for r, k in chunk})
-        remap = {b: n for n, b in enumerate(ids)}
-        idx = torch.tensor(ids, dtype=torch.int64, device=pools[0].device)
-        mini = []
-        for p in pools:
-            sub = p.index_select(0 if w.layout == "MLA" else 1, idx).contiguous()
-            mini.append(sub.view(torch.int16).cpu().numpy().view(np.uint16))
-        t0 = time.perf_counter()
-        vals = [oracle.kv_checksum.checksum_position(mini, w.layout, w.layer_numbers, w.bases,
-                                                     remap[int(w.req.block_table[r, k])],
-                                                     int(w.req.start_pos[r]) + k, int(w.req.num_tokens[r]),
-                                                     w.head_begin, w.head_count) for r, k in chunk]
-        elapsed += time.perf_counter() - t0
-        if gpu_out is not None:
-            mismatches += sum(int(gpu_out[r, k]) != v for (r, k), v in zip(chunk, vals))
-        for r, k in chunk:
-            pos = int(w.req.start_pos[r]) + k
-            v = min(w.req.block_size, max(0, int(w.req.num_tokens[r]) - pos * w.req.block_size))
-            nbytes += v * row
-        done += len(chunk)
-    res = {"value": nbytes / elapsed / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    L = w.num_layers
+    shard = np.array_split(np.arange(L), min(workers, L))
+    shard = [[int(i) for i in s] for s in shard if len(s)]
+    row = w.heads_used * w.planes * w.head_size * wl.ELEM_BYTES[w.elem] * L
+    shape = (L,) + wl.pool_shape(w.layout, chunk, w.req.block_size, w.num_heads, w.head_size)
+    bits = wl.HOST_BITS[w.elem]
+    shm_dir = "/dev/shm" if os.path.isdir("/dev/shm") else None
+    fd, path = tempfile.mkstemp(prefix="kvck_oracle_", suffix=".npy", dir=shm_dir)
+    os.close(fd)
+    done = nbytes = mismatches = pmis = 0
+    single_s = par_wall = par_busy = 0.0
+    i = 0
+    pool = None
+    try:
+        host = np.lib.format.open_memmap(path, mode="w+", dtype=bits, shape=shape)
+        pool = mp.get_context("spawn").Pool(len(shard))
+        # start the workers (imports) before the first timed chunk
+        pool.map(abs, range(len(shard)))
+        while single_s < seconds and i < len(order):
+            sel = [allpos[j] for j in order[i:i + chunk]]
+            i += chunk
+            ids = sorted({int(w.req.block_table[r, k]) for r, k in sel})
+            remap = {b: n for n, b in enumerate(ids)}
+            idx = torch.tensor(ids, dtype=torch.int64, device=pools[0].device)
+            ax = _block_axis(w.layout)
+            for li, p in enumerate(pools):
+                dst = host[li][(slice(None),) * ax + (slice(0, len(ids)),)]
+                dst[...] = _host_bits(p.index_select(ax, idx))
+            host.flush()
+            items = [(remap[int(w.req.block_table[r, k])], int(w.req.start_pos[r]) + k, int(w.req.num_tokens[r]))
+                     for r, k in sel]
+            caches = [host[li] for li in range(L)]
+            t0 = time.perf_counter()
+            vals = [oracle.kv_checksum.checksum_position(caches, w.layout, w.layer_numbers, w.bases, b, pos, ntok,
+                                                         w.head_begin, w.head_count) for b, pos, ntok in items]
+            single_s += time.perf_counter() - t0
+            mismatches += sum(int(gpu_out[r, k]) != v for (r, k), v in zip(sel, vals))
+            args = [(path, w.layout, s, list(w.layer_numbers), list(w.bases), items, w.head_begin, w.head_count)
+                    for s in shard]
+            t0 = time.perf_counter()
+            parts = pool.map(_layer_worker, args)
+            par_wall += time.perf_counter() - t0
+            par_busy = max(par_busy, max(dt for _, dt in parts))
+            with np.errstate(over="ignore"):
+                tot = np.zeros(len(items), dtype=np.uint64)
+                for pv, _ in parts:
+                    tot += np.array(pv, dtype=np.uint64)
+            pmis += int(np.sum(tot != np.array(vals, dtype=np.uint64)))
+            for r, k in sel:
+                pos = int(w.req.start_pos[r]) + k
+                nbytes += min(w.req.block_size, max(0, int(w.req.num_tokens[r]) - pos * w.req.block_size)) * row
+            done += len(sel)
+            del caches
+        del host
+    finally:
+        if pool is not None:
+            pool.terminate()
+            pool.join()
+        if os.path.exists(path):
+            os.unlink(path)
+    res = {"value": nbytes / single_s / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": f"{done} random listed positions of the same workload ({nbytes} valid bytes, all layers and "
-                     f"heads), numpy single-threaded, {elapsed:.1f} s of oracle time; host copies excluded"}
-    if gpu_out is not None:
-        # the same positions of the timed GPU steps, compared bit for bit
-        res["gpu_checked_positions"] = done
-        res["gpu_mismatches"] = mismatches
+                     f"heads), in chunks of {chunk}; numpy in one process, {single_s:.1f} s of oracle time; host "
+                     f"copies excluded",
+           "gpu_checked_positions": done, "gpu_mismatches": mismatches}
+    res["parallel"] = {
+        "value": nbytes / par_wall / 1e9, "unit": "GB/s", "cores": len(shard), "kind": "oracle",
+        "sample": f"the same {done} positions and bytes, each chunk split over {len(shard)} processes by layer "
+                  f"(layers {shard[0][0]}-{shard[0][-1]} in the first, ...): {par_wall:.2f} s of wall time around "
+                  f"the processes, dispatch included",
+        "split": "layer subsets (a PP-style partition); partials added mod 2^64",
+        "positions_compared": done, "partial_sum_mismatches": pmis}
     return res
 
 
-def _oracle_worker(args):
-    """One process of the parallel CPU baseline: the oracle on host pools of
-    the workload's shapes (random bits), full blocks at random positions, for
-    about ``seconds``.  Uses numpy only; never touches the GPU."""
-    seed, seconds, layout, nb, bs, nh, d, elem, layers, bases, head_begin, head_count = args
-    import numpy as np
-    import oracle
-    from paged_kv_cache_kvck_amd import workloads as wl
-    rng = np.random.default_rng(seed)
-    pools = [wl.host_random_bits(rng, wl.pool_shape(layout, nb, bs, nh, d), elem) for _ in layers]
-    n = nh - head_begin if head_count is None else head_count
-    per_block = bs * n * 2 * d * wl.ELEM_BYTES[elem] * len(layers)
-    done, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < seconds:
-        b, pos = int(rng.integers(0, nb)), int(rng.integers(0, 512))
-        oracle.kv_checksum.checksum_position(pools, layout, layers, bases, b, pos, (pos + 1) * bs, head_begin,
-                                             head_count)
-        done += 1
-    return done * per_block, time.perf_counter() - t0
+# ----------------------------------------------------------------- configuration rows
+
+CONFIG_NAMES = ("gpt2_nhd_bs16", "gpt2_nhd_bs64", "gpt2_hnd_bs16", "fp8_nhd_bs16", "fp8_nhd_bs64", "mla_bs64",
+                "mla_bs16", "hybrid_attn", "hybrid_mamba")
 
 
-def cpu_baseline_parallel(w, seconds, workers):
-    """The oracle in ``workers`` fresh processes at once (spawned: numpy only),
-    each on its own host pools of the workload's shapes: aggregate GB/s."""
-    import multiprocessing as mp
-    args = [(1000 + i, seconds, w.layout, 64, w.req.block_size, w.num_heads, w.head_size, w.elem,
-             list(w.layer_numbers), list(w.bases), w.head_begin, w.head_count) for i in range(workers)]
-    pool = mp.get_context("spawn").Pool(workers)
+def _timed_main_pass(call, calls):
+    """Median and minimum main-pass milliseconds over ``calls`` calls (after
+    two untimed ones), each read from the library's own HIP events."""
+    import torch
+    import paged_kv_cache_kvck_amd as kvck
+    kvck.kvck_instrument(True)
     try:
-        # bounded: workers that cannot start (no importable main module) would be respawned forever
-        res = pool.map_async(_oracle_worker, args).get(timeout=seconds + 120)
-    except Exception as e:  # timeout or a worker error: no parallel figure
-        print(f"[bench] parallel cpu baseline skipped: {e!r}", file=sys.stderr, flush=True)
-        return None
+        call()
+        call()
+        torch.cuda.synchronize()
+        kvck.kvck_instrument_read()
+        ts = []
+        for _ in range(calls):
+            call()
+            torch.cuda.synchronize()
+            ms, c = kvck.kvck_instrument_read()
+            ts.append(ms / max(c, 1))
     finally:
-        pool.terminate()
-        pool.join()
-    nbytes = sum(r[0] for r in res)
-    wall = max(r[1] for r in res)
-    return {"value": nbytes / wall / 1e9, "unit": "GB/s", "cores": workers,
-            "sample": f"{workers} processes x {seconds:.0f} s, each the oracle on its own host pools of the "
-                      f"workload's shapes (64 blocks per layer, random bits), full blocks at random positions"}
+        kvck.kvck_instrument(False)
+    return statistics.median(ts), min(ts)
 
+
+def _row(name, desc, valid, med, mn, checked, mism):
+    gbs = valid / (med * 1e-3) / 1e9
+    return {"config": name, "workload": desc, "valid_bytes": valid, "main_pass_ms": med, "main_pass_ms_min": mn,
+            "GB_per_s": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "oracle_checked_positions": checked,
+            "oracle_mismatches": mism}
+
+
+def _blocks_row(dev, name, desc, pools, layout, layers, req, valid, calls, n_check, seed, bases=None, head_begin=0,
+                head_count=None):
+    import numpy as np
+    import torch
+    import paged_kv_cache_kvck_amd as kvck
+    bt, nb, sp, nt = (torch.from_numpy(x).to(dev) for x in
+                      (req.block_table, req.num_blocks, req.start_pos, req.num_tokens))
+    out = torch.zeros((req.num_reqs, req.max_blocks), dtype=torch.uint64, device=dev)
+    ws = torch.empty(kvck.kvck_blocks_workspace_bytes(len(pools), req.num_reqs, req.max_blocks), dtype=torch.uint8,
+                     device=dev)
+    bases = [head_begin] * len(pools) if bases is None else list(bases)
+    pc = kvck.prepare_caches(pools, layout, layers, global_head_base=bases, head_begin=head_begin,
+                             head_count=head_count)
+    med, mn = _timed_main_pass(lambda: kvck.kvck_checksum_blocks(pc, None, None, bt, nb, sp, nt, out=out,
+                                                                 workspace=ws), calls)
+    got = out.cpu().numpy().view(np.uint64)
+    checked, mism = (0, 0)
+    if n_check:
+        checked, mism = oracle_check(pools, layout, layers, bases, req, got, sample_positions(req, n_check, seed),
+                                     head_begin, head_count)
+    row = _row(name, desc, valid, med, mn, checked, mism)
+    print(f"[config] {name:14s} {valid / 1e9:7.2f} GB {med:8.3f} ms {row['GB_per_s']:8.1f} GB/s "
+          f"{row['frac_of_hbm_peak'] * 100:5.1f} %  oracle {checked} positions, {mism} mismatches",
+          file=sys.stderr, flush=True)
+    return row
+
+
+def config_row(name, dev, calls=10, n_check=200):
+    """Build one configuration's pools on the device, time its main pass and
+    check sampled positions against the oracle; frees the pools on return."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_kvck_amd as kvck
+    from paged_kv_cache_kvck_amd import workloads as wl
+
+    def repaged(src_pools, layout, req, block_size, seed, shape_fn, dtype):
+        r2, n2 = wl.page_requests(np.random.default_rng(seed), req.num_tokens, block_size, spare_frac=0.05)
+        dst = [torch.zeros(shape_fn(n2), dtype=dtype, device=dev) for _ in src_pools]
+        for s_, d_ in zip(src_pools, dst):
+            wl.repage_torch(s_, layout, req, d_, layout, r2)
+        return dst, r2
+
+    if name.startswith("gpt2"):
+        g = wl.gpt2()
+        p = g.device_pools()
+        desc = ("gpt2-shaped paged KV cache: 12 layers x 12 KV heads x head 64 fp16 random bits, 64 requests of "
+                "128-2048 tokens (69,569 tokens); ")
+        if name == "gpt2_nhd_bs16":
+            return _blocks_row(dev, name, desc + "NHD pool (2,18545,16,12,64) per layer, block 16", p, "NHD",
+                               g.layer_numbers, g.req, g.valid_bytes(), calls, n_check, 11)
+        if name == "gpt2_nhd_bs64":
+            p64, r64 = repaged(p, "NHD", g.req, 64, 40, lambda n: wl.pool_shape("NHD", n, 64, 12, 64), p[0].dtype)
+            del p
+            return _blocks_row(dev, name, desc + "the same tokens re-paged at block 64, NHD", p64, "NHD",
+                               g.layer_numbers, r64, g.valid_bytes(), calls, n_check, 12)
+        if name == "gpt2_hnd_bs16":
+            ph = [x.permute(0, 1, 3, 2, 4).contiguous() for x in p]
+            del p
+            return _blocks_row(dev, name, desc + "the same pool permuted to HND, block 16", ph, "HND",
+                               g.layer_numbers, g.req, g.valid_bytes(), calls, n_check, 13)
+    if name.startswith("fp8"):
+        f = wl.gpt2(seed=41, elem="fp8")
+        f16 = f.device_pools()
+        desc = ("fp8 KV bits (P = head/4): 12 layers x 12 KV heads x head 64 (64-byte rows), NHD, the gpt2-shaped "
+                "request lengths; ")
+        if name == "fp8_nhd_bs16":
+            return _blocks_row(dev, name, desc + "block 16", f16, "NHD", f.layer_numbers, f.req, f.valid_bytes(),
+                               calls, n_check, 14)
+        if name == "fp8_nhd_bs64":
+            f64, r64 = repaged(f16, "NHD", f.req, 64, 42, lambda n: wl.pool_shape("NHD", n, 64, 12, 64), torch.uint8)
+            del f16
+            return _blocks_row(dev, name, desc + "re-paged at block 64", f64, "NHD", f.layer_numbers, r64,
+                               f.valid_bytes(), calls, n_check, 15)
+    if name.startswith("mla"):
+        m = wl.mla()
+        m64 = m.device_pools()
+        desc = "MLA-style latent cache: 61 layers x 1 head of 576 bf16 bits, 64 requests of 128-2048 tokens; "
+        if name == "mla_bs64":
+            return _blocks_row(dev, name, desc + "block 64", m64, "MLA", m.layer_numbers, m.req, m.valid_bytes(),
+                               calls, n_check, 16)
+        if name == "mla_bs16":
+            m16, r16 = repaged(m64, "MLA", m.req, 16, 43, lambda n: (n, 16, 576), m64[0].dtype)
+            del m64
+            return _blocks_row(dev, name, desc + "re-paged at block 16", m16, "MLA", m.layer_numbers, r16,
+                               m.valid_bytes(), calls, n_check, 17)
+    if name == "hybrid_attn":
+        attn, _ = wl.hybrid()
+        pa = attn.device_pools()
+        return _blocks_row(dev, name, "hybrid model attention group: 24 layers (numbers 0,2,..,46) x 8 KV heads x "
+                                      "head 128 bf16, block 16, HND, 128 requests of 512-8192 tokens", pa,
+                           attn.layout, attn.layer_numbers, attn.req, attn.valid_bytes(), calls, n_check, 18)
+    if name == "hybrid_mamba":
+        import oracle
+        _, mamba = wl.hybrid()
+        states = mamba.device_states()
+        sid = torch.from_numpy(mamba.slot_ids).to(dev)
+        sout = torch.zeros(len(mamba.slot_ids), dtype=torch.uint64, device=dev)
+        sws = torch.empty(max(256, kvck.kvck_states_workspace_bytes(len(mamba.layer_numbers), mamba.rows_used,
+                                                                    len(mamba.slot_ids))), dtype=torch.uint8,
+                          device=dev)
+        med, mn = _timed_main_pass(lambda: kvck.kvck_checksum_states(states, mamba.layer_numbers, sid, out=sout,
+                                                                     workspace=sws), calls)
+        got = sout.cpu().numpy().view(np.uint64)
+        # every request (its position 0), from host copies of its slot in every state
+        mism = 0
+        R = len(mamba.slot_ids)
+        for r0 in range(0, R, 32):
+            rs = list(range(r0, min(R, r0 + 32)))
+            idx = torch.from_numpy(mamba.slot_ids[rs].astype(np.int64)).to(dev)
+            host = [[_host_bits(s.index_select(0, idx)) for s in lay] for lay in states]
+            want = oracle.checksum_states(host, mamba.layer_numbers, mamba.bases, np.arange(len(rs)))
+            mism += int(np.sum(got[rs] != want))
+        row = _row(name, "hybrid model Mamba group: 24 layers (numbers 1,3,..,47) x 128 requests x 64 rows of fp32 "
+                         "SSM [128x16] + fp16 conv [4x256] state, position 0", mamba.valid_bytes(), med, mn, R, mism)
+        print(f"[config] {name:14s} {row['valid_bytes'] / 1e9:7.2f} GB {med:8.3f} ms {row['GB_per_s']:8.1f} GB/s "
+              f"{row['frac_of_hbm_peak'] * 100:5.1f} %  oracle {R} requests, {mism} mismatches",
+              file=sys.stderr, flush=True)
+        return row
+    raise SystemExit(f"unknown configuration {name!r}; one of {CONFIG_NAMES}")
+
+
+def config_rows(names, dev, calls=10, n_check=200):
+    import torch
+    rows = []
+    for n in names:
+        rows.append(config_row(n, dev, calls, n_check))
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return rows
+
+
+def copy_calibration(dev, gib):
+    """One plain device copy of ``gib`` GiB (the runtime's copy kernel): the
+    reference that rocprofv3 counter runs scale FETCH_SIZE / WRITE_SIZE by."""
+    import torch
+    n = int(gib * (1 << 30))
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    return n
+
+
+# ----------------------------------------------------------------- main
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -159,15 +421,16 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--cpu-workers", type=int, default=0,
-                    help="processes of the parallel CPU baseline (0: the host's CPUs, at most 16)")
-    ap.add_argument("--cpu-parallel-seconds", type=float, default=5.0)
+                    help="processes of the parallel oracle leg (0: the host's CPUs, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-shard", action="store_true", help="skip the TP-shard timing")
-    ap.add_argument("--no-states", action="store_true", help="skip the Mamba-state timing")
+    ap.add_argument("--no-shard", action="store_true", help="skip the TP-shard row")
     ap.add_argument("--no-copy", action="store_true", help="skip the fused copy + checksum timing")
     ap.add_argument("--no-small", action="store_true", help="skip the tiny-call latency timing")
-    ap.add_argument("--survey", action="store_true",
-                    help="after the headline, time the main pass of every other configuration (extra.survey)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other configurations' rows")
+    ap.add_argument("--only", default="", help="comma-separated configuration rows to run alone (no headline)")
+    ap.add_argument("--config-calls", type=int, default=10, help="timed calls per configuration row")
+    ap.add_argument("--oracle-positions", type=int, default=200,
+                    help="random positions per configuration checked against the oracle (plus every tail)")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
                     help="after timing, run one plain device copy of this many GiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -181,6 +444,15 @@ def main(argv=None):
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if args.only:
+        names = [n for n in args.only.split(",") if n]
+        rows = config_rows(names, dev, args.config_calls, args.oracle_positions)
+        res = {"configs": rows}
+        if args.copy_calibration_gib > 0:
+            res["copy_calibration_bytes"] = copy_calibration(dev, args.copy_calibration_gib)
+        print(json.dumps(res), flush=True)
+        return 0
+
     w, desc = make_workload(args.workload)
     print(f"[bench] building {args.workload}: pools {w.shape} x {w.num_layers}", file=sys.stderr, flush=True)
     pools = w.device_pools()
@@ -195,12 +467,12 @@ def main(argv=None):
     stream = torch.cuda.current_stream(dev)
     prepared = {}
 
-    def step(head_begin=w.head_begin, head_count=w.head_count, bases=None):
+    def step(head_begin=w.head_begin, head_count=w.head_count, bases=None, o=out):
         key = (head_begin, head_count, None if bases is None else tuple(bases))
         if key not in prepared:
             prepared[key] = kvck.prepare_caches(pools, w.layout, w.layer_numbers, global_head_base=bases,
                                                 head_begin=head_begin, head_count=head_count)
-        kvck.kvck_checksum_blocks(prepared[key], None, None, bt, nb, sp, nt, out=out, workspace=ws, stream=stream)
+        kvck.kvck_checksum_blocks(prepared[key], None, None, bt, nb, sp, nt, out=o, workspace=ws, stream=stream)
 
     valid = w.valid_bytes()
     kvck.kvck_instrument(True)
@@ -231,44 +503,56 @@ def main(argv=None):
              "step_ms_median": statistics.median(per_step), "step_ms_min": min(per_step),
              "listed_positions": int(req.num_blocks.sum()),
              "metadata_bytes_per_step": int(req.num_blocks.sum()) * (4 + 8 + 32) + req.num_reqs * 20}
-    if not args.no_shard and w.layout == "HND" and w.num_heads == 8:
-        # TP = 4 shard over heads {2, 3}, global numbering from 2
+    configs = []
+    if not args.no_shard:
+        # TP = 4 shard over heads {2, 3}, global numbering from 2: every step
+        # timed with the headline's instrumentation, then sampled positions of
+        # the last step checked against the oracle
         shard_bytes = valid // 4
+        sbases = [2] * w.num_layers
+        sout = torch.zeros_like(out)
         for _ in range(2):
-            step(2, 2, [2] * w.num_layers)
+            step(2, 2, sbases, sout)
         torch.cuda.synchronize()
         kvck.kvck_instrument_read()
         e0.record(stream)
         for _ in range(args.steps):
-            step(2, 2, [2] * w.num_layers)
+            step(2, 2, sbases, sout)
         e1.record(stream)
         torch.cuda.synchronize()
         sms = e0.elapsed_time(e1) / args.steps
         smain, sc = kvck.kvck_instrument_read()
-        extra["tp4_shard_heads_2_3"] = {"valid_bytes": shard_bytes, "ms_per_step": sms,
-                                        "GB_per_s": shard_bytes / (sms * 1e-3) / 1e9,
-                                        "main_pass_ms": smain / max(sc, 1),
-                                        "main_pass_GB_per_s": shard_bytes / (smain / max(sc, 1) * 1e-3) / 1e9}
+        got = sout.cpu().numpy().view("uint64")
+        checked, mism = oracle_check(pools, w.layout, w.layer_numbers, sbases, req, got,
+                                     sample_positions(req, args.oracle_positions, 10), 2, 2)
+        row = _row("llama3_8b_tp4_shard", "the headline pools, TP = 4 shard: local heads {2,3} with global numbering "
+                   "from 2", shard_bytes, smain / max(sc, 1), smain / max(sc, 1), checked, mism)
+        row["ms_per_step"] = sms
+        row["step_GB_per_s"] = shard_bytes / (sms * 1e-3) / 1e9
+        configs.append(row)
+        print(f"[config] shard: {row['main_pass_ms']:.3f} ms {row['frac_of_hbm_peak'] * 100:.1f} %, oracle "
+              f"{checked} positions, {mism} mismatches", file=sys.stderr, flush=True)
+        del sout
     # offloaded-checksum check of every listed position: tag, compare, count
     hashes = torch.randint(0, 256, (req.num_reqs * req.max_blocks, 32), dtype=torch.uint8, device=dev)
     stored, _ = kvck.kvck_tag_checksums(out.view(-1), hashes, 0x1234, num_blocks_per_req=nb, stream=stream)
-    mism = torch.zeros(req.num_reqs * req.max_blocks, dtype=torch.uint8, device=dev)
+    mism_t = torch.zeros(req.num_reqs * req.max_blocks, dtype=torch.uint8, device=dev)
     cnt = torch.zeros(1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
         kvck.kvck_tag_checksums(out.view(-1), hashes, 0x1234, num_blocks_per_req=nb, tagged=False, stored=stored,
-                                mismatch=mism, mismatch_count=cnt, stream=stream)
+                                mismatch=mism_t, mismatch_count=cnt, stream=stream)
     e1.record(stream)
     torch.cuda.synchronize()
-    extra["offload_check"] = {"positions": int(req.num_blocks.sum()), "us_per_call": e0.elapsed_time(e1) / args.steps * 1e3,
-                              "mismatches": int(cnt.item())}
-    del hashes, stored, mism
+    extra["offload_check"] = {"positions": int(req.num_blocks.sum()),
+                              "us_per_call": e0.elapsed_time(e1) / args.steps * 1e3, "mismatches": int(cnt.item())}
+    del hashes, stored, mism_t
 
-    if not args.no_copy and w.layout == "HND":
+    if not args.no_copy:
         # connector save / load fused with the checksum, on the first half of the requests
         half = req.num_reqs // 2
-        hb_t, hn_t, hs_t, ht_t = bt[:half].contiguous(), nb[:half].contiguous(), sp[:half].contiguous(), nt[:half].contiguous()
+        hb_t, hn_t, hs_t, ht_t = (x[:half].contiguous() for x in (bt, nb, sp, nt))
         entries = int(req.num_blocks[:half].sum())
         per = kvck.kvck_staging_bytes(pools[0], w.layout, w.num_layers)
         staging = torch.empty(entries * per, dtype=torch.uint8, device=dev)
@@ -282,6 +566,7 @@ def main(argv=None):
             moved += max(0, hi - lo)
         moved *= w.num_layers * w.heads_used * w.planes * w.head_size * 2
         res = {"valid_bytes": moved, "bytes_moved": 2 * moved}
+        ncalls = max(2, args.steps // 4)
         for name, direction in (("save", kvck.KVCK_COPY_SAVE), ("load", kvck.KVCK_COPY_LOAD)):
             def cstep():
                 kvck.kvck_copy_checksum_blocks(direction, pools, w.layout, w.layer_numbers, hb_t, hn_t, hs_t, ht_t,
@@ -290,51 +575,40 @@ def main(argv=None):
             torch.cuda.synchronize()
             kvck.kvck_instrument_read()
             e0.record(stream)
-            for _ in range(max(2, args.steps // 4)):
+            for _ in range(ncalls):
                 cstep()
             e1.record(stream)
             torch.cuda.synchronize()
-            cms = e0.elapsed_time(e1) / max(2, args.steps // 4)
+            cms = e0.elapsed_time(e1) / ncalls
             cmain, cc = kvck.kvck_instrument_read()
             cmain /= max(cc, 1)
             res[name] = {"ms_per_call": cms, "main_pass_ms": cmain,
                          "read_plus_write_GB_per_s": 2 * moved / (cmain * 1e-3) / 1e9,
                          "frac_of_hbm_peak": 2 * moved / (cmain * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        # the load wrote back what the save read: the pool is unchanged, and so are its checksums
+        got = cout.cpu().numpy().view("uint64")
+        res["load_checksums_equal_timed_steps"] = bool(all(int(got[r, k]) == int(out_main[r, k])
+                                                           for r in range(half)
+                                                           for k in range(int(req.num_blocks[r]))))
         extra["fused_copy_half_batch"] = res
         del staging
-
-    if not args.no_states:
-        # Mamba running-state rows: the hybrid workload's 24 Mamba layers
-        from paged_kv_cache_kvck_amd import workloads as wl
-        mamba = wl.hybrid()[1]
-        states = mamba.device_states()
-        sid = torch.from_numpy(mamba.slot_ids).to(dev)
-        sout = torch.zeros(len(mamba.slot_ids), dtype=torch.uint64, device=dev)
-        sws = torch.empty(max(256, kvck.kvck_states_workspace_bytes(len(mamba.layer_numbers), mamba.rows_used,
-                                                                    len(mamba.slot_ids))), dtype=torch.uint8,
-                          device=dev)
-
-        def sstep():
-            kvck.kvck_checksum_states(states, mamba.layer_numbers, sid, out=sout, workspace=sws, stream=stream)
-
-        for _ in range(2):
-            sstep()
-        torch.cuda.synchronize()
-        kvck.kvck_instrument_read()
-        e0.record(stream)
-        for _ in range(args.steps):
-            sstep()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        sms = e0.elapsed_time(e1) / args.steps
-        smain, sc = kvck.kvck_instrument_read()
-        sb = mamba.valid_bytes()
-        extra["mamba_states"] = {"workload": "24 Mamba layers x 128 requests x 64 rows of fp32 SSM [128x16] + fp16 "
-                                             "conv [4x256] state", "valid_bytes": sb, "ms_per_step": sms,
-                                 "GB_per_s": sb / (sms * 1e-3) / 1e9, "main_pass_ms": smain / max(sc, 1),
-                                 "main_pass_GB_per_s": sb / (smain / max(sc, 1) * 1e-3) / 1e9}
-        del states
     kvck.kvck_instrument(False)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        workers = args.cpu_workers or min(16, os.cpu_count() or 1)
+        print(f"[bench] cpu baseline (oracle): one process, then {workers} over layer subsets", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(pools, w, args.cpu_seconds, out_main, workers)
+        cpu["host_cpu"] = _cpu_model()
+    del pools, prepared
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    if not args.no_configs:
+        configs += config_rows(CONFIG_NAMES, dev, args.config_calls, args.oracle_positions)
+    if configs:
+        extra["configs"] = configs
     if not args.no_small:
         # the tiny configuration (one 50-token request on 4 blocks, 2 layers x 2 heads): latency-bound,
         # so each call is timed on its own, event to event, with caches prepared as a hot loop would
@@ -356,35 +630,15 @@ def main(argv=None):
             torch.cuda.synchronize()
             if i >= 10:
                 lat.append(t0.elapsed_time(t1) * 1e3)
+        got = tout.cpu().numpy().view("uint64")
+        checked, mism = oracle_check(tpools, tw.layout, tw.layer_numbers, tw.bases, tr, got, tr.listed())
         extra["tiny_call_latency"] = {"workload": "2 layers x 2 KV heads x head 64 bf16, block 16, NHD, one 50-token "
                                                   "request on 4 blocks (51,200 valid bytes)",
-                                      "us_median": statistics.median(lat), "us_min": min(lat), "calls": len(lat)}
+                                      "us_median": statistics.median(lat), "us_min": min(lat), "calls": len(lat),
+                                      "oracle_checked_positions": checked, "oracle_mismatches": mism}
         del tpools, tpc
     if args.copy_calibration_gib > 0:
-        n = int(args.copy_calibration_gib * (1 << 30))
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b = torch.empty(n, dtype=torch.uint8, device=dev)
-        a.fill_(1)
-        torch.cuda.synchronize()
-        b.copy_(a)
-        torch.cuda.synchronize()
-        extra["copy_calibration_bytes"] = n
-        del a, b
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(pools, w, args.cpu_seconds, gpu_out=out_main)
-        cpu["host_cpu"] = _cpu_model()
-        workers = args.cpu_workers or min(16, os.cpu_count() or 1)
-        print(f"[bench] cpu baseline, {workers} processes", file=sys.stderr, flush=True)
-        cpu["parallel"] = cpu_baseline_parallel(w, args.cpu_parallel_seconds, workers)
-
-    if args.survey:
-        del pools
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
-        extra["survey"] = config_survey(dev)
+        extra["copy_calibration_bytes"] = copy_calibration(dev, args.copy_calibration_gib)
 
     line = {
         "metric": "checksummed KV GB/s and % of MI355X HBM peak; bit-exact vs CPU oracle",
@@ -409,108 +663,6 @@ def main(argv=None):
     }
     print(json.dumps(line), flush=True)
     return 0
-
-
-def config_survey(dev, calls=10):
-    """Main-pass time of each other configuration (median of `calls` calls,
-    HIP events around the main pass), one after another in this process: the
-    GPT-2-shaped pool and its re-pagings (block 64, HND, fp8 bits at blocks 16
-    and 64), the 61-layer MLA latent at blocks 64 and 16, and the hybrid
-    model's attention group and Mamba states.  Rows are printed to stderr as
-    they finish."""
-    import numpy as np
-    import torch
-    import paged_kv_cache_kvck_amd as kvck
-    from paged_kv_cache_kvck_amd import workloads as wl
-
-    rows = []
-
-    def timed(call):
-        kvck.kvck_instrument(True)
-        call()
-        call()
-        torch.cuda.synchronize()
-        kvck.kvck_instrument_read()
-        ts = []
-        for _ in range(calls):
-            call()
-            torch.cuda.synchronize()
-            ms, c = kvck.kvck_instrument_read()
-            ts.append(ms / c)
-        kvck.kvck_instrument(False)
-        return statistics.median(ts)
-
-    def report(name, valid, ms):
-        gbs = valid / (ms * 1e-3) / 1e9
-        rows.append({"config": name, "valid_bytes": valid, "main_pass_ms": ms, "GB_per_s": gbs,
-                     "pct_of_hbm_peak": gbs / HBM_PEAK_GBS * 100})
-        print(f"[survey] {name:52s} {valid / 1e9:7.2f} GB {ms:8.3f} ms {gbs:8.1f} GB/s "
-              f"{gbs / HBM_PEAK_GBS * 100:5.1f} %", file=sys.stderr, flush=True)
-
-    def blocks(name, pools, layout, layers, req, valid):
-        bt, nb, sp, nt = (torch.from_numpy(x).to(dev) for x in
-                          (req.block_table, req.num_blocks, req.start_pos, req.num_tokens))
-        out = torch.zeros((req.num_reqs, req.max_blocks), dtype=torch.uint64, device=dev)
-        ws = torch.empty(kvck.kvck_blocks_workspace_bytes(len(pools), req.num_reqs, req.max_blocks),
-                         dtype=torch.uint8, device=dev)
-        pc = kvck.prepare_caches(pools, layout, layers)
-        report(name, valid, timed(lambda: kvck.kvck_checksum_blocks(pc, None, None, bt, nb, sp, nt, out=out,
-                                                                    workspace=ws)))
-
-    def free():
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
-
-    g = wl.gpt2()
-    p = g.device_pools()
-    blocks("gpt2 NHD fp16, block 16", p, "NHD", g.layer_numbers, g.req, g.valid_bytes())
-    r64, n64 = wl.page_requests(np.random.default_rng(40), g.req.num_tokens, 64, spare_frac=0.05)
-    p64 = [torch.zeros(wl.pool_shape("NHD", n64, 64, 12, 64), dtype=p[0].dtype, device=dev) for _ in p]
-    for s_, d_ in zip(p, p64):
-        wl.repage_torch(s_, "NHD", g.req, d_, "NHD", r64)
-    blocks("gpt2 tokens re-paged at block 64 (NHD)", p64, "NHD", g.layer_numbers, r64, g.valid_bytes())
-    del p64
-    free()
-    ph = [x.permute(0, 1, 3, 2, 4).contiguous() for x in p]
-    blocks("gpt2 pool as HND, block 16", ph, "HND", g.layer_numbers, g.req, g.valid_bytes())
-    del ph, p
-    free()
-    f = wl.gpt2(seed=41, elem="fp8")
-    f16 = f.device_pools()
-    blocks("fp8 bits 12 x 64 (64-byte rows) NHD, block 16", f16, "NHD", f.layer_numbers, f.req, f.valid_bytes())
-    rf64, nf64 = wl.page_requests(np.random.default_rng(42), f.req.num_tokens, 64, spare_frac=0.05)
-    f64 = [torch.zeros(wl.pool_shape("NHD", nf64, 64, 12, 64), dtype=torch.uint8, device=dev) for _ in f16]
-    for s_, d_ in zip(f16, f64):
-        wl.repage_torch(s_, "NHD", f.req, d_, "NHD", rf64)
-    blocks("fp8 bits NHD, block 64", f64, "NHD", f.layer_numbers, rf64, f.valid_bytes())
-    del f16, f64
-    free()
-    m = wl.mla()
-    m64 = m.device_pools()
-    blocks("MLA 61 x 576 bf16, block 64", m64, "MLA", m.layer_numbers, m.req, m.valid_bytes())
-    rm16, nm16 = wl.page_requests(np.random.default_rng(43), m.req.num_tokens, 16, spare_frac=0.05)
-    m16 = [torch.zeros((nm16, 16, 576), dtype=m64[0].dtype, device=dev) for _ in m64]
-    for s_, d_ in zip(m64, m16):
-        wl.repage_torch(s_, "MLA", m.req, d_, "MLA", rm16)
-    blocks("MLA, block 16", m16, "MLA", m.layer_numbers, rm16, m.valid_bytes())
-    del m64, m16
-    free()
-    attn, mamba = wl.hybrid()
-    pa = attn.device_pools()
-    blocks("hybrid attention group (24 x 8 x 128 bf16 HND)", pa, attn.layout, attn.layer_numbers, attn.req,
-           attn.valid_bytes())
-    del pa
-    free()
-    states = mamba.device_states()
-    sid = torch.from_numpy(mamba.slot_ids).to(dev)
-    sout = torch.zeros(len(mamba.slot_ids), dtype=torch.uint64, device=dev)
-    sws = torch.empty(max(256, kvck.kvck_states_workspace_bytes(len(mamba.layer_numbers), mamba.rows_used,
-                                                                len(mamba.slot_ids))), dtype=torch.uint8, device=dev)
-    report("hybrid Mamba states (24 layers x 128 requests)", mamba.valid_bytes(),
-           timed(lambda: kvck.kvck_checksum_states(states, mamba.layer_numbers, sid, out=sout, workspace=sws)))
-    del states
-    free()
-    return rows
 
 
 def _cpu_model():
