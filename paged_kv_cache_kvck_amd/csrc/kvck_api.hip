@@ -167,6 +167,15 @@ void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_ca
   const bool fits = cand != nullptr && (shp->merged || fills(cand->slots));
   const bool one_task = dense && !copy && cand != nullptr && num_caches <= lpt;
   bool pipe = (fits && num_caches > 1 && tasks >= kPipeMinTasksPerWave * waves) || one_task;
+  if (!copy && !dense && shp->merged) {
+    // The planned pipelined checksum of merged rows streams its units across
+    // task boundaries (no drain between tasks), so a task may be as small as
+    // one cache: halve the caches per task until every resident wave has
+    // kPipeMinTasksPerWave tasks to balance the load, and pipeline whenever
+    // the shape allows.
+    while (lpt > 1 && max_items * ((num_caches + lpt - 1) / lpt) < kPipeMinTasksPerWave * waves) lpt /= 2;
+    pipe = fits;
+  }
   // KVCK_SCHEDULE=pipelined|simple overrides the choice (results are identical
   // either way)
   if (const char* force = getenv("KVCK_SCHEDULE")) {

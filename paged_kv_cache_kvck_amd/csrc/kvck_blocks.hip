@@ -177,7 +177,8 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
 //
 // PIPE = false: each unit's loads are issued, then consumed.
 // PIPE = true:  two unit buffers in ping-pong, so the loads of unit i+1 are in
-//               flight while unit i is consumed, across the caches of a task.
+//               flight while unit i is consumed, across the caches of a task
+//               (for planned merged rows also across the wave's tasks).
 // MERGED:       pools whose heads sit side by side in a slot (NHD-like): a
 //               lane-table row is the slot's whole run of heads, so a load
 //               instruction covers contiguous bytes even when one head's row
@@ -185,6 +186,57 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
 // DENSE:        a call planned in place: tasks index every (request, block
 //               slot) and each wave runs exactly one task (the grid covers them
 //               all), so no request pointer stays live across the unit loop.
+// Weighted sum of one unit's chunks: x[p][h][s] is chunk s (lane-table entry)
+// of plane step p and head h0 + h of a row group whose first piece term is
+// up0 (2(t*P + plane piece offset) + 1 for the group's first token t);
+// chunk pieces xa, xb contribute m((xa + xb)u + 2xb) with u = up0 + urel[s].
+template <int CHUNK, int S, int HU, int PU, bool MERGED>
+__device__ __forceinline__ uint64_t unit_sum(const typename ChunkType<CHUNK>::T (&x)[PU][HU][S],
+                                             const LaneTable<S>& lt, const uint32_t (&lhead)[S], uint64_t up0,
+                                             uint64_t plane_term, uint64_t mb, int h0) {
+  uint64_t acc = 0;
+#pragma unroll
+  for (int p = 0; p < PU; ++p) {
+    const uint64_t up = up0 + (uint64_t)p * plane_term;
+#pragma unroll
+    for (int h = 0; h < HU; ++h) {
+      // sh: sum of the unit's terms; sl (merged rows): the same weighted by
+      // each chunk's local head, so that sum_s t_s (mb + 2 head_s) costs one
+      // 64-bit multiply per unit: mb * sh + 2 sl
+      uint64_t sh = 0, sl = 0;
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const uint64_t u = up + lt.urel[s];
+        const uint64_t xa = (uint64_t)x[p][h][s].x | ((uint64_t)x[p][h][s].y << 32);
+        uint64_t t;
+        if constexpr (CHUNK == 16) {
+          const uint64_t xb = (uint64_t)x[p][h][s].z | ((uint64_t)x[p][h][s].w << 32);
+          t = (xa + xb) * u + (xb << 1);
+        } else {
+          t = xa * u;
+        }
+        sh += t;
+        if constexpr (MERGED) sl += t * (uint64_t)lhead[s];
+      }
+      if constexpr (MERGED)
+        acc += sh * mb + (sl << 1);
+      else
+        acc += sh * (mb + 2ull * (uint64_t)(h0 + h));
+    }
+  }
+  return acc;
+}
+
+// What the consuming side needs of an issued unit (all uniform).
+struct UnitDesc {
+  uint64_t t0;       // first token of the unit's block
+  int64_t out_idx;   // the task's output entry (direct writes)
+  int64_t task;      // the task (its group and listed position)
+  int cache, group, plane, hbatch;
+  bool live;         // a real unit (else every load was out of range)
+  bool last;         // the task's last unit: reduce and write after it
+};
+
 template <int CHUNK, int S, int HU, int PU, bool PIPE, bool MERGED, bool DENSE>
 __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs a) {
   using V = typename ChunkType<CHUNK>::T;
@@ -205,6 +257,125 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
   const int rg = a.rows_per_group;
   const uint64_t plane_term = 2ull * (P / (uint64_t)a.planes_total);
   const int nhb = (a.heads + HU - 1) / HU;
+
+  if constexpr (PIPE && !DENSE && MERGED) {
+    // Planned, pipelined, merged rows: the wave's tasks (wave, wave + nwaves,
+    // ...) form one stream of units.  The issue side runs one unit ahead of
+    // the consuming side -- also into the next task -- so both unit buffers
+    // stay in flight across task boundaries: a task's reduction, its write and
+    // the next task's record are taken while the other buffer's loads are
+    // under way.  Merged rows (short rows, single latent heads) have few units
+    // per task and gain from it (same-box A/B: fp8 64-byte rows +0.8-0.9
+    // points of 8 TB/s, MLA +0.4-0.8); pools of separate head rows, whose
+    // tasks are long, ran 0.1-1.1 points slower with it and keep one task at
+    // a time.
+    const int nplanes = a.planes / PU;  // plane steps per row group (PU divides planes)
+    int64_t i_task = wave;              // task of the next unit to issue
+    int i_left = 0;                     // its units still to issue (0: read its record first)
+    int i_ngr = 1;
+    int32_t i_v = 0;
+    uint64_t i_t0 = 0;
+    int64_t i_boff = 0, i_out = 0;
+    UnitCursor ic{0, 0, 0, 0};
+    // Issue the stream's next unit into x, described by d; past the stream's
+    // end every load is out of range (zeros, no memory touched).
+    auto issue = [&](V(&x)[PU][HU][S], UnitDesc& d) {
+      if (i_left == 0 && i_task < total) {
+        const int64_t grp = i_task / n_items;
+        const TaskRecord rec = task_record<false>(a, i_task - grp * n_items, false, lane);
+        const int c_begin = (int)grp * lpt;
+        const int c_end = min(a.num_caches, c_begin + lpt);
+        i_v = rec.valid;
+        i_t0 = rec.t0;
+        i_out = rec.out_idx;
+        i_boff = (int64_t)rec.block * a.block_stride;
+        i_ngr = max(1, (i_v + rg - 1) / rg);
+        // a position with no valid slot still gets one (empty) unit, so its
+        // zero is written like any other task's result
+        i_left = i_v > 0 ? i_ngr * nplanes * nhb * (c_end - c_begin) : 1;
+        ic = UnitCursor{c_begin, 0, 0, 0};
+      }
+      const bool live = i_task < total;
+      const int rows = live ? min(rg, i_v - ic.group * rg) : 0;
+      // uniform by construction; taken through readfirstlane because the
+      // compiler cannot prove it across the stream's loop, and a descriptor
+      // it believes divergent costs a per-lane loop around every load
+      const uint8_t* base = reinterpret_cast<const uint8_t*>(
+          uniform64(reinterpret_cast<int64_t>(a.base[live ? ic.cache : 0] + i_boff +
+                                              (int64_t)(ic.group * rg) * a.slot_stride +
+                                              (int64_t)(ic.plane * PU) * a.plane_stride)));
+      uint32_t voff[S];
+#pragma unroll
+      for (int s = 0; s < S; ++s) voff[s] = lt.row[s] < rows ? lt.off[s] : kOOB;
+#pragma unroll
+      for (int p = 0; p < PU; ++p) {
+#pragma unroll
+        for (int h = 0; h < HU; ++h) {
+          const int hh = ic.hbatch * HU + h;
+          const uint32_t hmask = hh < a.heads ? 0u : kOOB;
+          const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)p * a.plane_stride + (int64_t)hh * a.head_stride);
+#pragma unroll
+          for (int s = 0; s < S; ++s) x[p][h][s] = load_chunk<CHUNK>(rs, voff[s] | hmask);
+        }
+      }
+      d.t0 = i_t0;
+      d.out_idx = i_out;
+      d.task = i_task;
+      d.cache = ic.cache;
+      d.group = ic.group;
+      d.plane = ic.plane;
+      d.hbatch = ic.hbatch;
+      d.live = live;
+      d.last = live && i_left == 1;
+      if (live) {
+        ic.next(nhb, nplanes, i_ngr);
+        if (--i_left == 0) i_task += nwaves;
+      }
+    };
+    uint64_t acc = 0;
+    // Consume a live unit; after a task's last unit, reduce and write.
+    // Returns the unit's own sum, which depends on every chunk of x.
+    auto consume = [&](const V(&x)[PU][HU][S], const UnitDesc& d) {
+      const uint64_t up0 = 2ull * (d.t0 + (uint64_t)(d.group * rg)) * P + 1ull + a.piece_base +
+                           (uint64_t)(d.plane * PU) * plane_term;
+      const uint64_t us = unit_sum<CHUNK, S, HU, PU, MERGED>(x, lt, lhead, up0, plane_term, a.mbase[d.cache],
+                                                             d.hbatch * HU);
+      acc += us;
+      if (d.last) {
+        const uint64_t tot = wave_sum(acc);
+        acc = 0;
+        if (lane == 0) {
+          if (a.direct) {
+            // the entry is this task's alone: read it with a scalar load,
+            // whose wait does not also wait for the unit loads in flight
+            uint64_t* o = a.out + d.out_idx;
+            *o = a.accumulate ? read_const(o) + tot : tot;
+          } else {
+            const int64_t grp = d.task / n_items;
+            a.partials[(int64_t)(a.group_offset + grp) * a.max_items + (d.task - grp * n_items)] = tot;
+          }
+        }
+      }
+      return us;
+    };
+    // Both buffers are issued at every step (past the stream's end with every
+    // load out of range): with no branch around an issue, the waits before
+    // consuming one buffer count the other buffer's loads as still to come
+    // and leave them in flight.  order_after keeps a buffer's next loads after
+    // the last use of its data, so each buffer keeps its registers.
+    V A[PU][HU][S], B[PU][HU][S];
+    UnitDesc da, db;
+    issue(A, da);
+    for (;;) {
+      issue(B, db);
+      if (!da.live) break;  // uniform
+      order_after(consume(A, da));
+      issue(A, da);
+      if (!db.live) break;
+      order_after(consume(B, db));
+    }
+    return;
+  }
 
   for (int64_t task = wave; task < total; task += nwaves) {
     const int64_t grp = task / n_items;
@@ -249,37 +420,9 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
         if (live) ic.next(nhb, nplanes, ngr);
       };
       auto consume = [&](const V(&x)[PU][HU][S]) {
-        const uint64_t mb = a.mbase[cc.cache];
-#pragma unroll
-        for (int p = 0; p < PU; ++p) {
-          const uint64_t up = 2ull * (t0 + (uint64_t)(cc.group * rg)) * P + 1ull + a.piece_base +
-                              (uint64_t)(cc.plane * PU + p) * plane_term;
-#pragma unroll
-          for (int h = 0; h < HU; ++h) {
-            // sh: sum of the unit's terms; sl (merged rows): the same weighted by
-            // each chunk's local head, so that sum_s t_s (mb + 2 head_s) costs one
-            // 64-bit multiply per unit: mb * sh + 2 sl
-            uint64_t sh = 0, sl = 0;
-#pragma unroll
-            for (int s = 0; s < S; ++s) {
-              const uint64_t u = up + lt.urel[s];
-              const uint64_t xa = (uint64_t)x[p][h][s].x | ((uint64_t)x[p][h][s].y << 32);
-              uint64_t t;
-              if constexpr (CHUNK == 16) {
-                const uint64_t xb = (uint64_t)x[p][h][s].z | ((uint64_t)x[p][h][s].w << 32);
-                t = (xa + xb) * u + (xb << 1);
-              } else {
-                t = xa * u;
-              }
-              sh += t;
-              if constexpr (MERGED) sl += t * (uint64_t)lhead[s];
-            }
-            if constexpr (MERGED)
-              acc += sh * mb + (sl << 1);
-            else
-              acc += sh * (mb + 2ull * (uint64_t)(cc.hbatch * HU + h));
-          }
-        }
+        const uint64_t up0 = 2ull * (t0 + (uint64_t)(cc.group * rg)) * P + 1ull + a.piece_base +
+                             (uint64_t)(cc.plane * PU) * plane_term;
+        acc += unit_sum<CHUNK, S, HU, PU, MERGED>(x, lt, lhead, up0, plane_term, a.mbase[cc.cache], cc.hbatch * HU);
         cc.next(nhb, nplanes, ngr);
       };
 
