@@ -236,15 +236,26 @@ CONFIG_NAMES = ("gpt2_nhd_bs16", "gpt2_nhd_bs64", "gpt2_hnd_bs16", "fp8_nhd_bs16
                 "mla_bs16", "hybrid_attn", "hybrid_mamba")
 
 
-def _timed_main_pass(call, calls):
-    """Median and minimum main-pass milliseconds over ``calls`` calls (after
-    two untimed ones), each read from the library's own HIP events."""
+WARMUP_MS = 100.0
+
+
+def _timed_main_pass(call, calls, warmup_ms=None):
+    """Median and minimum main-pass milliseconds over ``calls`` calls, each
+    read from the library's own HIP events, after untimed calls: two, then
+    more until about ``warmup_ms`` of them have run (the first pass over
+    freshly written pools reads several points slower than later ones)."""
     import torch
     import paged_kv_cache_kvck_amd as kvck
+    warmup_ms = WARMUP_MS if warmup_ms is None else warmup_ms
     kvck.kvck_instrument(True)
     try:
         call()
         call()
+        torch.cuda.synchronize()
+        ms, c = kvck.kvck_instrument_read()
+        extra = int(warmup_ms / max(ms / max(c, 1), 1e-3)) if warmup_ms > 0 else 0
+        for _ in range(extra):
+            call()
         torch.cuda.synchronize()
         kvck.kvck_instrument_read()
         ts = []
@@ -396,6 +407,34 @@ def config_rows(names, dev, calls=10, n_check=200):
     return rows
 
 
+def config_rows_isolated(names, calls=10, n_check=200, timeout=300):
+    """Each configuration row in a child process of its own (``bench.py
+    --only NAME``), started after this process has freed its pools.  Pool
+    placement follows the process's allocation history: the same hybrid
+    attention pools read at 87.6 % of 8 TB/s as a process's first allocation
+    and at 81.7-84.8 % after other pool sets had come and gone, so every row
+    is measured as a first allocation, like the headline.  A row whose child
+    fails is reported with its error."""
+    import subprocess
+    rows = []
+    for n in names:
+        cmd = [sys.executable, os.path.abspath(__file__), "--only", n, "--config-calls", str(calls),
+               "--oracle-positions", str(n_check), "--config-warmup-ms", str(WARMUP_MS)]
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=timeout)
+        except subprocess.TimeoutExpired:
+            rows.append({"config": n, "error": f"timed out after {timeout} s"})
+            continue
+        sys.stderr.write("".join(ln + "\n" for ln in r.stderr.splitlines() if ln.startswith("[config]")))
+        sys.stderr.flush()
+        lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+        if r.returncode != 0 or not lines:
+            rows.append({"config": n, "error": f"exit status {r.returncode}: {r.stderr[-400:]}"})
+            continue
+        rows += json.loads(lines[-1])["configs"]
+    return rows
+
+
 def copy_calibration(dev, gib):
     """One plain device copy of ``gib`` GiB (the runtime's copy kernel): the
     reference that rocprofv3 counter runs scale FETCH_SIZE / WRITE_SIZE by."""
@@ -414,6 +453,7 @@ def copy_calibration(dev, gib):
 # ----------------------------------------------------------------- main
 
 def main(argv=None):
+    global WARMUP_MS
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -429,6 +469,8 @@ def main(argv=None):
     ap.add_argument("--no-configs", action="store_true", help="skip the other configurations' rows")
     ap.add_argument("--only", default="", help="comma-separated configuration rows to run alone (no headline)")
     ap.add_argument("--config-calls", type=int, default=10, help="timed calls per configuration row")
+    ap.add_argument("--config-warmup-ms", type=float, default=WARMUP_MS,
+                    help="untimed calls before a row's timed ones: two, then about this many ms more (0: two)")
     ap.add_argument("--oracle-positions", type=int, default=200,
                     help="random positions per configuration checked against the oracle (plus every tail)")
     ap.add_argument("--copy-calibration-gib", type=float, default=0.0,
@@ -444,6 +486,7 @@ def main(argv=None):
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    WARMUP_MS = args.config_warmup_ms
     if args.only:
         names = [n for n in args.only.split(",") if n]
         rows = config_rows(names, dev, args.config_calls, args.oracle_positions)
@@ -606,7 +649,7 @@ def main(argv=None):
     torch.cuda.empty_cache()
 
     if not args.no_configs:
-        configs += config_rows(CONFIG_NAMES, dev, args.config_calls, args.oracle_positions)
+        configs += config_rows_isolated(CONFIG_NAMES, args.config_calls, args.oracle_positions)
     if configs:
         extra["configs"] = configs
     if not args.no_small:
