@@ -633,3 +633,57 @@ def test_calls_from_several_host_threads():
     for i, (layout, got) in results.items():
         for r, k in req.listed():
             assert got[r, k] == want[layout][r, k], (i, r, k)
+
+
+@pytest.mark.parametrize("layout,elem,nh,d,bs", [("NHD", "fp8", 12, 64, 16), ("NHD", "bf16", 8, 32, 16),
+                                                 ("MLA", "bf16", 1, 576, 16), ("MLA", "bf16", 1, 576, 64),
+                                                 ("NHD", "fp8", 3, 64, 8)])
+@pytest.mark.parametrize("ncaches", [1, 5])
+def test_merged_rows_stream_across_tasks(layout, elem, nh, d, bs, ncaches, monkeypatch):
+    """Merged rows stream their units across task boundaries in planned calls:
+    a wave's tasks follow one another with both load buffers in flight.  Many
+    tasks per wave (the plan forced, one or five caches), positions with no
+    valid slot and bad block ids in the middle of the stream, start offsets,
+    and (one cache: a direct write) accumulate onto the previous values -- every
+    position equal to the oracle, unlisted entries untouched."""
+    log(f"[merged stream] {layout} {elem} {nh}x{d} bs{bs} caches {ncaches}")
+    monkeypatch.setenv("KVCK_PLAN", "compact")
+    rng = np.random.default_rng(zlib.crc32(f"stream{layout}{elem}{nh}{d}{bs}{ncaches}".encode()))
+    R = 300
+    lengths = list(rng.integers(1, 12 * bs, R))
+    start = [int(x) if i % 7 == 3 else 0 for i, x in enumerate(rng.integers(0, 3, R))]
+    extra = [1 if i % 5 == 0 else 0 for i in range(R)]          # positions past the last token: no valid slot
+    req, nb = wl.page_requests(rng, lengths, bs, start_pos=start, extra_blocks=extra, spare_frac=0.2)
+    layers = [int(x) for x in rng.choice(1000, ncaches, replace=False)]
+    hp = [wl.host_random_bits(rng, wl.pool_shape(layout, nb, bs, nh, d), elem) for _ in layers]
+    pools = [to_device_bits(p) for p in hp]
+    want = oracle.checksum_blocks(hp, layout, layers, [0] * ncaches, req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens)
+    got = gpu_blocks(pools, layout, layers, req)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k]), (r, k)
+    assert_unlisted_untouched(got, req)
+    # accumulate onto the previous output: every listed entry doubles (mod 2^64)
+    prev = torch.from_numpy(got.view(np.int64).copy()).to(DEV).view(torch.uint64)
+    got2 = gpu_blocks(pools, layout, layers, req, out=prev, accumulate=True)
+    with np.errstate(over="ignore"):
+        for r, k in req.listed():
+            assert got2[r, k] == np.uint64(want[r, k]) * np.uint64(2), (r, k)
+    # bad ids scattered through the stream: those positions contribute 0 and are flagged
+    bad = req.block_table.copy()
+    listed = req.listed()
+    hit = [listed[i] for i in rng.choice(len(listed), 9, replace=False)]
+    for r, k in hit:
+        bad[r, k] = nb + 3 + r
+    breq = wl.Requests(req.block_size, req.num_tokens, req.start_pos, req.num_blocks, bad)
+    flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got3 = gpu_blocks(pools, layout, layers, breq, check=False,
+                      out=torch.full((R, req.max_blocks), SENTINEL, dtype=torch.int64, device=DEV).view(torch.uint64))
+    bt, nbt, sp, nt = req_tensors(breq)
+    kvck.kvck_checksum_blocks(pools, layout, layers, bt, nbt, sp, nt, error_flags=flags)
+    torch.cuda.synchronize()
+    valid_hit = [(r, k) for r, k in hit
+                 if oracle.num_valid_tokens(int(req.start_pos[r]) + k, bs, int(req.num_tokens[r])) > 0]
+    assert (int(flags.item()) & kvck.KVCK_FLAG_BAD_BLOCK_ID) == (kvck.KVCK_FLAG_BAD_BLOCK_ID if valid_hit else 0)
+    for r, k in listed:
+        assert int(got3[r, k]) == (0 if (r, k) in hit else int(want[r, k])), (r, k)
