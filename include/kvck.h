@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define KVCK_ABI_VERSION 2
+#define KVCK_ABI_VERSION 3
 
 /* The page attribute MAX_KV_HEADS_PER_LAYER (2^16): H of the slice factor and
  * a bound on a layer's KV heads (or Mamba rows); calls beyond it are refused. */
@@ -57,6 +57,23 @@ extern "C" {
 #define KVCK_MAX_CACHES 4096
 /* States per Mamba layer. */
 #define KVCK_MAX_STATES_PER_LAYER 4
+/* Largest out_stride of the checksum entry points and `columns` of
+ * kvck_tag_checksums: the number of replica-key columns a partial result may
+ * have (see "Replica columns" below). */
+#define KVCK_MAX_OUT_STRIDE 65536
+
+/*
+ * Replica columns.  The checksum page (module docstring; attribute ReplicaKey;
+ * class KVChecksumGroup) keys a worker's partial checksums by the
+ * (replicas, replica_index) of the layers they cover, so that replicated KV
+ * (MLA, or GQA on more TP ranks than KV heads) is compared replica by
+ * replica: a group's values are (num_positions, len(replica_keys)), one column
+ * per key, and what is offloaded with a block is its row summed.  Every
+ * checksum entry point writes its results out_stride elements apart, so with
+ * out_stride = C and out at element c of a row-major [..., C] array a call
+ * fills column c; a worker makes one call per replica key, over that key's
+ * caches, each into its own column.  out_stride = 1 is a dense array.
+ */
 
 typedef enum kvck_status {
   KVCK_OK = 0,
@@ -154,8 +171,9 @@ typedef struct kvck_kv_layout {
  * global_head_base[i]+k (TP shard: a subset of heads with global numbering;
  * PP stage: a subset of layers -- partial results sum to the full value).
  *
- * Output: out[r*max_blocks + k] (device, uint64) for every listed position
- * k < num_blocks_per_req[r]; other entries are not written.  With
+ * Output: out[(r*max_blocks + k)*out_stride] (device, uint64) for every
+ * listed position k < num_blocks_per_req[r]; other entries are not written.
+ * out_stride is 1..KVCK_MAX_OUT_STRIDE (one replica column of C: C).  With
  * accumulate != 0 the checksum is added (mod 2^64) to what out holds.
  *
  * Workspace: device, at least kvck_blocks_workspace_bytes(num_caches,
@@ -197,7 +215,8 @@ kvck_status kvck_checksum_blocks(
     const int64_t* start_pos,              /* device [num_reqs] */
     const int64_t* num_tokens,             /* device [num_reqs] */
     int32_t num_reqs, int32_t max_blocks,
-    uint64_t* out,                         /* device [num_reqs * max_blocks] */
+    uint64_t* out,                         /* device [num_reqs * max_blocks * out_stride] */
+    int64_t out_stride,                    /* elements, 1..KVCK_MAX_OUT_STRIDE */
     int32_t accumulate,
     void* workspace, size_t workspace_bytes,
     uint32_t* error_flags,                 /* device, optional */
@@ -234,7 +253,7 @@ kvck_status kvck_checksum_blocks_noalloc(
     const int32_t* global_head_base, int32_t num_caches, int32_t head_begin, int32_t head_count,
     const int32_t* block_table, int64_t block_table_row_stride, const int32_t* num_blocks_per_req,
     const int64_t* start_pos, const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks,
-    uint64_t* out, int32_t accumulate, uint32_t* error_flags, kvck_stream_t stream);
+    uint64_t* out, int64_t out_stride, int32_t accumulate, uint32_t* error_flags, kvck_stream_t stream);
 
 /*
  * Shape of one Mamba state, shared by every Mamba layer of a call.  A state
@@ -255,8 +274,8 @@ typedef struct kvck_state_desc {
  * global_row_base[l]+g) of every state of the layer, concatenated in the
  * order of `states`, elements numbered from 0 across the concatenation:
  *   s = sum_e x_e (2e + 1),  c = sum_{layer, g} m * s,  m = 2(layer*H + g_global) + 1.
- * Request r's state slot is slot_ids[r]; out[r] receives its checksum (added
- * to out[r] when accumulate != 0).
+ * Request r's state slot is slot_ids[r]; out[r*out_stride] receives its
+ * checksum (added to what it holds when accumulate != 0).
  *
  * state_ptrs holds num_layers*states_per_layer device pointers, layer-major
  * (state_ptrs[l*states_per_layer + i] is state i of layer l).
@@ -274,7 +293,8 @@ kvck_status kvck_checksum_states(
     int32_t row_begin, int32_t row_count,
     const int32_t* slot_ids,               /* device [num_reqs] */
     int32_t num_reqs,
-    uint64_t* out,                         /* device [num_reqs] */
+    uint64_t* out,                         /* device [num_reqs * out_stride] */
+    int64_t out_stride,                    /* elements, 1..KVCK_MAX_OUT_STRIDE */
     int32_t accumulate,
     void* workspace, size_t workspace_bytes,
     uint32_t* error_flags,                 /* device, optional */
@@ -320,7 +340,7 @@ kvck_status kvck_copy_checksum_blocks(
     const int32_t* num_blocks_per_req, const int64_t* start_pos, const int64_t* num_tokens,
     int32_t num_reqs, int32_t max_blocks,
     void* staging, int64_t staging_positions,  /* device */
-    uint64_t* out, int32_t accumulate,
+    uint64_t* out, int64_t out_stride, int32_t accumulate,
     void* workspace, size_t workspace_bytes,
     uint32_t* error_flags,
     kvck_stream_t stream);
@@ -336,9 +356,13 @@ size_t kvck_staging_bytes(const kvck_kv_layout* layout, int32_t num_caches, int3
  * value of its hash's leading 8 bytes, XOR the group's fingerprint; the
  * checksum offloaded with a block (one uint64, the page's BLOCK_CHECKSUM_BYTES)
  * is XORed with the tag, which ties it to that block hash and group of layers.
- * For every entry i (only listed positions i = r*max_blocks + k,
- * k < num_blocks_per_req[r], when num_blocks_per_req is given):
- *   t_i = checksums[i] ^ LE64(block_hashes + i*hash_stride) ^ fingerprint
+ * A position's checksum is its row of `columns` replica columns summed
+ * (class KVChecksumGroup: the stored value is the row's partials summed when
+ * the KV was offloaded; columns = 1 for one column).  For every entry i (only
+ * listed positions i = r*max_blocks + k, k < num_blocks_per_req[r], when
+ * num_blocks_per_req is given):
+ *   c_i = sum over col < columns of checksums[i*columns + col]
+ *   t_i = c_i ^ LE64(block_hashes + i*hash_stride) ^ fingerprint
  *   tagged[i] = t_i                               (if tagged: the value to offload)
  *   mismatch[i] = (t_i != stored[i])              (if stored: a load of offloaded KV)
  *   *mismatch_count += number of mismatches       (if mismatch_count)
@@ -347,11 +371,13 @@ size_t kvck_staging_bytes(const kvck_kv_layout* layout, int32_t num_caches, int3
  * negative or too large for block_size (the rule under which
  * kvck_checksum_blocks skips a request and leaves its entries unwritten), so
  * a rejected request is neither tagged nor compared.  All pointers are device
- * pointers; block_hashes must be 8-byte aligned with hash_stride a multiple
- * of 8 (vLLM block hashes are 32 bytes).  At least one of tagged / stored.
+ * pointers; the uint64 arrays and block_hashes must be 8-byte aligned, with
+ * hash_stride a multiple of 8 (vLLM block hashes are 32 bytes).  At least one
+ * of tagged / stored.
  */
 kvck_status kvck_tag_checksums(
-    const uint64_t* checksums,             /* device [n] */
+    const uint64_t* checksums,             /* device [n][columns] */
+    int32_t columns,                       /* 1..KVCK_MAX_OUT_STRIDE */
     const uint8_t* block_hashes,           /* device [n][hash_stride] */
     int64_t hash_stride,                   /* bytes, >= 8, multiple of 8 */
     uint64_t fingerprint,

@@ -15,6 +15,8 @@ from ._binding import (  # noqa: F401
     KVCK_COPY_SAVE,
     KVCK_FLAG_BAD_STATE_SLOT,
     KVCK_FLAG_STAGING_FULL,
+    KVCK_ABI_VERSION,
+    KVCK_MAX_OUT_STRIDE,
     KVCK_SCRATCH_BYTES,
     KvckDeviceError,
     KvckError,

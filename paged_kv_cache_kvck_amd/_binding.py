@@ -22,7 +22,9 @@ STATUS_NAMES = {
     0: "KVCK_OK", -1: "KVCK_ERR_INVALID_ARGUMENT", -2: "KVCK_ERR_UNSUPPORTED", -3: "KVCK_ERR_MISALIGNED",
     -4: "KVCK_ERR_WORKSPACE", -5: "KVCK_ERR_HIP", -6: "KVCK_ERR_NO_DEVICE", -7: "KVCK_ERR_SCRATCH",
 }
+KVCK_ABI_VERSION = 3
 KVCK_SCRATCH_BYTES = 32 << 20
+KVCK_MAX_OUT_STRIDE = 65536
 KVCK_FLAG_BAD_BLOCK_ID = 1
 KVCK_FLAG_BAD_REQUEST = 2
 KVCK_FLAG_BAD_STATE_SLOT = 4
@@ -84,17 +86,17 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kvck_checksum_blocks.restype = i32
     lib.kvck_checksum_blocks.argtypes = [
         ctypes.POINTER(kvck_kv_layout), ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(i32), i32,
-        i32, i32, vp, i64, vp, vp, vp, i32, i32, vp, i32, vp, sz, vp, vp]
+        i32, i32, vp, i64, vp, vp, vp, i32, i32, vp, i64, i32, vp, sz, vp, vp]
     lib.kvck_checksum_blocks_noalloc.restype = i32
     lib.kvck_checksum_blocks_noalloc.argtypes = [
         ctypes.POINTER(kvck_kv_layout), ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(i32), i32,
-        i32, i32, vp, i64, vp, vp, vp, i32, i32, vp, i32, vp, vp]
+        i32, i32, vp, i64, vp, vp, vp, i32, i32, vp, i64, i32, vp, vp]
     lib.kvck_blocks_workspace_bytes.restype = sz
     lib.kvck_blocks_workspace_bytes.argtypes = [i32, i32, i32]
     lib.kvck_checksum_states.restype = i32
     lib.kvck_checksum_states.argtypes = [
         ctypes.POINTER(kvck_state_desc), i32, ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(i32), i32,
-        i32, i32, i32, i32, vp, i32, vp, i32, vp, sz, vp, vp]
+        i32, i32, i32, i32, vp, i32, vp, i64, i32, vp, sz, vp, vp]
     lib.kvck_states_workspace_bytes.restype = sz
     lib.kvck_states_workspace_bytes.argtypes = [i32, i32, i32]
     lib.kvck_status_string.restype = ctypes.c_char_p
@@ -106,15 +108,18 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.kvck_copy_checksum_blocks.restype = i32
     lib.kvck_copy_checksum_blocks.argtypes = [
         i32, ctypes.POINTER(kvck_kv_layout), ctypes.POINTER(vp), ctypes.POINTER(i32), ctypes.POINTER(i32), i32,
-        i32, i32, vp, i64, vp, vp, vp, i32, i32, vp, i64, vp, i32, vp, sz, vp, vp]
+        i32, i32, vp, i64, vp, vp, vp, i32, i32, vp, i64, vp, i64, i32, vp, sz, vp, vp]
     lib.kvck_staging_bytes.restype = sz
     lib.kvck_staging_bytes.argtypes = [ctypes.POINTER(kvck_kv_layout), i32, i32]
     lib.kvck_tag_checksums.restype = i32
-    lib.kvck_tag_checksums.argtypes = [vp, vp, i64, ctypes.c_uint64, i64, vp, vp, i32, i32, vp, vp, vp, vp, vp]
+    lib.kvck_tag_checksums.argtypes = [vp, i32, vp, i64, ctypes.c_uint64, i64, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.kvck_instrument.restype = i32
     lib.kvck_instrument.argtypes = [i32]
     lib.kvck_instrument_read.restype = i32
     lib.kvck_instrument_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    if lib.kvck_abi_version() != KVCK_ABI_VERSION:
+        raise RuntimeError(f"{p} has ABI version {lib.kvck_abi_version()}, this binding needs {KVCK_ABI_VERSION}: "
+                           "rebuild it with `python -m paged_kv_cache_kvck_amd.build`")
     if path is None:
         _lib = lib
     return lib
@@ -322,6 +327,27 @@ def prepare_caches(caches, layout, layer_numbers, global_head_base=None, head_be
     return PreparedCaches(caches, layout, layer_numbers, global_head_base, head_begin, head_count, planes)
 
 
+def _out_stride(out, entries: int, dev) -> int:
+    """Element stride of an output tensor whose entries, in row-major order,
+    are evenly spaced in memory: 1 for a contiguous tensor, C for one column
+    ``values[..., c]`` of a row-major array with C replica columns."""
+    if not isinstance(out, torch.Tensor) or out.dtype not in (torch.uint64, torch.int64) or out.device != dev:
+        raise ValueError(f"out must be a uint64 tensor on {dev}")
+    if out.numel() < entries:
+        raise ValueError(f"out holds {out.numel()} entries, the call writes up to {entries}")
+    if out.is_contiguous():
+        return 1
+    step = out.stride(-1) if out.dim() else 1
+    inner = 1
+    for d in range(out.dim() - 1, -1, -1):
+        if out.shape[d] > 1 and out.stride(d) != step * inner:
+            raise ValueError("out's entries must be evenly spaced in row-major order (e.g. values[..., c])")
+        inner *= out.shape[d]
+    if not 1 <= step <= KVCK_MAX_OUT_STRIDE:
+        raise ValueError(f"out's element stride {step} is outside 1..{KVCK_MAX_OUT_STRIDE}")
+    return step
+
+
 def _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req, start_pos, num_tokens,
                  global_head_base, head_begin, head_count, out, workspace, check, error_flags, planes=None):
     lib = load_library()
@@ -340,9 +366,7 @@ def _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req,
     if out is None:
         out = torch.zeros((R, max_blocks), dtype=torch.uint64, device=dev)
         allocated.append(out)
-    elif out.dtype not in (torch.uint64, torch.int64) or out.device != dev or not out.is_contiguous() \
-            or out.numel() < R * max_blocks:
-        raise ValueError("out must be a contiguous uint64 tensor of num_reqs*max_blocks entries")
+    out_stride = _out_stride(out, R * max_blocks, dev)
     need = int(lib.kvck_blocks_workspace_bytes(n, R, max_blocks))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -352,7 +376,7 @@ def _blocks_args(caches, layout, layer_numbers, block_table, num_blocks_per_req,
     if fresh_flags:
         allocated.append(error_flags)
     return dict(lib=lib, dev=dev, L=pc.layout, n=n, head_begin=pc.head_begin, head_count=pc.head_count, R=R,
-                max_blocks=max_blocks, out=out, workspace=workspace, error_flags=error_flags, ptrs=pc.ptrs,
+                max_blocks=max_blocks, out=out, out_stride=out_stride, workspace=workspace, error_flags=error_flags, ptrs=pc.ptrs,
                 layers=pc.layers, bases=pc.bases, allocated=allocated)
 
 
@@ -397,7 +421,10 @@ def kvck_checksum_blocks(caches, layout: str | None, layer_numbers: Sequence[int
     checksum of both.
 
     Returns ``out``: uint64 (num_reqs, max_blocks) on the caches' device;
-    entries past a request's listed positions are left as they were.
+    entries past a request's listed positions are left as they were.  A
+    given ``out`` may be one replica column ``values[..., c]`` of a
+    (num_reqs, max_blocks, C) array (any view whose entries are evenly
+    spaced): the call then fills that column.
     ``check=True`` zeroes a flag word, synchronizes, and raises
     ``KvckDeviceError`` if the kernels flagged a bad block id or request.
     """
@@ -407,8 +434,9 @@ def kvck_checksum_blocks(caches, layout: str | None, layer_numbers: Sequence[int
     st = a["lib"].kvck_checksum_blocks(
         ctypes.byref(a["L"]), a["ptrs"], a["layers"], a["bases"], a["n"], a["head_begin"], a["head_count"],
         block_table.data_ptr(), block_table.stride(0), num_blocks_per_req.data_ptr(), start_pos.data_ptr(),
-        num_tokens.data_ptr(), a["R"], a["max_blocks"], a["out"].data_ptr(), int(bool(accumulate)), ws.data_ptr(),
-        ws.numel() * ws.element_size(), _ptr(a["error_flags"]), _stream_handle(stream, a["dev"], a["allocated"]))
+        num_tokens.data_ptr(), a["R"], a["max_blocks"], a["out"].data_ptr(), a["out_stride"], int(bool(accumulate)),
+        ws.data_ptr(), ws.numel() * ws.element_size(), _ptr(a["error_flags"]),
+        _stream_handle(stream, a["dev"], a["allocated"]))
     _check(st, "kvck_checksum_blocks")
     return _finish(a, check)
 
@@ -435,14 +463,12 @@ def kvck_checksum_blocks_noalloc(caches, layout: str | None, layer_numbers: Sequ
     _meta(num_blocks_per_req, torch.int32, "num_blocks_per_req", dev, R)
     _meta(start_pos, torch.int64, "start_pos", dev, R)
     _meta(num_tokens, torch.int64, "num_tokens", dev, R)
-    if not isinstance(out, torch.Tensor) or out.dtype not in (torch.uint64, torch.int64) or out.device != dev \
-            or not out.is_contiguous() or out.numel() < R * max_blocks:
-        raise ValueError("out must be a contiguous uint64 tensor of num_reqs*max_blocks entries")
+    out_stride = _out_stride(out, R * max_blocks, dev)
     error_flags = _flag_word(error_flags, False, dev)
     st = lib.kvck_checksum_blocks_noalloc(
         ctypes.byref(pc.layout), pc.ptrs, pc.layers, pc.bases, pc.n, pc.head_begin, pc.head_count,
         block_table.data_ptr(), block_table.stride(0), num_blocks_per_req.data_ptr(), start_pos.data_ptr(),
-        num_tokens.data_ptr(), R, max_blocks, out.data_ptr(), int(bool(accumulate)), _ptr(error_flags),
+        num_tokens.data_ptr(), R, max_blocks, out.data_ptr(), out_stride, int(bool(accumulate)), _ptr(error_flags),
         _stream_handle(stream, dev))
     _check(st, "kvck_checksum_blocks_noalloc")
     return out
@@ -477,7 +503,7 @@ def kvck_copy_checksum_blocks(direction: int, caches, layout: str | None,
         int(direction), ctypes.byref(a["L"]), a["ptrs"], a["layers"], a["bases"], a["n"], a["head_begin"],
         a["head_count"], block_table.data_ptr(), block_table.stride(0), num_blocks_per_req.data_ptr(),
         start_pos.data_ptr(), num_tokens.data_ptr(), a["R"], a["max_blocks"], staging.data_ptr(), positions,
-        a["out"].data_ptr(), int(bool(accumulate)), ws.data_ptr(), ws.numel() * ws.element_size(),
+        a["out"].data_ptr(), a["out_stride"], int(bool(accumulate)), ws.data_ptr(), ws.numel() * ws.element_size(),
         _ptr(a["error_flags"]), _stream_handle(stream, a["dev"], a["allocated"]))
     _check(st, "kvck_copy_checksum_blocks")
     return _finish(a, check)
@@ -502,7 +528,8 @@ def kvck_checksum_states(layer_states: Sequence[Sequence[torch.Tensor]], layer_n
                          row_count: int | None = None, out: torch.Tensor | None = None, accumulate: bool = False,
                          workspace: torch.Tensor | None = None, error_flags: torch.Tensor | None = None,
                          stream=None, check: bool = False) -> torch.Tensor:
-    """Mamba running-state checksums, one uint64 per request (position 0)."""
+    """Mamba running-state checksums, one uint64 per request (position 0);
+    a given ``out`` may be one replica column ``values[:, c]``."""
     lib = load_library()
     layer_states = [list(s) for s in layer_states]
     nl = len(layer_states)
@@ -535,6 +562,7 @@ def kvck_checksum_states(layer_states: Sequence[Sequence[torch.Tensor]], layer_n
     if out is None:
         out = torch.zeros(R, dtype=torch.uint64, device=dev)
         allocated.append(out)
+    out_stride = _out_stride(out, R, dev)
     descs = (kvck_state_desc * k)(*[state_desc(s) for s in ref])
     ptrs = (ctypes.c_void_p * (nl * k))(*[s.data_ptr() for sts in layer_states for s in sts])
     layers = (ctypes.c_int32 * nl)(*[int(x) for x in layer_numbers])
@@ -550,8 +578,8 @@ def kvck_checksum_states(layer_states: Sequence[Sequence[torch.Tensor]], layer_n
         error_flags = _flag_word(error_flags, check, dev)
     st = lib.kvck_checksum_states(
         descs, k, ptrs, layers, bases, nl, slots, rows, int(row_begin), int(row_count), slot_ids.data_ptr(), R,
-        out.data_ptr(), int(bool(accumulate)), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        _ptr(error_flags), _stream_handle(stream, dev, allocated))
+        out.data_ptr(), out_stride, int(bool(accumulate)), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _ptr(error_flags), _stream_handle(stream, dev, allocated))
     _check(st, "kvck_checksum_states")
     if check:
         torch.cuda.synchronize(dev)
@@ -565,20 +593,25 @@ def kvck_tag_checksums(checksums: torch.Tensor, block_hashes: torch.Tensor, fing
                        num_blocks_per_req: torch.Tensor | None = None, tagged: torch.Tensor | bool | None = True,
                        stored: torch.Tensor | None = None, mismatch: torch.Tensor | bool | None = None,
                        mismatch_count: torch.Tensor | None = None, stream=None, start_pos: torch.Tensor | None = None,
-                       block_size: int = 0):
+                       block_size: int = 0, columns: int = 1):
     """Tags of offloaded checksums (the page's block_checksum_tags) and the
     load-time comparison; see include/kvck.h.
 
     ``checksums``: uint64 tensor (e.g. the (num_reqs, max_blocks) output of
-    kvck_checksum_blocks); ``block_hashes``: uint8 (n, hash_bytes >= 8) tensor,
-    row i the hash of the block at entry i.  With ``num_blocks_per_req`` only
+    kvck_checksum_blocks, or with ``columns`` = C a (num_reqs, max_blocks, C)
+    array of replica columns, each entry's row summed before tagging);
+    ``block_hashes``: uint8 (n, hash_bytes >= 8) tensor, row i the hash of the
+    block at entry i.  With ``num_blocks_per_req`` only
     listed positions are touched; ``start_pos`` and ``block_size`` (those of
     the checksum call) also skip requests that call rejected.  Returns
     (tagged, mismatch) -- each a tensor or None.
     """
     lib = load_library()
     dev = checksums.device
-    n = checksums.numel()
+    columns = int(columns)
+    if not 1 <= columns <= KVCK_MAX_OUT_STRIDE or checksums.numel() % columns:
+        raise ValueError(f"columns must be in 1..{KVCK_MAX_OUT_STRIDE} and divide the checksum count")
+    n = checksums.numel() // columns
     if checksums.dtype not in (torch.uint64, torch.int64) or not checksums.is_contiguous():
         raise ValueError("checksums must be a contiguous uint64 tensor")
     if block_hashes.dtype != torch.uint8 or block_hashes.dim() != 2 or block_hashes.shape[0] != n \
@@ -603,7 +636,7 @@ def kvck_tag_checksums(checksums: torch.Tensor, block_hashes: torch.Tensor, fing
         allocated.append(mismatch)
     elif mismatch is False:
         mismatch = None
-    st = lib.kvck_tag_checksums(checksums.data_ptr(), block_hashes.data_ptr(), block_hashes.stride(0),
+    st = lib.kvck_tag_checksums(checksums.data_ptr(), columns, block_hashes.data_ptr(), block_hashes.stride(0),
                                 ctypes.c_uint64(int(fingerprint) & ((1 << 64) - 1)), n, _ptr(num_blocks_per_req),
                                 _ptr(start_pos), max_blocks, int(block_size), _ptr(tagged), _ptr(stored),
                                 _ptr(mismatch), _ptr(mismatch_count), _stream_handle(stream, dev, allocated))

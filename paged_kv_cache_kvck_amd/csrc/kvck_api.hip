@@ -348,7 +348,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
                         int32_t head_begin, int32_t head_count, const int32_t* block_table,
                         int64_t block_table_row_stride, const int32_t* num_blocks_per_req, const int64_t* start_pos,
                         const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks, uint64_t* out,
-                        int32_t accumulate, void* workspace, size_t workspace_bytes, uint32_t* error_flags,
+                        int64_t out_stride, int32_t accumulate, void* workspace, size_t workspace_bytes, uint32_t* error_flags,
                         void* staging, int64_t staging_positions, kvck_stream_t stream, bool use_scratch = false) {
   if (mode != kModeChecksum && mode != KVCK_COPY_SAVE && mode != KVCK_COPY_LOAD) return KVCK_ERR_INVALID_ARGUMENT;
   if (use_scratch && mode != kModeChecksum) return KVCK_ERR_INVALID_ARGUMENT;
@@ -370,6 +370,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   }
   // ---- requests
   if (num_reqs < 0 || max_blocks < 0) return KVCK_ERR_INVALID_ARGUMENT;
+  if (out_stride < 1 || out_stride > KVCK_MAX_OUT_STRIDE) return KVCK_ERR_INVALID_ARGUMENT;
   if (num_reqs == 0 || max_blocks == 0) return KVCK_OK;
   if (!block_table || !num_blocks_per_req || !start_pos || !num_tokens || !out) return KVCK_ERR_INVALID_ARGUMENT;
   // arrays aligned to their element size (small calls read the request arrays with scalar loads)
@@ -503,7 +504,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   }
 
   if (!dense && launch_plan(block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens,
-                            num_reqs, max_blocks, L.block_size, L.num_blocks, workspace, error_flags,
+                            num_reqs, max_blocks, L.block_size, L.num_blocks, out_stride, workspace, error_flags,
                             st) != hipSuccess)
     return KVCK_ERR_HIP;
 
@@ -518,6 +519,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   a.n_items = reinterpret_cast<const uint32_t*>(ws);
   a.partials = reinterpret_cast<uint64_t*>(ws + w.partials_off);
   a.out = out;
+  a.out_stride = out_stride;
   a.max_items = max_items;
   a.chunk_stride = L.chunk_stride;
   a.piece_base = 2ull * (uint64_t)L.plane_begin * (uint64_t)(pieces / L.planes);
@@ -584,9 +586,10 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   if (timed && hipEventRecord(ev1, st) != hipSuccess) return KVCK_ERR_HIP;
   if (total_groups > 1) {
     const hipError_t e = dense ? launch_reduce_dense(a.partials, max_items, total_groups, num_blocks_per_req,
-                                                     start_pos, max_blocks, max_start, out, a.accumulate, st)
+                                                     start_pos, max_blocks, max_start, out, out_stride,
+                                                     a.accumulate, st)
                                : launch_reduce(a.partials, max_items, total_groups, a.n_items, 0, a.recs, out,
-                                               a.accumulate, st);
+                                               out_stride, a.accumulate, st);
     if (e != hipSuccess) return KVCK_ERR_HIP;
   }
   return KVCK_OK;
@@ -599,13 +602,13 @@ KVCK_EXPORT kvck_status kvck_checksum_blocks(const kvck_kv_layout* layout, const
                                              const int32_t* block_table, int64_t block_table_row_stride,
                                              const int32_t* num_blocks_per_req, const int64_t* start_pos,
                                              const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks,
-                                             uint64_t* out, int32_t accumulate, void* workspace,
-                                             size_t workspace_bytes, uint32_t* error_flags,
+                                             uint64_t* out, int64_t out_stride, int32_t accumulate,
+                                             void* workspace, size_t workspace_bytes, uint32_t* error_flags,
                                              kvck_stream_t stream) {
   return blocks_call(kModeChecksum, layout, cache_ptrs, layer_numbers, global_head_base, num_caches, head_begin,
                      head_count, block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens,
-                     num_reqs, max_blocks, out, accumulate, workspace, workspace_bytes, error_flags, nullptr, 0,
-                     stream);
+                     num_reqs, max_blocks, out, out_stride, accumulate, workspace, workspace_bytes, error_flags,
+                     nullptr, 0, stream);
 }
 
 KVCK_EXPORT kvck_status kvck_checksum_blocks_noalloc(
@@ -613,10 +616,10 @@ KVCK_EXPORT kvck_status kvck_checksum_blocks_noalloc(
     const int32_t* global_head_base, int32_t num_caches, int32_t head_begin, int32_t head_count,
     const int32_t* block_table, int64_t block_table_row_stride, const int32_t* num_blocks_per_req,
     const int64_t* start_pos, const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks, uint64_t* out,
-    int32_t accumulate, uint32_t* error_flags, kvck_stream_t stream) {
+    int64_t out_stride, int32_t accumulate, uint32_t* error_flags, kvck_stream_t stream) {
   return blocks_call(kModeChecksum, layout, cache_ptrs, layer_numbers, global_head_base, num_caches, head_begin,
                      head_count, block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens,
-                     num_reqs, max_blocks, out, accumulate, nullptr, 0, error_flags, nullptr, 0, stream,
+                     num_reqs, max_blocks, out, out_stride, accumulate, nullptr, 0, error_flags, nullptr, 0, stream,
                      /*use_scratch=*/true);
 }
 
@@ -628,13 +631,14 @@ KVCK_EXPORT kvck_status kvck_copy_checksum_blocks(int32_t direction, const kvck_
                                                   const int32_t* num_blocks_per_req, const int64_t* start_pos,
                                                   const int64_t* num_tokens, int32_t num_reqs, int32_t max_blocks,
                                                   void* staging, int64_t staging_positions, uint64_t* out,
-                                                  int32_t accumulate, void* workspace, size_t workspace_bytes,
-                                                  uint32_t* error_flags, kvck_stream_t stream) {
+                                                  int64_t out_stride, int32_t accumulate, void* workspace,
+                                                  size_t workspace_bytes, uint32_t* error_flags,
+                                                  kvck_stream_t stream) {
   if (direction != KVCK_COPY_SAVE && direction != KVCK_COPY_LOAD) return KVCK_ERR_INVALID_ARGUMENT;
   return blocks_call(direction, layout, cache_ptrs, layer_numbers, global_head_base, num_caches, head_begin,
                      head_count, block_table, block_table_row_stride, num_blocks_per_req, start_pos, num_tokens,
-                     num_reqs, max_blocks, out, accumulate, workspace, workspace_bytes, error_flags, staging,
-                     staging_positions, stream);
+                     num_reqs, max_blocks, out, out_stride, accumulate, workspace, workspace_bytes, error_flags,
+                     staging, staging_positions, stream);
 }
 
 KVCK_EXPORT size_t kvck_staging_bytes(const kvck_kv_layout* layout, int32_t num_caches, int32_t head_count) {
@@ -667,8 +671,8 @@ KVCK_EXPORT kvck_status kvck_checksum_states(const kvck_state_desc* states, int3
                                              const int32_t* global_row_base, int32_t num_layers, int32_t num_slots,
                                              int32_t num_rows, int32_t row_begin, int32_t row_count,
                                              const int32_t* slot_ids, int32_t num_reqs, uint64_t* out,
-                                             int32_t accumulate, void* workspace, size_t workspace_bytes,
-                                             uint32_t* error_flags, kvck_stream_t stream) {
+                                             int64_t out_stride, int32_t accumulate, void* workspace,
+                                             size_t workspace_bytes, uint32_t* error_flags, kvck_stream_t stream) {
   if (!states || !state_ptrs || !layer_numbers || !global_row_base) return KVCK_ERR_INVALID_ARGUMENT;
   if (states_per_layer < 1 || states_per_layer > KVCK_MAX_STATES_PER_LAYER) return KVCK_ERR_UNSUPPORTED;
   if (num_layers < 1 || num_layers > KVCK_MAX_CACHES) return KVCK_ERR_UNSUPPORTED;
@@ -696,8 +700,11 @@ KVCK_EXPORT kvck_status kvck_checksum_states(const kvck_state_desc* states, int3
     }
   }
   if (num_reqs < 0) return KVCK_ERR_INVALID_ARGUMENT;
+  if (out_stride < 1 || out_stride > KVCK_MAX_OUT_STRIDE) return KVCK_ERR_INVALID_ARGUMENT;
   if (num_reqs == 0) return KVCK_OK;
   if (!slot_ids || !out) return KVCK_ERR_INVALID_ARGUMENT;
+  if (!aligned(slot_ids, 4) || !aligned(out, 8) || (error_flags && !aligned(error_flags, 4)))
+    return KVCK_ERR_MISALIGNED;
   const int32_t groups = row_groups(row_count);
   const int64_t splits = (int64_t)num_layers * groups;
   int64_t items = 0;
@@ -726,6 +733,7 @@ KVCK_EXPORT kvck_status kvck_checksum_states(const kvck_state_desc* states, int3
   a.slot_ids = slot_ids;
   a.partials = splits > 1 ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + kAlign) : nullptr;
   a.out = out;
+  a.out_stride = out_stride;
   a.error_flags = error_flags;
   a.nstates = states_per_layer;
   a.num_slots = num_slots;
@@ -753,26 +761,30 @@ KVCK_EXPORT kvck_status kvck_checksum_states(const kvck_state_desc* states, int3
   }
   if (timed && hipEventRecord(ev1, st) != hipSuccess) return KVCK_ERR_HIP;
   if (splits > 1) {
-    if (launch_reduce(a.partials, num_reqs, (int32_t)splits, nullptr, num_reqs, nullptr, out, a.accumulate, st) !=
-        hipSuccess)
+    if (launch_reduce(a.partials, num_reqs, (int32_t)splits, nullptr, num_reqs, nullptr, out, out_stride,
+                      a.accumulate, st) != hipSuccess)
       return KVCK_ERR_HIP;
   }
   return KVCK_OK;
 }
 
-KVCK_EXPORT kvck_status kvck_tag_checksums(const uint64_t* checksums, const uint8_t* block_hashes, int64_t hash_stride,
-                                           uint64_t fingerprint, int64_t n, const int32_t* num_blocks_per_req,
+KVCK_EXPORT kvck_status kvck_tag_checksums(const uint64_t* checksums, int32_t columns, const uint8_t* block_hashes,
+                                           int64_t hash_stride, uint64_t fingerprint, int64_t n,
+                                           const int32_t* num_blocks_per_req,
                                            const int64_t* start_pos, int32_t max_blocks, int32_t block_size,
                                            uint64_t* tagged, const uint64_t* stored, uint8_t* mismatch,
                                            uint32_t* mismatch_count, kvck_stream_t stream) {
   if (n < 0) return KVCK_ERR_INVALID_ARGUMENT;
   if (n == 0) return KVCK_OK;
   if (!checksums || !block_hashes) return KVCK_ERR_INVALID_ARGUMENT;
+  if (columns < 1 || columns > KVCK_MAX_OUT_STRIDE) return KVCK_ERR_INVALID_ARGUMENT;
   if (!tagged && !stored) return KVCK_ERR_INVALID_ARGUMENT;       // nothing to do
   if ((mismatch || mismatch_count) && !stored) return KVCK_ERR_INVALID_ARGUMENT;
   if (hash_stride < 8) return KVCK_ERR_INVALID_ARGUMENT;
-  if (hash_stride % 8 != 0 || !aligned(block_hashes, 8)) return KVCK_ERR_MISALIGNED;
-  if (!extent_ok({{n, hash_stride}}, 8)) return KVCK_ERR_UNSUPPORTED;
+  if (hash_stride % 8 != 0 || !aligned(block_hashes, 8) || !aligned(checksums, 8) || !aligned(tagged, 8) ||
+      !aligned(stored, 8) || !aligned(mismatch_count, 4))
+    return KVCK_ERR_MISALIGNED;
+  if (!extent_ok({{n, hash_stride}}, 8) || !extent_ok({{n, (int64_t)columns * 8}}, 8)) return KVCK_ERR_UNSUPPORTED;
   if (num_blocks_per_req && (max_blocks < 1 || n % max_blocks != 0)) return KVCK_ERR_INVALID_ARGUMENT;
   if (start_pos && (!num_blocks_per_req || block_size < 1)) return KVCK_ERR_INVALID_ARGUMENT;
   if ((num_blocks_per_req && !aligned(num_blocks_per_req, 4)) || (start_pos && !aligned(start_pos, 8)))
@@ -782,8 +794,9 @@ KVCK_EXPORT kvck_status kvck_tag_checksums(const uint64_t* checksums, const uint
   int dev = 0;
   const kvck_status ds = current_device(&dev);
   if (ds != KVCK_OK) return ds;
-  if (launch_tags(checksums, block_hashes, hash_stride, fingerprint, n, num_blocks_per_req, start_pos, max_blocks,
-                  max_start, tagged, stored, mismatch, mismatch_count, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (launch_tags(checksums, columns, block_hashes, hash_stride, fingerprint, n, num_blocks_per_req, start_pos,
+                  max_blocks, max_start, tagged, stored, mismatch, mismatch_count,
+                  static_cast<hipStream_t>(stream)) != hipSuccess)
     return KVCK_ERR_HIP;
   return KVCK_OK;
 }

@@ -80,7 +80,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(const int32_t* __restri
 __global__ __launch_bounds__(256) void plan_fill_kernel(
     const int32_t* __restrict__ block_table, int64_t bt_stride, const int64_t* __restrict__ start_pos,
     const int64_t* __restrict__ num_tokens, int32_t num_reqs, int32_t max_blocks, int32_t block_size,
-    int64_t num_blocks, const int32_t* __restrict__ prefix, PosRecord* __restrict__ recs,
+    int64_t num_blocks, int64_t out_stride, const int32_t* __restrict__ prefix, PosRecord* __restrict__ recs,
     uint32_t* __restrict__ error_flags) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)num_reqs * max_blocks) return;
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void plan_fill_kernel(
   }
   PosRecord rec;
   rec.t0 = t0;
-  rec.out_idx = idx;
+  rec.out_idx = idx * out_stride;
   rec.block = b;
   rec.valid = v;
   rec.pad = 0;
@@ -110,8 +110,8 @@ __global__ __launch_bounds__(256) void plan_fill_kernel(
 __global__ __launch_bounds__(1024) void plan_small_kernel(
     const int32_t* __restrict__ block_table, int64_t bt_stride, const int32_t* __restrict__ nbpr,
     const int64_t* __restrict__ start_pos, const int64_t* __restrict__ num_tokens, int32_t num_reqs,
-    int32_t max_blocks, int32_t block_size, int64_t num_blocks, int64_t max_start, uint32_t* __restrict__ n_items,
-    PosRecord* __restrict__ recs, uint32_t* __restrict__ error_flags) {
+    int32_t max_blocks, int32_t block_size, int64_t num_blocks, int64_t max_start, int64_t out_stride,
+    uint32_t* __restrict__ n_items, PosRecord* __restrict__ recs, uint32_t* __restrict__ error_flags) {
   __shared__ int32_t scan[1024];
   const int tid = threadIdx.x;
   int n = 0;
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(1024) void plan_small_kernel(
   }
   PosRecord rec;
   rec.t0 = t0;
-  rec.out_idx = idx;
+  rec.out_idx = idx * out_stride;
   rec.block = b;
   rec.valid = v;
   rec.pad = 0;
@@ -469,12 +469,13 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
 __global__ __launch_bounds__(256) void reduce_kernel(const uint64_t* __restrict__ partials, int64_t stride,
                                                      int32_t splits, const uint32_t* __restrict__ n_items,
                                                      int64_t n_fixed, const PosRecord* __restrict__ recs,
-                                                     uint64_t* __restrict__ out, int32_t accumulate) {
+                                                     uint64_t* __restrict__ out, int64_t out_stride,
+                                                     int32_t accumulate) {
   const int64_t n = n_items ? (int64_t)*n_items : n_fixed;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     uint64_t s = 0;
     for (int32_t sp = 0; sp < splits; ++sp) s += partials[(int64_t)sp * stride + i];
-    const int64_t o = recs ? recs[i].out_idx : i;
+    const int64_t o = recs ? recs[i].out_idx : i * out_stride;
     out[o] = accumulate ? out[o] + s : s;
   }
 }
@@ -484,7 +485,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(const uint64_t* __restrict_
 __global__ __launch_bounds__(256) void reduce_wave_kernel(const uint64_t* __restrict__ partials, int64_t stride,
                                                           int32_t splits, const uint32_t* __restrict__ n_items,
                                                           int64_t n_fixed, const PosRecord* __restrict__ recs,
-                                                          uint64_t* __restrict__ out, int32_t accumulate) {
+                                                          uint64_t* __restrict__ out, int64_t out_stride,
+                                                          int32_t accumulate) {
   const int64_t n = n_items ? (int64_t)*n_items : n_fixed;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
@@ -493,7 +495,7 @@ __global__ __launch_bounds__(256) void reduce_wave_kernel(const uint64_t* __rest
     for (int32_t sp = lane; sp < splits; sp += kWave) s += partials[(int64_t)sp * stride + i];
     s = wave_sum(s);
     if (lane == 0) {
-      const int64_t o = recs ? recs[i].out_idx : i;
+      const int64_t o = recs ? recs[i].out_idx : i * out_stride;
       out[o] = accumulate ? out[o] + s : s;
     }
   }
@@ -506,7 +508,7 @@ __global__ __launch_bounds__(256) void reduce_dense_kernel(const uint64_t* __res
                                                            int32_t splits, const int32_t* __restrict__ nbpr,
                                                            const int64_t* __restrict__ start_pos, int32_t max_blocks,
                                                            int64_t max_start, uint64_t* __restrict__ out,
-                                                           int32_t accumulate) {
+                                                           int64_t out_stride, int32_t accumulate) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
   for (int64_t i = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; i < stride; i += waves) {
@@ -517,7 +519,10 @@ __global__ __launch_bounds__(256) void reduce_dense_kernel(const uint64_t* __res
     uint64_t s = 0;
     for (int32_t sp = lane; sp < splits; sp += kWave) s += partials[(int64_t)sp * stride + i];
     s = wave_sum(s);
-    if (lane == 0) out[i] = accumulate ? out[i] + s : s;
+    if (lane == 0) {
+      uint64_t* o = out + i * out_stride;
+      *o = accumulate ? *o + s : s;
+    }
   }
 }
 
@@ -614,8 +619,8 @@ int workgroups_per_cu(int fits, int preferred) {
 
 hipError_t launch_plan(const int32_t* block_table, int64_t bt_stride, const int32_t* nbpr,
                        const int64_t* start_pos, const int64_t* num_tokens, int32_t num_reqs,
-                       int32_t max_blocks, int32_t block_size, int64_t num_blocks, void* workspace,
-                       uint32_t* error_flags, hipStream_t stream) {
+                       int32_t max_blocks, int32_t block_size, int64_t num_blocks, int64_t out_stride,
+                       void* workspace, uint32_t* error_flags, hipStream_t stream) {
   const BlocksWorkspace w = BlocksWorkspace::make(1, num_reqs, max_blocks);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint32_t* n_items = reinterpret_cast<uint32_t*>(ws);
@@ -626,7 +631,7 @@ hipError_t launch_plan(const int32_t* block_table, int64_t bt_stride, const int3
   if (num_reqs <= 1024) {
     hipLaunchKernelGGL(plan_small_kernel, dim3((unsigned)((items + 1023) / 1024)), dim3(1024), 0, stream,
                        block_table, bt_stride, nbpr, start_pos, num_tokens, num_reqs, max_blocks, block_size,
-                       num_blocks, max_start, n_items, recs, error_flags);
+                       num_blocks, max_start, out_stride, n_items, recs, error_flags);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, stream, nbpr, start_pos, num_reqs, max_blocks,
@@ -635,7 +640,7 @@ hipError_t launch_plan(const int32_t* block_table, int64_t bt_stride, const int3
   if (e != hipSuccess) return e;
   const int64_t grid = (items + 255) / 256;
   hipLaunchKernelGGL(plan_fill_kernel, dim3((unsigned)grid), dim3(256), 0, stream, block_table, bt_stride,
-                     start_pos, num_tokens, num_reqs, max_blocks, block_size, num_blocks, prefix, recs,
+                     start_pos, num_tokens, num_reqs, max_blocks, block_size, num_blocks, out_stride, prefix, recs,
                      error_flags);
   return hipGetLastError();
 }
@@ -659,32 +664,32 @@ hipError_t launch_blocks(const BlocksArgs& a, const BlocksShape& shp, int grid, 
 }
 
 hipError_t launch_reduce(const uint64_t* partials, int64_t stride, int32_t splits, const uint32_t* n_items,
-                         int64_t n_fixed, const PosRecord* recs, uint64_t* out, int32_t accumulate,
-                         hipStream_t stream) {
+                         int64_t n_fixed, const PosRecord* recs, uint64_t* out, int64_t out_stride,
+                         int32_t accumulate, hipStream_t stream) {
   if (splits >= 64) {
     int64_t grid = (stride + 3) / 4;
     if (grid > 4096) grid = 4096;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(reduce_wave_kernel, dim3((unsigned)grid), dim3(256), 0, stream, partials, stride, splits,
-                       n_items, n_fixed, recs, out, accumulate);
+                       n_items, n_fixed, recs, out, out_stride, accumulate);
     return hipGetLastError();
   }
   int64_t grid = (stride + 255) / 256;
   if (grid > 4096) grid = 4096;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream, partials, stride, splits, n_items,
-                     n_fixed, recs, out, accumulate);
+                     n_fixed, recs, out, out_stride, accumulate);
   return hipGetLastError();
 }
 
 hipError_t launch_reduce_dense(const uint64_t* partials, int64_t stride, int32_t splits, const int32_t* nbpr,
                                const int64_t* start_pos, int32_t max_blocks, int64_t max_start, uint64_t* out,
-                               int32_t accumulate, hipStream_t stream) {
+                               int64_t out_stride, int32_t accumulate, hipStream_t stream) {
   int64_t grid = (stride + 3) / 4;
   if (grid > 4096) grid = 4096;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(reduce_dense_kernel, dim3((unsigned)grid), dim3(256), 0, stream, partials, stride, splits, nbpr,
-                     start_pos, max_blocks, max_start, out, accumulate);
+                     start_pos, max_blocks, max_start, out, out_stride, accumulate);
   return hipGetLastError();
 }
 

@@ -205,7 +205,7 @@ __device__ __forceinline__ TaskRecord task_record(const BlocksArgs& a, int64_t i
   const int64_t s = uniform64(read_const(a.start_pos + r));
   const int64_t ntok = uniform64(read_const(a.num_tokens + r));
   const int32_t b = __builtin_amdgcn_readfirstlane(read_const(a.block_table + (int64_t)r * a.bt_stride + k));
-  t.out_idx = item;
+  t.out_idx = item * a.out_stride;
   t.block = b;
   t.valid = 0;
   t.t0 = 0;

@@ -32,7 +32,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // One listed block position, built on the device from the request arrays.
 struct alignas(16) PosRecord {
   int64_t t0;       // first token the position holds: pos * block_size
-  int64_t out_idx;  // r * max_blocks + k
+  int64_t out_idx;  // (r * max_blocks + k) * out_stride: the position's output element
   int32_t block;    // physical block id
   int32_t valid;    // slots to checksum (0: none, or a bad id)
   int64_t pad;
@@ -61,6 +61,7 @@ struct BlocksArgs {
   const uint32_t* n_items;   // device: listed positions
   uint64_t* partials;        // [num_caches][max_items] when not direct
   uint64_t* out;
+  int64_t out_stride;                        // elements between consecutive slots' outputs
   int64_t max_items;
   int64_t chunk_stride;                      // bytes between a row's contiguous runs
   uint64_t piece_base;                       // 2 * (first covered plane) * pieces per plane
@@ -111,6 +112,7 @@ struct StatesArgs {
   const int32_t* slot_ids;
   uint64_t* partials;  // [splits][num_reqs]
   uint64_t* out;
+  int64_t out_stride;  // elements between consecutive requests' outputs
   uint32_t* error_flags;
   int32_t nstates, num_layers, num_slots, num_reqs;
   int32_t row_begin, row_count, rows_per_task, groups_per_layer;
@@ -139,16 +141,16 @@ struct BlocksShape {
 // launchers (return hipSuccess or the first HIP error)
 hipError_t launch_plan(const int32_t* block_table, int64_t bt_stride, const int32_t* nbpr,
                        const int64_t* start_pos, const int64_t* num_tokens, int32_t num_reqs,
-                       int32_t max_blocks, int32_t block_size, int64_t num_blocks, void* workspace,
-                       uint32_t* error_flags, hipStream_t stream);
+                       int32_t max_blocks, int32_t block_size, int64_t num_blocks, int64_t out_stride,
+                       void* workspace, uint32_t* error_flags, hipStream_t stream);
 hipError_t launch_blocks(const BlocksArgs& a, const BlocksShape& shp, int grid, hipStream_t stream);
 int blocks_grid(const BlocksShape& shp, int device, int64_t max_tasks);
 hipError_t launch_reduce(const uint64_t* partials, int64_t stride, int32_t splits, const uint32_t* n_items,
-                         int64_t n_fixed, const PosRecord* recs, uint64_t* out, int32_t accumulate,
-                         hipStream_t stream);
+                         int64_t n_fixed, const PosRecord* recs, uint64_t* out, int64_t out_stride,
+                         int32_t accumulate, hipStream_t stream);
 hipError_t launch_reduce_dense(const uint64_t* partials, int64_t stride, int32_t splits, const int32_t* nbpr,
                                const int64_t* start_pos, int32_t max_blocks, int64_t max_start, uint64_t* out,
-                               int32_t accumulate, hipStream_t stream);
+                               int64_t out_stride, int32_t accumulate, hipStream_t stream);
 hipError_t launch_states(const StatesArgs& a, int grid, hipStream_t stream);
 hipError_t launch_tblocks(const BlocksArgs& a, const BlocksShape& shp, int grid, hipStream_t stream);
 int tblocks_grid(const BlocksShape& shp, int device, int64_t max_tasks);
@@ -156,8 +158,8 @@ hipError_t launch_copy(const CopyArgs& a, const BlocksShape& shp, int direction,
 int copy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks);
 hipError_t launch_tcopy(const CopyArgs& a, const BlocksShape& shp, int direction, int grid, hipStream_t stream);
 int tcopy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks, int32_t block_size);
-hipError_t launch_tags(const uint64_t* checksums, const uint8_t* hashes, int64_t hash_stride, uint64_t fingerprint,
-                       int64_t n, const int32_t* nbpr, const int64_t* start_pos, int32_t max_blocks,
+hipError_t launch_tags(const uint64_t* checksums, int32_t columns, const uint8_t* hashes, int64_t hash_stride,
+                       uint64_t fingerprint, int64_t n, const int32_t* nbpr, const int64_t* start_pos, int32_t max_blocks,
                        int64_t max_start, uint64_t* tagged, const uint64_t* stored, uint8_t* mismatch,
                        uint32_t* count, hipStream_t stream);
 int states_grid(int device, int64_t tasks);

@@ -92,7 +92,8 @@ __global__ __launch_bounds__(kBlockThreads) void states_kernel(const StatesArgs 
     acc = wave_sum(acc);
     if (lane == 0) {
       if (a.direct) {
-        a.out[r] = a.accumulate ? a.out[r] + acc : acc;
+        uint64_t* o = a.out + (int64_t)r * a.out_stride;
+        *o = a.accumulate ? *o + acc : acc;
       } else {
         a.partials[(int64_t)(a.split_offset + split) * a.num_reqs + r] = acc;
       }

@@ -52,7 +52,7 @@ static int run(const kvck_kv_layout* L, void* const* pools, const int32_t* layer
   uint32_t flags = 0;
   HIP_OK(hipMemset(d_flags, 0, sizeof(uint32_t)));
   kvck_status st = kvck_checksum_blocks(L, (const void* const*)pools, layers, bases, LAYERS, head_begin, head_count,
-                                        d_table, MAXB, d_nb, d_start, d_tokens, R, MAXB, d_out, 0, d_ws, ws_bytes,
+                                        d_table, MAXB, d_nb, d_start, d_tokens, R, MAXB, d_out, 1, 0, d_ws, ws_bytes,
                                         d_flags, NULL);
   if (st != KVCK_OK) {
     fprintf(stderr, "kvck_checksum_blocks: %s\n", kvck_status_string(st));

@@ -60,6 +60,7 @@ struct BlocksCall {
   int32_t num_reqs = 4, max_blocks = 8;
   int64_t bt_stride = 8;
   void* out = kFake;
+  int64_t out_stride = 1;
   void* ws = kFake;
   size_t ws_bytes = 0;  // 0: the size kvck_blocks_workspace_bytes gives
   int32_t direction = -1;  // -1: kvck_checksum_blocks; -2: kvck_checksum_blocks_noalloc; else the fused copy
@@ -76,17 +77,17 @@ struct BlocksCall {
     if (direction == -2)
       return kvck_checksum_blocks_noalloc(&L, ptrs.data(), layers.data(), bases.data(), (int32_t)ptrs.size(),
                                           head_begin, head_count, bt, bt_stride, nb, i64, i64, num_reqs, max_blocks,
-                                          static_cast<uint64_t*>(out), 0, nullptr, nullptr);
+                                          static_cast<uint64_t*>(out), out_stride, 0, nullptr, nullptr);
     if (direction < 0)
       return kvck_checksum_blocks(&L, ptrs.data(), layers.data(), bases.data(), (int32_t)ptrs.size(), head_begin,
                                   head_count, bt, bt_stride, nb, i64, i64, num_reqs, max_blocks,
-                                  static_cast<uint64_t*>(out), 0, ws, need, nullptr, nullptr);
+                                  static_cast<uint64_t*>(out), out_stride, 0, ws, need, nullptr, nullptr);
     std::vector<void*> mptrs;
     for (const void* p : ptrs) mptrs.push_back(const_cast<void*>(p));
     return kvck_copy_checksum_blocks(direction, &L, mptrs.data(), layers.data(), bases.data(), (int32_t)ptrs.size(),
                                      head_begin, head_count, bt, bt_stride, nb, i64, i64, num_reqs, max_blocks,
-                                     staging, staging_positions, static_cast<uint64_t*>(out), 0, ws, need, nullptr,
-                                     nullptr);
+                                     staging, staging_positions, static_cast<uint64_t*>(out), out_stride, 0, ws,
+                                     need, nullptr, nullptr);
   }
 };
 
@@ -111,6 +112,14 @@ void blocks_checks(bool have_device) {
   EXPECT_EQ(call([](BlocksCall& c) { c.ptrs[1] = nullptr; }), KVCK_ERR_INVALID_ARGUMENT);
   EXPECT_EQ(call([](BlocksCall& c) { c.out = nullptr; }), KVCK_ERR_INVALID_ARGUMENT);
   EXPECT_EQ(call([](BlocksCall& c) { c.bt_stride = 4; }), KVCK_ERR_INVALID_ARGUMENT);
+  // output stride: one replica column of at most KVCK_MAX_OUT_STRIDE
+  EXPECT_EQ(call([](BlocksCall& c) { c.out_stride = 0; }), KVCK_ERR_INVALID_ARGUMENT);
+  EXPECT_EQ(call([](BlocksCall& c) { c.out_stride = -3; }), KVCK_ERR_INVALID_ARGUMENT);
+  EXPECT_EQ(call([](BlocksCall& c) { c.out_stride = KVCK_MAX_OUT_STRIDE + 1; }), KVCK_ERR_INVALID_ARGUMENT);
+  EXPECT_EQ(call([](BlocksCall& c) { c.out_stride = kI64Max; }), KVCK_ERR_INVALID_ARGUMENT);
+  EXPECT_EQ(call([](BlocksCall& c) { c.out_stride = 0, c.num_reqs = 0; }), KVCK_ERR_INVALID_ARGUMENT);
+  EXPECT_EQ(call([](BlocksCall& c) { c.out_stride = 0, c.direction = KVCK_COPY_SAVE; }), KVCK_ERR_INVALID_ARGUMENT);
+  if (!have_device) EXPECT_EQ(call([](BlocksCall& c) { c.out_stride = KVCK_MAX_OUT_STRIDE; }), KVCK_ERR_NO_DEVICE);
   // request arrays and out aligned to their element size
   EXPECT_EQ(call([](BlocksCall& c) { c.bt_off = 2; }), KVCK_ERR_MISALIGNED);
   EXPECT_EQ(call([](BlocksCall& c) { c.nb_off = 2; }), KVCK_ERR_MISALIGNED);
@@ -219,10 +228,11 @@ void states_checks(bool have_device) {
   const void* ptrs[4] = {kFake, kFake, kFake, kFake};
   const int32_t layers[2] = {1, 3}, base[2] = {0, 0};
   auto call = [&](int nstates = 2, int32_t nrows = 64, int32_t rb = 0, int32_t rc = 64, void* ws = kFake,
-                  size_t ws_bytes = 1 << 20, int32_t num_reqs = 8, int32_t num_slots = 160) {
+                  size_t ws_bytes = 1 << 20, int32_t num_reqs = 8, int32_t num_slots = 160,
+                  int64_t out_stride = 1, void* out = kFake) {
     return kvck_checksum_states(D, nstates, ptrs, layers, base, 2, num_slots, nrows, rb, rc,
-                                static_cast<const int32_t*>(kFake), num_reqs, static_cast<uint64_t*>(kFake), 0, ws,
-                                ws_bytes, nullptr, nullptr);
+                                static_cast<const int32_t*>(kFake), num_reqs, static_cast<uint64_t*>(out), out_stride,
+                                0, ws, ws_bytes, nullptr, nullptr);
   };
   D[1].elem_bytes = 1;
   EXPECT_EQ(call(), KVCK_ERR_UNSUPPORTED);
@@ -237,6 +247,10 @@ void states_checks(bool have_device) {
   EXPECT_EQ(call(2, 64, 0, 64, fake(8)), KVCK_ERR_WORKSPACE);
   EXPECT_EQ(call(2, 64, 0, 64, kFake, 1 << 20, 0), KVCK_OK);
   EXPECT_EQ(call(2, 64, 0, 64, kFake, 1 << 20, -1), KVCK_ERR_INVALID_ARGUMENT);
+  EXPECT_EQ(call(2, 64, 0, 64, kFake, 1 << 20, 8, 160, 0), KVCK_ERR_INVALID_ARGUMENT);
+  EXPECT_EQ(call(2, 64, 0, 64, kFake, 1 << 20, 8, 160, KVCK_MAX_OUT_STRIDE + 1), KVCK_ERR_INVALID_ARGUMENT);
+  EXPECT_EQ(call(2, 64, 0, 64, kFake, 1 << 20, 8, 160, 1, fake(4)), KVCK_ERR_MISALIGNED);
+  if (!have_device) EXPECT_EQ(call(2, 64, 0, 64, kFake, 1 << 20, 8, 160, KVCK_MAX_OUT_STRIDE), KVCK_ERR_NO_DEVICE);
   D[0].slot_stride = kI64Max / 16 * 16;
   EXPECT_EQ(call(), KVCK_ERR_UNSUPPORTED);
   reset();
@@ -261,8 +275,9 @@ void states_checks(bool have_device) {
 
 void tags_checks(bool have_device) {
   auto call = [](const void* cs, const void* h, int64_t stride, int64_t n, const void* nbpr, int32_t mb,
-                 void* tagged, const void* stored, void* mm) {
-    return kvck_tag_checksums(static_cast<const uint64_t*>(cs), static_cast<const uint8_t*>(h), stride, 0x1234, n,
+                 void* tagged, const void* stored, void* mm, int32_t columns = 1) {
+    return kvck_tag_checksums(static_cast<const uint64_t*>(cs), columns, static_cast<const uint8_t*>(h), stride,
+                              0x1234, n,
                               static_cast<const int32_t*>(nbpr), nullptr, mb, 0, static_cast<uint64_t*>(tagged),
                               static_cast<const uint64_t*>(stored), static_cast<uint8_t*>(mm), nullptr, nullptr);
   };
@@ -277,7 +292,18 @@ void tags_checks(bool have_device) {
   EXPECT_EQ(call(kFake, kFake, 32, 16, kFake, 5, kFake, nullptr, nullptr), KVCK_ERR_INVALID_ARGUMENT);
   EXPECT_EQ(call(kFake, kFake, 32, kI64Max, nullptr, 0, kFake, nullptr, nullptr), KVCK_ERR_UNSUPPORTED);
   EXPECT_EQ(call(kFake, kFake, kI64Max / 8 * 8, 16, nullptr, 0, kFake, nullptr, nullptr), KVCK_ERR_UNSUPPORTED);
+  // replica columns summed per entry; uint64 arrays 8-byte aligned
+  EXPECT_EQ(call(kFake, kFake, 32, 16, nullptr, 0, kFake, nullptr, nullptr, 0), KVCK_ERR_INVALID_ARGUMENT);
+  EXPECT_EQ(call(kFake, kFake, 32, 16, nullptr, 0, kFake, nullptr, nullptr, KVCK_MAX_OUT_STRIDE + 1),
+            KVCK_ERR_INVALID_ARGUMENT);
+  EXPECT_EQ(call(kFake, kFake, 32, (int64_t)1 << 40, nullptr, 0, kFake, nullptr, nullptr, 4096),
+            KVCK_ERR_UNSUPPORTED);
+  EXPECT_EQ(call(fake(4), kFake, 32, 16, nullptr, 0, kFake, nullptr, nullptr), KVCK_ERR_MISALIGNED);
+  EXPECT_EQ(call(kFake, kFake, 32, 16, nullptr, 0, fake(4), nullptr, nullptr), KVCK_ERR_MISALIGNED);
+  EXPECT_EQ(call(kFake, kFake, 32, 16, nullptr, 0, nullptr, fake(4), nullptr), KVCK_ERR_MISALIGNED);
   if (!have_device) EXPECT_EQ(call(kFake, kFake, 32, 16, nullptr, 0, kFake, nullptr, nullptr), KVCK_ERR_NO_DEVICE);
+  if (!have_device)
+    EXPECT_EQ(call(kFake, kFake, 32, 16, nullptr, 0, kFake, nullptr, nullptr, KVCK_MAX_OUT_STRIDE), KVCK_ERR_NO_DEVICE);
 }
 
 void noalloc_checks(bool have_device) {
@@ -291,6 +317,7 @@ void noalloc_checks(bool have_device) {
   EXPECT_EQ(call([](BlocksCall& c) { c.out = nullptr; }), KVCK_ERR_INVALID_ARGUMENT);
   EXPECT_EQ(call([](BlocksCall& c) { c.layers = {0, -1}; }), KVCK_ERR_INVALID_ARGUMENT);
   EXPECT_EQ(call([](BlocksCall& c) { c.bt_off = 2; }), KVCK_ERR_MISALIGNED);
+  EXPECT_EQ(call([](BlocksCall& c) { c.out_stride = 0; }), KVCK_ERR_INVALID_ARGUMENT);
   // position records alone past the scratch: 32 bytes per request slot
   EXPECT_EQ(call([](BlocksCall& c) { c.num_reqs = 1100, c.max_blocks = 1024, c.bt_stride = 1024; }),
             KVCK_ERR_SCRATCH);
@@ -300,7 +327,7 @@ void noalloc_checks(bool have_device) {
 }
 
 void misc_checks() {
-  EXPECT_EQ(kvck_abi_version(), 2);
+  EXPECT_EQ(kvck_abi_version(), 3);
   const int32_t codes[] = {KVCK_OK,           KVCK_ERR_INVALID_ARGUMENT, KVCK_ERR_UNSUPPORTED, KVCK_ERR_MISALIGNED,
                            KVCK_ERR_WORKSPACE, KVCK_ERR_HIP,             KVCK_ERR_NO_DEVICE,   KVCK_ERR_SCRATCH,
                            7,                 -1000,                     kI32Max};

@@ -29,7 +29,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(B.EXPORTS) == decl
-    assert kvck.kvck_abi_version() == 2
+    assert kvck.kvck_abi_version() == B.KVCK_ABI_VERSION == 3
     assert kvck.kvck_status_string(-4) == "KVCK_ERR_WORKSPACE"
     assert kvck.kvck_status_string(-7) == "KVCK_ERR_SCRATCH"
     assert kvck.kvck_status_string(7) == "KVCK_UNKNOWN_STATUS"
@@ -55,7 +55,7 @@ def _layout(**kw):
 
 
 def _call(L=None, ncaches=2, layers=(0, 1), bases=(0, 0), head_begin=0, head_count=8, num_reqs=4, max_blocks=8,
-          bt_stride=8, ws_bytes=None, ptr=FAKE, out=FAKE, ws=FAKE):
+          bt_stride=8, ws_bytes=None, ptr=FAKE, out=FAKE, ws=FAKE, out_stride=1):
     lib = kvck.load_library()
     L = L or _layout()
     ptrs = (ctypes.c_void_p * ncaches)(*([ptr] * ncaches))
@@ -63,7 +63,7 @@ def _call(L=None, ncaches=2, layers=(0, 1), bases=(0, 0), head_begin=0, head_cou
     bs = (ctypes.c_int32 * ncaches)(*bases)
     need = lib.kvck_blocks_workspace_bytes(ncaches, num_reqs, max_blocks)
     return lib.kvck_checksum_blocks(ctypes.byref(L), ptrs, ly, bs, ncaches, head_begin, head_count, FAKE, bt_stride,
-                                    FAKE, FAKE, FAKE, num_reqs, max_blocks, out, 0, ws,
+                                    FAKE, FAKE, FAKE, num_reqs, max_blocks, out, out_stride, 0, ws,
                                     need if ws_bytes is None else ws_bytes, None, None)
 
 
@@ -79,6 +79,10 @@ def _call(L=None, ncaches=2, layers=(0, 1), bases=(0, 0), head_begin=0, head_cou
     (dict(ptr=0), -1),
     (dict(out=0), -1),
     (dict(bt_stride=4), -1),
+    (dict(out_stride=0), -1),
+    (dict(out_stride=B.KVCK_MAX_OUT_STRIDE + 1), -1),
+    (dict(out_stride=0, num_reqs=0), -1),
+    (dict(out=FAKE + 4), -3),
     (dict(ws_bytes=64), -4),
     (dict(ws=FAKE + 8), -4),                          # workspace not 256-byte aligned
     (dict(ptr=FAKE + 4, L=_layout(row_bytes=8, slot_stride=8, head_stride=128, block_stride=2048)), -3),
@@ -97,6 +101,8 @@ def test_valid_call_without_gpu_reports_no_device():
     assert _call() == -6
     # any non-negative int32 layer number passes validation (64-bit slice factors)
     assert _call(layers=(40000, 2**31 - 1)) == -6
+    # one replica column of up to KVCK_MAX_OUT_STRIDE
+    assert _call(out_stride=B.KVCK_MAX_OUT_STRIDE) == -6
     assert kvck.kvck_platform_supported() is False
 
 
@@ -109,12 +115,13 @@ def test_states_rejects_before_launch():
     ly = (ctypes.c_int32 * 2)(1, 3)
     base = (ctypes.c_int32 * 2)(0, 0)
 
-    def call(nstates=2, elem=None, rows=(0, 64), nrows=64, ws=FAKE, ws_bytes=1 << 20, num_reqs=8):
+    def call(nstates=2, elem=None, rows=(0, 64), nrows=64, ws=FAKE, ws_bytes=1 << 20, num_reqs=8, out=FAKE,
+             out_stride=1):
         if elem:
             D[1].elem_bytes = elem
         try:
             return lib.kvck_checksum_states(D, nstates, ptrs, ly, base, 2, 160, nrows, rows[0], rows[1], FAKE,
-                                            num_reqs, FAKE, 0, ws, ws_bytes, None, None)
+                                            num_reqs, out, out_stride, 0, ws, ws_bytes, None, None)
         finally:
             D[1].elem_bytes = 2
 
@@ -124,8 +131,11 @@ def test_states_rejects_before_launch():
     assert call(rows=(60, 8)) == -1
     assert call(ws_bytes=8) == -4
     assert call(num_reqs=0) == 0
+    assert call(out_stride=0) == -1
+    assert call(out=FAKE + 4) == -3
     if not torch.cuda.is_available():
         assert call() == -6
+        assert call(out_stride=3) == -6
 
 
 def test_binding_argument_checks():
@@ -154,8 +164,8 @@ def test_tags_rejects_before_launch():
     lib = kvck.load_library()
 
     def call(cs=FAKE, h=FAKE, stride=32, n=16, nbpr=None, mb=0, tagged=FAKE, stored=None, mm=None, cnt=None,
-             sp=None, bs=0):
-        return lib.kvck_tag_checksums(cs, h, stride, 0, n, nbpr, sp, mb, bs, tagged, stored, mm, cnt, None)
+             sp=None, bs=0, columns=1):
+        return lib.kvck_tag_checksums(cs, columns, h, stride, 0, n, nbpr, sp, mb, bs, tagged, stored, mm, cnt, None)
 
     assert call(n=0) == 0
     assert call(n=-1) == -1
@@ -170,8 +180,13 @@ def test_tags_rejects_before_launch():
     assert call(nbpr=FAKE, mb=4, sp=FAKE) == -1  # start positions without a block size
     assert call(nbpr=FAKE + 2, mb=4) == -3       # counts not 4-byte aligned
     assert call(nbpr=FAKE, mb=4, sp=FAKE + 4, bs=16) == -3
+    assert call(columns=0) == -1
+    assert call(columns=B.KVCK_MAX_OUT_STRIDE + 1) == -1
+    assert call(cs=FAKE + 4) == -3               # uint64 arrays 8-byte aligned
+    assert call(tagged=FAKE + 4) == -3
     if not torch.cuda.is_available():
         assert call() == -6
+        assert call(columns=4) == -6
 
 
 def test_noalloc_rejects_before_launch():
@@ -181,16 +196,17 @@ def test_noalloc_rejects_before_launch():
     lib = kvck.load_library()
     L = _layout()
 
-    def call(num_reqs=4, max_blocks=8, out=FAKE, layers=(0, 1)):
+    def call(num_reqs=4, max_blocks=8, out=FAKE, layers=(0, 1), out_stride=1):
         ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
         ly = (ctypes.c_int32 * 2)(*layers)
         bs = (ctypes.c_int32 * 2)(0, 0)
         return lib.kvck_checksum_blocks_noalloc(ctypes.byref(L), ptrs, ly, bs, 2, 0, 8, FAKE, max_blocks, FAKE, FAKE,
-                                                FAKE, num_reqs, max_blocks, out, 0, None, None)
+                                                FAKE, num_reqs, max_blocks, out, out_stride, 0, None, None)
 
     assert call(num_reqs=0) == 0
     assert call(out=0) == -1
     assert call(layers=(0, -1)) == -1
+    assert call(out_stride=0) == -1
     slots = B.KVCK_SCRATCH_BYTES // 32 + 1024
     assert call(num_reqs=slots // 1024, max_blocks=1024) == -7
     if not torch.cuda.is_available():

@@ -12,6 +12,7 @@ import types
 import numpy as np
 import pytest
 
+import oracle
 from oracle import tags
 
 
@@ -49,7 +50,35 @@ def pin_involution_and_detection(t):
     assert t.offload_mismatches(c2, hashes, fp, stored).tolist() == [i == 5 for i in range(64)]
 
 
-TAG_PINS = [pin_little_endian_first_eight_bytes, pin_fingerprint_xor, pin_involution_and_detection]
+def pin_offloaded_row_sum(t):
+    # one column is the value itself; columns add modulo 2^64 over the last axis
+    assert t.offloaded_value(np.array([[5], [2**64 - 1]], np.uint64)).tolist() == [5, 2**64 - 1]
+    assert t.offloaded_value(np.array([[2**63, 2**63, 7], [1, 2, 3]], np.uint64)).tolist() == [7, 6]
+    x = np.arange(24, dtype=np.uint64).reshape(2, 3, 4)
+    assert t.offloaded_value(x).tolist() == [[6, 22, 38], [54, 70, 86]]
+
+
+def pin_offloaded_columns_are_partials_of_one_checksum(t):
+    """Columns over disjoint sets of a group's layers (each set with its own
+    replica key) are partial checksums, which the page says sum to the
+    group's checksum c: their row sum equals the checksum over all layers."""
+    rng = np.random.default_rng(5)
+    bs, heads, hd, nb = 4, 2, 8, 6
+    pools = [rng.integers(0, 2**16, size=(2, nb, bs, heads, hd), dtype=np.uint16) for _ in range(3)]
+    bt = np.array([[3, 1, 4], [0, 5, 2]], np.int32)
+    nblk, sp, nt = np.array([3, 2], np.int32), np.array([0, 7], np.int64), np.array([11, 37], np.int64)
+    layers = [0, 4, 9]
+    full = oracle.checksum_blocks(pools, "NHD", layers, [0] * 3, bt, nblk, sp, nt)
+    cols = [oracle.checksum_blocks(pools[:1], "NHD", layers[:1], [0], bt, nblk, sp, nt),
+            oracle.checksum_blocks(pools[1:], "NHD", layers[1:], [0] * 2, bt, nblk, sp, nt)]
+    got = t.offloaded_value(np.stack(cols, axis=-1))
+    for r in range(2):
+        assert got[r, :nblk[r]].tolist() == full[r, :nblk[r]].tolist()
+        assert got[r, :nblk[r]].tolist() != cols[0][r, :nblk[r]].tolist()
+
+
+TAG_PINS = [pin_little_endian_first_eight_bytes, pin_fingerprint_xor, pin_involution_and_detection,
+            pin_offloaded_row_sum, pin_offloaded_columns_are_partials_of_one_checksum]
 
 
 @pytest.mark.parametrize("pin", TAG_PINS, ids=lambda f: f.__name__)
@@ -69,6 +98,9 @@ MUTATIONS = {
     "stored value is the tag alone": ("np.asarray(checksums, dtype=np.uint64) ^ block_checksum_tags",
                                       "0 * np.asarray(checksums, dtype=np.uint64) ^ block_checksum_tags"),
     "mismatch test inverted": ("!= np.asarray(stored, dtype=np.uint64)", "== np.asarray(stored, dtype=np.uint64)"),
+    "row sum over the first axis": ("v.sum(axis=-1, dtype=np.uint64)", "v.sum(axis=0, dtype=np.uint64)"),
+    "first replica column only": ("v.sum(axis=-1, dtype=np.uint64)", "v[..., 0]"),
+    "row sum cut to 32 bits": ("v.sum(axis=-1, dtype=np.uint64)", "v.sum(axis=-1, dtype=np.uint64) & np.uint64(0xFFFFFFFF)"),
 }
 
 
