@@ -211,3 +211,30 @@ def test_noalloc_rejects_before_launch():
     assert call(num_reqs=slots // 1024, max_blocks=1024) == -7
     if not torch.cuda.is_available():
         assert call() == -6
+
+
+def test_output_stride_of_replica_columns():
+    """The binding's element stride of an output view: 1 for a dense array, C
+    for one column of a row-major (..., C) array; views whose entries are not
+    evenly spaced in row-major order, or too few, are refused."""
+    cpu = torch.device("cpu")
+    values = torch.zeros((4, 6, 3), dtype=torch.uint64)
+    assert B._out_stride(values[..., 0], 24, cpu) == 3
+    assert B._out_stride(values[..., 2], 24, cpu) == 3
+    assert B._out_stride(torch.zeros(24, dtype=torch.int64), 24, cpu) == 1
+    assert B._out_stride(values[:1, :, 1], 6, cpu) == 3       # a single request row
+    assert B._out_stride(values.view(-1)[::5], 10, cpu) == 5
+    with pytest.raises(ValueError):
+        B._out_stride(values[..., 0].t(), 24, cpu)             # column-major walk
+    assert B._out_stride(values[:, ::2, 0], 12, cpu) == 6     # every other position: still evenly spaced
+    with pytest.raises(ValueError):
+        B._out_stride(values[:, 0], 12, cpu)                   # rows 18 apart, entries 1 apart
+    with pytest.raises(ValueError):
+        B._out_stride(values[..., 0], 25, cpu)                 # fewer entries than the call writes
+    with pytest.raises(ValueError):
+        B._out_stride(torch.zeros(1, dtype=torch.int64).expand(8), 8, cpu)  # entries share memory
+    with pytest.raises(ValueError):
+        B._out_stride(values[..., 0].to(torch.int32), 24, cpu)
+    big = torch.zeros((2, B.KVCK_MAX_OUT_STRIDE + 1), dtype=torch.int64)
+    with pytest.raises(ValueError):
+        B._out_stride(big[:, 0], 2, cpu)
