@@ -231,7 +231,10 @@ size_t kvck_blocks_workspace_bytes(int32_t num_caches, int32_t num_reqs, int32_t
  * the workspace.  In its place the call uses a scratch array of
  * KVCK_SCRATCH_BYTES that the library holds on each device it runs on, from
  * the first such call until the process ends.  The call allocates nothing
- * and records no events (instrumentation does not time it).
+ * and records no events (instrumentation does not time it).  Its first call
+ * on a device also looks up that array's device address (a runtime query,
+ * no allocation): make one call on the device before capturing the call
+ * into a HIP graph.
  *
  * It needs the plan's position records (32 bytes per num_reqs*max_blocks
  * slot, plus a few KiB) and, when its caches form more than one task group

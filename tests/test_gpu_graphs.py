@@ -122,3 +122,44 @@ def test_graph_replays_fused_copy(layout):
         assert all(torch.equal(a, b.cpu()) for a, b in zip(got[1], ds2)), rep
         for rr, kk in listed:
             assert got[2][rr, kk] == o2s.cpu().numpy()[rr, kk] == got[3][rr, kk], (rep, rr, kk)
+
+
+@pytest.mark.parametrize("schedule,ncaches", [("default", 3), ("simple", 20)])
+def test_graph_replays_noalloc(schedule, ncaches, monkeypatch):
+    """The allocation-free call captured into a graph, writing one replica
+    column: each replay, after eager changes to the cache, equals an eager
+    kvck_checksum_blocks with its own workspace.  Twenty caches under the
+    simple schedule keep per-group partials in the library's scratch array
+    and reduce them in a second launch; three caches form one group.  A first
+    call outside the capture looks up the scratch array's address."""
+    if schedule != "default":
+        monkeypatch.setenv("KVCK_SCHEDULE", schedule)
+    log(f"[graphs] allocation-free {schedule} caches={ncaches}")
+    rng = np.random.default_rng(42)
+    req, nb = wl.page_requests(rng, [100, 37, 300, 5], 16, start_pos=[0, 1, 0, 0], spare_frac=0.2)
+    layers = list(range(0, 2 * ncaches, 2))
+    pools = [to_device_bits(wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 16, 4, 64), "bf16"))
+             for _ in layers]
+    pc = kvck.prepare_caches(pools, "NHD", layers)
+    bt, nbt, sp, nt = req_tensors(req)
+    values = torch.zeros((req.num_reqs, req.max_blocks, 2), dtype=torch.uint64, device=DEV)
+    col = values[..., 1]
+    kvck.kvck_checksum_blocks_noalloc(pc, None, None, bt, nbt, sp, nt, col)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kvck.kvck_checksum_blocks_noalloc(pc, None, None, bt, nbt, sp, nt, col)
+    listed = req.listed()
+    for rep in range(4):
+        values.view(torch.int64).zero_()
+        r, k = listed[(3 * rep) % len(listed)]
+        b = int(req.block_table[r, k])
+        pools[rep % len(pools)].view(torch.int16)[rep % 2, b, 0, rep % 4, 5] ^= 1 << (rep + 2)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = values.cpu().view(torch.int64).numpy()
+        want = kvck.kvck_checksum_blocks(pc, None, None, bt, nbt, sp, nt).cpu().view(torch.int64).numpy()
+        for rr, kk in listed:
+            assert got[rr, kk, 1] == want[rr, kk], (rep, rr, kk)
+        assert not got[..., 0].any()
