@@ -199,8 +199,9 @@ typedef struct kvck_kv_layout {
  * = "0" (merged rows unpipelined), KVCK_COPY_BUFFERS = "2" (fused copy with
  * two load buffers per wave), KVCK_TCOPY = "regs" (fused copy of
  * element-transposed planes transposed in registers instead of through LDS),
- * KVCK_GRID_PER_CU = n (workgroups per compute unit of every launch, up to
- * what fits).
+ * KVCK_COPY_ORDER = "listing" (fused copy of row layouts visits positions in
+ * listing order instead of grouped by block id), KVCK_GRID_PER_CU = n
+ * (workgroups per compute unit of every launch, up to what fits).
  */
 kvck_status kvck_checksum_blocks(
     const kvck_kv_layout* layout,          /* host */

@@ -507,6 +507,18 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
                             num_reqs, max_blocks, L.block_size, L.num_blocks, out_stride, workspace, error_flags,
                             st) != hipSuccess)
     return KVCK_ERR_HIP;
+  // The fused copy visits positions grouped by block id (KVCK_COPY_ORDER=listing: in listing order;
+  // results are identical either way)
+  int32_t* order = nullptr;
+  if (mode != kModeChecksum && !transposed) {
+    const char* o = getenv("KVCK_COPY_ORDER");
+    if (!o || strcmp(o, "listing") != 0) {
+      order = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) + w.order_off);
+      const PosRecord* recs = reinterpret_cast<const PosRecord*>(static_cast<uint8_t*>(workspace) + w.recs_off);
+      if (launch_order(recs, static_cast<const uint32_t*>(workspace), L.num_blocks, order, st) != hipSuccess)
+        return KVCK_ERR_HIP;
+    }
+  }
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   BlocksArgs a;
@@ -574,6 +586,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
       ca.num_caches_total = num_caches;
       ca.cache_offset = c0;
       ca.block_size = L.block_size;
+      ca.order = order;
       if (transposed) {
         const int grid = tcopy_grid(shp, mode, dev, tasks, L.block_size);
         if (launch_tcopy(ca, shp, mode, grid, st) != hipSuccess) return KVCK_ERR_HIP;

@@ -77,7 +77,9 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
 
   for (int64_t task = wave; task < total; task += nwaves) {
     const int64_t grp = task / n_items;
-    const int64_t item = task - grp * n_items;
+    const int64_t idx = task - grp * n_items;
+    // listed position (staging entry) the task covers, in the visiting order
+    const int64_t item = ca.order ? (int64_t)__builtin_amdgcn_readfirstlane(read_const(ca.order + idx)) : idx;
     const int c_begin = (int)grp * lpt;
     const int c_end = min(a.num_caches, c_begin + lpt);
     const TaskRecord rec = task_record<false>(a, item, false, lane);
@@ -199,6 +201,81 @@ __global__ __launch_bounds__(kBlockThreads) void copy_kernel(const CopyArgs ca) 
   }
 }
 
+// Visiting order of the fused copy: the listed positions grouped by block id
+// (a counting sort into kOrderBins buckets of block ids, in one workgroup, its
+// histogram in 128 KiB of LDS), so the waves resident at any moment touch
+// nearby pool blocks.  The order within a bucket is whatever the atomics give;
+// results never depend on it.  Same-box A/B over the 128-request llama3-shaped
+// batch (73k pool blocks), whole calls: listing order 24.38 ms load / 23.27 ms
+// save; 8192 buckets 24.11 / 22.75; 32768 buckets 23.93 / 22.73 (the sort
+// itself ~0.07 ms).
+constexpr int kOrderBins = 32768;
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderUnroll = 8;
+
+__device__ __forceinline__ uint32_t order_bin(const PosRecord* recs, int64_t i, int shift) {
+  // a negative id (flagged, no valid slots) in the first bucket, one past the pool in the last
+  const int32_t b = recs[i].block;
+  const uint32_t q = (uint32_t)b >> shift;
+  return b < 0 ? 0u : (q < (uint32_t)kOrderBins ? q : (uint32_t)kOrderBins - 1u);
+}
+
+__global__ __launch_bounds__(kOrderThreads) void order_kernel(const PosRecord* __restrict__ recs,
+                                                              const uint32_t* __restrict__ n_items, int shift,
+                                                              int32_t* __restrict__ order) {
+  __shared__ uint32_t hist[kOrderBins];
+  __shared__ uint32_t sums[kOrderThreads];
+  const int tid = threadIdx.x;
+  const int64_t n = (int64_t)*n_items;
+  for (int b = tid; b < kOrderBins; b += kOrderThreads) hist[b] = 0;
+  __syncthreads();
+  constexpr int64_t kStep = (int64_t)kOrderThreads * kOrderUnroll;
+  for (int64_t i0 = 0; i0 < n; i0 += kStep) {
+    uint32_t bin[kOrderUnroll];
+#pragma unroll
+    for (int k = 0; k < kOrderUnroll; ++k) {
+      const int64_t i = i0 + (int64_t)k * kOrderThreads + tid;
+      bin[k] = i < n ? order_bin(recs, i, shift) : kOrderBins;
+    }
+#pragma unroll
+    for (int k = 0; k < kOrderUnroll; ++k)
+      if (bin[k] < kOrderBins) atomicAdd(&hist[bin[k]], 1u);
+  }
+  __syncthreads();
+  // exclusive scan: each thread owns kOrderBins / kOrderThreads consecutive buckets
+  constexpr int kPer = kOrderBins / kOrderThreads;
+  uint32_t own = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) own += hist[tid * kPer + j];
+  sums[tid] = own;
+  __syncthreads();
+  for (int o = 1; o < kOrderThreads; o <<= 1) {
+    const uint32_t t = tid >= o ? sums[tid - o] : 0u;
+    __syncthreads();
+    sums[tid] += t;
+    __syncthreads();
+  }
+  uint32_t run = sums[tid] - own;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const uint32_t c = hist[tid * kPer + j];
+    hist[tid * kPer + j] = run;
+    run += c;
+  }
+  __syncthreads();
+  for (int64_t i0 = 0; i0 < n; i0 += kStep) {
+    uint32_t bin[kOrderUnroll];
+#pragma unroll
+    for (int k = 0; k < kOrderUnroll; ++k) {
+      const int64_t i = i0 + (int64_t)k * kOrderThreads + tid;
+      bin[k] = i < n ? order_bin(recs, i, shift) : kOrderBins;
+    }
+#pragma unroll
+    for (int k = 0; k < kOrderUnroll; ++k)
+      if (bin[k] < kOrderBins) order[atomicAdd(&hist[bin[k]], 1u)] = (int32_t)(i0 + (int64_t)k * kOrderThreads + tid);
+  }
+}
+
 using CopyFn = void (*)(const CopyArgs);
 
 template <int CHUNK, int S, int PU, int DIR, bool MERGED>
@@ -246,6 +323,15 @@ int copy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tas
   const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
   const int64_t cap = (int64_t)per_cu * cus;
   return (int)(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
+hipError_t launch_order(const PosRecord* recs, const uint32_t* n_items, int64_t num_blocks, int32_t* order,
+                        hipStream_t stream) {
+  // bucket = block >> shift, with every block id of the pool below kOrderBins << shift
+  int shift = 0;
+  while (shift < 31 && ((num_blocks - 1) >> shift) >= kOrderBins) ++shift;
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, recs, n_items, shift, order);
+  return hipGetLastError();
 }
 
 hipError_t launch_copy(const CopyArgs& a, const BlocksShape& shp, int direction, int grid, hipStream_t stream) {

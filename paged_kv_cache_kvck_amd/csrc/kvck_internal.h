@@ -40,16 +40,17 @@ struct alignas(16) PosRecord {
 static_assert(sizeof(PosRecord) == 32, "record is 32 bytes");
 
 // Workspace of kvck_checksum_blocks:
-//   [header 256 B: uint32 n_items] [prefix int32 x (R+1)] [records] [partials]
+//   [header 256 B: uint32 n_items] [prefix int32 x (R+1)] [records] [partials] [order int32 x R*max_blocks]
 struct BlocksWorkspace {
-  size_t prefix_off, recs_off, partials_off, total;
+  size_t prefix_off, recs_off, partials_off, order_off, total;
   static BlocksWorkspace make(int32_t num_caches, int32_t num_reqs, int32_t max_blocks) {
     BlocksWorkspace w;
     const size_t items = (size_t)num_reqs * (size_t)max_blocks;
     w.prefix_off = kAlign;
     w.recs_off = w.prefix_off + align_up(sizeof(int32_t) * ((size_t)num_reqs + 1));
     w.partials_off = w.recs_off + align_up(sizeof(PosRecord) * items);
-    w.total = w.partials_off + (num_caches > 1 ? align_up(sizeof(uint64_t) * items * (size_t)num_caches) : 0);
+    w.order_off = w.partials_off + (num_caches > 1 ? align_up(sizeof(uint64_t) * items * (size_t)num_caches) : 0);
+    w.total = w.order_off + align_up(sizeof(int32_t) * items);  // the fused copy's visiting order
     return w;
   }
 };
@@ -101,6 +102,7 @@ struct CopyArgs {
   int32_t num_caches_total;  // caches of the call (images per entry)
   int32_t cache_offset;      // global index of this launch's first cache
   int32_t block_size;
+  const int32_t* order;      // listed positions in visiting order (null: listing order)
 };
 
 struct StatesArgs {
@@ -155,6 +157,8 @@ hipError_t launch_states(const StatesArgs& a, int grid, hipStream_t stream);
 hipError_t launch_tblocks(const BlocksArgs& a, const BlocksShape& shp, int grid, hipStream_t stream);
 int tblocks_grid(const BlocksShape& shp, int device, int64_t max_tasks);
 hipError_t launch_copy(const CopyArgs& a, const BlocksShape& shp, int direction, int grid, hipStream_t stream);
+hipError_t launch_order(const PosRecord* recs, const uint32_t* n_items, int64_t num_blocks, int32_t* order,
+                        hipStream_t stream);
 int copy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks);
 hipError_t launch_tcopy(const CopyArgs& a, const BlocksShape& shp, int direction, int grid, hipStream_t stream);
 int tcopy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks, int32_t block_size);

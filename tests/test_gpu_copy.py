@@ -57,15 +57,20 @@ def _expected_images(pools, layout, req, head_begin, head_count, bs, row_bytes):
     return img
 
 
-@pytest.fixture(params=["1", "2", "1-merge0", "2-merge1"])
+@pytest.fixture(params=["1", "2", "1-merge0", "2-merge1", "1-listing"])
 def copy_buffers(request, monkeypatch):
     """Run the test with one unit buffer per wave and with two
     (KVCK_COPY_BUFFERS), under the library's choice of reading a slot's heads as
-    one row, and with that choice forced off or on (KVCK_MERGE_HEADS)."""
-    buffers, _, merge = request.param.partition("-merge")
+    one row, with that choice forced off or on (KVCK_MERGE_HEADS), and with
+    positions visited in listing order instead of grouped by block id
+    (KVCK_COPY_ORDER)."""
+    buffers, *flags = request.param.split("-")
     monkeypatch.setenv("KVCK_COPY_BUFFERS", buffers)
-    if merge:
-        monkeypatch.setenv("KVCK_MERGE_HEADS", merge)
+    for f in flags:
+        if f.startswith("merge"):
+            monkeypatch.setenv("KVCK_MERGE_HEADS", f[len("merge"):])
+        elif f == "listing":
+            monkeypatch.setenv("KVCK_COPY_ORDER", "listing")
     return request.param
 
 
@@ -245,3 +250,51 @@ def test_copy_element_transposed_many_caches():
                                   req.num_tokens)
     for r, k in req.listed():
         assert int(got_t[r, k]) == int(got_h[r, k]) == int(want[r, k]), (r, k)
+
+
+def test_copy_order_over_a_large_pool(monkeypatch):
+    """Visiting positions grouped by block id over a pool of more than 32768
+    blocks (several ids per bucket), with ids at both ends of the pool and an
+    id past the pool at a position with valid slots:
+    save and load give the same staging bytes, destination pool, checksums
+    and error bits as listing order, and the checksums equal the oracle's
+    (the bad id's position contributes nothing and is flagged)."""
+    log("[copy] visiting order, large pool")
+    rng = np.random.default_rng(61)
+    nb_pool = 70001
+    lengths = rng.integers(1, 65, size=300)
+    req, nb = wl.page_requests(rng, lengths, 16, pool_blocks=nb_pool)
+    tab = req.block_table
+    tab[0, 0] = 0
+    tab[1, 0] = nb_pool - 1
+    tab[4, 0] = nb_pool                             # past the pool, valid slots: flagged, contributes 0
+    layers = [1, 2]
+    hp = [wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 16, 2, 16), "bf16") for _ in layers]
+    pools = [to_device_bits(p) for p in hp]
+    bt, nbt, sp, nt = req_tensors(req)
+    per = kvck.kvck_staging_bytes(pools[0], "NHD", len(layers))
+    n_entries = int(req.num_blocks.sum())
+    res = {}
+    for order in ("grouped", "listing"):
+        if order == "listing":
+            monkeypatch.setenv("KVCK_COPY_ORDER", "listing")
+        staging = torch.zeros(n_entries * per, dtype=torch.uint8, device=DEV)
+        flags = torch.zeros(1, dtype=torch.int32, device=DEV)
+        saved = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, pools, "NHD", layers, bt, nbt, sp, nt, staging,
+                                               error_flags=flags)
+        dst = [torch.zeros_like(p) for p in pools]
+        loaded = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_LOAD, dst, "NHD", layers, bt, nbt, sp, nt, staging,
+                                                error_flags=flags)
+        torch.cuda.synchronize()
+        res[order] = (saved.cpu().numpy().copy(), loaded.cpu().numpy().copy(), staging.cpu(), [d.cpu() for d in dst],
+                      int(flags.item()))
+    a, b = res["grouped"], res["listing"]
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert torch.equal(a[2], b[2]) and all(torch.equal(x, y) for x, y in zip(a[3], b[3]))
+    assert a[4] == b[4] == kvck.KVCK_FLAG_BAD_BLOCK_ID
+    good = tab.copy()
+    good[4, 0] = 0
+    want = oracle.checksum_blocks(hp, "NHD", layers, [0, 0], good, req.num_blocks, req.start_pos, req.num_tokens)
+    for r, k in req.listed():
+        expect = 0 if (r, k) == (4, 0) else int(want[r, k])
+        assert int(a[0][r, k]) == expect == int(a[1][r, k]), (r, k)
