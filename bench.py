@@ -409,12 +409,15 @@ def config_rows(names, dev, calls=10, n_check=200):
 
 def config_rows_isolated(names, calls=10, n_check=200, timeout=300):
     """Each configuration row in a child process of its own (``bench.py
-    --only NAME``), started after this process has freed its pools.  Pool
-    placement follows the process's allocation history: the same hybrid
-    attention pools read at 87.6 % of 8 TB/s as a process's first allocation
-    and at 81.7-84.8 % after other pool sets had come and gone, so every row
-    is measured as a first allocation, like the headline.  A row whose child
-    fails is reported with its error."""
+    --only NAME``), before the headline allocates anything.  Pool placement
+    follows the allocation history.  The same hybrid attention pools read at
+    87.6 % of 8 TB/s as a process's first allocation, and at 81.7-84.8 % after
+    other pool sets had come and gone in that process, so every row is
+    measured as a first allocation, like the headline.  The device's history
+    counts too: right after a process has held the headline's 154 GB, every
+    row, and the headline itself, read 1-6 points lower (hybrid attention
+    84.6 %, headline 83.4 %).  With the rows run first, the same box read
+    87.6 % and 86.9 %.  A row whose child fails is reported with its error."""
     import subprocess
     rows = []
     for n in names:
@@ -468,6 +471,8 @@ def main(argv=None):
     ap.add_argument("--no-small", action="store_true", help="skip the tiny-call latency timing")
     ap.add_argument("--no-configs", action="store_true", help="skip the other configurations' rows")
     ap.add_argument("--only", default="", help="comma-separated configuration rows to run alone (no headline)")
+    ap.add_argument("--configs-after", action="store_true",
+                    help="run the configuration rows' child processes after the headline instead of before it")
     ap.add_argument("--config-calls", type=int, default=10, help="timed calls per configuration row")
     ap.add_argument("--config-warmup-ms", type=float, default=WARMUP_MS,
                     help="untimed calls before a row's timed ones: two, then about this many ms more (0: two)")
@@ -496,6 +501,11 @@ def main(argv=None):
         print(json.dumps(res), flush=True)
         return 0
 
+    # The configuration rows run first, each in a child process, before this
+    # process allocates anything: see config_rows_isolated.
+    early_rows = None
+    if not args.configs_after and not args.no_configs:
+        early_rows = config_rows_isolated(CONFIG_NAMES, args.config_calls, args.oracle_positions)
     w, desc = make_workload(args.workload)
     print(f"[bench] building {args.workload}: pools {w.shape} x {w.num_layers}", file=sys.stderr, flush=True)
     pools = w.device_pools()
@@ -649,7 +659,8 @@ def main(argv=None):
     torch.cuda.empty_cache()
 
     if not args.no_configs:
-        configs += config_rows_isolated(CONFIG_NAMES, args.config_calls, args.oracle_positions)
+        configs += early_rows if early_rows is not None else config_rows_isolated(CONFIG_NAMES, args.config_calls,
+                                                                                  args.oracle_positions)
     if configs:
         extra["configs"] = configs
     if not args.no_small:
