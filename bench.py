@@ -243,7 +243,9 @@ def _timed_main_pass(call, calls, warmup_ms=None):
     """Median and minimum main-pass milliseconds over ``calls`` calls, each
     read from the library's own HIP events, after untimed calls: two, then
     more until about ``warmup_ms`` of them have run (the first pass over
-    freshly written pools reads several points slower than later ones)."""
+    freshly written pools reads several points slower than later ones).
+    Also returns the number of untimed calls, so that a kernel trace of the
+    run can leave them out."""
     import torch
     import paged_kv_cache_kvck_amd as kvck
     warmup_ms = WARMUP_MS if warmup_ms is None else warmup_ms
@@ -266,14 +268,17 @@ def _timed_main_pass(call, calls, warmup_ms=None):
             ts.append(ms / max(c, 1))
     finally:
         kvck.kvck_instrument(False)
-    return statistics.median(ts), min(ts)
+    return statistics.median(ts), min(ts), 2 + extra
 
 
-def _row(name, desc, valid, med, mn, checked, mism):
+def _row(name, desc, valid, med, mn, checked, mism, untimed=None):
     gbs = valid / (med * 1e-3) / 1e9
-    return {"config": name, "workload": desc, "valid_bytes": valid, "main_pass_ms": med, "main_pass_ms_min": mn,
-            "GB_per_s": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "oracle_checked_positions": checked,
-            "oracle_mismatches": mism}
+    row = {"config": name, "workload": desc, "valid_bytes": valid, "main_pass_ms": med, "main_pass_ms_min": mn,
+           "GB_per_s": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS, "oracle_checked_positions": checked,
+           "oracle_mismatches": mism}
+    if untimed is not None:
+        row["untimed_calls"] = untimed
+    return row
 
 
 def _blocks_row(dev, name, desc, pools, layout, layers, req, valid, calls, n_check, seed, bases=None, head_begin=0,
@@ -289,14 +294,14 @@ def _blocks_row(dev, name, desc, pools, layout, layers, req, valid, calls, n_che
     bases = [head_begin] * len(pools) if bases is None else list(bases)
     pc = kvck.prepare_caches(pools, layout, layers, global_head_base=bases, head_begin=head_begin,
                              head_count=head_count)
-    med, mn = _timed_main_pass(lambda: kvck.kvck_checksum_blocks(pc, None, None, bt, nb, sp, nt, out=out,
-                                                                 workspace=ws), calls)
+    med, mn, untimed = _timed_main_pass(lambda: kvck.kvck_checksum_blocks(pc, None, None, bt, nb, sp, nt, out=out,
+                                                                          workspace=ws), calls)
     got = out.cpu().numpy().view(np.uint64)
     checked, mism = (0, 0)
     if n_check:
         checked, mism = oracle_check(pools, layout, layers, bases, req, got, sample_positions(req, n_check, seed),
                                      head_begin, head_count)
-    row = _row(name, desc, valid, med, mn, checked, mism)
+    row = _row(name, desc, valid, med, mn, checked, mism, untimed)
     print(f"[config] {name:14s} {valid / 1e9:7.2f} GB {med:8.3f} ms {row['GB_per_s']:8.1f} GB/s "
           f"{row['frac_of_hbm_peak'] * 100:5.1f} %  oracle {checked} positions, {mism} mismatches",
           file=sys.stderr, flush=True)
@@ -376,8 +381,8 @@ def config_row(name, dev, calls=10, n_check=200):
         sws = torch.empty(max(256, kvck.kvck_states_workspace_bytes(len(mamba.layer_numbers), mamba.rows_used,
                                                                     len(mamba.slot_ids))), dtype=torch.uint8,
                           device=dev)
-        med, mn = _timed_main_pass(lambda: kvck.kvck_checksum_states(states, mamba.layer_numbers, sid, out=sout,
-                                                                     workspace=sws), calls)
+        med, mn, untimed = _timed_main_pass(lambda: kvck.kvck_checksum_states(states, mamba.layer_numbers, sid,
+                                                                              out=sout, workspace=sws), calls)
         got = sout.cpu().numpy().view(np.uint64)
         # every request (its position 0), from host copies of its slot in every state
         mism = 0
@@ -389,7 +394,8 @@ def config_row(name, dev, calls=10, n_check=200):
             want = oracle.checksum_states(host, mamba.layer_numbers, mamba.bases, np.arange(len(rs)))
             mism += int(np.sum(got[rs] != want))
         row = _row(name, "hybrid model Mamba group: 24 layers (numbers 1,3,..,47) x 128 requests x 64 rows of fp32 "
-                         "SSM [128x16] + fp16 conv [4x256] state, position 0", mamba.valid_bytes(), med, mn, R, mism)
+                         "SSM [128x16] + fp16 conv [4x256] state, position 0", mamba.valid_bytes(), med, mn, R, mism,
+                   untimed)
         print(f"[config] {name:14s} {row['valid_bytes'] / 1e9:7.2f} GB {med:8.3f} ms {row['GB_per_s']:8.1f} GB/s "
               f"{row['frac_of_hbm_peak'] * 100:5.1f} %  oracle {R} requests, {mism} mismatches",
               file=sys.stderr, flush=True)
