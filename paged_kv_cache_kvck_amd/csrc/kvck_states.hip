@@ -39,7 +39,11 @@ __device__ __forceinline__ uint64_t chunk_u16(u32x4 x, uint32_t u) {
   return (uint64_t)X * u + 2ull * Y;
 }
 
-constexpr int kUnroll = 8;
+// Loads in flight per lane per batch.  Same-box interleaved A/B on the hybrid
+// model's 24 Mamba layers (2.01 GB): 2 loads (128 chunks, a whole fp16 conv
+// row) read 0.8-1.3 points of 8 TB/s faster than 8, and 1 or 4 were slower;
+// fewer registers leave room for more resident waves.
+constexpr int kUnroll = 2;
 
 __global__ __launch_bounds__(kBlockThreads) void states_kernel(const StatesArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
