@@ -11,12 +11,15 @@
 // holding only the valid slots of the position (slots at or past num_tokens
 // are neither read nor written, on either side).
 //
-// The kernel is the pipelined main pass with a second lane table for the
-// staging side: unit i+1's loads are in flight while unit i is stored to the
-// other side and folded into the checksum.  MERGED: pools whose heads sit side
-// by side in a slot with short rows are walked as one row per slot (as in the
-// checksum pass), and each lane chunk's staging offset lands in its own head's
-// image rows.
+// The kernel keeps the main pass's task structure, with a second lane table
+// for the staging side: each unit is loaded from one side, stored to the other
+// and folded into the checksum.  By default a wave holds one unit buffer (more
+// resident waves keep more stores in flight); the ping-pong variant (PIPE)
+// keeps unit i+1's loads in flight while unit i is stored.  Positions are
+// visited grouped by block id (order_kernel below).  MERGED: pools whose heads
+// sit side by side in a slot with short rows are walked as one row per slot
+// (as in the checksum pass), and each lane chunk's staging offset lands in its
+// own head's image rows.
 #include "kvck_device.h"
 
 namespace kvck {
