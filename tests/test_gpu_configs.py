@@ -67,6 +67,62 @@ def test_llama3_8b_shaped_full_and_tp_shard():
     _free()
 
 
+
+def test_llama3_8b_fused_copy_full():
+    """The fused save and load in the benchmark's configuration: the llama3-shaped
+    pools (32 layers), the first 128 requests, positions visited grouped by block
+    id.  The save's checksums equal the checksum call's at every position and the
+    oracle's at sampled ones; sampled staging entries hold the pool rows of their
+    valid slots; a load into the zeroed pools restores the sampled blocks' valid
+    slots and gives the same checksums."""
+    w = wl.llama3_8b()
+    log(f"[llama3 copy] pools {w.shape} x {w.num_layers}")
+    pools = w.device_pools()
+    r0 = w.req
+    half = r0.num_reqs // 2
+    req = wl.Requests(r0.block_size, r0.num_tokens[:half].copy(), r0.start_pos[:half].copy(),
+                      r0.num_blocks[:half].copy(), np.ascontiguousarray(r0.block_table[:half]))
+    bt, nbt, sp, nt = (torch.from_numpy(x).to(DEV) for x in (req.block_table, req.num_blocks, req.start_pos,
+                                                             req.num_tokens))
+    per = kvck.kvck_staging_bytes(pools[0], w.layout, w.num_layers)
+    entries = int(req.num_blocks.sum())
+    staging = torch.empty(entries * per, dtype=torch.uint8, device=DEV)
+    saved = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, pools, w.layout, w.layer_numbers, bt, nbt, sp, nt,
+                                           staging, check=True).cpu().numpy()
+    ref = gpu_blocks(pools, w.layout, w.layer_numbers, req)
+    for r, k in req.listed():
+        assert saved[r, k] == ref[r, k], (r, k)
+    pos = sample_positions(req, 32, seed=12)
+    assert_match(saved, oracle_at(pools, w.layout, w.layer_numbers, req, pos), "llama3 save")
+    # staging images of sampled positions: [plane][head][slot][row] per cache, valid slots only
+    first = np.concatenate([[0], np.cumsum(req.num_blocks.astype(np.int64))])
+    img = per // w.num_layers
+    bs, nh, rb = req.block_size, w.num_heads, w.head_size * 2
+    kept = {}
+    for r, k in pos:
+        e = int(first[r]) + k
+        b = int(req.block_table[r, k])
+        v = oracle.num_valid_tokens(int(req.start_pos[r]) + k, bs, int(req.num_tokens[r]))
+        blocks = [to_host_bits(p[:, b]).view(np.uint8).reshape(2, nh, bs, rb) for p in pools]
+        kept[(r, k)] = (b, v, blocks)
+        ent = staging[e * per:(e + 1) * per].cpu().numpy().reshape(w.num_layers, 2, nh, bs, rb)
+        for c in range(w.num_layers):
+            assert np.array_equal(ent[c][:, :, :v], blocks[c][:, :, :v]), (r, k, c)
+    # load into the zeroed pools
+    for p in pools:
+        p.zero_()
+    loaded = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_LOAD, pools, w.layout, w.layer_numbers, bt, nbt, sp, nt,
+                                            staging, check=True).cpu().numpy()
+    for r, k in req.listed():
+        assert loaded[r, k] == saved[r, k], (r, k)
+    for (r, k), (b, v, blocks) in kept.items():
+        for c, p in enumerate(pools):
+            back = to_host_bits(p[:, b]).view(np.uint8).reshape(2, nh, bs, rb)
+            assert np.array_equal(back[:, :, :v], blocks[c][:, :, :v]), (r, k, c)
+            assert not back[:, :, v:].any(), (r, k, c)
+    del pools, staging
+    _free()
+
 def test_invariance_set():
     """Config-2 tokens re-paged at block size 64, in HND, as fp8 bits, and an
     MLA 61 x 576 latent cache: per-request sums agree across block sizes and
