@@ -84,11 +84,18 @@ def test_blocks_fill_one_replica_column(case, col, monkeypatch):
                                   req.num_tokens)
     values = _values((req.num_reqs, req.max_blocks))
     bt, nbt, sp, nt = req_tensors(req)
-    got = kvck.kvck_checksum_blocks([to_device_bits(p) for p in host], layout, layers, bt, nbt, sp, nt,
-                                    global_head_base=bases, out=values[..., col], check=True)
+    dev_pools = [to_device_bits(p) for p in host]
+    got = kvck.kvck_checksum_blocks(dev_pools, layout, layers, bt, nbt, sp, nt, global_head_base=bases,
+                                    out=values[..., col], check=True)
     assert got.data_ptr() == values[..., col].data_ptr()
     torch.cuda.synchronize()
     _check_column(values, col, req, want)
+    # accumulate into the same column: every listed entry doubles, nothing else moves
+    kvck.kvck_checksum_blocks(dev_pools, layout, layers, bt, nbt, sp, nt, global_head_base=bases,
+                              out=values[..., col], accumulate=True, check=True)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore"):
+        _check_column(values, col, req, want * np.uint64(2))
 
 
 def test_transposed_planes_fill_one_replica_column(monkeypatch):
