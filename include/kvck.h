@@ -196,8 +196,9 @@ typedef struct kvck_kv_layout {
  * Other switches, read at each call, that change how the work is done but
  * never the results: KVCK_MERGE_HEADS = "0" / "1" (read a slot's heads as one
  * row: automatic for rows under 128 bytes and single heads), KVCK_MERGED_PIPE
- * = "0" (merged rows unpipelined), KVCK_COPY_BUFFERS = "2" (fused copy with
- * two load buffers per wave), KVCK_TCOPY = "regs" (fused copy of
+ * = "0" (merged rows unpipelined), KVCK_COPY_BUFFERS = "1" / "2" (fused copy
+ * with one or two load buffers per wave; the default is two for a save, one
+ * for a load), KVCK_TCOPY = "regs" (fused copy of
  * element-transposed planes transposed in registers instead of through LDS),
  * KVCK_COPY_ORDER = "listing" (fused copy of row layouts visits positions in
  * listing order instead of grouped by block id), KVCK_GRID_PER_CU = n

@@ -152,7 +152,7 @@ bool merged_pipe_off() {
 }
 
 void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_caches, int64_t max_items,
-                     int64_t block_bytes, int planes, int heads, int cus, bool copy, bool dense) {
+                     int64_t block_bytes, int planes, int heads, int cus, bool copy, bool dense, bool save) {
   const int64_t waves = (int64_t)cus * 4 * kMainWorkgroupsPerCU;  // resident waves of the main pass
   int lpt = 1;
   while (lpt < kPipeMaxCaches && (int64_t)(2 * lpt) * block_bytes <= kPipeTaskBytes) lpt *= 2;
@@ -184,10 +184,15 @@ void choose_schedule(BlocksShape* shp, const BlocksShape* narrow, int32_t num_ca
   }
   if (merged_pipe_off() && shp->merged && !copy) pipe = false;
   if (copy) {
-    // One unit buffer per wave: twice the resident waves of the ping-pong
-    // kernel, which keeps more stores in flight (A/B on one GPU: load 5.6 ->
-    // 5.9 TB/s read+write, save unchanged).  KVCK_COPY_BUFFERS=2 selects the
-    // ping-pong kernel (results are identical).
+    // A load keeps one unit buffer per wave, as many waves as fit: its stores
+    // into pool blocks gain from more waves in flight (same-box A/B, llama3-
+    // shaped batch: the ping-pong kernel 23.8 -> 24.4 ms at all that fit, 26.2
+    // at one workgroup per CU).  A save runs the ping-pong kernel at one
+    // workgroup per CU (copy_grid): 22.66 -> 22.42 ms on the same batch, and
+    // on 64-request batches +0.4 % (GPT-2-shaped fp16), +0.5 % (MLA) and
+    // +8.3 % (fp8 64-byte merged rows).  KVCK_COPY_BUFFERS=1|2 forces one or
+    // the other (results are identical).
+    shp->copy_buffers = save ? 2 : 1;
     if (const char* b = getenv("KVCK_COPY_BUFFERS")) shp->copy_buffers = b[0] == '2' ? 2 : 1;
   }
   if (copy) pipe = true;  // the fused copy kernel always runs the pipelined structure
@@ -488,7 +493,7 @@ kvck_status blocks_call(int mode, const kvck_kv_layout* layout, const void* cons
   if (const char* force = getenv("KVCK_PLAN"))
     if (strcmp(force, "compact") == 0) dense = false;
   choose_schedule(&shp, has_narrow ? &narrow : nullptr, num_caches, max_items, image_bytes, planes_cov, head_count,
-                  cus, mode != kModeChecksum, dense);
+                  cus, mode != kModeChecksum, dense, mode == KVCK_COPY_SAVE);
   shp.dense = dense;
   const int32_t lpt = shp.caches_per_task;
   const int32_t total_groups = (num_caches + lpt - 1) / lpt;

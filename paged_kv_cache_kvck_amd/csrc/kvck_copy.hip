@@ -13,13 +13,13 @@
 //
 // The kernel keeps the main pass's task structure, with a second lane table
 // for the staging side: each unit is loaded from one side, stored to the other
-// and folded into the checksum.  By default a wave holds one unit buffer (more
-// resident waves keep more stores in flight); the ping-pong variant (PIPE)
-// keeps unit i+1's loads in flight while unit i is stored.  Positions are
-// visited grouped by block id (order_kernel below).  MERGED: pools whose heads
-// sit side by side in a slot with short rows are walked as one row per slot
-// (as in the checksum pass), and each lane chunk's staging offset lands in its
-// own head's image rows.
+// and folded into the checksum.  For a load a wave holds one unit buffer (more
+// resident waves keep more stores in flight); a save runs the ping-pong
+// variant (PIPE), which keeps unit i+1's loads in flight while unit i is
+// stored, at one workgroup per CU.  Positions are visited grouped by block id
+// (order_kernel below).  MERGED: pools whose heads sit side by side in a slot
+// with short rows are walked as one row per slot (as in the checksum pass),
+// and each lane chunk's staging offset lands in its own head's image rows.
 #include "kvck_device.h"
 
 namespace kvck {
@@ -320,7 +320,9 @@ CopyFn copy_fn(const BlocksShape& shp, int direction) {
 int copy_grid(const BlocksShape& shp, int direction, int device, int64_t max_tasks) {
   CopyFn fn = copy_fn(shp, direction);
   const int fits = fn ? kernel_occupancy(reinterpret_cast<const void*>(fn), device, 1) : 1;
-  const int per_cu = workgroups_per_cu(fits, kAllThatFit);
+  // the save's ping-pong kernel at one workgroup per CU; otherwise as many as fit
+  const int per_cu = workgroups_per_cu(
+      fits, shp.copy_buffers == 2 && direction == KVCK_COPY_SAVE ? kMainWorkgroupsPerCU : kAllThatFit);
   const int cus = device_cus(device);
   const int64_t waves_per_block = kBlockThreads / kWave;
   const int64_t need = (max_tasks + waves_per_block - 1) / waves_per_block;
