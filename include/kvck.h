@@ -200,8 +200,9 @@ typedef struct kvck_kv_layout {
  * with one or two load buffers per wave; the default is two for a save, one
  * for a load), KVCK_TCOPY = "regs" (fused copy of
  * element-transposed planes transposed in registers instead of through LDS),
- * KVCK_COPY_ORDER = "listing" (fused copy of row layouts visits positions in
- * listing order instead of grouped by block id), KVCK_GRID_PER_CU = n
+ * KVCK_COPY_ORDER = "listing" / "grouped" (fused copy of row layouts visits
+ * positions in listing order, or grouped by block id; by default grouped when
+ * each cache's pool spans at least 2 GiB), KVCK_GRID_PER_CU = n
  * (workgroups per compute unit of every launch, up to what fits).
  */
 kvck_status kvck_checksum_blocks(

@@ -57,20 +57,20 @@ def _expected_images(pools, layout, req, head_begin, head_count, bs, row_bytes):
     return img
 
 
-@pytest.fixture(params=["1", "2", "1-merge0", "2-merge1", "1-listing"])
+@pytest.fixture(params=["1", "2", "1-merge0", "2-merge1", "1-grouped", "2-grouped"])
 def copy_buffers(request, monkeypatch):
     """Run the test with one unit buffer per wave and with two
     (KVCK_COPY_BUFFERS), under the library's choice of reading a slot's heads as
     one row, with that choice forced off or on (KVCK_MERGE_HEADS), and with
-    positions visited in listing order instead of grouped by block id
-    (KVCK_COPY_ORDER)."""
+    positions visited grouped by block id instead of in listing order (forced
+    with KVCK_COPY_ORDER: these small pools take listing order by default)."""
     buffers, *flags = request.param.split("-")
     monkeypatch.setenv("KVCK_COPY_BUFFERS", buffers)
     for f in flags:
         if f.startswith("merge"):
             monkeypatch.setenv("KVCK_MERGE_HEADS", f[len("merge"):])
-        elif f == "listing":
-            monkeypatch.setenv("KVCK_COPY_ORDER", "listing")
+        elif f == "grouped":
+            monkeypatch.setenv("KVCK_COPY_ORDER", "grouped")
     return request.param
 
 
@@ -276,8 +276,7 @@ def test_copy_order_over_a_large_pool(monkeypatch):
     n_entries = int(req.num_blocks.sum())
     res = {}
     for order in ("grouped", "listing"):
-        if order == "listing":
-            monkeypatch.setenv("KVCK_COPY_ORDER", "listing")
+        monkeypatch.setenv("KVCK_COPY_ORDER", order)
         staging = torch.zeros(n_entries * per, dtype=torch.uint8, device=DEV)
         flags = torch.zeros(1, dtype=torch.int32, device=DEV)
         saved = kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, pools, "NHD", layers, bt, nbt, sp, nt, staging,

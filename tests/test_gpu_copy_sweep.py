@@ -41,8 +41,9 @@ def _case(i):
     hc = int(rng.integers(1, heads - hb + 1))
     buffers = ["1", "2"][int(rng.integers(0, 2))]
     merge = [None, "0", "1"][int(rng.integers(0, 3))]   # a slot's heads read as one row: auto, off, on
+    order = ["listing", "grouped"][i % 2]               # positions in listing order or grouped by block id
     return dict(i=i, layout=layout, elem=elem, heads=heads, d=d, bs=bs, layers=layers, lengths=lengths,
-                start=start, extra=extra, hb=hb, hc=hc, buffers=buffers, merge=merge)
+                start=start, extra=extra, hb=hb, hc=hc, buffers=buffers, merge=merge, order=order)
 
 
 CASES = [_case(i) for i in range(120)]
@@ -50,7 +51,7 @@ CASES = [_case(i) for i in range(120)]
 
 def _ids(c):
     return (f"{c['i']}-{c['layout']}-{c['elem']}-h{c['heads']}-d{c['d']}-bs{c['bs']}-b{c['buffers']}"
-            f"-m{c['merge'] or 'auto'}")
+            f"-m{c['merge'] or 'auto'}-{c['order']}")
 
 
 def _rows(pool, layout, pl, b, v, hb, n):
@@ -85,6 +86,7 @@ def _images(pools, layout, req, hb, n, bs, row_bytes):
 @pytest.mark.parametrize("case", CASES, ids=_ids)
 def test_copy_sweep_case(case, monkeypatch):
     monkeypatch.setenv("KVCK_COPY_BUFFERS", case["buffers"])
+    monkeypatch.setenv("KVCK_COPY_ORDER", case["order"])
     if case["merge"] is not None:
         monkeypatch.setenv("KVCK_MERGE_HEADS", case["merge"])
     log(f"[copy sweep] {_ids(case)} heads {case['hb']}+{case['hc']}")
