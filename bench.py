@@ -692,11 +692,26 @@ def main(argv=None):
                 lat.append(t0.elapsed_time(t1) * 1e3)
         got = tout.cpu().numpy().view("uint64")
         checked, mism = oracle_check(tpools, tw.layout, tw.layer_numbers, tw.bases, tr, got, tr.listed())
+        # the same call through a PreparedCall (every argument marshalled once)
+        pout = torch.zeros_like(tout)
+        pcall = kvck.prepare_call(tpc, *tt, pout, tws, stream=stream)
+        plat = []
+        for i in range(60):
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            pcall()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 10:
+                plat.append(t0.elapsed_time(t1) * 1e3)
+        same = bool(torch.equal(pout.view(torch.int64), tout.view(torch.int64)))
         extra["tiny_call_latency"] = {"workload": "2 layers x 2 KV heads x head 64 bf16, block 16, NHD, one 50-token "
                                                   "request on 4 blocks (51,200 valid bytes)",
                                       "us_median": statistics.median(lat), "us_min": min(lat), "calls": len(lat),
+                                      "prepared_call_us_median": statistics.median(plat),
+                                      "prepared_call_us_min": min(plat), "prepared_call_equals": same,
                                       "oracle_checked_positions": checked, "oracle_mismatches": mism}
-        del tpools, tpc
+        del tpools, tpc, pcall
     if args.copy_calibration_gib > 0:
         extra["copy_calibration_bytes"] = copy_calibration(dev, args.copy_calibration_gib)
 

@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     KvckDeviceError,
     KvckError,
     LAYOUT_NAMES,
+    PreparedCall,
     PreparedCaches,
     kv_layout,
     kvck_abi_version,
@@ -37,6 +38,7 @@ from ._binding import (  # noqa: F401
     kvck_status_string,
     kvck_tag_checksums,
     load_library,
+    prepare_call,
     prepare_caches,
     state_desc,
 )

@@ -441,6 +441,56 @@ def kvck_checksum_blocks(caches, layout: str | None, layer_numbers: Sequence[int
     return _finish(a, check)
 
 
+class PreparedCall:
+    """One kvck_checksum_blocks call with every argument marshalled once, for
+    the smallest calls in a hot loop, where the wrapper's checks cost more
+    than the kernel: calling the object makes the C call and checks its
+    status, nothing else.  Made by prepare_call; it keeps its tensors alive,
+    and their storage must not move between calls."""
+
+    def __init__(self, caches: PreparedCaches, block_table, num_blocks_per_req, start_pos, num_tokens, out,
+                 workspace, accumulate=False, error_flags=None, stream=None):
+        if not isinstance(caches, PreparedCaches):
+            raise ValueError("prepare_call takes a PreparedCaches (see prepare_caches)")
+        dev = caches.device
+        _meta(block_table, torch.int32, "block_table", dev)
+        if block_table.dim() != 2 or block_table.stride(1) != 1:
+            raise ValueError("block_table must be 2-D with contiguous rows")
+        R, max_blocks = block_table.shape
+        _meta(num_blocks_per_req, torch.int32, "num_blocks_per_req", dev, R)
+        _meta(start_pos, torch.int64, "start_pos", dev, R)
+        _meta(num_tokens, torch.int64, "num_tokens", dev, R)
+        out_stride = _out_stride(out, R * max_blocks, dev)
+        lib = load_library()
+        need = int(lib.kvck_blocks_workspace_bytes(caches.n, R, max_blocks))
+        if not isinstance(workspace, torch.Tensor) or workspace.device != dev or \
+                workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace must be a tensor of at least {need} bytes on {dev}")
+        error_flags = _flag_word(error_flags, False, dev)
+        self._keep = (caches, block_table, num_blocks_per_req, start_pos, num_tokens, out, workspace, error_flags)
+        self.out = out
+        self._fn = lib.kvck_checksum_blocks
+        self._args = (ctypes.byref(caches.layout), caches.ptrs, caches.layers, caches.bases, caches.n,
+                      caches.head_begin, caches.head_count, block_table.data_ptr(), block_table.stride(0),
+                      num_blocks_per_req.data_ptr(), start_pos.data_ptr(), num_tokens.data_ptr(), R, max_blocks,
+                      out.data_ptr(), out_stride, int(bool(accumulate)), workspace.data_ptr(),
+                      workspace.numel() * workspace.element_size(), _ptr(error_flags), _stream_handle(stream, dev))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            raise KvckError(int(st), "kvck_checksum_blocks")
+        return self.out
+
+
+def prepare_call(caches: PreparedCaches, block_table, num_blocks_per_req, start_pos, num_tokens, out, workspace,
+                 accumulate=False, error_flags=None, stream=None) -> PreparedCall:
+    """A PreparedCall of kvck_checksum_blocks on prepared caches, with a given
+    ``out`` and workspace (and the stream, the current one by default)."""
+    return PreparedCall(caches, block_table, num_blocks_per_req, start_pos, num_tokens, out, workspace, accumulate,
+                        error_flags, stream)
+
+
 def kvck_checksum_blocks_noalloc(caches, layout: str | None, layer_numbers: Sequence[int] | None,
                                  block_table: torch.Tensor, num_blocks_per_req: torch.Tensor, start_pos: torch.Tensor,
                                  num_tokens: torch.Tensor, out: torch.Tensor, global_head_base=None,

@@ -687,3 +687,33 @@ def test_merged_rows_stream_across_tasks(layout, elem, nh, d, bs, ncaches, monke
     assert (int(flags.item()) & kvck.KVCK_FLAG_BAD_BLOCK_ID) == (kvck.KVCK_FLAG_BAD_BLOCK_ID if valid_hit else 0)
     for r, k in listed:
         assert int(got3[r, k]) == (0 if (r, k) in hit else int(want[r, k])), (r, k)
+
+
+def test_prepared_call_equals_the_wrapper():
+    """A PreparedCall gives the wrapper's results, also into one replica column
+    and with accumulate, and can be called repeatedly."""
+    log("[small] prepared call")
+    rng = np.random.default_rng(77)
+    req, nb = wl.page_requests(rng, [50, 17, 33], 16, start_pos=[0, 1, 0], spare_frac=0.3)
+    pools = [to_device_bits(wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 16, 2, 64), "bf16")) for _ in range(3)]
+    pc = kvck.prepare_caches(pools, "NHD", [0, 4, 9])
+    bt, nbt, sp, nt = req_tensors(req)
+    ws = torch.empty(kvck.kvck_blocks_workspace_bytes(3, req.num_reqs, req.max_blocks), dtype=torch.uint8,
+                     device=DEV)
+    want = kvck.kvck_checksum_blocks(pc, None, None, bt, nbt, sp, nt, check=True).cpu().view(torch.int64).numpy()
+    want = want.view(np.uint64)
+    values = torch.zeros((req.num_reqs, req.max_blocks, 2), dtype=torch.uint64, device=DEV)
+    call = kvck.prepare_call(pc, bt, nbt, sp, nt, values[..., 1], ws)
+    for _ in range(3):
+        call()
+    acc = kvck.prepare_call(pc, bt, nbt, sp, nt, values[..., 0], ws, accumulate=True)
+    acc()
+    acc()
+    torch.cuda.synchronize()
+    got = values.cpu().view(torch.int64).numpy().view(np.uint64)
+    for r, k in req.listed():
+        assert got[r, k, 1] == want[r, k]
+        with np.errstate(over="ignore"):
+            assert got[r, k, 0] == want[r, k] * np.uint64(2)
+    with pytest.raises(ValueError):
+        kvck.prepare_call(pc, bt, nbt, sp, nt, values[..., 1], ws[:8])      # workspace too small
