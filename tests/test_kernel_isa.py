@@ -113,6 +113,7 @@ MAC, STORE = "v_mad_u64_u32", "buffer_store"
     ("kvck_tblocks.hip", "tblocks_kernelILi16ELi2ELi4ELi4ELb1ELb0E", MAC, 16),
     # copy_kernel<chunk, slots, heads per unit, planes per unit, direction, pipelined, merged>: ping-pong save
     ("kvck_copy.hip", "copy_kernelILi16ELi4ELi4ELi1ELi0ELb1ELb0E", STORE, 16),
+    ("kvck_copy.hip", "copy_kernelILi16ELi8ELi1ELi1ELi0ELb1ELb1E", STORE, 8),    # ping-pong save, merged rows
     # tcopy_lds_kernel<element bytes, slots, direction>: bf16 save through LDS (checksum by dot products)
     ("kvck_tcopy.hip", "tcopy_lds_kernelILi2ELi4ELi0E", "v_dot2_u32_u16", 4),
 ])
