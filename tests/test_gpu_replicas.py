@@ -252,3 +252,29 @@ def test_binding_rejects_unevenly_spaced_outputs():
         kvck.kvck_checksum_blocks(pools, "NHD", [0], bt, nbt, sp, nt, out=values[..., 0].t())
     with pytest.raises(ValueError):   # too few entries
         kvck.kvck_checksum_blocks(pools, "NHD", [0], bt, nbt, sp, nt, out=values[:1, :, 0])
+
+
+def test_transposed_fused_copy_fills_one_replica_column():
+    """The fused save of element-transposed K and V planes (K_TRANS, then
+    V_TRANS accumulated) into column 0 equals the oracle on the HND pools
+    holding the same tokens; no other entry moves."""
+    log("[replicas] transposed fused copy")
+    rng = np.random.default_rng(78)
+    bs, nh, d = 16, 2, 64
+    req, nb = wl.page_requests(rng, [70, 20, 5], bs, extra_blocks=[0, 1, 0], spare_frac=0.3)
+    layers = [1, 2]
+    hp = [wl.host_random_bits(rng, wl.pool_shape("HND", nb, bs, nh, d), "bf16") for _ in layers]
+    want = oracle.checksum_blocks(hp, "HND", layers, [0, 0], req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens)
+    kt = [to_device_bits(np.ascontiguousarray(p[0].transpose(0, 1, 3, 2))) for p in hp]
+    vt = [to_device_bits(np.ascontiguousarray(p[1].transpose(0, 1, 3, 2))) for p in hp]
+    bt, nbt, sp, nt = req_tensors(req)
+    entries = int(req.num_blocks.sum())
+    values = _values((req.num_reqs, req.max_blocks))
+    for i, (planes, layout) in enumerate(((kt, "K_TRANS"), (vt, "V_TRANS"))):
+        staging = torch.zeros(entries * kvck.kvck_staging_bytes(planes[0], layout, len(layers)), dtype=torch.uint8,
+                              device=DEV)
+        kvck.kvck_copy_checksum_blocks(kvck.KVCK_COPY_SAVE, planes, layout, layers, bt, nbt, sp, nt, staging,
+                                       out=values[..., 0], accumulate=i > 0, check=True)
+    torch.cuda.synchronize()
+    _check_column(values, 0, req, want)
