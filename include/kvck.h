@@ -400,9 +400,11 @@ kvck_status kvck_tag_checksums(
 
 /*
  * Instrumentation (optional, process-wide).  While enabled, every
- * kvck_checksum_blocks / kvck_checksum_states call records one pair of HIP
- * events on its stream around its main pass -- the kernel launches that
- * stream the cache bytes -- so a benchmark can time that kernel alone.
+ * kvck_checksum_blocks, kvck_copy_checksum_blocks and kvck_checksum_states
+ * call records one pair of HIP events on its stream around its main pass --
+ * the kernel launches that stream the cache bytes (not the plan, the copy's
+ * visiting order or the second pass) -- so a benchmark can time that kernel
+ * alone.  kvck_checksum_blocks_noalloc records none.
  * kvck_instrument_read waits for the recorded events, returns the summed
  * elapsed milliseconds and the number of calls timed, and starts a new tally.
  */
