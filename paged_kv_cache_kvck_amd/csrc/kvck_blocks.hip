@@ -261,10 +261,10 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
   if constexpr (PIPE && !DENSE && MERGED) {
     // Planned, pipelined, merged rows: the wave's tasks (wave, wave + nwaves,
     // ...) form one stream of units.  The issue side runs one unit ahead of
-    // the consuming side -- also into the next task -- so both unit buffers
-    // stay in flight across task boundaries: a task's reduction, its write and
-    // the next task's record are taken while the other buffer's loads are
-    // under way.  Merged rows (short rows, single latent heads) have few units
+    // the consuming side -- also into the next task -- so loads stay in
+    // flight across task boundaries: a task's reduction, its write and the
+    // next task's record are taken while the other buffer's loads are under
+    // way.  Merged rows (short rows, single latent heads) have few units
     // per task and gain from it (same-box A/B: fp8 64-byte rows +0.8-0.9
     // points of 8 TB/s, MLA +0.4-0.8); pools of separate head rows, whose
     // tasks are long, ran 0.1-1.1 points slower with it and keep one task at
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
       d.t0 = i_t0;
       d.out_idx = i_out;
       d.task = i_task;
-      d.cache = ic.cache;
+      d.cache = live ? ic.cache : 0;  // a dead unit is consumed too: keep its factor index in range
       d.group = ic.group;
       d.plane = ic.plane;
       d.hbatch = ic.hbatch;
@@ -358,22 +358,28 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
       }
       return us;
     };
-    // Both buffers are issued at every step (past the stream's end with every
-    // load out of range): with no branch around an issue, the waits before
-    // consuming one buffer count the other buffer's loads as still to come
-    // and leave them in flight.  order_after keeps a buffer's next loads after
-    // the last use of its data, so each buffer keeps its registers.
+    // Both buffers are issued and consumed at every step (past the stream's
+    // end with every load out of range; such a unit's data are zeros, so its
+    // sum is 0 and, not being a task's last unit, it writes nothing), and the
+    // loop has a single exit, so the compiler's waits follow the buffers: the
+    // wait before consuming B leaves A's loads in flight.  B's loads, though,
+    // are issued only once A's have landed (wait_vector_memory), so a wave
+    // has one or two units in flight, not always two.  These short-row pools
+    // read faster that way: same-box A/B, twelve interleaved rounds, against
+    // two units always in flight: fp8 64-byte rows at blocks 16 / 64 +0.8 /
+    // +0.5 points of 8 TB/s, MLA at blocks 16 / 64 +1.8 / +0.2.  order_after
+    // keeps a buffer's next loads after the last use of its data, so each
+    // buffer keeps its registers.
     V A[PU][HU][S], B[PU][HU][S];
     UnitDesc da, db;
-    issue(A, da);
-    for (;;) {
+    issue(A, da);  // live: the wave has at least one task
+    do {
+      wait_vector_memory();
       issue(B, db);
-      if (!da.live) break;  // uniform
       order_after(consume(A, da));
       issue(A, da);
-      if (!db.live) break;
       order_after(consume(B, db));
-    }
+    } while (da.live);  // uniform; once A is past the end, so is every later unit
     return;
   }
 

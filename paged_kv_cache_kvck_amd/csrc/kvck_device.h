@@ -162,6 +162,11 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 // waited for) at every step.
 __device__ __forceinline__ void order_after(uint64_t v) { asm volatile("" ::"v"(v) : "memory"); }
 
+// Wait until every vector memory access the wave has issued is complete
+// (s_waitcnt vmcnt(0); the scalar-memory and export counters are not waited
+// for).
+__device__ __forceinline__ void wait_vector_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Read-only inputs of a launch (the plan, the request arrays) read through
 // the constant address space: at a uniform address that is a scalar load,
 // counted apart from the vector loads of cache bytes, so waiting for a task's

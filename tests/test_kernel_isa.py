@@ -124,3 +124,35 @@ def test_pipelined_waits_leave_the_other_buffer_in_flight(src, variant, marker, 
     waits = _consume_waits(next(iter(ks.values())), marker)
     assert waits, "no block using loaded data found"
     assert min(waits) >= other_buffer, sorted(set(waits))
+
+
+def _loop_waits(text, variant):
+    """vmcnt of every wait inside a loop of the one kernel whose name holds
+    `variant` (the compiler marks a loop's blocks in its label comments)."""
+    names = [m for m in re.finditer(r"^(_Z\S+):", text, re.M) if variant in m.group(1)]
+    assert len(names) == 1, [m.group(1) for m in names]
+    m = names[0]
+    body = text[m.end():text.find(".Lfunc_end", m.start())]
+    waits, in_loop = [], False
+    for line in body.split("\n"):
+        label = re.match(r"^(\.LBB\S+):(.*)$", line.strip())
+        if label:
+            in_loop = "Loop" in label.group(2)
+            continue
+        w = re.match(r"s_waitcnt.*vmcnt\((\d+)\)", line.split(";")[0].strip())
+        if w and in_loop:
+            waits.append(int(w.group(1)))
+    return waits
+
+
+def test_merged_stream_drains_once_per_step():
+    """The planned merged-row checksum streams units through two buffers and
+    lets the first buffer's loads land before the second is issued: exactly
+    one wait for every load per step, and the wait before the second buffer
+    is used leaves the first buffer's eight loads in flight.  A second full
+    wait (e.g. from a loop with two exits, whose path back to the loop head
+    merges a pending buffer) would fail this."""
+    waits = _loop_waits(assembly()["kvck_blocks.hip"], "blocks_kernelILi16ELi8ELi1ELi1ELb1ELb1ELb0E")
+    assert waits.count(0) == 1, waits
+    assert min(w for w in waits if w) >= 8, waits
+
