@@ -486,7 +486,10 @@ class PreparedCall:
 def prepare_call(caches: PreparedCaches, block_table, num_blocks_per_req, start_pos, num_tokens, out, workspace,
                  accumulate=False, error_flags=None, stream=None) -> PreparedCall:
     """A PreparedCall of kvck_checksum_blocks on prepared caches, with a given
-    ``out`` and workspace (and the stream, the current one by default)."""
+    ``out`` and workspace.  Every call runs on ``stream``, else on the stream
+    that is current when the call is prepared (not when it is made); ordering
+    ``out``, the workspace and the inputs against other work on other streams
+    is the caller's, as with any call given its own buffers."""
     return PreparedCall(caches, block_table, num_blocks_per_req, start_pos, num_tokens, out, workspace, accumulate,
                         error_flags, stream)
 
