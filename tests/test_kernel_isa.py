@@ -145,14 +145,16 @@ def _loop_waits(text, variant):
     return waits
 
 
-def test_merged_stream_drains_once_per_step():
+@pytest.mark.parametrize("chunk,slots", [(16, 8), (16, 4), (16, 2), (8, 8), (8, 4)])
+def test_merged_stream_drains_once_per_step(chunk, slots):
     """The planned merged-row checksum streams units through two buffers and
     lets the first buffer's loads land before the second is issued: exactly
     one wait for every load per step, and the wait before the second buffer
-    is used leaves the first buffer's eight loads in flight.  A second full
+    is used leaves the first buffer's `slots` loads in flight.  A second full
     wait (e.g. from a loop with two exits, whose path back to the loop head
     merges a pending buffer) would fail this."""
-    waits = _loop_waits(assembly()["kvck_blocks.hip"], "blocks_kernelILi16ELi8ELi1ELi1ELb1ELb1ELb0E")
+    variant = f"blocks_kernelILi{chunk}ELi{slots}ELi1ELi1ELb1ELb1ELb0E"
+    waits = _loop_waits(assembly()["kvck_blocks.hip"], variant)
     assert waits.count(0) == 1, waits
-    assert min(w for w in waits if w) >= 8, waits
+    assert min(w for w in waits if w) >= slots, waits
 
