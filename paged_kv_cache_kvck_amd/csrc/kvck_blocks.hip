@@ -328,7 +328,10 @@ __global__ __launch_bounds__(kBlockThreads) void blocks_kernel(const BlocksArgs 
       d.live = live;
       d.last = live && i_left == 1;
       if (live) {
-        ic.next(nhb, nplanes, i_ngr);
+        // a plane's row groups back to back (same-box A/B, twenty interleaved
+        // rounds: fp8 64-byte rows +0.5 points of 8 TB/s at blocks 16 and 64;
+        // MLA, one plane, unchanged)
+        ic.next_group_first(nhb, nplanes, i_ngr);
         if (--i_left == 0) i_task += nwaves;
       }
     };

@@ -232,8 +232,10 @@ __device__ __forceinline__ TaskRecord task_record(const BlocksArgs& a, int64_t i
 }
 
 // Position of the next unit of a task: cache, row group, plane, head batch.
+// Both orders visit the nhb * planes * ngr units of every cache once.
 struct UnitCursor {
   int cache, group, plane, hbatch;
+  // head batches, then planes, then row groups, then caches
   __device__ __forceinline__ void next(int nhb, int planes, int ngr) {
     if (++hbatch == nhb) {
       hbatch = 0;
@@ -241,6 +243,21 @@ struct UnitCursor {
         plane = 0;
         if (++group == ngr) {
           group = 0;
+          ++cache;
+        }
+      }
+    }
+  }
+  // head batches, then row groups, then planes, then caches: a plane's row
+  // groups are visited back to back, so consecutive units of a block lie side
+  // by side in memory instead of alternating between its K and V planes
+  __device__ __forceinline__ void next_group_first(int nhb, int planes, int ngr) {
+    if (++hbatch == nhb) {
+      hbatch = 0;
+      if (++group == ngr) {
+        group = 0;
+        if (++plane == planes) {
+          plane = 0;
           ++cache;
         }
       }
