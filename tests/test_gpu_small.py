@@ -441,6 +441,45 @@ def test_more_than_1024_requests(schedule):
     assert_unlisted_untouched(got, req)
 
 
+_MANY = {}
+
+
+def _seventy_thousand_requests():
+    """70,000 requests of 0-12 tokens at block size 4, start positions 0-2 and
+    up to one listed position past the last token: 69 chunks of the plan's
+    1024-request scan, about 107k listed positions among 280k slots; the
+    oracle's values, computed once."""
+    if not _MANY:
+        rng = np.random.default_rng(31)
+        n = 70000
+        lengths = rng.integers(0, 13, size=n)
+        start = rng.integers(0, 3, size=n)
+        req, nb = wl.page_requests(rng, lengths, 4, start_pos=start, extra_blocks=rng.integers(0, 2, size=n),
+                                   spare_frac=0.1)
+        hp = [wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 4, 2, 16), "bf16") for _ in range(3)]
+        want = oracle.checksum_blocks(hp, "NHD", [0, 1, 2], [0] * 3, req.block_table, req.num_blocks,
+                                      req.start_pos, req.num_tokens)
+        _MANY.update(req=req, hp=hp, want=want)
+    return _MANY["req"], _MANY["hp"], _MANY["want"]
+
+
+@pytest.mark.parametrize("sched", ["auto", "simple", "pipelined"])
+def test_seventy_thousand_requests(sched, monkeypatch):
+    """A batch far past one scan chunk: the plan carries its prefix across 69
+    chunks of 1024 requests; every listed position equals the oracle and no
+    other entry is written."""
+    log(f"[70000 requests] {sched}")
+    if sched != "auto":
+        monkeypatch.setenv("KVCK_SCHEDULE", sched)
+    req, hp, want = _seventy_thousand_requests()
+    got = gpu_blocks([to_device_bits(p) for p in hp], "NHD", [0, 1, 2], req)
+    listed = np.arange(req.max_blocks)[None, :] < req.num_blocks[:, None]
+    assert int(listed.sum()) > 100000
+    bad = np.argwhere(listed & (got != want))
+    assert bad.size == 0, f"{len(bad)} mismatches, first at (request, position) {tuple(bad[0])}"
+    assert np.all(got[~listed] == np.uint64(SENTINEL)), "unlisted entries were written"
+
+
 def test_largest_numbering(schedule):
     """The largest numbering the method allows: layer 32767 with 65536 heads
     per layer, so the slice factor m = 2(layer*65536 + head) + 1 reaches
