@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     KVCK_FLAG_BAD_STATE_SLOT,
     KVCK_FLAG_STAGING_FULL,
     KVCK_ABI_VERSION,
+    KVCK_MAX_CACHES,
     KVCK_MAX_OUT_STRIDE,
     KVCK_SCRATCH_BYTES,
     KvckDeviceError,

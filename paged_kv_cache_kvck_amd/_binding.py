@@ -25,6 +25,7 @@ STATUS_NAMES = {
 KVCK_ABI_VERSION = 3
 KVCK_SCRATCH_BYTES = 32 << 20
 KVCK_MAX_OUT_STRIDE = 65536
+KVCK_MAX_CACHES = 4096
 KVCK_FLAG_BAD_BLOCK_ID = 1
 KVCK_FLAG_BAD_REQUEST = 2
 KVCK_FLAG_BAD_STATE_SLOT = 4

@@ -35,6 +35,23 @@ def test_library_loads_and_exports_every_declared_symbol():
     assert kvck.kvck_status_string(7) == "KVCK_UNKNOWN_STATUS"
 
 
+def test_binding_constants_match_the_header():
+    """Every constant the binding restates has the value include/kvck.h defines."""
+    with open(os.path.join(ROOT, "include", "kvck.h")) as f:
+        text = f.read()
+    define = re.compile(r"^#define[ \t]+(KVCK_\w+)[ \t]+(.+?)[ \t]*(?:/\*.*)?$", re.M)
+    defines = {m.group(1): m.group(2) for m in define.finditer(text)}
+
+    def value(expr):
+        return eval(re.sub(r"(\d+)u\b", r"\1", expr), {})  # integer literals and shifts only
+
+    names = [n for n in dir(B) if n.startswith("KVCK_") and isinstance(getattr(B, n), int) and n in defines]
+    assert {"KVCK_ABI_VERSION", "KVCK_MAX_CACHES", "KVCK_MAX_OUT_STRIDE", "KVCK_SCRATCH_BYTES",
+            "KVCK_FLAG_BAD_BLOCK_ID", "KVCK_COPY_LOAD"} <= set(names)
+    for n in names:
+        assert getattr(B, n) == value(defines[n]), n
+
+
 def test_workspace_sizes():
     assert kvck.kvck_blocks_workspace_bytes(0, 1, 1) == 0
     one = kvck.kvck_blocks_workspace_bytes(1, 256, 512)

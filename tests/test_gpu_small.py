@@ -219,6 +219,26 @@ def test_many_caches_several_launches(schedule):
         assert int(got[r, k]) == int(want[r, k])
 
 
+def test_the_most_caches_one_call_takes(schedule):
+    """KVCK_MAX_CACHES (4096) caches in one call: 64 launches of the argument
+    block, thousands of partial groups summed by the second pass; layer numbers
+    spread over the whole int32 range and global heads over all 65536."""
+    log("[4096 caches]")
+    assert kvck.KVCK_MAX_CACHES == 4096
+    rng = np.random.default_rng(32)
+    req, nb = wl.page_requests(rng, [9, 4, 0, 7], 2, start_pos=[0, 3, 0, 1], extra_blocks=[1, 0, 0, 0],
+                               spare_frac=0.5)
+    hp = [wl.host_random_bits(rng, wl.pool_shape("NHD", nb, 2, 1, 8), "bf16") for _ in range(4096)]
+    layers = [int(x) for x in rng.choice(1 << 31, size=4096, replace=False)]
+    bases = [int(x) for x in rng.integers(0, 65536, size=4096)]
+    got = gpu_blocks([to_device_bits(p) for p in hp], "NHD", layers, req, bases=bases)
+    want = oracle.checksum_blocks(hp, "NHD", layers, bases, req.block_table, req.num_blocks, req.start_pos,
+                                  req.num_tokens)
+    for r, k in req.listed():
+        assert int(got[r, k]) == int(want[r, k]), (r, k)
+    assert_unlisted_untouched(got, req)
+
+
 def test_empty_and_past_end_positions(schedule):
     log("[empty]")
     rng = np.random.default_rng(9)
