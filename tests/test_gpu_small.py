@@ -445,6 +445,27 @@ def test_states_small_parity():
         kvck.kvck_checksum_states(ds, layers, bad, check=True)
 
 
+@pytest.mark.parametrize("nlayers", [33, 70, 4096])
+def test_states_many_layers(nlayers):
+    """More Mamba layers than one argument block carries (32): several launches
+    whose partials the second pass sums, up to the most layers a call takes
+    (KVCK_MAX_CACHES); layer numbers and row bases spread over their ranges."""
+    log(f"[states] {nlayers} layers")
+    rng = np.random.default_rng(1000 + nlayers)
+    layers = [int(x) for x in rng.choice(1 << 31, size=nlayers, replace=False)]
+    bases = [int(x) for x in rng.integers(0, 65536 - 3, size=nlayers)]
+    hs = [[wl.host_random_bits(rng, (3, 3, 8), "fp16"), wl.host_random_bits(rng, (3, 3, 4), "fp32")]
+          for _ in layers]
+    slots = np.array([2, 0, 2, 1, 0], np.int32)
+    ds = [[to_device_bits(a) for a in l] for l in hs]
+    sid = torch.from_numpy(slots).to(DEV)
+    for rb, rc in [(0, None), (1, 2)]:
+        got = kvck.kvck_checksum_states(ds, layers, sid, global_row_base=bases, row_begin=rb, row_count=rc,
+                                        check=True)
+        want = oracle.checksum_states(hs, layers, bases, slots, row_begin=rb, row_count=rc)
+        assert np.array_equal(got.cpu().numpy(), want), (rb, rc)
+
+
 def test_more_than_1024_requests(schedule):
     """Batches above 1024 requests take the two-kernel plan (scan, then fill)."""
     log("[1500 requests]")
