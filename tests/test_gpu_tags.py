@@ -45,6 +45,37 @@ def test_tags_match_oracle():
     assert int(count.item()) == 17
 
 
+def test_tags_beyond_one_grid():
+    """2.5M entries of two replica columns: more than one grid covers (8192
+    workgroups of 256 threads), so the kernel strides.  Tags equal the oracle
+    on 20k sampled entries (the first and last 1000 among them); in compare
+    mode exactly the 33 planted mismatches are flagged and counted."""
+    log("[tags] 2.5M entries")
+    rng = np.random.default_rng(23)
+    n, cols = 2_500_000, 2
+    c = rng.integers(0, 2**63, size=(n, cols), dtype=np.int64).view(np.uint64)
+    h = _hashes(rng, n)
+    fp = 0x0123456789ABCDEF
+    ct = torch.from_numpy(c.reshape(-1).view(np.int64)).to(DEV).view(torch.uint64)
+    ht = torch.from_numpy(h).to(DEV)
+    tagged, _ = kvck.kvck_tag_checksums(ct, ht, fp, columns=cols)
+    got = tagged.cpu().numpy()
+    sample = np.unique(np.concatenate([np.arange(1000), np.arange(n - 1000, n), rng.choice(n, 18000, replace=False)]))
+    row_sum = oracle.tags.offloaded_value(c[sample])
+    want = oracle.tags.tag_checksums(row_sum, [bytes(r) for r in h[sample]], fp)
+    assert np.array_equal(got[sample], want)
+    stored = got.copy()
+    planted = rng.choice(n, 33, replace=False)
+    stored[planted] ^= np.uint64(1) << np.uint64(40)
+    count = torch.zeros(1, dtype=torch.int32, device=DEV)
+    _, mm = kvck.kvck_tag_checksums(ct, ht, fp, columns=cols, tagged=False,
+                                    stored=torch.from_numpy(stored.view(np.int64)).to(DEV).view(torch.uint64),
+                                    mismatch_count=count)
+    torch.cuda.synchronize()
+    assert np.array_equal(np.flatnonzero(mm.cpu().numpy()), np.sort(planted))
+    assert int(count.item()) == 33
+
+
 def test_offload_round_trip():
     log("[tags] offload round trip")
     rng = np.random.default_rng(21)
