@@ -17,7 +17,7 @@ import oracle
 import paged_kv_cache_kvck_amd as kvck
 from paged_kv_cache_kvck_amd import workloads as wl
 from gpu_helpers import (DEV, SENTINEL, assert_match, assert_unlisted_untouched, gpu_blocks, log, oracle_at,
-                         req_tensors, to_device_bits, to_host_bits)
+                         req_tensors, sample_positions, to_device_bits, to_host_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -519,6 +519,33 @@ def test_seventy_thousand_requests(sched, monkeypatch):
     bad = np.argwhere(listed & (got != want))
     assert bad.size == 0, f"{len(bad)} mismatches, first at (request, position) {tuple(bad[0])}"
     assert np.all(got[~listed] == np.uint64(SENTINEL)), "unlisted entries were written"
+
+
+@pytest.mark.parametrize("ncaches", [3, 70])
+def test_second_pass_beyond_one_grid(ncaches, monkeypatch):
+    """1.1M listed positions, one cache per partial group (the simple
+    schedule): more positions than one grid of the second pass covers, so it
+    strides (the partials sum for 3 groups, its wave-per-output variant for
+    70).  Every position equals the sum, mod 2^64, of one-cache calls, which
+    write their values directly; 3000 sampled positions equal the oracle."""
+    log(f"[1.1M positions] {ncaches} caches")
+    monkeypatch.setenv("KVCK_SCHEDULE", "simple")
+    rng = np.random.default_rng(40 + ncaches)
+    req, nb = wl.page_requests(rng, np.full(275_000, 8), 2, spare_frac=0.02)
+    assert int(req.num_blocks.sum()) > 1 << 20
+    g = torch.Generator(device=DEV)
+    g.manual_seed(41 + ncaches)
+    pools = [wl.device_fill(wl.pool_shape("NHD", nb, 2, 1, 8), "bf16", "bits", g, DEV) for _ in range(ncaches)]
+    layers = [int(x) for x in rng.choice(1 << 20, size=ncaches, replace=False)]
+    got = gpu_blocks(pools, "NHD", layers, req)
+    total = np.zeros_like(got)
+    with np.errstate(over="ignore"):
+        for p, layer in zip(pools, layers):
+            total += gpu_blocks([p], "NHD", [layer], req)
+    listed = np.arange(req.max_blocks)[None, :] < req.num_blocks[:, None]
+    assert np.array_equal(got[listed], total[listed])
+    pos = sample_positions(req, 3000, seed=ncaches, include_tails=False)
+    assert_match(got, oracle_at(pools, "NHD", layers, req, pos), "sampled positions")
 
 
 def test_largest_numbering(schedule):
